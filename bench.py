@@ -1,0 +1,255 @@
+"""Benchmark: the 37-layer YOLO26n-shaped fused Conv2d + BN + SiLU list on one MI355X.
+
+One step = one pass of the whole list (every layer's fused conv + folded BN +
+SiLU, inputs already resident in HBM in the library's NHWC layout), replayed
+as one captured HIP graph of the 37 launches.  The headline is FP32 at batch 1
+(the configuration of the vision-rs "YOLO26N Inference Optimisation" page:
+YOLO26N, FP32, batch 1, 640x640); the same line also carries INT8 and batch 16.
+
+Printed (stdout, one JSON line): value = list FLOPs / step time (TFLOP/s),
+ms_per_step, per-layer roofline of the dominant kernel (HIP events on the
+launch stream), and the CPU oracle timed on the host cores as a baseline.
+Per-layer details go to gpurun_out/bench_layers.json when that folder exists.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused conv-BN-SiLU TFLOP/s + total µs for YOLO26n layer list, bs1 FP32/INT8"
+# MI355X published peaks (dense): FP32 matrix 157.3 TFLOP/s, INT8 5.0 POP/s, HBM3E 8 TB/s.
+PEAK_FP32 = 157.3e12
+PEAK_INT8 = 5.0e15
+PEAK_HBM = 8.0e12
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class ListBench:
+    """Device-resident inputs/outputs and created layers for one (dtype, batch)."""
+
+    def __init__(self, cbs, W, torch, dtype, batch, seed=0):
+        self.cbs, self.torch = cbs, torch
+        self.dtype = dtype
+        self.batch = batch
+        dev = torch.device("cuda", 0)
+        self.layers, self.ins, self.outs, self.infos, self.specs = [], [], [], [], []
+        for L in W.generate("yolo26n", n=batch, seed=seed):
+            sp = L.spec
+            cpad = -(-sp.c_in // 4) * 4
+            x = torch.from_numpy(L.x).to(dev)
+            if dtype == cbs.CBS_F32:
+                desc = cbs.make_desc(batch, sp.c_in, sp.h, sp.w, sp.c_out, sp.k, sp.stride, sp.pad, dtype, 0, 0.0,
+                                     L.eps)
+                xin = torch.empty(batch * sp.h * sp.w * cpad, dtype=torch.float32, device=dev)
+                cbs.cbs_pack_nhwc_f32(x, xin, batch, sp.c_in, sp.h, sp.w, cpad)
+            else:
+                s_x = W.calibration_scale(L.x)
+                desc = cbs.make_desc(batch, sp.c_in, sp.h, sp.w, sp.c_out, sp.k, sp.stride, sp.pad, dtype, 0,
+                                     float(s_x), L.eps)
+                xin = torch.empty(batch * sp.h * sp.w * cpad, dtype=torch.int8, device=dev)
+                cbs.cbs_quantize_nhwc_i8(x, xin, s_x, batch, sp.c_in, sp.h, sp.w, cpad)
+            layer = cbs.cbs_create_layer(desc, L.w, L.gamma, L.beta, L.mean, L.var)
+            info = cbs.cbs_layer_info(layer)
+            out = torch.empty(info["out_bytes"] // 4, dtype=torch.float32, device=dev)
+            self.layers.append(layer)
+            self.ins.append(xin)
+            self.outs.append(out)
+            self.infos.append(info)
+            self.specs.append(sp)
+            del x
+        torch.cuda.synchronize()
+        self.flops = sum(i["flops"] for i in self.infos)
+        self.graph = cbs.cbs_graph_create(self.layers, self.ins, self.outs)
+
+    def time_steps(self, steps, warmup, use_graph=True):
+        torch, cbs = self.torch, self.cbs
+        for _ in range(warmup):
+            self._step(use_graph)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self._step(use_graph)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall / steps * 1e3
+
+    def _step(self, use_graph):
+        if use_graph:
+            self.cbs.cbs_graph_launch(self.graph)
+        else:
+            self.cbs.cbs_run_layer_list(self.layers, self.ins, self.outs)
+
+    def time_layers(self, min_ms=2.0, reps=5):
+        """Per layer: median over `reps` of (event pair around R back-to-back launches)/R,
+        on the stream the library launches on (torch's current stream)."""
+        torch, cbs = self.torch, self.cbs
+        res = []
+        for layer, xin, out in zip(self.layers, self.ins, self.outs):
+            for _ in range(3):
+                cbs.cbs_run_layer(layer, xin, out)
+            torch.cuda.synchronize()
+            # calibrate R so that one repeat takes >= min_ms
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                cbs.cbs_run_layer(layer, xin, out)
+            e1.record()
+            torch.cuda.synchronize()
+            per = max(e0.elapsed_time(e1) / 10, 1e-4)
+            r = int(min(2000, max(10, min_ms / per)))
+            ts = []
+            for _ in range(reps):
+                e0.record()
+                for _ in range(r):
+                    cbs.cbs_run_layer(layer, xin, out)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) / r)
+            res.append(float(np.median(ts)) * 1e3)  # microseconds
+        return res
+
+
+def layer_rows(bench, us):
+    int8 = bench.dtype == bench.cbs.CBS_I8
+    peak = PEAK_INT8 if int8 else PEAK_FP32
+    rows = []
+    for sp, info, t in zip(bench.specs, bench.infos, us):
+        fl, by = info["flops"], info["alg_bytes"]
+        t_mfma, t_hbm = fl / peak, by / PEAK_HBM
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        roof_us = max(t_mfma, t_hbm) * 1e6
+        rows.append({"layer": sp.name, "c_in": sp.c_in, "c_out": sp.c_out, "h_in": sp.h, "k": sp.k, "s": sp.stride,
+                     "us": round(t, 3), "tflops": round(fl / (t * 1e-6) / 1e12, 3),
+                     "gbs": round(by / (t * 1e-6) / 1e9, 1), "flops": fl, "alg_bytes": by, "bound": bound,
+                     "roof_us": round(roof_us, 3), "frac": round(roof_us / t, 4), "config": info["config_name"],
+                     "grid": info["grid"]})
+    return rows
+
+
+def cpu_baseline(W, max_seconds=30.0):
+    """The oracle (plain C, double accumulation, OpenMP) on the batch-1 FP32 list:
+    every layer in list order until the whole list is done or the time budget
+    runs out; returns TFLOP/s over the layers done."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    done_flops, t_total, done = 0, 0.0, 0
+    layers = W.generate("yolo26n", n=1, seed=0)
+    for L in layers:
+        t0 = time.perf_counter()
+        oracle.conv_bn_silu_f32(L.x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride, L.spec.pad,
+                                with_bound=False)
+        t_total += time.perf_counter() - t0
+        done_flops += L.spec.flops(1)
+        done += 1
+        if t_total > max_seconds:
+            break
+    sample = ("yolo26n list, batch 1, FP32, %d of %d layers (%.3f GFLOP), oracle conv+BN+SiLU in double"
+              % (done, len(layers), done_flops / 1e9))
+    return {"value": round(done_flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(t_total, 3), "us_per_list": round(t_total * 1e6 * len(layers) / done, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--quick", action="store_true", help="batch-1 FP32 only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the batch-16 list shards over images with no "
+              "exchange, see the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from convolution_implicit_gemm_02_amd import cbs
+    from convolution_implicit_gemm_02_amd import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log("device: %s, %d CUs" % (props.name, props.multi_processor_count))
+
+    results = {}
+    combos = [("f32", cbs.CBS_F32, 1)] if args.quick else [("f32", cbs.CBS_F32, 1), ("int8", cbs.CBS_I8, 1),
+                                                           ("f32", cbs.CBS_F32, 16), ("int8", cbs.CBS_I8, 16)]
+    layer_tables = {}
+    for name, dt, bs in combos:
+        b = ListBench(cbs, W, torch, dt, bs)
+        steps = args.steps if bs == 1 else max(10, args.steps // 8)
+        ms_graph, wall_graph = b.time_steps(steps, args.warmup, use_graph=True)
+        ms_list, _ = b.time_steps(steps, args.warmup, use_graph=False)
+        us_layers = b.time_layers()
+        rows = layer_rows(b, us_layers)
+        key = "%s_bs%d" % (name, bs)
+        layer_tables[key] = rows
+        results[key] = {"ms_per_step": ms_graph, "wall_ms_per_step": wall_graph, "ms_per_step_plain_launches": ms_list,
+                        "flops": b.flops, "rows": rows}
+        log("%s: list %.1f us (graph), %.1f us (plain launches), %.2f T(FL)OP/s, sum of per-layer %.1f us, "
+            "roofline sum %.1f us" % (key, ms_graph * 1e3, ms_list * 1e3, b.flops / (ms_graph * 1e-3) / 1e12,
+                                      sum(us_layers), sum(r["roof_us"] for r in rows)))
+        for r in rows:
+            log("  %-13s %4d->%-4d %4d k%d s%d  %8.2f us  %7.2f TF/s  %7.1f GB/s  roof %6.2f us (%s)  frac %.3f  %s"
+                % (r["layer"], r["c_in"], r["c_out"], r["h_in"], r["k"], r["s"], r["us"], r["tflops"], r["gbs"],
+                   r["roof_us"], r["bound"], r["frac"], r["config"]))
+        del b
+        torch.cuda.empty_cache()
+
+    head = results["f32_bs1"]
+    rows = head["rows"]
+    dom = max(rows, key=lambda r: r["us"])
+    if dom["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": round(dom["alg_bytes"] / (dom["us"] * 1e-6) / 1e9, 1),
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(dom["flops"] / (dom["us"] * 1e-6) / 1e12, 3),
+                "peak": PEAK_FP32 / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "conv_igemm %s (%s)" % (dom["layer"], dom["config"])
+    roof["us_per_launch"] = dom["us"]
+
+    line = {"metric": METRIC, "value": round(head["flops"] / (head["ms_per_step"] * 1e-3) / 1e12, 4),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(head["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "yolo26n 37-layer fused conv+BN+SiLU list, 640x640 input, batch 1, FP32, "
+                                   "one hipGraph replay per step", "batch": 1, "layers": len(rows),
+                       "gflop_per_step": round(head["flops"] / 1e9, 4)},
+            "total_us": round(head["ms_per_step"] * 1e3, 2),
+            "total_us_plain_launches": round(head["ms_per_step_plain_launches"] * 1e3, 2),
+            "roofline": roof}
+    for key, r in results.items():
+        if key == "f32_bs1":
+            continue
+        int8 = key.startswith("int8")
+        line[key] = {"value": round(r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12, 4),
+                     "unit": "TOP/s" if int8 else "TFLOP/s", "total_us": round(r["ms_per_step"] * 1e3, 2),
+                     "total_us_plain_launches": round(r["ms_per_step_plain_launches"] * 1e3, 2)}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(W)
+    outdir = os.path.join(ROOT, "gpurun_out")
+    if os.path.isdir(outdir):
+        with open(os.path.join(outdir, "bench_layers.json"), "w") as f:
+            json.dump({"device": props.name, "results": results}, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

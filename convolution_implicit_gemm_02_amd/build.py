@@ -1,0 +1,52 @@
+"""Build libcbs.so (the HIP kernels and the C-ABI host library) in-tree with hipcc
+for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+BUILD_DIR = os.path.join(PKG_DIR, "_build")
+LIB_PATH = os.path.join(PKG_DIR, "libcbs.so")
+ARCH = "gfx950"
+
+# No packed-fp32 instructions (v_pk_*_f32) are emitted for the device code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["--offload-arch=" + ARCH, "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+          "-Wno-unused-command-line-argument"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.sep not in cand or os.path.exists(cand)):
+            return cand
+    return "hipcc"
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link libcbs.so.  Always recompiles."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    hipcc = _hipcc()
+    k_obj = os.path.join(BUILD_DIR, "cbs_kernels.o")
+    h_obj = os.path.join(BUILD_DIR, "cbs_host.o")
+    # kernels: -O3, device code without packed fp32
+    _run([hipcc, "-c", os.path.join(CSRC, "cbs_kernels.hip"), "-o", k_obj, "-O3"] + COMMON + DEVICE_FLAGS)
+    # host library: every double product/sum rounded as written (no FMA contraction)
+    _run([hipcc, "-c", os.path.join(CSRC, "cbs_host.cpp"), "-o", h_obj, "-O2", "-ffp-contract=off"]
+         + COMMON + DEVICE_FLAGS)
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    _run([hipcc, "-shared", "-o", tmp, k_obj, h_obj, "--offload-arch=" + ARCH, "-fPIC"])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,272 @@
+"""Thin ctypes binding of libcbs (include/cbs.h), same entry-point names.
+
+Argument marshalling only: every step of the fused conv path runs in the HIP
+kernels of libcbs.so.  Device buffers may be given as torch tensors (their
+``data_ptr()`` is passed) or as raw integer addresses; streams as
+``torch.cuda.Stream`` objects, raw handles or None (the current torch stream).
+Host arrays (weights, BN parameters) are numpy arrays.
+
+torch is imported before libcbs.so is loaded so that both share the one HIP
+runtime (libamdhip64.so.7) that torch loads.  If libcbs.so is missing this
+module raises at import: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch  # noqa: F401  (loads the HIP runtime first)
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libcbs.so")
+
+CBS_OK = 0
+CBS_EINVAL = -1
+CBS_EUNSUPPORTED = -2
+CBS_ENOMEM = -3
+CBS_EDEVICE = -4
+CBS_ELAUNCH = -5
+CBS_F32 = 0
+CBS_I8 = 1
+
+_STATUS_NAMES = {0: "CBS_OK", -1: "CBS_EINVAL", -2: "CBS_EUNSUPPORTED", -3: "CBS_ENOMEM",
+                 -4: "CBS_EDEVICE", -5: "CBS_ELAUNCH"}
+
+
+class CbsError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (where, _STATUS_NAMES.get(status, status), message))
+
+
+class cbs_conv_desc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("c_in", ctypes.c_int32), ("h", ctypes.c_int32),
+                ("w", ctypes.c_int32), ("c_out", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("stride", ctypes.c_int32), ("pad", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_row_pitch", ctypes.c_int32), ("in_scale", ctypes.c_float),
+                ("bn_eps", ctypes.c_float)]
+
+
+class cbs_layer_info_t(ctypes.Structure):
+    _fields_ = [("c_in_pad", ctypes.c_int32), ("c_out_pad", ctypes.c_int32), ("oh", ctypes.c_int32),
+                ("ow", ctypes.c_int32), ("out_row_pitch", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("in_bytes", ctypes.c_int64), ("out_bytes", ctypes.c_int64), ("flops", ctypes.c_int64),
+                ("alg_bytes", ctypes.c_int64), ("config", ctypes.c_int32), ("splitk", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("threads", ctypes.c_int32), ("config_name", ctypes.c_char * 48)]
+
+
+# Every symbol the header declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGNATURES = {
+    "cbs_create_layer": (_I, [ctypes.POINTER(cbs_conv_desc), _P, _P, _P, _P, _P, ctypes.POINTER(_P)]),
+    "cbs_create_layer_folded": (_I, [ctypes.POINTER(cbs_conv_desc), _P, _P, _P, ctypes.POINTER(_P)]),
+    "cbs_destroy_layer": (None, [_P]),
+    "cbs_run_layer": (_I, [_P, _P, _P, _P]),
+    "cbs_run_layer_list": (_I, [ctypes.POINTER(_P), _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
+    "cbs_graph_create": (_I, [ctypes.POINTER(_P), _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _P,
+                              ctypes.POINTER(_P)]),
+    "cbs_graph_launch": (_I, [_P, _P]),
+    "cbs_graph_destroy": (None, [_P]),
+    "cbs_layer_info": (_I, [_P, ctypes.POINTER(cbs_layer_info_t)]),
+    "cbs_layer_set_config": (_I, [_P, _I, _I]),
+    "cbs_num_configs": (_I, []),
+    "cbs_config_name": (ctypes.c_char_p, [_I]),
+    "cbs_last_error": (ctypes.c_char_p, []),
+    "cbs_pack_nhwc_f32": (_I, [_P, _P, _I, _I, _I, _I, _I, _P]),
+    "cbs_quantize_nhwc_i8": (_I, [_P, _P, ctypes.c_float, _I, _I, _I, _I, _I, _P]),
+    "cbs_run_layer_raw_acc": (_I, [_P, _P, _P, _P]),
+    "cbs_get_qweights": (_I, [_P, _P, _P]),
+    "cbs_get_folded": (_I, [_P, _P, _P]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libcbs.so not built at %s (run __graft_entry__.build())" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int, where: str) -> None:
+    if status != CBS_OK:
+        msg = lib.cbs_last_error()
+        raise CbsError(status, where, msg.decode() if msg else "")
+
+
+def _dev_ptr(buf) -> int:
+    if buf is None:
+        return 0
+    if isinstance(buf, int):
+        return buf
+    return int(buf.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _host(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+@dataclass
+class Layer:
+    """Handle of a created layer (a cbs_layer*), destroyed on garbage collection."""
+    handle: int
+    desc: cbs_conv_desc
+
+    def __del__(self):
+        if getattr(self, "handle", 0):
+            lib.cbs_destroy_layer(self.handle)
+            self.handle = 0
+
+
+def make_desc(n, c_in, h, w, c_out, k, stride, pad, dtype=CBS_F32, out_row_pitch=0, in_scale=0.0,
+              bn_eps=1e-3) -> cbs_conv_desc:
+    return cbs_conv_desc(n, c_in, h, w, c_out, k, stride, pad, dtype, out_row_pitch, float(in_scale),
+                         float(bn_eps))
+
+
+def cbs_create_layer(desc: cbs_conv_desc, w_oihw, gamma, beta, mean, var) -> Layer:
+    ws = [_host(a, np.float32) for a in (w_oihw, gamma, beta, mean, var)]
+    h = _P()
+    _check(lib.cbs_create_layer(ctypes.byref(desc), *[p for _, p in ws], ctypes.byref(h)), "cbs_create_layer")
+    return Layer(h.value, desc)
+
+
+def cbs_create_layer_folded(desc: cbs_conv_desc, w_oihw, scale, bias) -> Layer:
+    ws = [_host(a, np.float32) for a in (w_oihw, scale, bias)]
+    h = _P()
+    _check(lib.cbs_create_layer_folded(ctypes.byref(desc), *[p for _, p in ws], ctypes.byref(h)),
+           "cbs_create_layer_folded")
+    return Layer(h.value, desc)
+
+
+def cbs_destroy_layer(layer: Layer) -> None:
+    if layer.handle:
+        lib.cbs_destroy_layer(layer.handle)
+        layer.handle = 0
+
+
+def cbs_run_layer(layer: Layer, inp, out, stream=None) -> None:
+    _check(lib.cbs_run_layer(layer.handle, _dev_ptr(inp), _dev_ptr(out), _stream(stream)), "cbs_run_layer")
+
+
+def _ptr_array(items):
+    arr = (_P * max(1, len(items)))()
+    for i, it in enumerate(items):
+        arr[i] = it
+    return arr
+
+
+def cbs_run_layer_list(layers, ins, outs, stream=None) -> None:
+    n = len(layers)
+    _check(lib.cbs_run_layer_list(_ptr_array([l.handle for l in layers]), n,
+                                  _ptr_array([_dev_ptr(b) for b in ins]),
+                                  _ptr_array([_dev_ptr(b) for b in outs]), _stream(stream)),
+           "cbs_run_layer_list")
+
+
+class Graph:
+    """A captured layer list (cbs_graph*), destroyed on garbage collection."""
+
+    def __init__(self, handle: int, keep):
+        self.handle = handle
+        self._keep = keep  # layers and buffers must outlive the graph
+
+    def __del__(self):
+        if getattr(self, "handle", 0):
+            lib.cbs_graph_destroy(self.handle)
+            self.handle = 0
+
+
+def cbs_graph_create(layers, ins, outs, stream=None) -> Graph:
+    h = _P()
+    _check(lib.cbs_graph_create(_ptr_array([l.handle for l in layers]), len(layers),
+                                _ptr_array([_dev_ptr(b) for b in ins]),
+                                _ptr_array([_dev_ptr(b) for b in outs]), _stream(stream), ctypes.byref(h)),
+           "cbs_graph_create")
+    return Graph(h.value, (list(layers), list(ins), list(outs)))
+
+
+def cbs_graph_launch(graph: Graph, stream=None) -> None:
+    _check(lib.cbs_graph_launch(graph.handle, _stream(stream)), "cbs_graph_launch")
+
+
+def cbs_graph_destroy(graph: Graph) -> None:
+    if graph.handle:
+        lib.cbs_graph_destroy(graph.handle)
+        graph.handle = 0
+
+
+def cbs_layer_info(layer: Layer) -> dict:
+    info = cbs_layer_info_t()
+    _check(lib.cbs_layer_info(layer.handle, ctypes.byref(info)), "cbs_layer_info")
+    d = {name: getattr(info, name) for name, _ in cbs_layer_info_t._fields_}
+    d["config_name"] = info.config_name.decode()
+    return d
+
+
+def cbs_layer_set_config(layer: Layer, config: int, splitk: int = 0) -> None:
+    _check(lib.cbs_layer_set_config(layer.handle, int(config), int(splitk)), "cbs_layer_set_config")
+
+
+def cbs_num_configs() -> int:
+    return int(lib.cbs_num_configs())
+
+
+def cbs_config_name(config: int):
+    r = lib.cbs_config_name(int(config))
+    return r.decode() if r else None
+
+
+def cbs_last_error() -> str:
+    r = lib.cbs_last_error()
+    return r.decode() if r else ""
+
+
+def cbs_pack_nhwc_f32(nchw, nhwc, n, c, h, w, c_pad, stream=None) -> None:
+    _check(lib.cbs_pack_nhwc_f32(_dev_ptr(nchw), _dev_ptr(nhwc), n, c, h, w, c_pad, _stream(stream)),
+           "cbs_pack_nhwc_f32")
+
+
+def cbs_quantize_nhwc_i8(nchw, nhwc, s_x, n, c, h, w, c_pad, stream=None) -> None:
+    _check(lib.cbs_quantize_nhwc_i8(_dev_ptr(nchw), _dev_ptr(nhwc), float(s_x), n, c, h, w, c_pad,
+                                    _stream(stream)), "cbs_quantize_nhwc_i8")
+
+
+def cbs_run_layer_raw_acc(layer: Layer, inp, acc, stream=None) -> None:
+    _check(lib.cbs_run_layer_raw_acc(layer.handle, _dev_ptr(inp), _dev_ptr(acc), _stream(stream)),
+           "cbs_run_layer_raw_acc")
+
+
+def cbs_get_qweights(layer: Layer):
+    d = layer.desc
+    q = np.empty((d.c_out, d.c_in, d.k, d.k), np.int8)
+    s = np.empty((d.c_out,), np.float64)
+    _check(lib.cbs_get_qweights(layer.handle, q.ctypes.data_as(_P), s.ctypes.data_as(_P)), "cbs_get_qweights")
+    return q, s
+
+
+def cbs_get_folded(layer: Layer):
+    d = layer.desc
+    w = np.empty((d.c_out, d.c_in, d.k, d.k), np.float32) if d.dtype == CBS_F32 else None
+    b = np.empty((d.c_out,), np.float32)
+    _check(lib.cbs_get_folded(layer.handle, w.ctypes.data_as(_P) if w is not None else None,
+                              b.ctypes.data_as(_P)), "cbs_get_folded")
+    return w, b

@@ -1,0 +1,641 @@
+// cbs_host.cpp -- host side of libcbs: descriptor validation, batch-norm
+// folding, weight re-layout into MFMA fragment order, per-channel int8 weight
+// quantisation, per-shape kernel selection, device memory, launches, layer
+// lists and graph capture.  The public contract is include/cbs.h.
+//
+// Folding and quantisation follow the vision-rs "YOLO26N Inference
+// Optimisation" page (section "Baseline benchmark": BN folded into the
+// weights at load; section "NHWC migration -- Weight layout": a one-time
+// re-layout of the OIHW weights at load so that C_in is contiguous along K)
+// and the edge-optimization README ("Highlights", "Design notes": one
+// symmetric int8 scale per output channel).  The arithmetic is in double and
+// this file is compiled with -ffp-contract=off, so every product and sum is
+// rounded exactly as written.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/cbs.h"
+#include "cbs_internal.h"
+
+using namespace cbs;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cbs_status fail(cbs_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int out_dim(int in, int k, int s, int p) {
+  if (in + 2 * p < k) return 0;
+  return (in + 2 * p - k) / s + 1;
+}
+
+#include "tile_table.inc"
+
+}  // namespace
+
+struct cbs_layer {
+  cbs_conv_desc d;
+  int oh, ow, pitch, cin_pad, cout_pad, co_blocks, M;
+  int variant;       // fused-epilogue variant
+  int raw_variant;   // raw-accumulator variant (INT8), -1 for fp32
+  int chunk_ch, chunks_per_tap, total_chunks, steps;
+  unsigned cpt_magic;
+  int config, splitk;
+  int device;
+  // device memory
+  void *d_wfrag = nullptr;
+  float *d_bias = nullptr;
+  float *d_dq = nullptr;
+  float *d_ws = nullptr;
+  unsigned *d_counters = nullptr;
+  size_t ws_bytes = 0, counters_len = 0;
+  // host copies for the test hooks
+  std::vector<float> h_wfold;   // fp32 W' OIHW
+  std::vector<float> h_bias;    // fp32 b'
+  std::vector<int8_t> h_qw;     // int8 q_w OIHW
+  std::vector<double> h_sw;     // s_w
+};
+
+struct cbs_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+// --------------------------------------------------------------- shapes --
+
+cbs_status validate(const cbs_conv_desc *d) {
+  if (!d) return fail(CBS_EINVAL, "desc is NULL");
+  if (d->n < 1 || d->c_in < 1 || d->h < 1 || d->w < 1 || d->c_out < 1)
+    return fail(CBS_EINVAL, "n, c_in, h, w, c_out must be >= 1 (got %d %d %d %d %d)", d->n, d->c_in,
+                d->h, d->w, d->c_out);
+  if (d->k != 1 && d->k != 3) return fail(CBS_EUNSUPPORTED, "kernel size %d not in {1,3}", d->k);
+  if (d->stride != 1 && d->stride != 2) return fail(CBS_EUNSUPPORTED, "stride %d not in {1,2}", d->stride);
+  if (d->pad < 0 || d->pad > d->k / 2) return fail(CBS_EUNSUPPORTED, "pad %d not in [0, k/2]", d->pad);
+  if (d->dtype != CBS_F32 && d->dtype != CBS_I8) return fail(CBS_EINVAL, "dtype %d unknown", d->dtype);
+  if (d->dtype == CBS_I8 && !(d->in_scale > 0.0f && std::isfinite(d->in_scale)))
+    return fail(CBS_EINVAL, "INT8 layer needs a finite in_scale > 0");
+  if (!(d->bn_eps >= 0.0f) || !std::isfinite(d->bn_eps)) return fail(CBS_EINVAL, "bn_eps must be finite and >= 0");
+  if (d->c_in > 4096 || d->c_out > 4096) return fail(CBS_EUNSUPPORTED, "channels above 4096");
+  const int oh = out_dim(d->h, d->k, d->stride, d->pad), ow = out_dim(d->w, d->k, d->stride, d->pad);
+  if (oh < 1 || ow < 1) return fail(CBS_EINVAL, "empty output (%dx%d)", oh, ow);
+  if (d->out_row_pitch != 0 && d->out_row_pitch < ow)
+    return fail(CBS_EINVAL, "out_row_pitch %d < OW %d", d->out_row_pitch, ow);
+  const int pitch = d->out_row_pitch ? d->out_row_pitch : ow;
+  const double in_elems = (double)d->n * d->h * d->w * round_up(d->c_in, 4);
+  const double out_elems = (double)d->n * oh * pitch * round_up(d->c_out, 4);
+  if (in_elems >= 2147483647.0 || out_elems >= 2147483647.0)
+    return fail(CBS_EUNSUPPORTED, "tensor above 2^31 elements");
+  return CBS_OK;
+}
+
+// ------------------------------------------------------ kernel selection --
+
+struct Choice {
+  int config, splitk;
+};
+
+// Tiles of a configuration for this layer.
+void tiles_of(const cbs_layer *L, int cfg, int *px_tiles, int *co_tiles) {
+  const KernelConfig &c = config(cfg);
+  const int tco = c.cb * 16 * c.wco, tpx = c.pb * 16 * c.wpx;
+  *co_tiles = ceil_div(L->co_blocks * 16, tco);
+  *px_tiles = ceil_div(L->M, tpx);
+}
+
+// Rough cost model (cycles at one SIMD) used when the tile table has no entry:
+// waves are spread over 1024 SIMDs, each wave runs its K slice on MFMA with a
+// fixed per-wave overhead, split-K adds a publish/reduce phase.
+double model_cost(const cbs_layer *L, int cfg, int splitk) {
+  const KernelConfig &c = config(cfg);
+  int pxt, cot;
+  tiles_of(L, cfg, &pxt, &cot);
+  const int kslices = splitk * c.wk;
+  const double steps_per_wave = std::ceil((double)L->steps / kslices);
+  const double mfma_step = L->d.dtype == CBS_F32 ? 4 * 32.0 : 16.0;
+  const double load_step = 40.0 * (c.cb + c.pb);
+  const double per_wave = steps_per_wave * std::max(mfma_step * c.cb * c.pb, load_step) + 1500.0;
+  const double waves = (double)pxt * cot * splitk * c.wco * c.wpx * c.wk;
+  const double rounds = std::ceil(waves / 1024.0);
+  double cost = rounds * per_wave;
+  if (splitk > 1) cost += 2500.0;
+  // L2 -> CU traffic (bytes) against ~8 KB/cycle aggregate
+  const double esz = L->d.dtype == CBS_F32 ? 4.0 : 1.0;
+  const double kbytes = (double)L->steps * (L->d.dtype == CBS_F32 ? 16 : 64) * esz;
+  const double traffic = kbytes * ((double)L->M * cot + (double)L->co_blocks * 16 * pxt);
+  cost = std::max(cost, traffic / 8192.0);
+  return cost;
+}
+
+bool config_fits(const cbs_layer *L, int cfg, int splitk) {
+  const KernelConfig &c = config(cfg);
+  if (splitk < 1 || splitk > 64) return false;
+  if (splitk > 1 && L->steps < splitk * c.wk) return false;
+  int pxt, cot;
+  tiles_of(L, cfg, &pxt, &cot);
+  const double grid = (double)pxt * cot * splitk;
+  return grid < 2147483647.0;
+}
+
+Choice choose(const cbs_layer *L) {
+  // 1) the offline-tuned table
+  for (const TileEntry &e : kTileTable) {
+    if (e.n == L->d.n && e.c_in == L->d.c_in && e.c_out == L->d.c_out && e.h == L->d.h &&
+        e.w == L->d.w && e.k == L->d.k && e.s == L->d.stride && e.dtype == L->d.dtype &&
+        e.config < num_configs() && config_fits(L, e.config, e.splitk))
+      return {e.config, e.splitk};
+  }
+  // 2) the cost model
+  Choice best{2, 1};
+  double best_cost = 1e300;
+  for (int cfg = 0; cfg < num_configs(); cfg++) {
+    for (int sk : {1, 2, 3, 4, 6, 8, 12, 16}) {
+      if (!config_fits(L, cfg, sk)) continue;
+      const double cost = model_cost(L, cfg, sk);
+      if (cost < best_cost * 0.999) {
+        best_cost = cost;
+        best = {cfg, sk};
+      }
+    }
+  }
+  return best;
+}
+
+// ----------------------------------------------------------- device side --
+
+cbs_status dev_alloc(void **p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return CBS_OK;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return fail(CBS_ENOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+  }
+  return CBS_OK;
+}
+
+void release(cbs_layer *L) {
+  if (!L) return;
+  if (L->d_wfrag) (void)hipFree(L->d_wfrag);
+  if (L->d_bias) (void)hipFree(L->d_bias);
+  if (L->d_dq) (void)hipFree(L->d_dq);
+  if (L->d_ws) (void)hipFree(L->d_ws);
+  if (L->d_counters) (void)hipFree(L->d_counters);
+  L->d_wfrag = nullptr;
+  L->d_bias = L->d_dq = L->d_ws = nullptr;
+  L->d_counters = nullptr;
+}
+
+// (Re)allocate the split-K workspace and the zeroed arrival counters for the
+// layer's current configuration.  Runs at create / set_config only.
+cbs_status setup_splitk(cbs_layer *L) {
+  if (L->d_ws) (void)hipFree(L->d_ws);
+  if (L->d_counters) (void)hipFree(L->d_counters);
+  L->d_ws = nullptr;
+  L->d_counters = nullptr;
+  L->ws_bytes = 0;
+  L->counters_len = 0;
+  if (L->splitk <= 1) return CBS_OK;
+  const KernelConfig &c = config(L->config);
+  int pxt, cot;
+  tiles_of(L, L->config, &pxt, &cot);
+  const size_t tiles = (size_t)pxt * cot;
+  const size_t tile_vecs = (size_t)c.wco * c.wpx * c.cb * c.pb * 64;
+  L->ws_bytes = tiles * L->splitk * tile_vecs * 16;
+  L->counters_len = tiles;
+  cbs_status st = dev_alloc((void **)&L->d_ws, L->ws_bytes);
+  if (st != CBS_OK) return st;
+  st = dev_alloc((void **)&L->d_counters, tiles * sizeof(unsigned));
+  if (st != CBS_OK) return st;
+  hipError_t e = hipMemset(L->d_counters, 0, tiles * sizeof(unsigned));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(CBS_EDEVICE, "counter init: %s", hipGetErrorString(e));
+  return CBS_OK;
+}
+
+ConvParams make_params(const cbs_layer *L, const void *in, void *out) {
+  ConvParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = in;
+  p.wfrag = L->d_wfrag;
+  p.bias = L->d_bias;
+  p.dq = L->d_dq;
+  p.out = out;
+  p.ws = L->d_ws;
+  p.counters = L->d_counters;
+  p.N = L->d.n;
+  p.H = L->d.h;
+  p.W = L->d.w;
+  p.cin_pad = L->cin_pad;
+  p.OH = L->oh;
+  p.OW = L->ow;
+  p.cout_pad = L->cout_pad;
+  p.pitch = L->pitch;
+  p.k = L->d.k;
+  p.stride = L->d.stride;
+  p.pad = L->d.pad;
+  p.M = L->M;
+  p.chunk_ch = L->chunk_ch;
+  p.chunks_per_tap = L->chunks_per_tap;
+  p.cpt_magic = L->cpt_magic;
+  p.total_chunks = L->total_chunks;
+  p.steps = L->steps;
+  p.splitk = L->splitk;
+  p.steps_per_split = ceil_div(L->steps, L->splitk);
+  p.co_blocks = L->co_blocks;
+  tiles_of(L, L->config, &p.px_tiles, &p.co_tiles);
+  return p;
+}
+
+cbs_status launch(const cbs_layer *L, int variant, const void *in, void *out, void *stream) {
+  ConvParams p = make_params(L, in, out);
+  hipError_t e = launch_conv(variant, L->config, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CBS_ELAUNCH, "conv launch: %s", hipGetErrorString(e));
+  return CBS_OK;
+}
+
+// ------------------------------------------------------------ create ----
+
+cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *gamma, const float *beta,
+                       const float *mean, const float *var, const float *scale, const float *bias,
+                       cbs_layer **out) {
+  if (!out) return fail(CBS_EINVAL, "out is NULL");
+  *out = nullptr;
+  cbs_status st = validate(desc);
+  if (st != CBS_OK) return st;
+  if (!w) return fail(CBS_EINVAL, "weights are NULL");
+  if (!scale && (!gamma || !beta || !mean || !var)) return fail(CBS_EINVAL, "BN parameters are NULL");
+  if (scale && !bias) return fail(CBS_EINVAL, "bias is NULL");
+
+  int dev_count = 0;
+  if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count < 1) {
+    (void)hipGetLastError();
+    return fail(CBS_EDEVICE, "no HIP device");
+  }
+
+  cbs_layer *L = new (std::nothrow) cbs_layer();
+  if (!L) return fail(CBS_ENOMEM, "host allocation");
+  L->d = *desc;
+  const cbs_conv_desc &d = L->d;
+  if (hipGetDevice(&L->device) != hipSuccess) {
+    delete L;
+    return fail(CBS_EDEVICE, "hipGetDevice failed");
+  }
+  L->oh = out_dim(d.h, d.k, d.stride, d.pad);
+  L->ow = out_dim(d.w, d.k, d.stride, d.pad);
+  L->pitch = d.out_row_pitch ? d.out_row_pitch : L->ow;
+  L->cin_pad = round_up(d.c_in, 4);
+  L->cout_pad = round_up(d.c_out, 4);
+  L->co_blocks = ceil_div(L->cout_pad, 16);
+  L->M = d.n * L->oh * L->ow;
+  const int taps = d.k * d.k;
+  int vec = 1;
+  if (d.dtype == CBS_F32) {
+    L->chunk_ch = 4;
+    L->variant = VAR_F32;
+    L->raw_variant = -1;
+  } else if (L->cin_pad % 16 == 0) {
+    L->chunk_ch = 16;
+    L->variant = VAR_I8_C16;
+    L->raw_variant = VAR_I8_C16_RAW;
+  } else {
+    L->chunk_ch = 4;
+    vec = 4;
+    L->variant = VAR_I8_C4;
+    L->raw_variant = VAR_I8_C4_RAW;
+  }
+  L->chunks_per_tap = L->cin_pad / L->chunk_ch;
+  L->total_chunks = taps * L->chunks_per_tap;
+  const int chunks_per_step = 4 * vec;
+  L->steps = ceil_div(L->total_chunks, chunks_per_step);
+  // chunk -> tap by multiply-shift; checked for every chunk index the kernel decodes
+  L->cpt_magic = (unsigned)(((1u << 20) + L->chunks_per_tap - 1) / L->chunks_per_tap);
+  for (int c = 0; c < L->steps * chunks_per_step; c++) {
+    if ((int)(((unsigned)c * L->cpt_magic) >> 20) != c / L->chunks_per_tap) {
+      delete L;
+      return fail(CBS_EUNSUPPORTED, "chunk decode not exact for this shape");
+    }
+  }
+
+  // ---- fold batch norm in double
+  const int per_co = d.c_in * taps;
+  std::vector<double> wf((size_t)d.c_out * per_co), bf(d.c_out);
+  for (int co = 0; co < d.c_out; co++) {
+    double sc, b;
+    if (scale) {
+      sc = (double)scale[co];
+      b = (double)bias[co];
+    } else {
+      sc = (double)gamma[co] / std::sqrt((double)var[co] + (double)d.bn_eps);
+      b = (double)beta[co] - (double)mean[co] * sc;
+    }
+    for (int i = 0; i < per_co; i++) wf[(size_t)co * per_co + i] = (double)w[(size_t)co * per_co + i] * sc;
+    bf[co] = b;
+  }
+  L->h_bias.assign(d.c_out, 0.f);
+  for (int co = 0; co < d.c_out; co++) L->h_bias[co] = (float)bf[co];
+
+  // ---- per-output-channel int8 quantisation (double)
+  std::vector<float> dq;
+  if (d.dtype == CBS_I8) {
+    L->h_qw.assign((size_t)d.c_out * per_co, 0);
+    L->h_sw.assign(d.c_out, 1.0);
+    dq.assign((size_t)L->co_blocks * 16, 0.f);
+    for (int co = 0; co < d.c_out; co++) {
+      double m = 0.0;
+      for (int i = 0; i < per_co; i++) m = std::max(m, std::fabs(wf[(size_t)co * per_co + i]));
+      const double s = m > 0.0 ? m / 127.0 : 1.0;
+      L->h_sw[co] = s;
+      for (int i = 0; i < per_co; i++) {
+        double q = std::nearbyint(wf[(size_t)co * per_co + i] / s);
+        q = std::min(127.0, std::max(-127.0, q));
+        L->h_qw[(size_t)co * per_co + i] = (int8_t)q;
+      }
+      dq[co] = (float)((double)d.in_scale * s);
+    }
+  } else {
+    L->h_wfold.resize((size_t)d.c_out * per_co);
+    for (size_t i = 0; i < wf.size(); i++) L->h_wfold[i] = (float)wf[i];
+  }
+
+  // ---- weights in MFMA fragment order: [co_block][step][lane][16 bytes]
+  // lane = 16*g + r: output channel co_block*16 + r; chunks (4*step + g)*vec + j.
+  const size_t frag_bytes = (size_t)L->co_blocks * L->steps * 64 * 16;
+  std::vector<unsigned char> frag(frag_bytes, 0);
+  for (int cob = 0; cob < L->co_blocks; cob++)
+    for (int s = 0; s < L->steps; s++)
+      for (int lane = 0; lane < 64; lane++) {
+        const int r = lane & 15, g = lane >> 4, co = cob * 16 + r;
+        unsigned char *dst = &frag[(((size_t)cob * L->steps + s) * 64 + lane) * 16];
+        if (co >= d.c_out) continue;
+        for (int j = 0; j < vec; j++) {
+          const int c = (4 * s + g) * vec + j;
+          if (c >= L->total_chunks) continue;
+          const int tap = c / L->chunks_per_tap;
+          const int ci0 = (c % L->chunks_per_tap) * L->chunk_ch;
+          const int kh = tap / d.k, kw = tap % d.k;
+          for (int e = 0; e < L->chunk_ch; e++) {
+            const int ci = ci0 + e;
+            if (ci >= d.c_in) continue;
+            const size_t src = (((size_t)co * d.c_in + ci) * d.k + kh) * d.k + kw;
+            if (d.dtype == CBS_F32) {
+              const float v = L->h_wfold[src];
+              std::memcpy(dst + 4 * e, &v, 4);
+            } else {
+              dst[j * 4 + e] = (unsigned char)L->h_qw[src];
+            }
+          }
+        }
+      }
+
+  // ---- kernel configuration
+  const Choice ch = choose(L);
+  L->config = ch.config;
+  L->splitk = ch.splitk;
+
+  // ---- device memory
+  std::vector<float> biasv((size_t)L->co_blocks * 16, 0.f);
+  for (int co = 0; co < d.c_out; co++) biasv[co] = L->h_bias[co];
+  st = dev_alloc(&L->d_wfrag, frag_bytes);
+  if (st == CBS_OK) st = dev_alloc((void **)&L->d_bias, biasv.size() * sizeof(float));
+  if (st == CBS_OK && d.dtype == CBS_I8) st = dev_alloc((void **)&L->d_dq, dq.size() * sizeof(float));
+  if (st == CBS_OK) st = setup_splitk(L);
+  if (st == CBS_OK) {
+    hipError_t e = hipMemcpy(L->d_wfrag, frag.data(), frag_bytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(L->d_bias, biasv.data(), biasv.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess && d.dtype == CBS_I8)
+      e = hipMemcpy(L->d_dq, dq.data(), dq.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) st = fail(CBS_EDEVICE, "weight upload: %s", hipGetErrorString(e));
+  }
+  if (st != CBS_OK) {
+    release(L);
+    delete L;
+    return st;
+  }
+  *out = L;
+  return CBS_OK;
+}
+
+}  // namespace
+
+// ================================================================= C ABI ==
+
+extern "C" {
+
+cbs_status cbs_create_layer(const cbs_conv_desc *desc, const float *w_oihw, const float *gamma,
+                            const float *beta, const float *mean, const float *var, cbs_layer **out) {
+  return create_impl(desc, w_oihw, gamma, beta, mean, var, nullptr, nullptr, out);
+}
+
+cbs_status cbs_create_layer_folded(const cbs_conv_desc *desc, const float *w_oihw, const float *scale,
+                                   const float *bias, cbs_layer **out) {
+  if (!scale) {
+    if (out) *out = nullptr;
+    return fail(CBS_EINVAL, "scale is NULL");
+  }
+  return create_impl(desc, w_oihw, nullptr, nullptr, nullptr, nullptr, scale, bias, out);
+}
+
+void cbs_destroy_layer(cbs_layer *layer) {
+  if (!layer) return;
+  release(layer);
+  delete layer;
+}
+
+cbs_status cbs_run_layer(const cbs_layer *layer, const void *in, void *out, void *stream) {
+  if (!layer || !in || !out) return fail(CBS_EINVAL, "run_layer: null layer or buffer");
+  return launch(layer, layer->variant, in, out, stream);
+}
+
+cbs_status cbs_run_layer_list(cbs_layer *const *layers, int32_t n, const void *const *ins,
+                              void *const *outs, void *stream) {
+  if (n < 0 || (n > 0 && (!layers || !ins || !outs))) return fail(CBS_EINVAL, "run_layer_list: bad arguments");
+  for (int32_t i = 0; i < n; i++) {
+    if (!layers[i] || !ins[i] || !outs[i]) return fail(CBS_EINVAL, "run_layer_list: null entry %d", i);
+    cbs_status st = launch(layers[i], layers[i]->variant, ins[i], outs[i], stream);
+    if (st != CBS_OK) return st;
+  }
+  return CBS_OK;
+}
+
+cbs_status cbs_graph_create(cbs_layer *const *layers, int32_t n, const void *const *ins, void *const *outs,
+                            void *stream, cbs_graph **out) {
+  (void)stream;
+  if (!out) return fail(CBS_EINVAL, "graph_create: out is NULL");
+  *out = nullptr;
+  if (n < 1 || !layers || !ins || !outs) return fail(CBS_EINVAL, "graph_create: bad arguments");
+  for (int32_t i = 0; i < n; i++)
+    if (!layers[i] || !ins[i] || !outs[i]) return fail(CBS_EINVAL, "graph_create: null entry %d", i);
+  cbs_graph *G = new (std::nothrow) cbs_graph();
+  if (!G) return fail(CBS_ENOMEM, "host allocation");
+  // Capture on a private stream (the caller's may be the null stream, which
+  // cannot be captured); default priority.
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete G;
+    return fail(CBS_EDEVICE, "capture stream: %s", hipGetErrorString(e));
+  }
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  cbs_status st = CBS_OK;
+  if (e != hipSuccess) st = fail(CBS_EDEVICE, "begin capture: %s", hipGetErrorString(e));
+  if (st == CBS_OK) {
+    for (int32_t i = 0; i < n && st == CBS_OK; i++)
+      st = launch(layers[i], layers[i]->variant, ins[i], outs[i], cs);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(cs, &g);
+    if (st == CBS_OK && e != hipSuccess) st = fail(CBS_EDEVICE, "end capture: %s", hipGetErrorString(e));
+    G->graph = g;
+  }
+  if (st == CBS_OK) {
+    e = hipGraphInstantiate(&G->exec, G->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) st = fail(CBS_EDEVICE, "graph instantiate: %s", hipGetErrorString(e));
+  }
+  (void)hipStreamDestroy(cs);
+  if (st != CBS_OK) {
+    cbs_graph_destroy(G);
+    return st;
+  }
+  *out = G;
+  return CBS_OK;
+}
+
+cbs_status cbs_graph_launch(const cbs_graph *graph, void *stream) {
+  if (!graph || !graph->exec) return fail(CBS_EINVAL, "graph_launch: null graph");
+  hipError_t e = hipGraphLaunch(graph->exec, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CBS_ELAUNCH, "graph launch: %s", hipGetErrorString(e));
+  return CBS_OK;
+}
+
+void cbs_graph_destroy(cbs_graph *graph) {
+  if (!graph) return;
+  if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
+  if (graph->graph) (void)hipGraphDestroy(graph->graph);
+  delete graph;
+}
+
+cbs_status cbs_layer_info(const cbs_layer *L, cbs_layer_info_t *info) {
+  if (!L || !info) return fail(CBS_EINVAL, "layer_info: null argument");
+  std::memset(info, 0, sizeof(*info));
+  const cbs_conv_desc &d = L->d;
+  info->c_in_pad = L->cin_pad;
+  info->c_out_pad = L->cout_pad;
+  info->oh = L->oh;
+  info->ow = L->ow;
+  info->out_row_pitch = L->pitch;
+  info->dtype = d.dtype;
+  const int64_t esz = d.dtype == CBS_F32 ? 4 : 1;
+  info->in_bytes = (int64_t)d.n * d.h * d.w * L->cin_pad * esz;
+  info->out_bytes = (int64_t)d.n * L->oh * L->pitch * L->cout_pad * 4;
+  const int64_t kk = (int64_t)d.k * d.k;
+  info->flops = 2 * (int64_t)d.n * L->oh * L->ow * d.c_out * d.c_in * kk;
+  info->alg_bytes = (int64_t)d.n * d.h * d.w * d.c_in * esz + (int64_t)d.c_out * d.c_in * kk * esz +
+                    (int64_t)d.n * L->oh * L->ow * d.c_out * 4 + 8 * (int64_t)d.c_out;
+  info->config = L->config;
+  info->splitk = L->splitk;
+  int pxt, cot;
+  tiles_of(L, L->config, &pxt, &cot);
+  info->grid = pxt * cot * L->splitk;
+  const KernelConfig &c = config(L->config);
+  info->threads = 64 * c.wco * c.wpx * c.wk;
+  std::snprintf(info->config_name, sizeof(info->config_name), "%s/sk%d", c.name, L->splitk);
+  return CBS_OK;
+}
+
+cbs_status cbs_layer_set_config(cbs_layer *L, int32_t cfg, int32_t splitk) {
+  if (!L) return fail(CBS_EINVAL, "set_config: null layer");
+  if (cfg < 0 || cfg >= num_configs()) return fail(CBS_EINVAL, "config %d out of range", cfg);
+  if (splitk < 0) return fail(CBS_EINVAL, "splitk %d < 0", splitk);
+  if (splitk == 0) splitk = 1;
+  if (!config_fits(L, cfg, splitk))
+    return fail(CBS_EUNSUPPORTED, "config %s with splitk %d does not fit this layer", config(cfg).name, splitk);
+  const int old_cfg = L->config, old_sk = L->splitk;
+  L->config = cfg;
+  L->splitk = splitk;
+  cbs_status st = setup_splitk(L);
+  if (st != CBS_OK) {
+    L->config = old_cfg;
+    L->splitk = old_sk;
+    (void)setup_splitk(L);
+  }
+  return st;
+}
+
+int32_t cbs_num_configs(void) { return num_configs(); }
+
+const char *cbs_config_name(int32_t cfg) {
+  if (cfg < 0 || cfg >= num_configs()) return nullptr;
+  return config(cfg).name;
+}
+
+const char *cbs_last_error(void) { return g_last_error.c_str(); }
+
+cbs_status cbs_pack_nhwc_f32(const float *nchw, float *nhwc, int32_t n, int32_t c, int32_t h, int32_t w,
+                             int32_t c_pad, void *stream) {
+  if (!nchw || !nhwc) return fail(CBS_EINVAL, "pack: null buffer");
+  if (n < 0 || c < 1 || h < 0 || w < 0 || c_pad < c || c_pad % 4 != 0)
+    return fail(CBS_EINVAL, "pack: bad sizes");
+  if ((double)n * h * w * c_pad >= 2147483647.0) return fail(CBS_EUNSUPPORTED, "pack: tensor above 2^31 elements");
+  hipError_t e = launch_pack_nhwc_f32(nchw, nhwc, n, c, h * w, c_pad, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CBS_ELAUNCH, "pack launch: %s", hipGetErrorString(e));
+  return CBS_OK;
+}
+
+cbs_status cbs_quantize_nhwc_i8(const float *nchw, int8_t *nhwc, float s_x, int32_t n, int32_t c, int32_t h,
+                                int32_t w, int32_t c_pad, void *stream) {
+  if (!nchw || !nhwc) return fail(CBS_EINVAL, "quantize: null buffer");
+  if (!(s_x > 0.0f) || !std::isfinite(s_x)) return fail(CBS_EINVAL, "quantize: s_x must be finite and > 0");
+  if (n < 0 || c < 1 || h < 0 || w < 0 || c_pad < c || c_pad % 4 != 0)
+    return fail(CBS_EINVAL, "quantize: bad sizes");
+  if ((double)n * h * w * c_pad >= 2147483647.0) return fail(CBS_EUNSUPPORTED, "quantize: tensor above 2^31 elements");
+  hipError_t e = launch_quantize_nhwc_i8(nchw, nhwc, s_x, n, c, h * w, c_pad, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CBS_ELAUNCH, "quantize launch: %s", hipGetErrorString(e));
+  return CBS_OK;
+}
+
+cbs_status cbs_run_layer_raw_acc(const cbs_layer *L, const void *in, int32_t *acc, void *stream) {
+  if (!L || !in || !acc) return fail(CBS_EINVAL, "run_layer_raw_acc: null layer or buffer");
+  if (L->raw_variant < 0) return fail(CBS_EINVAL, "run_layer_raw_acc: not an INT8 layer");
+  return launch(L, L->raw_variant, in, acc, stream);
+}
+
+cbs_status cbs_get_qweights(const cbs_layer *L, int8_t *q_oihw, double *s_w) {
+  if (!L) return fail(CBS_EINVAL, "get_qweights: null layer");
+  if (L->d.dtype != CBS_I8) return fail(CBS_EINVAL, "get_qweights: not an INT8 layer");
+  if (q_oihw) std::memcpy(q_oihw, L->h_qw.data(), L->h_qw.size());
+  if (s_w) std::memcpy(s_w, L->h_sw.data(), L->h_sw.size() * sizeof(double));
+  return CBS_OK;
+}
+
+cbs_status cbs_get_folded(const cbs_layer *L, float *w_oihw, float *bias) {
+  if (!L) return fail(CBS_EINVAL, "get_folded: null layer");
+  if (w_oihw) {
+    if (L->d.dtype != CBS_F32) return fail(CBS_EINVAL, "get_folded: INT8 layers keep quantised weights");
+    std::memcpy(w_oihw, L->h_wfold.data(), L->h_wfold.size() * sizeof(float));
+  }
+  if (bias) std::memcpy(bias, L->h_bias.data(), L->h_bias.size() * sizeof(float));
+  return CBS_OK;
+}
+
+}  // extern "C"

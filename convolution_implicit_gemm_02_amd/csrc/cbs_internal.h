@@ -1,0 +1,60 @@
+// cbs_internal.h -- shared between the host library (cbs_host.cpp) and the
+// kernels (cbs_kernels.hip) of libcbs.  Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cbs {
+
+// Kernel configuration: one wave computes CB x PB blocks of 16 output
+// channels x 16 output pixels; a workgroup holds WCO x WPX x WK waves (WK
+// waves split K inside the workgroup and are reduced through LDS).
+struct KernelConfig {
+  int cb, pb, wco, wpx, wk;
+  const char *name;
+};
+
+// Kernel-variant families (dtype x operand gathering x epilogue).
+enum Variant {
+  VAR_F32 = 0,         // fp32 activations, 4-channel chunks, SiLU epilogue
+  VAR_I8_C16 = 1,      // int8, 16-channel chunks (C_in_pad % 16 == 0), dequant+SiLU
+  VAR_I8_C4 = 2,       // int8, 4-channel chunks (any C_in_pad % 4 == 0), dequant+SiLU
+  VAR_I8_C16_RAW = 3,  // as VAR_I8_C16, stores raw int32 accumulators
+  VAR_I8_C4_RAW = 4,   // as VAR_I8_C4, stores raw int32 accumulators
+  VAR_COUNT = 5
+};
+
+// Everything a launch needs; filled at create, passed by value.
+struct ConvParams {
+  const void *x;         // NHWC input [N][H][W][cin_pad]
+  const void *wfrag;     // weights in MFMA fragment order [co_blocks][steps][64 lanes][16 bytes]
+  const float *bias;     // folded bias [co_blocks*16] (zero beyond C_out)
+  const float *dq;       // INT8 dequant factors f[co] [co_blocks*16] (null for fp32)
+  void *out;             // NHWC output [N][OH][pitch][cout_pad] (fp32, or int32 for raw)
+  float *ws;             // split-K partial tiles (null when splitk == 1)
+  unsigned *counters;    // split-K arrival counters, one per output tile (zero between launches)
+  int N, H, W, cin_pad;
+  int OH, OW, cout_pad, pitch;
+  int k, stride, pad;
+  int M;                 // N*OH*OW output pixels
+  int chunk_ch;          // channels per chunk (4 or 16)
+  int chunks_per_tap;    // cin_pad / chunk_ch
+  unsigned cpt_magic;    // chunk / chunks_per_tap == (chunk * cpt_magic) >> 20 for the chunks in use
+  int total_chunks;      // k*k*chunks_per_tap
+  int steps;             // K steps (each 16 fp32 or 64 int8 channels of K)
+  int steps_per_split;   // K steps per split-K workgroup
+  int splitk;            // workgroups per output tile along K
+  int co_blocks;         // 16-channel output blocks holding real channels
+  int px_tiles, co_tiles;// workgroup tiles along pixels and output channels
+};
+
+int num_configs();
+const KernelConfig &config(int i);
+// Launch variant `var` with configuration `cfg`; returns the hipError_t of the launch.
+hipError_t launch_conv(int var, int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_pack_nhwc_f32(const float *x, float *y, int n, int c, int hw, int c_pad,
+                                hipStream_t stream);
+hipError_t launch_quantize_nhwc_i8(const float *x, int8_t *y, float s_x, int n, int c, int hw,
+                                   int c_pad, hipStream_t stream);
+
+}  // namespace cbs

@@ -1,0 +1,427 @@
+// cbs_kernels.hip -- gfx950 kernels of libcbs: implicit-GEMM fused
+// Conv2d + folded BN + SiLU on MFMA (fp32 and int8), and the graph-entry
+// NCHW -> NHWC pack / quantise kernels.
+//
+// The convolution is computed as the implicit GEMM described on the vision-rs
+// "YOLO26N Inference Optimisation" page, section "NHWC migration -- What NHWC
+// is and why it matters": rows = output pixels (n, oh, ow), K = (kh, kw, c_in)
+// with c_in contiguous, columns = output channels.  Here the MFMA "A" operand
+// is the weights (16 output channels per block) and the "B" operand is the
+// gathered activations (16 output pixels per block), so every lane of the
+// accumulator holds 4 consecutive output channels of one pixel and the
+// epilogue stores one 16-byte NHWC vector per lane.
+//
+// K is walked in "chunks": 4 consecutive input channels of one tap (fp32 and
+// small-channel int8) or 16 (int8 with C_in_pad % 16 == 0).  At each K step,
+// lane group g = lane/16 of a wave loads chunk (4*step + g) (times 4 chunks
+// for the small-channel int8 gather); the weights were laid out at create in
+// exactly this order ("fragment order"), so each weight load is one
+// contiguous 1 KiB read per wave.  Chunks that fall in the zero padding of
+// the image, past K, or on pixels past the end of the tile are not loaded
+// and count as zeros, which is the zero padding of the definition.
+//
+// Output pixels are indexed by their logical position m = (n*OH + oh)*OW + ow
+// and stored at ((n*OH + oh)*pitch + ow), so a tail tile can never write into
+// the guard pixels of a row or into the next row: the overflow documented in
+// the same page's section "Bug fixed: TMA overflow" cannot happen by
+// construction, whatever the tile shape.
+//
+// Small-M layers (batch 1 at 20x20 or 40x40) split K across the waves of a
+// workgroup (reduced in LDS) and, optionally, across workgroups: each
+// workgroup writes its partial tile to a workspace, and the last one to
+// arrive (atomic ticket per tile) sums all partials in split order, runs the
+// epilogue and re-arms the ticket, so no memset is ever needed and the result
+// is bitwise deterministic.
+#include "cbs_internal.h"
+
+namespace cbs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int VAR> struct Var;
+template <> struct Var<VAR_F32> {
+  using Frag = f32x4; using Acc = f32x4;
+  static constexpr int VEC = 1, ESIZE = 4; static constexpr bool I8 = false, RAW = false;
+};
+template <> struct Var<VAR_I8_C16> {
+  using Frag = i32x4; using Acc = i32x4;
+  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = false;
+};
+template <> struct Var<VAR_I8_C4> {
+  using Frag = i32x4; using Acc = i32x4;
+  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = false;
+};
+template <> struct Var<VAR_I8_C16_RAW> {
+  using Frag = i32x4; using Acc = i32x4;
+  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = true;
+};
+template <> struct Var<VAR_I8_C4_RAW> {
+  using Frag = i32x4; using Acc = i32x4;
+  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = true;
+};
+
+__device__ __forceinline__ float silu_f(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
+
+// Decoded K chunk: tap offset (dy, dx) and first channel.
+struct Chunk {
+  int dy, dx, ci;
+  bool ok;
+};
+
+__device__ __forceinline__ Chunk decode_chunk(const ConvParams &p, int c) {
+  Chunk r;
+  const int tap = (int)(((unsigned)c * p.cpt_magic) >> 20);
+  r.ci = (c - tap * p.chunks_per_tap) * p.chunk_ch;
+  r.dy = (p.k == 1) ? 0 : ((tap * 11) >> 5);  // tap / 3 for tap < 9
+  r.dx = tap - r.dy * p.k;
+  r.ok = c < p.total_chunks;
+  return r;
+}
+
+template <int VAR, int CB, int PB, int WCO, int WPX, int WK>
+__global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) {
+  using V = Var<VAR>;
+  using Frag = typename V::Frag;
+  using Acc = typename V::Acc;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wk = wave % WK;
+  const int wco = (wave / WK) % WCO;
+  const int wpx = wave / (WK * WCO);
+  const int slot = wco + WCO * wpx;
+  const int r = lane & 15, g = lane >> 4;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs; remap so that each
+  // XCD receives a contiguous range of logical tiles (the co tiles and K
+  // splits of one pixel tile then share that XCD's L2).
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int per = nb >> 3, rem = nb & 7, xcd = bid & 7, loc = bid >> 3;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  const int split = logical % p.splitk;
+  const int tile = logical / p.splitk;
+  const int co_tile = tile % p.co_tiles;
+  const int px_tile = tile / p.co_tiles;
+
+  // The 16-pixel blocks of this wave: lane r owns pixel r of each block.
+  int pixbase[PB], iy0[PB], ix0[PB], outpix[PB];
+  bool mval[PB];
+#pragma unroll
+  for (int b = 0; b < PB; b++) {
+    const int m = ((px_tile * WPX + wpx) * PB + b) * 16 + r;
+    mval[b] = m < p.M;
+    const int mm = mval[b] ? m : 0;
+    const int ow = mm % p.OW;
+    const int t = mm / p.OW;
+    const int oh = t % p.OH;
+    const int n = t / p.OH;
+    iy0[b] = oh * p.stride - p.pad;
+    ix0[b] = ow * p.stride - p.pad;
+    pixbase[b] = (n * p.H + iy0[b]) * p.W + ix0[b];
+    outpix[b] = (n * p.OH + oh) * p.pitch + ow;
+  }
+  const int cob0 = (co_tile * WCO + wco) * CB;
+  const int s_begin = split * p.steps_per_split;
+  const int s_end = min(p.steps, s_begin + p.steps_per_split);
+  const char *xb = (const char *)p.x;
+  const char *wb = (const char *)p.wfrag;
+
+  auto load = [&](int s, Frag(&aa)[CB], Frag(&bb)[PB]) {
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+      const int cob = cob0 + cb;
+      if (cob < p.co_blocks)
+        aa[cb] = *(const Frag *)(wb + ((size_t)(cob * p.steps + s) * 64 + lane) * 16);
+      else
+        aa[cb] = Frag{};
+    }
+    if constexpr (V::VEC == 1) {
+      const Chunk c = decode_chunk(p, s * 4 + g);
+      const int doff = (c.dy * p.W + c.dx) * p.cin_pad + c.ci;
+#pragma unroll
+      for (int b = 0; b < PB; b++) {
+        const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
+        const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+        if (v)
+          bb[b] = *(const Frag *)(xb + (size_t)(pixbase[b] * p.cin_pad + doff) * V::ESIZE);
+        else
+          bb[b] = Frag{};
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < PB; b++) bb[b] = Frag{};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const Chunk c = decode_chunk(p, (s * 4 + g) * 4 + j);
+        const int doff = (c.dy * p.W + c.dx) * p.cin_pad + c.ci;
+#pragma unroll
+        for (int b = 0; b < PB; b++) {
+          const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
+          const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+          if (v) bb[b][j] = *(const int *)(xb + (size_t)(pixbase[b] * p.cin_pad + doff));
+        }
+      }
+    }
+  };
+
+  Acc acc[CB][PB];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+    for (int b = 0; b < PB; b++) acc[cb][b] = Acc{};
+
+  auto mma = [&](const Frag(&aa)[CB], const Frag(&bb)[PB]) {
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+      for (int b = 0; b < PB; b++) {
+        if constexpr (!V::I8) {
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[cb][j], bb[b][j], acc[cb][b], 0, 0, 0);
+        } else {
+          acc[cb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[cb], bb[b], acc[cb][b], 0, 0, 0);
+        }
+      }
+  };
+
+  // Main loop, two register sets in ping-pong: the loads of step s+WK are in
+  // flight while the MFMAs of step s run.
+  {
+    Frag a0[CB], b0[PB], a1[CB], b1[PB];
+    int s = s_begin + wk;
+    if (s < s_end) load(s, a0, b0);
+    for (; s < s_end; s += 2 * WK) {
+      const bool h1 = s + WK < s_end;
+      if (h1) load(s + WK, a1, b1);
+      mma(a0, b0);
+      if (s + 2 * WK < s_end) load(s + 2 * WK, a0, b0);
+      if (h1) mma(a1, b1);
+    }
+  }
+
+  // Reduce the WK K-slices of the workgroup through LDS, in slice order.
+  if constexpr (WK > 1) {
+    __shared__ Acc red[(WK - 1) * WCO * WPX * CB * PB][64];
+    if (wk > 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int b = 0; b < PB; b++)
+          red[(((wk - 1) * WCO * WPX + slot) * CB + cb) * PB + b][lane] = acc[cb][b];
+    }
+    __syncthreads();
+    if (wk == 0) {
+      for (int w = 1; w < WK; w++)
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+          for (int b = 0; b < PB; b++)
+            acc[cb][b] += red[(((w - 1) * WCO * WPX + slot) * CB + cb) * PB + b][lane];
+    }
+  }
+
+  // Cross-workgroup split-K: publish the partial tile, take a ticket; the
+  // last workgroup of the tile sums every partial in split order.
+  if (p.splitk > 1) {
+    __shared__ int s_last;
+    constexpr int TILE_VECS = WCO * WPX * CB * PB * 64;
+    Acc *wsb = (Acc *)p.ws + (size_t)tile * p.splitk * TILE_VECS;
+    if (wk == 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int b = 0; b < PB; b++)
+          wsb[(size_t)split * TILE_VECS + ((slot * CB + cb) * PB + b) * 64 + lane] = acc[cb][b];
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned prev = atomicAdd(&p.counters[tile], 1u);
+      s_last = (prev == (unsigned)(p.splitk - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (wk == 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int b = 0; b < PB; b++) {
+          Acc sum = Acc{};
+          for (int sp = 0; sp < p.splitk; sp++) {
+            const Acc v = (sp == split)
+                              ? acc[cb][b]
+                              : __builtin_nontemporal_load(
+                                    &wsb[(size_t)sp * TILE_VECS + ((slot * CB + cb) * PB + b) * 64 + lane]);
+            sum += v;
+          }
+          acc[cb][b] = sum;
+        }
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if (wk != 0) return;
+
+  // Epilogue: bias (+ dequant) + SiLU in registers, masked 16-byte NHWC stores.
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+    const int co0 = (cob0 + cb) * 16 + 4 * g;
+    if (co0 >= p.cout_pad) continue;
+    if constexpr (V::RAW) {
+#pragma unroll
+      for (int b = 0; b < PB; b++)
+        if (mval[b]) *(i32x4 *)((int *)p.out + (size_t)outpix[b] * p.cout_pad + co0) = acc[cb][b];
+    } else {
+      const f32x4 bias = *(const f32x4 *)(p.bias + co0);
+      f32x4 dq = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (V::I8) dq = *(const f32x4 *)(p.dq + co0);
+#pragma unroll
+      for (int b = 0; b < PB; b++) {
+        if (!mval[b]) continue;
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float z;
+          if constexpr (V::I8)
+            z = (float)acc[cb][b][i] * dq[i] + bias[i];
+          else
+            z = acc[cb][b][i] + bias[i];
+          y[i] = silu_f(z);
+        }
+        *(f32x4 *)((float *)p.out + (size_t)outpix[b] * p.cout_pad + co0) = y;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------- config table --
+// id, CB, PB, WCO, WPX, WK, name
+#define CBS_CONFIG_LIST(X)                 \
+  X(0, 1, 4, 1, 4, 1, "c16p256")           \
+  X(1, 2, 2, 1, 4, 1, "c32p128")           \
+  X(2, 2, 2, 2, 2, 1, "c64p64")            \
+  X(3, 4, 2, 1, 4, 1, "c64p128")           \
+  X(4, 4, 2, 2, 2, 1, "c128p64")           \
+  X(5, 4, 4, 2, 2, 1, "c128p128")          \
+  X(6, 2, 2, 1, 1, 4, "c32p32k4")          \
+  X(7, 4, 1, 1, 1, 4, "c64p16k4")          \
+  X(8, 1, 4, 1, 1, 4, "c16p64k4")          \
+  X(9, 2, 1, 1, 1, 4, "c32p16k4")          \
+  X(10, 1, 2, 1, 2, 2, "c16p64k2")         \
+  X(11, 2, 2, 2, 1, 2, "c64p32k2")
+
+static const KernelConfig kConfigs[] = {
+#define X(id, cb, pb, wco, wpx, wk, name) {cb, pb, wco, wpx, wk, name},
+    CBS_CONFIG_LIST(X)
+#undef X
+};
+
+int num_configs() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
+const KernelConfig &config(int i) { return kConfigs[i]; }
+
+template <int VAR, int CB, int PB, int WCO, int WPX, int WK>
+static hipError_t launch_one(const ConvParams &p, hipStream_t stream) {
+  const unsigned grid = (unsigned)p.px_tiles * (unsigned)p.co_tiles * (unsigned)p.splitk;
+  hipLaunchKernelGGL((conv_igemm<VAR, CB, PB, WCO, WPX, WK>), dim3(grid), dim3(64 * WCO * WPX * WK), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int VAR>
+static hipError_t launch_var(int cfg, const ConvParams &p, hipStream_t stream) {
+  switch (cfg) {
+#define X(id, cb, pb, wco, wpx, wk, name) \
+  case id:                                \
+    return launch_one<VAR, cb, pb, wco, wpx, wk>(p, stream);
+    CBS_CONFIG_LIST(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_conv(int var, int cfg, const ConvParams &p, hipStream_t stream) {
+  switch (var) {
+    case VAR_F32: return launch_var<VAR_F32>(cfg, p, stream);
+    case VAR_I8_C16: return launch_var<VAR_I8_C16>(cfg, p, stream);
+    case VAR_I8_C4: return launch_var<VAR_I8_C4>(cfg, p, stream);
+    case VAR_I8_C16_RAW: return launch_var<VAR_I8_C16_RAW>(cfg, p, stream);
+    case VAR_I8_C4_RAW: return launch_var<VAR_I8_C4_RAW>(cfg, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ------------------------------------------------------ graph-entry packs --
+// One thread per (pixel, 4-channel group); consecutive threads take
+// consecutive pixels so the NCHW plane reads are coalesced.
+__global__ __launch_bounds__(256) void pack_nhwc_f32_kernel(const float *__restrict__ x,
+                                                            float *__restrict__ y, int n, int c, int hw,
+                                                            int c_pad) {
+  const long total = (long)n * hw * (c_pad >> 2);
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const long npix = (long)n * hw;
+  const int q = (int)(idx / npix);
+  const long pix = idx - (long)q * npix;
+  const int b = (int)(pix / hw);
+  const int i = (int)(pix - (long)b * hw);
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int ch = 4 * q + e;
+    v[e] = ch < c ? x[((long)b * c + ch) * hw + i] : 0.0f;
+  }
+  *(f32x4 *)(y + pix * c_pad + 4 * q) = v;
+}
+
+__global__ __launch_bounds__(256) void quantize_nhwc_i8_kernel(const float *__restrict__ x,
+                                                               int8_t *__restrict__ y, float s_x, int n,
+                                                               int c, int hw, int c_pad) {
+  const long total = (long)n * hw * (c_pad >> 2);
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const long npix = (long)n * hw;
+  const int q = (int)(idx / npix);
+  const long pix = idx - (long)q * npix;
+  const int b = (int)(pix / hw);
+  const int i = (int)(pix - (long)b * hw);
+  unsigned word = 0;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int ch = 4 * q + e;
+    int qv = 0;
+    if (ch < c) {
+      // fp32 division, correctly rounded, then round half to even and clamp
+      const float t = __fdiv_rn(x[((long)b * c + ch) * hw + i], s_x);
+      float rr = rintf(t);
+      rr = fminf(fmaxf(rr, -127.0f), 127.0f);
+      qv = (int)rr;
+    }
+    word |= ((unsigned)(qv & 0xff)) << (8 * e);
+  }
+  *(unsigned *)(y + pix * c_pad + 4 * q) = word;
+}
+
+hipError_t launch_pack_nhwc_f32(const float *x, float *y, int n, int c, int hw, int c_pad,
+                                hipStream_t stream) {
+  const long total = (long)n * hw * (c_pad >> 2);
+  if (total == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(pack_nhwc_f32_kernel, dim3(grid), dim3(256), 0, stream, x, y, n, c, hw, c_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_nhwc_i8(const float *x, int8_t *y, float s_x, int n, int c, int hw,
+                                   int c_pad, hipStream_t stream) {
+  const long total = (long)n * hw * (c_pad >> 2);
+  if (total == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(quantize_nhwc_i8_kernel, dim3(grid), dim3(256), 0, stream, x, y, s_x, n, c, hw,
+                     c_pad);
+  return hipGetLastError();
+}
+
+}  // namespace cbs

@@ -1,0 +1,214 @@
+/*
+ * cbs.h -- C ABI of libcbs, fused Conv2d + folded BatchNorm + SiLU ("cbs") for
+ * AMD Instinct MI355X (gfx950), in FP32 and INT8.
+ *
+ * The operation (cited from the pages it comes from):
+ *   - "YOLO26N Inference Optimisation" (vision-rs docs), section "nsys
+ *     kernel-level breakdown" and "Key observations" 1-3: one fused
+ *     convolution + batch norm + SiLU op is where the inference time goes;
+ *     section "Baseline benchmark": batch norm is folded into the weights at
+ *     load; section "Improvements" #1 and #3: one code path with a tile chosen
+ *     per layer shape; section "NHWC migration": NHWC activations, weights as
+ *     [C_out][kH][kW][C_in], the convolution as an implicit GEMM
+ *     A[N*OH*OW, C_in*kH*kW] x B[C_in*kH*kW, C_out]; section "Bug fixed: TMA
+ *     overflow": tail tiles must never write past the logical output row.
+ *   - "Edge optimisation of YOLO26" (edge-optimization README), "Highlights"
+ *     and "Design notes": INT8 with one symmetric weight scale per output
+ *     channel and one percentile-calibrated activation scale per tensor.
+ *
+ * Per output element (n, oh, ow, co), with x~ the zero-padded input:
+ *   conv = sum_{ci,i,j} W'[co,ci,i,j] * x~[n, oh*s - p + i, ow*s - p + j, ci]
+ *   y    = SiLU(conv + b'[co]),  SiLU(z) = z / (1 + exp(-z))
+ * where, folded at create time in double precision,
+ *   sc[co] = gamma[co] / sqrt(var[co] + eps),  W' = W * sc,  b' = beta - mean * sc.
+ * INT8 (dtype CBS_I8):
+ *   s_w[co] = max|W'[co,:]| / 127 (1 for an all-zero channel),
+ *   q_w = clamp(rne(W' / s_w), -127, 127)                        (double)
+ *   q_x = clamp(rne(fp32(x / s_x)), -127, 127)                   (fp32 divide)
+ *   acc = sum q_w * q_x                                          (exact int32)
+ *   y   = SiLU(float(acc) * f[co] + b'[co]),  f[co] = fp32(s_x * s_w[co])
+ *
+ * Layouts (all device buffers are caller-owned and dense):
+ *   input  : NHWC [N][H][W][C_in_pad]; fp32 for CBS_F32, int8 for CBS_I8.
+ *            C_in_pad = round_up(C_in, 4); padded lanes must hold 0.
+ *   output : NHWC fp32 [N][OH][out_row_pitch][C_out_pad],
+ *            C_out_pad = round_up(C_out, 4).  Only pixels ow < OW of each row
+ *            are written (padded channels get +0.0); the out_row_pitch - OW
+ *            guard pixels after every row are never touched.
+ *   weights: host OIHW fp32 [C_out][C_in][k][k], copied at create.
+ *
+ * Execution: every cbs_run_* call only enqueues kernels on the given stream
+ * (a hipStream_t passed as void*, NULL = the null stream): no allocation, no
+ * memset, no copy, no synchronisation.  A layer may be run from one stream at
+ * a time (its split-K workspace is per layer); distinct layers may run
+ * concurrently.  Device faults surface at the caller's next synchronisation.
+ *
+ * Errors: every entry point returns a cbs_status; nothing throws or aborts.
+ * cbs_last_error() gives a message for the calling thread's last failure.
+ */
+#ifndef CBS_H_
+#define CBS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t cbs_status;
+#define CBS_OK 0
+#define CBS_EINVAL (-1)       /* bad argument (null pointer, negative size, ...) */
+#define CBS_EUNSUPPORTED (-2) /* valid but not supported (k not in {1,3}, stride not in {1,2}, ...) */
+#define CBS_ENOMEM (-3)       /* device or host allocation failed at create */
+#define CBS_EDEVICE (-4)      /* no usable HIP device, or a HIP runtime call failed */
+#define CBS_ELAUNCH (-5)      /* a kernel launch was rejected */
+
+#define CBS_F32 0
+#define CBS_I8 1
+
+typedef struct cbs_layer cbs_layer; /* opaque: one fused conv layer on one device */
+typedef struct cbs_graph cbs_graph; /* opaque: a captured layer list */
+
+typedef struct cbs_conv_desc {
+    int32_t n;             /* batch, >= 1 */
+    int32_t c_in;          /* input channels, >= 1 */
+    int32_t h, w;          /* input height and width, >= 1 */
+    int32_t c_out;         /* output channels, >= 1 */
+    int32_t k;             /* kernel size: 1 or 3 */
+    int32_t stride;        /* 1 or 2 */
+    int32_t pad;           /* zero padding, 0 <= pad <= k/2 */
+    int32_t dtype;         /* CBS_F32 or CBS_I8 */
+    int32_t out_row_pitch; /* output pixels between consecutive (n, oh) rows, >= OW; 0 means OW */
+    float in_scale;        /* CBS_I8: per-tensor activation scale s_x > 0; ignored for CBS_F32 */
+    float bn_eps;          /* batch-norm epsilon >= 0, used as (double)bn_eps */
+} cbs_conv_desc;
+
+typedef struct cbs_layer_info_t {
+    int32_t c_in_pad, c_out_pad;  /* padded channel counts of input and output */
+    int32_t oh, ow;               /* output height and width */
+    int32_t out_row_pitch;        /* pixels per output row (>= ow) */
+    int32_t dtype;                /* CBS_F32 or CBS_I8 */
+    int64_t in_bytes;             /* size of the input buffer run_layer reads */
+    int64_t out_bytes;            /* size of the output buffer run_layer writes into
+                                     (N*OH*pitch*C_out_pad*4; guards included) */
+    int64_t flops;                /* 2*N*OH*OW*C_out*C_in*k*k (logical channels) */
+    int64_t alg_bytes;            /* N*H*W*C_in*b_in + C_out*C_in*k*k*b_w + N*OH*OW*C_out*4 + 8*C_out */
+    int32_t config;               /* kernel configuration index in use */
+    int32_t splitk;               /* workgroups that share one output tile along K */
+    int32_t grid;                 /* workgroups per launch */
+    int32_t threads;              /* threads per workgroup */
+    char config_name[48];         /* human-readable configuration name */
+} cbs_layer_info_t;
+
+/*
+ * Create a layer: validate the descriptor, fold batch norm (double), re-lay
+ * the weights into MFMA fragment order, quantise them for CBS_I8, pick the
+ * kernel configuration for this shape from the tile table, and copy
+ * everything to the current HIP device.  Host arrays: w_oihw has
+ * C_out*C_in*k*k floats; gamma, beta, mean, var have C_out floats each; all
+ * are copied and may be freed afterwards.  On success *out owns device memory
+ * until cbs_destroy_layer.  Errors: CBS_EINVAL, CBS_EUNSUPPORTED, CBS_ENOMEM,
+ * CBS_EDEVICE (no device).  *out is set to NULL on failure.
+ */
+cbs_status cbs_create_layer(const cbs_conv_desc *desc, const float *w_oihw, const float *gamma,
+                            const float *beta, const float *mean, const float *var,
+                            cbs_layer **out);
+
+/*
+ * Same as cbs_create_layer with batch norm already folded into a per-channel
+ * scale and bias: W' = W * scale[co] (double), b' = bias[co].  scale = 1,
+ * bias = b gives a plain convolution + bias + SiLU.
+ */
+cbs_status cbs_create_layer_folded(const cbs_conv_desc *desc, const float *w_oihw,
+                                   const float *scale, const float *bias, cbs_layer **out);
+
+/* Release a layer's device and host memory.  NULL is a no-op.  The caller
+ * must make sure no enqueued run of the layer is still pending. */
+void cbs_destroy_layer(cbs_layer *layer);
+
+/*
+ * Enqueue the fused layer on `stream`: in (device, layout above) -> out
+ * (device, layout above).  in and out must not overlap.  Errors: CBS_EINVAL
+ * (null layer or buffer), CBS_ELAUNCH.
+ */
+cbs_status cbs_run_layer(const cbs_layer *layer, const void *in, void *out, void *stream);
+
+/*
+ * Enqueue layers[0..n-1] in order on one stream, layer i reading ins[i] and
+ * writing outs[i] (any of them may alias another layer's output to chain
+ * layers).  Stops at the first failing launch and returns its status.
+ */
+cbs_status cbs_run_layer_list(cbs_layer *const *layers, int32_t n, const void *const *ins,
+                              void *const *outs, void *stream);
+
+/*
+ * Capture the same layer list, with these buffers, into a HIP graph (stream
+ * capture on `stream`, which must not be capturing already), instantiate it
+ * and return it in *out.  The layers and buffers must outlive the graph.
+ */
+cbs_status cbs_graph_create(cbs_layer *const *layers, int32_t n, const void *const *ins,
+                            void *const *outs, void *stream, cbs_graph **out);
+/* Enqueue one replay of a captured list on `stream`. */
+cbs_status cbs_graph_launch(const cbs_graph *graph, void *stream);
+/* Release a captured list.  NULL is a no-op. */
+void cbs_graph_destroy(cbs_graph *graph);
+
+/* Fill *info with the layer's shapes, buffer sizes, work and configuration. */
+cbs_status cbs_layer_info(const cbs_layer *layer, cbs_layer_info_t *info);
+
+/*
+ * Override the kernel configuration chosen at create: config in
+ * [0, cbs_num_configs()), splitk >= 1 workgroups along K (0 keeps the
+ * default for that config).  Returns CBS_EUNSUPPORTED when the configuration
+ * cannot run this layer (the layer is then unchanged).  Used by tests, which
+ * force every configuration on every shape, and by the offline tile sweep.
+ */
+cbs_status cbs_layer_set_config(cbs_layer *layer, int32_t config, int32_t splitk);
+int32_t cbs_num_configs(void);
+/* Name of configuration i, or NULL when i is out of range.  Static storage. */
+const char *cbs_config_name(int32_t config);
+
+/* Message for the calling thread's last failure ("" if none).  Thread-local storage. */
+const char *cbs_last_error(void);
+
+/*
+ * Graph-entry layout change: NCHW fp32 [n][c][h][w] -> NHWC fp32
+ * [n][h][w][c_pad] with lanes c..c_pad-1 set to 0.  c_pad >= c, c_pad % 4 == 0.
+ */
+cbs_status cbs_pack_nhwc_f32(const float *nchw, float *nhwc, int32_t n, int32_t c, int32_t h,
+                             int32_t w, int32_t c_pad, void *stream);
+
+/*
+ * Graph-entry layout change with per-tensor INT8 quantisation:
+ * q = clamp(rne(fp32(x / s_x)), -127, 127), NCHW fp32 -> NHWC int8
+ * [n][h][w][c_pad], padded lanes 0.  s_x > 0, c_pad >= c, c_pad % 4 == 0.
+ */
+cbs_status cbs_quantize_nhwc_i8(const float *nchw, int8_t *nhwc, float s_x, int32_t n, int32_t c,
+                                int32_t h, int32_t w, int32_t c_pad, void *stream);
+
+/*
+ * Test hook (CBS_I8 layers only): run the integer part of the layer and store
+ * the raw int32 accumulators, NHWC [N][OH][out_row_pitch][C_out_pad], instead
+ * of the fp32 epilogue.  Same guard-pixel rule as cbs_run_layer.
+ */
+cbs_status cbs_run_layer_raw_acc(const cbs_layer *layer, const void *in, int32_t *acc, void *stream);
+
+/*
+ * Test hook: copy the layer's host-side quantised weights (CBS_I8) as OIHW
+ * int8 [C_out][C_in][k][k] and the per-channel scales s_w (double [C_out]).
+ * Either pointer may be NULL.  CBS_EINVAL for a CBS_F32 layer.
+ */
+cbs_status cbs_get_qweights(const cbs_layer *layer, int8_t *q_oihw, double *s_w);
+
+/*
+ * Test hook: copy the folded weights W' (OIHW, as the fp32 values the kernel
+ * uses for CBS_F32) and the folded bias b' (fp32 [C_out]).  Either may be NULL.
+ */
+cbs_status cbs_get_folded(const cbs_layer *layer, float *w_oihw, float *bias);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CBS_H_ */
