@@ -97,27 +97,27 @@ class ListBench:
 
     def time_layers(self, min_ms=2.0, reps=5):
         """Per layer: median over `reps` of (event pair around R back-to-back launches)/R,
-        on the stream the library launches on (torch's current stream)."""
+        on the stream the library launches on (torch's current stream).  The R
+        launches are enqueued by one cbs_run_layer_list call, so the host loop is C,
+        not Python."""
         torch, cbs = self.torch, self.cbs
         res = []
         for layer, xin, out in zip(self.layers, self.ins, self.outs):
-            for _ in range(3):
-                cbs.cbs_run_layer(layer, xin, out)
+            cbs.cbs_run_layer_list([layer] * 3, [xin] * 3, [out] * 3)
             torch.cuda.synchronize()
             # calibrate R so that one repeat takes >= min_ms
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(10):
-                cbs.cbs_run_layer(layer, xin, out)
+            cbs.cbs_run_layer_list([layer] * 10, [xin] * 10, [out] * 10)
             e1.record()
             torch.cuda.synchronize()
             per = max(e0.elapsed_time(e1) / 10, 1e-4)
             r = int(min(2000, max(10, min_ms / per)))
+            ls, ins, outs = [layer] * r, [xin] * r, [out] * r
             ts = []
             for _ in range(reps):
                 e0.record()
-                for _ in range(r):
-                    cbs.cbs_run_layer(layer, xin, out)
+                cbs.cbs_run_layer_list(ls, ins, outs)
                 e1.record()
                 torch.cuda.synchronize()
                 ts.append(e0.elapsed_time(e1) / r)
@@ -165,6 +165,34 @@ def cpu_baseline(W, max_seconds=30.0):
             "sample": sample, "seconds": round(t_total, 3), "us_per_list": round(t_total * 1e6 * len(layers) / done, 1)}
 
 
+def profile_layer(cbs, W, torch, name, dtype, batch, launches):
+    """Run only one layer of the list `launches` times back to back (for a profiler
+    run on exactly that kernel), then a plain device copy of known size (the
+    reference for scaling the profiler's byte counters).  Prints one JSON line."""
+    b = ListBench(cbs, W, torch, dtype, batch)
+    i = [s.name for s in b.specs].index(name)
+    layer, xin, out = b.layers[i], b.ins[i], b.outs[i]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cbs.cbs_run_layer_list([layer] * 10, [xin] * 10, [out] * 10)
+    torch.cuda.synchronize()
+    e0.record()
+    cbs.cbs_run_layer_list([layer] * launches, [xin] * launches, [out] * launches)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / launches * 1e3
+    copy_bytes = 256 << 20
+    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    info = b.infos[i]
+    print(json.dumps({"layer": name, "batch": batch, "dtype": "int8" if dtype else "f32", "launches": launches,
+                      "us_per_launch": round(us, 3), "config": info["config_name"], "grid": info["grid"],
+                      "flops": info["flops"], "alg_bytes": info["alg_bytes"], "copy_bytes_each": copy_bytes,
+                      "copies": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +200,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="batch-1 FP32 only")
+    ap.add_argument("--only-layer", default=None, help="profile mode: run only this layer of the list")
+    ap.add_argument("--dtype", default="f32", choices=["f32", "int8"], help="profile mode dtype")
+    ap.add_argument("--batch", type=int, default=1, help="profile mode batch")
+    ap.add_argument("--launches", type=int, default=200, help="profile mode launches")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the batch-16 list shards over images with no "
@@ -185,6 +217,10 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     log("device: %s, %d CUs" % (props.name, props.multi_processor_count))
+    if args.only_layer:
+        profile_layer(cbs, W, torch, args.only_layer, cbs.CBS_I8 if args.dtype == "int8" else cbs.CBS_F32,
+                      args.batch, args.launches)
+        return
 
     results = {}
     combos = [("f32", cbs.CBS_F32, 1)] if args.quick else [("f32", cbs.CBS_F32, 1), ("int8", cbs.CBS_I8, 1),
@@ -223,6 +259,7 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
     roof["kernel"] = "conv_igemm %s (%s)" % (dom["layer"], dom["config"])
+    roof["layer"] = dom["layer"]
     roof["us_per_launch"] = dom["us"]
 
     line = {"metric": METRIC, "value": round(head["flops"] / (head["ms_per_step"] * 1e-3) / 1e12, 4),

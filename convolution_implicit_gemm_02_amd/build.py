@@ -30,10 +30,38 @@ def _run(cmd):
     subprocess.run(cmd, check=True)
 
 
+def check_mfma_guards(hipcc: str) -> None:
+    """Fail the build if any MFMA of the conv kernels sits in an EXEC-masked
+    region.  MFMA ignores EXEC, so an MFMA under a per-lane condition would
+    still execute for the whole wave; every MFMA guard must be a scalar
+    (wave-uniform) branch.  Scans the device assembly of this build."""
+    import re
+    asm = os.path.join(BUILD_DIR, "cbs_kernels.s")
+    _run([hipcc, "--cuda-device-only", "-S", os.path.join(CSRC, "cbs_kernels.hip"), "-o", asm, "-O3"]
+         + COMMON + DEVICE_FLAGS)
+    text = open(asm).read()
+    bad = []
+    for name in re.findall(r"^(_ZN3cbs10conv_igemm\w+):", text, re.M):
+        body = text[text.index(name + ":"):text.index(".Lfunc_end", text.index(name + ":"))]
+        masked = False
+        for line in body.split("\n"):
+            t = line.strip()
+            if re.match(r"s_(and|andn2|xor|or)_saveexec", t):
+                masked = True
+            elif t.startswith("s_or_b64 exec") or t.startswith("s_mov_b64 exec"):
+                masked = False
+            elif t.startswith("v_mfma") and masked:
+                bad.append(name)
+                break
+    if bad:
+        raise RuntimeError("MFMA inside an EXEC-masked region in: %s" % ", ".join(bad))
+
+
 def build(verbose: bool = True) -> str:
     """Compile every source and link libcbs.so.  Always recompiles."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     hipcc = _hipcc()
+    check_mfma_guards(hipcc)
     k_obj = os.path.join(BUILD_DIR, "cbs_kernels.o")
     h_obj = os.path.join(BUILD_DIR, "cbs_host.o")
     # kernels: -O3, device code without packed fp32

@@ -166,11 +166,13 @@ Choice choose(const cbs_layer *L) {
         e.config < num_configs() && config_fits(L, e.config, e.splitk))
       return {e.config, e.splitk};
   }
-  // 2) the cost model
+  // 2) the cost model.  Cross-workgroup split-K is never picked here: its
+  // agent-scope release (an L2 write-back on a multi-XCD part) costs more than
+  // it saves; only the measured table may select it.
   Choice best{2, 1};
   double best_cost = 1e300;
   for (int cfg = 0; cfg < num_configs(); cfg++) {
-    for (int sk : {1, 2, 3, 4, 6, 8, 12, 16}) {
+    for (int sk : {1}) {
       if (!config_fits(L, cfg, sk)) continue;
       const double cost = model_cost(L, cfg, sk);
       if (cost < best_cost * 0.999) {

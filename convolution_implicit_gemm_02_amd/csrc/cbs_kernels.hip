@@ -79,13 +79,16 @@ __device__ __forceinline__ Chunk decode_chunk(const ConvParams &p, int c) {
   return r;
 }
 
-template <int VAR, int CB, int PB, int WCO, int WPX, int WK>
+template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
 __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) {
   using V = Var<VAR>;
   using Frag = typename V::Frag;
   using Acc = typename V::Acc;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The wave index is made explicitly wave-uniform: every condition that
+  // guards an MFMA below depends only on it, so it compiles to a scalar
+  // branch.  (MFMA ignores EXEC; an MFMA under a per-lane mask would run.)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wk = wave % WK;
   const int wco = (wave / WK) % WCO;
   const int wpx = wave / (WK * WCO);
@@ -170,33 +173,45 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
 #pragma unroll
     for (int b = 0; b < PB; b++) acc[cb][b] = Acc{};
 
+  // Independent accumulators are interleaved so consecutive MFMAs never wait
+  // on each other's result.
   auto mma = [&](const Frag(&aa)[CB], const Frag(&bb)[PB]) {
+    if constexpr (!V::I8) {
 #pragma unroll
-    for (int cb = 0; cb < CB; cb++)
+      for (int j = 0; j < 4; j++)
 #pragma unroll
-      for (int b = 0; b < PB; b++) {
-        if constexpr (!V::I8) {
+        for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-          for (int j = 0; j < 4; j++)
+          for (int b = 0; b < PB; b++)
             acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[cb][j], bb[b][j], acc[cb][b], 0, 0, 0);
-        } else {
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int b = 0; b < PB; b++)
           acc[cb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[cb], bb[b], acc[cb][b], 0, 0, 0);
-        }
-      }
+    }
   };
 
-  // Main loop, two register sets in ping-pong: the loads of step s+WK are in
-  // flight while the MFMAs of step s run.
+  // Main loop: a ring of PF register sets keeps the loads of the next PF K
+  // steps of this wave in flight while the MFMAs of the current step run
+  // (small layers are latency-bound otherwise).  Loads past the wave's last
+  // step are clamped onto it, so every iteration issues the same loads.
   {
-    Frag a0[CB], b0[PB], a1[CB], b1[PB];
-    int s = s_begin + wk;
-    if (s < s_end) load(s, a0, b0);
-    for (; s < s_end; s += 2 * WK) {
-      const bool h1 = s + WK < s_end;
-      if (h1) load(s + WK, a1, b1);
-      mma(a0, b0);
-      if (s + 2 * WK < s_end) load(s + 2 * WK, a0, b0);
-      if (h1) mma(a1, b1);
+    const int s0 = s_begin + wk;
+    if (s0 < s_end) {
+      const int s_last = s0 + ((s_end - 1 - s0) / WK) * WK;
+      Frag a[PF][CB], b[PF][PB];
+#pragma unroll
+      for (int i = 0; i < PF; i++) load(min(s0 + i * WK, s_last), a[i], b[i]);
+      for (int s = s0; s < s_end; s += PF * WK) {
+#pragma unroll
+        for (int i = 0; i < PF; i++) {
+          const int si = s + i * WK;
+          if (si < s_end) mma(a[i], b[i]);
+          load(min(si + PF * WK, s_last), a[i], b[i]);
+        }
+      }
     }
   }
 
@@ -298,23 +313,27 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
 }
 
 // ----------------------------------------------------------- config table --
-// id, CB, PB, WCO, WPX, WK, name
-#define CBS_CONFIG_LIST(X)                 \
-  X(0, 1, 4, 1, 4, 1, "c16p256")           \
-  X(1, 2, 2, 1, 4, 1, "c32p128")           \
-  X(2, 2, 2, 2, 2, 1, "c64p64")            \
-  X(3, 4, 2, 1, 4, 1, "c64p128")           \
-  X(4, 4, 2, 2, 2, 1, "c128p64")           \
-  X(5, 4, 4, 2, 2, 1, "c128p128")          \
-  X(6, 2, 2, 1, 1, 4, "c32p32k4")          \
-  X(7, 4, 1, 1, 1, 4, "c64p16k4")          \
-  X(8, 1, 4, 1, 1, 4, "c16p64k4")          \
-  X(9, 2, 1, 1, 1, 4, "c32p16k4")          \
-  X(10, 1, 2, 1, 2, 2, "c16p64k2")         \
-  X(11, 2, 2, 2, 1, 2, "c64p32k2")
+// id, CB, PB, WCO, WPX, WK, PF (prefetch depth), name
+#define CBS_CONFIG_LIST(X)                    \
+  X(0, 1, 4, 1, 4, 1, 4, "c16p256")           \
+  X(1, 2, 2, 1, 4, 1, 4, "c32p128")           \
+  X(2, 2, 2, 2, 2, 1, 4, "c64p64")            \
+  X(3, 4, 2, 1, 4, 1, 2, "c64p128")           \
+  X(4, 4, 2, 2, 2, 1, 2, "c128p64")           \
+  X(5, 4, 4, 2, 2, 1, 2, "c128p128")          \
+  X(6, 2, 2, 1, 1, 4, 4, "c32p32k4")          \
+  X(7, 4, 1, 1, 1, 4, 4, "c64p16k4")          \
+  X(8, 1, 4, 1, 1, 4, 4, "c16p64k4")          \
+  X(9, 2, 1, 1, 1, 4, 4, "c32p16k4")          \
+  X(10, 1, 2, 1, 2, 2, 4, "c16p64k2")         \
+  X(11, 2, 2, 2, 1, 2, 4, "c64p32k2")         \
+  X(12, 1, 1, 1, 1, 4, 4, "c16p16k4")         \
+  X(13, 2, 1, 1, 1, 8, 4, "c32p16k8")         \
+  X(14, 1, 2, 1, 1, 8, 4, "c16p32k8")         \
+  X(15, 1, 2, 1, 1, 4, 4, "c16p32k4")
 
 static const KernelConfig kConfigs[] = {
-#define X(id, cb, pb, wco, wpx, wk, name) {cb, pb, wco, wpx, wk, name},
+#define X(id, cb, pb, wco, wpx, wk, pf, name) {cb, pb, wco, wpx, wk, name},
     CBS_CONFIG_LIST(X)
 #undef X
 };
@@ -322,10 +341,10 @@ static const KernelConfig kConfigs[] = {
 int num_configs() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
 const KernelConfig &config(int i) { return kConfigs[i]; }
 
-template <int VAR, int CB, int PB, int WCO, int WPX, int WK>
+template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
 static hipError_t launch_one(const ConvParams &p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.px_tiles * (unsigned)p.co_tiles * (unsigned)p.splitk;
-  hipLaunchKernelGGL((conv_igemm<VAR, CB, PB, WCO, WPX, WK>), dim3(grid), dim3(64 * WCO * WPX * WK), 0,
+  hipLaunchKernelGGL((conv_igemm<VAR, CB, PB, WCO, WPX, WK, PF>), dim3(grid), dim3(64 * WCO * WPX * WK), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -333,9 +352,9 @@ static hipError_t launch_one(const ConvParams &p, hipStream_t stream) {
 template <int VAR>
 static hipError_t launch_var(int cfg, const ConvParams &p, hipStream_t stream) {
   switch (cfg) {
-#define X(id, cb, pb, wco, wpx, wk, name) \
-  case id:                                \
-    return launch_one<VAR, cb, pb, wco, wpx, wk>(p, stream);
+#define X(id, cb, pb, wco, wpx, wk, pf, name) \
+  case id:                                    \
+    return launch_one<VAR, cb, pb, wco, wpx, wk, pf>(p, stream);
     CBS_CONFIG_LIST(X)
 #undef X
     default:

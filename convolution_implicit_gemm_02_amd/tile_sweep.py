@@ -1,0 +1,139 @@
+"""Offline per-shape tile sweep: time every kernel configuration on every layer
+shape of the workloads, on the device, and write the winners to
+csrc/tile_table.inc (rebuild libcbs afterwards).
+
+The vision-rs "YOLO26N Inference Optimisation" page ranks per-shape tile
+autotuning first among its improvements (section "Improvements", #1): one
+fixed tile spans 5 to 556 us across the call sites.  This is that step, done
+once per device generation, offline, with the result compiled into the library.
+
+usage: python -m convolution_implicit_gemm_02_amd.tile_sweep [--out PATH] [--json PATH] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_OUT = os.path.join(PKG_DIR, "csrc", "tile_table.inc")
+
+HEADER = """// tile_table.inc -- per-shape kernel configuration chosen by measurement.
+// Written by convolution_implicit_gemm_02_amd/tile_sweep.py from a sweep of
+// every configuration (split-K 1, and 2/4 for the smallest grids) on %s;
+// shapes not listed fall back to the cost model in cbs_host.cpp.
+// Key: (n, c_in, c_out, h, w, k, stride, dtype) -> (config, splitk).
+struct TileEntry {
+  int n, c_in, c_out, h, w, k, s, dtype, config, splitk;
+};
+static const TileEntry kTileTable[] = {
+"""
+
+
+def sweep_shapes(W):
+    shapes = []
+    for name in ("single", "ragged", "stem", "yolo26n"):
+        for spec in W.WORKLOADS[name]():
+            for n in ((1, 16) if name in ("yolo26n", "ragged") else (1,)):
+                shapes.append((spec, n))
+    seen, out = set(), []
+    for spec, n in shapes:
+        key = (n, spec.c_in, spec.c_out, spec.h, spec.w, spec.k, spec.stride)
+        if key not in seen:
+            seen.add(key)
+            out.append((spec, n))
+    return out
+
+
+def time_layer(cbs, torch, layer, xin, out, min_ms=1.0, reps=3):
+    cbs.cbs_run_layer_list([layer] * 3, [xin] * 3, [out] * 3)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cbs.cbs_run_layer_list([layer] * 10, [xin] * 10, [out] * 10)
+    e1.record()
+    torch.cuda.synchronize()
+    per = max(e0.elapsed_time(e1) / 10, 1e-3)
+    r = int(min(1000, max(10, min_ms / per)))
+    ts = []
+    for _ in range(reps):
+        e0.record()
+        cbs.cbs_run_layer_list([layer] * r, [xin] * r, [out] * r)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / r * 1e3)
+    return float(np.median(ts))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=DEFAULT_OUT)
+    ap.add_argument("--json", default=None)
+    ap.add_argument("--quick", action="store_true", help="batch-1 shapes only")
+    args = ap.parse_args()
+
+    import torch
+    from convolution_implicit_gemm_02_amd import cbs
+    from convolution_implicit_gemm_02_amd import workloads as W
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    props = torch.cuda.get_device_properties(0)
+    name = "%s (%s)" % (props.name, getattr(props, "gcnArchName", "?").split(":")[0])
+    rng = np.random.default_rng(0)
+    entries, report = [], []
+    shapes = sweep_shapes(W)
+    if args.quick:
+        shapes = [s for s in shapes if s[1] == 1]
+    t_start = time.time()
+    for si, (spec, n) in enumerate(shapes):
+        w = (rng.standard_normal((spec.c_out, spec.c_in, spec.k, spec.k)) / np.sqrt(spec.c_in * spec.k * spec.k)
+             ).astype(np.float32)
+        ones, zeros = np.ones(spec.c_out, np.float32), np.zeros(spec.c_out, np.float32)
+        for dtype in (cbs.CBS_F32, cbs.CBS_I8):
+            desc = cbs.make_desc(n, spec.c_in, spec.h, spec.w, spec.c_out, spec.k, spec.stride, spec.pad, dtype, 0,
+                                 0.05, W.BN_EPS)
+            layer = cbs.cbs_create_layer(desc, w, ones, zeros, zeros, ones)
+            info = cbs.cbs_layer_info(layer)
+            xin = torch.zeros(info["in_bytes"], dtype=torch.int8, device=dev)
+            out = torch.empty(info["out_bytes"] // 4, dtype=torch.float32, device=dev)
+            results = []
+            for cfg in range(cbs.cbs_num_configs()):
+                for sk in (1, 2, 4):
+                    if sk > 1 and info["grid"] >= 128:
+                        continue
+                    try:
+                        cbs.cbs_layer_set_config(layer, cfg, sk)
+                    except cbs.CbsError:
+                        continue
+                    results.append((time_layer(cbs, torch, layer, xin, out), cfg, sk))
+            results.sort()
+            best_us, best_cfg, best_sk = results[0]
+            entries.append((n, spec.c_in, spec.c_out, spec.h, spec.w, spec.k, spec.stride, dtype, best_cfg, best_sk,
+                            best_us, spec.name))
+            report.append({"layer": spec.name, "n": n, "dtype": "int8" if dtype else "f32", "best_us": best_us,
+                           "config": cbs.cbs_config_name(best_cfg), "splitk": best_sk,
+                           "all": [(round(t, 3), cbs.cbs_config_name(c), s) for t, c, s in results[:6]]})
+            del layer, xin, out
+        print("[%3d/%d] %-14s n=%-2d f32 %s/%d %.2f us | int8 %s/%d %.2f us  (%.0f s)" % (
+            si + 1, len(shapes), spec.name, n, report[-2]["config"], report[-2]["splitk"], report[-2]["best_us"],
+            report[-1]["config"], report[-1]["splitk"], report[-1]["best_us"], time.time() - t_start), flush=True)
+
+    with open(args.out, "w") as f:
+        f.write(HEADER % name)
+        for e in entries:
+            f.write("    {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d},  // %s %s %.2f us\n" % (
+                e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7], e[8], e[9], e[11], "int8" if e[7] else "f32", e[10]))
+        f.write("    {0, 0, 0, 0, 0, 0, 0, 0, 0, 1},  // sentinel: n == 0 never matches\n};\n")
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(report, f, indent=1)
+    print("wrote %s (%d entries)" % (args.out, len(entries)), flush=True)
+
+
+if __name__ == "__main__":
+    sys.path.insert(0, os.path.dirname(PKG_DIR))
+    main()
