@@ -142,6 +142,30 @@ def layer_rows(bench, us):
     return rows
 
 
+KERNEL_SOURCES = ("convolution_implicit_gemm_02_amd/csrc/cbs_kernels.hip",
+                  "convolution_implicit_gemm_02_amd/csrc/cbs_host.cpp",
+                  "convolution_implicit_gemm_02_amd/csrc/cbs_internal.h",
+                  "convolution_implicit_gemm_02_amd/csrc/tile_table.inc")
+
+
+def measured_traffic(layer):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (profiles/traffic_dominant.json), scaled by
+    the counters of a plain copy of known size.  None when that summary is for
+    another layer or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_dominant.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("layer") != layer or rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec["traffic_bytes"]
+
+
 def cpu_baseline(W, max_seconds=30.0):
     """The oracle (plain C, double accumulation, OpenMP) on the batch-1 FP32 list:
     every layer in list order until the whole list is done or the time budget
@@ -257,7 +281,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(dom["flops"] / (dom["us"] * 1e-6) / 1e12, 3),
                 "peak": PEAK_FP32 / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom["layer"])
     roof["kernel"] = "conv_igemm %s (%s)" % (dom["layer"], dom["config"])
     roof["layer"] = dom["layer"]
     roof["us_per_launch"] = dom["us"]

@@ -359,6 +359,22 @@ def test_int8_extreme_accumulators_fit_int32():
     assert acc[0, 0, 0, 0] == -127 * 127 * 256 * 4
 
 
+def test_int8_epilogue_special_cases():
+    """Dequant + bias + SiLU at points with known values: acc*f + b' = 0, 1, -1
+    lands on the golden SiLU values; f = fp32(s_x * s_w) is exact for powers of two."""
+    g = read_golden("silu_values.txt")
+    s_x = np.float32(0.5)
+    s_w = np.array([0.25, 2.0, 1.0], np.float64)           # f = 0.125, 1.0, 0.5 exactly
+    b = np.array([0.0, -1.0, 1.5], np.float64)
+    acc = np.array([0, 8, 2, 0, -3, -5], np.int32).reshape(1, 3, 1, 2)
+    # z: co0: 0*0.125+0 = 0, 8*0.125+0 = 1 | co1: 2*1-1 = 1, 0-1 = -1 | co2: -3*0.5+1.5 = 0, -5*0.5+1.5 = -1
+    y, f = oracle.epilogue_i8(acc, s_x, s_w, b)
+    assert list(f) == [0.125, 1.0, 0.5]
+    exp = {0.0: g[0, 1], 1.0: g[1, 1], -1.0: g[2, 1]}
+    want = np.array([exp[0.0], exp[1.0], exp[1.0], exp[-1.0], exp[0.0], exp[-1.0]]).reshape(1, 3, 1, 2)
+    assert np.allclose(y, want, rtol=0, atol=1e-16)
+
+
 def test_int8_epilogue_and_composition():
     r = rng(12)
     spec = W.LayerSpec("t", 6, 5, 7, 6, 3, 1, 1)
