@@ -107,6 +107,9 @@ cbs_status validate(const cbs_conv_desc *d) {
   const double out_elems = (double)d->n * oh * pitch * round_up(d->c_out, 4);
   if (in_elems >= 2147483647.0 || out_elems >= 2147483647.0)
     return fail(CBS_EUNSUPPORTED, "tensor above 2^31 elements");
+  // the kernels address the input with 32-bit buffer offsets below 2^31
+  const double in_bytes = in_elems * (d->dtype == CBS_F32 ? 4.0 : 1.0);
+  if (in_bytes >= 2147483648.0 - 64.0) return fail(CBS_EUNSUPPORTED, "input above 2^31 bytes");
   return CBS_OK;
 }
 
@@ -266,6 +269,8 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out) {
   p.splitk = L->splitk;
   p.steps_per_split = ceil_div(L->steps, L->splitk);
   p.co_blocks = L->co_blocks;
+  p.x_bytes = (unsigned)((size_t)L->d.n * L->d.h * L->d.w * L->cin_pad * (L->d.dtype == CBS_F32 ? 4 : 1));
+  p.w_bytes = (unsigned)((size_t)L->co_blocks * L->steps * 64 * 16);
   tiles_of(L, L->config, &p.px_tiles, &p.co_tiles);
   return p;
 }
@@ -384,6 +389,10 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   // ---- weights in MFMA fragment order: [co_block][step][lane][16 bytes]
   // lane = 16*g + r: output channel co_block*16 + r; chunks (4*step + g)*vec + j.
   const size_t frag_bytes = (size_t)L->co_blocks * L->steps * 64 * 16;
+  if (frag_bytes >= ((size_t)1 << 31) - 2048) {
+    delete L;
+    return fail(CBS_EUNSUPPORTED, "weights above 2^31 bytes");
+  }
   std::vector<unsigned char> frag(frag_bytes, 0);
   for (int cob = 0; cob < L->co_blocks; cob++)
     for (int s = 0; s < L->steps; s++)

@@ -46,6 +46,8 @@ struct ConvParams {
   int splitk;            // workgroups per output tile along K
   int co_blocks;         // 16-channel output blocks holding real channels
   int px_tiles, co_tiles;// workgroup tiles along pixels and output channels
+  unsigned x_bytes;      // bytes of the input buffer (buffer-load range)
+  unsigned w_bytes;      // bytes of the fragment-ordered weights (buffer-load range)
 };
 
 int num_configs();

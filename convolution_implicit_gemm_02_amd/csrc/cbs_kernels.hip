@@ -61,6 +61,12 @@ template <> struct Var<VAR_I8_C4_RAW> {
   static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = true;
 };
 
+// Buffer resource word 3 (data format) for the gfx9 family, and an offset
+// that every buffer of this library lies below (sizes are checked < 2^31 at
+// create): loads at it return zero.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr unsigned kOutOfRange = 0x80000000u;
+
 __device__ __forceinline__ float silu_f(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
 
 // Decoded K chunk: tap offset (dy, dx) and first channel.
@@ -124,19 +130,38 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     outpix[b] = (n * p.OH + oh) * p.pitch + ow;
   }
   const int cob0 = (co_tile * WCO + wco) * CB;
+  // Epilogue operands are fetched now, so their latency overlaps the main loop
+  // (out-of-range channels read as zero).
+  f32x4 ep_bias[CB], ep_dq[CB];
+  {
+    const __amdgpu_buffer_rsrc_t br =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t dr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.dq, 0, V::I8 ? (int)(p.co_blocks * 64) : 0, kRsrcWord3);
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+      const unsigned off = (unsigned)(((cob0 + cb) * 16 + 4 * g) * 4);
+      ep_bias[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ep_dq[cb] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (!V::RAW) ep_bias[cb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0));
+      if constexpr (V::I8 && !V::RAW) ep_dq[cb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, off, 0, 0));
+    }
+  }
   const int s_begin = split * p.steps_per_split;
   const int s_end = min(p.steps, s_begin + p.steps_per_split);
-  const char *xb = (const char *)p.x;
-  const char *wb = (const char *)p.wfrag;
 
+  // Every operand load is a branch-free buffer load: an out-of-range byte
+  // offset returns zeros, which supplies the image's zero padding, the pixel
+  // tail, the K tail and output-channel blocks past the end without any
+  // condition around a load (so the compiler can count loads in flight and
+  // wait only for the oldest one).
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
   auto load = [&](int s, Frag(&aa)[CB], Frag(&bb)[PB]) {
 #pragma unroll
     for (int cb = 0; cb < CB; cb++) {
-      const int cob = cob0 + cb;
-      if (cob < p.co_blocks)
-        aa[cb] = *(const Frag *)(wb + ((size_t)(cob * p.steps + s) * 64 + lane) * 16);
-      else
-        aa[cb] = Frag{};
+      const unsigned off = ((unsigned)((cob0 + cb) * p.steps + s) * 64u + (unsigned)lane) * 16u;
+      aa[cb] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
     }
     if constexpr (V::VEC == 1) {
       const Chunk c = decode_chunk(p, s * 4 + g);
@@ -145,14 +170,10 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
       for (int b = 0; b < PB; b++) {
         const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
         const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
-        if (v)
-          bb[b] = *(const Frag *)(xb + (size_t)(pixbase[b] * p.cin_pad + doff) * V::ESIZE);
-        else
-          bb[b] = Frag{};
+        const unsigned off = v ? (unsigned)(pixbase[b] * p.cin_pad + doff) * (unsigned)V::ESIZE : kOutOfRange;
+        bb[b] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
       }
     } else {
-#pragma unroll
-      for (int b = 0; b < PB; b++) bb[b] = Frag{};
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const Chunk c = decode_chunk(p, (s * 4 + g) * 4 + j);
@@ -161,7 +182,8 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
         for (int b = 0; b < PB; b++) {
           const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
           const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
-          if (v) bb[b][j] = *(const int *)(xb + (size_t)(pixbase[b] * p.cin_pad + doff));
+          const unsigned off = v ? (unsigned)(pixbase[b] * p.cin_pad + doff) : kOutOfRange;
+          bb[b][j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
         }
       }
     }
@@ -290,9 +312,8 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
       for (int b = 0; b < PB; b++)
         if (mval[b]) *(i32x4 *)((int *)p.out + (size_t)outpix[b] * p.cout_pad + co0) = acc[cb][b];
     } else {
-      const f32x4 bias = *(const f32x4 *)(p.bias + co0);
-      f32x4 dq = {1.f, 1.f, 1.f, 1.f};
-      if constexpr (V::I8) dq = *(const f32x4 *)(p.dq + co0);
+      const f32x4 bias = ep_bias[cb];
+      const f32x4 dq = ep_dq[cb];
 #pragma unroll
       for (int b = 0; b < PB; b++) {
         if (!mval[b]) continue;
