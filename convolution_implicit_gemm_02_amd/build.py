@@ -41,7 +41,7 @@ def check_mfma_guards(hipcc: str) -> None:
          + COMMON + DEVICE_FLAGS)
     text = open(asm).read()
     bad = []
-    for name in re.findall(r"^(_ZN3cbs10conv_igemm\w+):", text, re.M):
+    for name in re.findall(r"^(_ZN3cbs(?:10conv_igemm|8conv_lds)\w+):", text, re.M):
         body = text[text.index(name + ":"):text.index(".Lfunc_end", text.index(name + ":"))]
         masked = False
         for line in body.split("\n"):

@@ -154,6 +154,7 @@ double model_cost(const cbs_layer *L, int cfg, int splitk) {
 bool config_fits(const cbs_layer *L, int cfg, int splitk) {
   const KernelConfig &c = config(cfg);
   if (splitk < 1 || splitk > 64) return false;
+  if (c.lds && splitk != 1) return false;
   if (splitk > 1 && L->steps < splitk * c.wk) return false;
   int pxt, cot;
   tiles_of(L, cfg, &pxt, &cot);

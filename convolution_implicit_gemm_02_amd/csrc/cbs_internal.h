@@ -11,6 +11,7 @@ namespace cbs {
 // waves split K inside the workgroup and are reduced through LDS).
 struct KernelConfig {
   int cb, pb, wco, wpx, wk;
+  int lds;  // 0: operands straight to registers (conv_igemm); 1: LDS-staged tiles (conv_lds)
   const char *name;
 };
 

@@ -333,6 +333,218 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   }
 }
 
+
+// ------------------------------------------------------ LDS-staged kernel --
+// The workgroup stages KS K-steps of weight and activation fragments in LDS
+// (double-buffered, same fragment order and branch-free buffer loads as
+// above); its WM x WN waves split the output tile and read their operands
+// from LDS, so each fetched byte feeds several waves.  Used for the larger
+// (batch-16, 80x80 and up) layers, where the register-direct kernel is bound
+// by vector-memory issue rather than by MFMA.
+
+struct Pix {
+  int base, iy0, ix0, out;
+  bool ok;
+};
+
+__device__ __forceinline__ Pix pixel_of(const ConvParams &p, int m) {
+  Pix q;
+  q.ok = m < p.M;
+  const int mm = q.ok ? m : 0;
+  const int ow = mm % p.OW;
+  const int t = mm / p.OW;
+  const int oh = t % p.OH;
+  const int n = t / p.OH;
+  q.iy0 = oh * p.stride - p.pad;
+  q.ix0 = ow * p.stride - p.pad;
+  q.base = (n * p.H + q.iy0) * p.W + q.ix0;
+  q.out = (n * p.OH + oh) * p.pitch + ow;
+  return q;
+}
+
+// The activation fragment of one lane: pixel q, K chunk group `cg` (= 4*step + g).
+template <class V>
+__device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu_buffer_rsrc_t xr, const Pix &q,
+                                                   int cg) {
+  using Frag = typename V::Frag;
+  if constexpr (V::VEC == 1) {
+    const Chunk c = decode_chunk(p, cg);
+    const int iy = q.iy0 + c.dy, ix = q.ix0 + c.dx;
+    const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+    const unsigned off =
+        v ? (unsigned)(q.base * p.cin_pad + (c.dy * p.W + c.dx) * p.cin_pad + c.ci) * (unsigned)V::ESIZE : kOutOfRange;
+    return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+  } else {
+    Frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const Chunk c = decode_chunk(p, cg * 4 + j);
+      const int iy = q.iy0 + c.dy, ix = q.ix0 + c.dx;
+      const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+      const unsigned off = v ? (unsigned)(q.base * p.cin_pad + (c.dy * p.W + c.dx) * p.cin_pad + c.ci) : kOutOfRange;
+      f[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
+    }
+    return f;
+  }
+}
+
+template <int VAR, int MB, int NB, int WM, int WN, int KS>
+__global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
+  using V = Var<VAR>;
+  using Frag = typename V::Frag;
+  using Acc = typename V::Acc;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BMB = MB * WM, BNB = NB * WN;     // 16-pixel and 16-channel blocks per workgroup
+  constexpr int SB = BMB + BNB;                   // fragment blocks per K step
+  constexpr int NA = KS * BNB * 64 / NT;          // weight slots per thread per stage
+  constexpr int NX = KS * BMB * 64 / NT;          // activation slots per thread per stage
+  static_assert((KS * BNB * 64) % NT == 0 && (KS * BMB * 64) % NT == 0, "stage must split evenly over threads");
+  __shared__ Frag lds[2][KS * SB * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (see conv_igemm)
+  const int wm = wave % WM, wn = wave / WM;
+  const int r = lane & 15, g = lane >> 4;
+
+  const int nb_ = gridDim.x, bid = blockIdx.x;
+  const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  const int co_tile = logical % p.co_tiles;
+  const int px_tile = logical / p.co_tiles;
+
+  // pixels of this thread's activation slots (the same for every stage)
+  Pix xpix[NX];
+#pragma unroll
+  for (int i = 0; i < NX; i++) {
+    const int j = tid + i * NT;
+    const int pxb = (j >> 6) % BMB;
+    xpix[i] = pixel_of(p, (px_tile * BMB + pxb) * 16 + r);
+  }
+  // epilogue operands of this wave's blocks
+  f32x4 ep_bias[NB], ep_dq[NB];
+  {
+    const __amdgpu_buffer_rsrc_t br =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t dr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.dq, 0, V::I8 ? (int)(p.co_blocks * 64) : 0, kRsrcWord3);
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      const unsigned off = (unsigned)((((co_tile * BNB + wn * NB + nb) * 16) + 4 * g) * 4);
+      ep_bias[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ep_dq[nb] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (!V::RAW) ep_bias[nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0));
+      if constexpr (V::I8 && !V::RAW) ep_dq[nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, off, 0, 0));
+    }
+  }
+
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
+  const int nst = (p.steps + KS - 1) / KS;
+
+  Frag ra[NA], rx[NX];
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < NA; i++) {
+      const int j = tid + i * NT;
+      const int ks = j / (BNB * 64), blk = (j >> 6) % BNB;
+      const int s = st * KS + ks;
+      const unsigned off = s < p.steps
+                               ? ((unsigned)((co_tile * BNB + blk) * p.steps + s) * 64u + (unsigned)lane) * 16u
+                               : kOutOfRange;
+      ra[i] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < NX; i++) {
+      const int j = tid + i * NT;
+      const int ks = j / (BMB * 64);
+      rx[i] = gather<V>(p, xr, xpix[i], (st * KS + ks) * 4 + g);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; i++) {
+      const int j = tid + i * NT;
+      const int ks = j / (BNB * 64), blk = (j >> 6) % BNB;
+      lds[buf][(ks * SB + blk) * 64 + lane] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NX; i++) {
+      const int j = tid + i * NT;
+      const int ks = j / (BMB * 64), pxb = (j >> 6) % BMB;
+      lds[buf][(ks * SB + BNB + pxb) * 64 + lane] = rx[i];
+    }
+  };
+
+  Acc acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) acc[nb][mb] = Acc{};
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      Frag a[NB], b[MB];
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) a[nb] = lds[buf][(ks * SB + wn * NB + nb) * 64 + lane];
+#pragma unroll
+      for (int mb = 0; mb < MB; mb++) b[mb] = lds[buf][(ks * SB + BNB + wm * MB + mb) * 64 + lane];
+      if constexpr (!V::I8) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++)
+              acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[nb][jj], b[mb][jj], acc[nb][mb], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+          for (int mb = 0; mb < MB; mb++)
+            acc[nb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+      }
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int st = 0; st < nst; st++) {
+    const bool more = st + 1 < nst;
+    if (more) gload(st + 1);
+    compute(st & 1);
+    if (more) sstore((st + 1) & 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++) {
+    const int co0 = (co_tile * BNB + wn * NB + nb) * 16 + 4 * g;
+    if (co0 >= p.cout_pad) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+      const Pix q = pixel_of(p, (px_tile * BMB + wm * MB + mb) * 16 + r);
+      if (!q.ok) continue;
+      if constexpr (V::RAW) {
+        *(i32x4 *)((int *)p.out + (size_t)q.out * p.cout_pad + co0) = acc[nb][mb];
+      } else {
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float z;
+          if constexpr (V::I8)
+            z = (float)acc[nb][mb][i] * ep_dq[nb][i] + ep_bias[nb][i];
+          else
+            z = acc[nb][mb][i] + ep_bias[nb][i];
+          y[i] = silu_f(z);
+        }
+        *(f32x4 *)((float *)p.out + (size_t)q.out * p.cout_pad + co0) = y;
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------- config table --
 // id, CB, PB, WCO, WPX, WK, PF (prefetch depth), name
 #define CBS_CONFIG_LIST(X)                    \
@@ -353,9 +565,23 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   X(14, 1, 2, 1, 1, 8, 4, "c16p32k8")         \
   X(15, 1, 2, 1, 1, 4, 4, "c16p32k4")
 
+// LDS-staged configurations: id, MB, NB (16-blocks per wave), WM, WN (waves), KS, name.
+// They are numbered after the register-direct ones.
+#define CBS_LDS_CONFIG_LIST(X)               \
+  X(16, 4, 2, 2, 2, 2, "L.p128c64")          \
+  X(17, 2, 2, 2, 2, 2, "L.p64c64")           \
+  X(18, 4, 4, 2, 2, 2, "L.p128c128")         \
+  X(19, 2, 4, 2, 2, 2, "L.p64c128")          \
+  X(20, 4, 4, 4, 1, 2, "L.p256c64")          \
+  X(21, 4, 2, 2, 1, 2, "L.p128c32")          \
+  X(22, 2, 2, 2, 1, 2, "L.p64c32")
+
 static const KernelConfig kConfigs[] = {
-#define X(id, cb, pb, wco, wpx, wk, pf, name) {cb, pb, wco, wpx, wk, name},
+#define X(id, cb, pb, wco, wpx, wk, pf, name) {cb, pb, wco, wpx, wk, 0, name},
     CBS_CONFIG_LIST(X)
+#undef X
+#define X(id, mb, nb, wm, wn, ks, name) {nb, mb, wn, wm, 1, 1, name},
+    CBS_LDS_CONFIG_LIST(X)
 #undef X
 };
 
@@ -370,6 +596,14 @@ static hipError_t launch_one(const ConvParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int VAR, int MB, int NB, int WM, int WN, int KS>
+static hipError_t launch_lds(const ConvParams &p, hipStream_t stream) {
+  if (p.splitk != 1) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)p.px_tiles * (unsigned)p.co_tiles;
+  hipLaunchKernelGGL((conv_lds<VAR, MB, NB, WM, WN, KS>), dim3(grid), dim3(64 * WM * WN), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int VAR>
 static hipError_t launch_var(int cfg, const ConvParams &p, hipStream_t stream) {
   switch (cfg) {
@@ -377,6 +611,11 @@ static hipError_t launch_var(int cfg, const ConvParams &p, hipStream_t stream) {
   case id:                                    \
     return launch_one<VAR, cb, pb, wco, wpx, wk, pf>(p, stream);
     CBS_CONFIG_LIST(X)
+#undef X
+#define X(id, mb, nb, wm, wn, ks, name) \
+  case id:                              \
+    return launch_lds<VAR, mb, nb, wm, wn, ks>(p, stream);
+    CBS_LDS_CONFIG_LIST(X)
 #undef X
     default:
       return hipErrorInvalidValue;
