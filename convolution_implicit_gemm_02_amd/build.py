@@ -30,29 +30,74 @@ def _run(cmd):
     subprocess.run(cmd, check=True)
 
 
-def check_mfma_guards(hipcc: str) -> None:
-    """Fail the build if any MFMA of the conv kernels sits in an EXEC-masked
-    region.  MFMA ignores EXEC, so an MFMA under a per-lane condition would
-    still execute for the whole wave; every MFMA guard must be a scalar
-    (wave-uniform) branch.  Scans the device assembly of this build."""
+# Two tiny kernels that calibrate the check: an MFMA under a per-lane
+# condition (must be flagged) and one under a wave-uniform condition (must not).
+_GUARD_PROBE = r"""
+#include <hip/hip_runtime.h>
+typedef float f4 __attribute__((ext_vector_type(4)));
+__global__ void probe_masked(const float *a, f4 *o, int n) {
+  f4 acc = {0, 0, 0, 0};
+  if ((int)threadIdx.x < n) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[threadIdx.x], a[threadIdx.x + 64], acc, 0, 0, 0);
+  o[threadIdx.x] = acc;
+}
+__global__ void probe_uniform(const float *a, f4 *o, int n) {
+  f4 acc = {0, 0, 0, 0};
+  if (n > 3) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[threadIdx.x], a[threadIdx.x + 64], acc, 0, 0, 0);
+  o[threadIdx.x] = acc;
+}
+"""
+
+
+def masked_mfma_kernels(text: str, pattern: str):
+    """Kernels of a device assembly whose MFMAs may run under a partial EXEC.
+
+    An EXEC-masked region opens at s_*_saveexec and closes where EXEC is
+    restored (s_or_b64/s_mov_b64 exec), at the label its s_cbranch_execz
+    jumps to, or at an unconditional branch out of the masked body."""
     import re
+    bad = []
+    for name in re.findall(pattern, text, re.M):
+        i = text.index(name + ":")
+        body = text[i:text.index(".Lfunc_end", i)].split("\n")
+        masked, target = False, None
+        for k, line in enumerate(body):
+            t = line.strip()
+            if re.match(r"s_(and|andn2|xor|or)_saveexec", t):
+                masked = True
+                nxt = body[k + 1].strip() if k + 1 < len(body) else ""
+                target = nxt.split()[1] if nxt.startswith("s_cbranch_execz") else None
+            elif masked and (t.startswith("s_or_b64 exec") or t.startswith("s_mov_b64 exec")
+                             or t.startswith("s_branch ") or t.startswith("s_endpgm")
+                             or (target is not None and t == target + ":")):
+                masked, target = False, None
+            elif t.startswith("v_mfma") and masked:
+                bad.append(name)
+                break
+    return bad
+
+
+def check_mfma_guards(hipcc: str) -> None:
+    """Fail the build if any MFMA of the conv kernels may run under a partial
+    EXEC mask.  MFMA ignores EXEC, so an MFMA under a per-lane condition would
+    still execute for the whole wave; every MFMA guard must be a scalar
+    (wave-uniform) branch.  Scans the device assembly of this build, after
+    checking that the scan flags a known-masked probe and passes a uniform one."""
+    probe_src = os.path.join(BUILD_DIR, "guard_probe.hip")
+    probe_asm = os.path.join(BUILD_DIR, "guard_probe.s")
+    with open(probe_src, "w") as f:
+        f.write(_GUARD_PROBE)
+    _run([hipcc, "--cuda-device-only", "-S", probe_src, "-o", probe_asm, "-O3"] + COMMON + DEVICE_FLAGS)
+    flagged = masked_mfma_kernels(open(probe_asm).read(), r"^(_Z\d+probe_\w+):")
+    if not any("probe_masked" in n for n in flagged) or any("probe_uniform" in n for n in flagged):
+        raise RuntimeError("MFMA guard check failed its calibration (flagged: %s)" % flagged)
     asm = os.path.join(BUILD_DIR, "cbs_kernels.s")
     _run([hipcc, "--cuda-device-only", "-S", os.path.join(CSRC, "cbs_kernels.hip"), "-o", asm, "-O3"]
          + COMMON + DEVICE_FLAGS)
     text = open(asm).read()
-    bad = []
-    for name in re.findall(r"^(_ZN3cbs(?:10conv_igemm|8conv_lds)\w+):", text, re.M):
-        body = text[text.index(name + ":"):text.index(".Lfunc_end", text.index(name + ":"))]
-        masked = False
-        for line in body.split("\n"):
-            t = line.strip()
-            if re.match(r"s_(and|andn2|xor|or)_saveexec", t):
-                masked = True
-            elif t.startswith("s_or_b64 exec") or t.startswith("s_mov_b64 exec"):
-                masked = False
-            elif t.startswith("v_mfma") and masked:
-                bad.append(name)
-                break
+    import re
+    if len(re.findall(r"^_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+:", text, re.M)) < 3:
+        raise RuntimeError("MFMA guard check found no conv kernels in the device assembly")
+    bad = masked_mfma_kernels(text, r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+):")
     if bad:
         raise RuntimeError("MFMA inside an EXEC-masked region in: %s" % ", ".join(bad))
 

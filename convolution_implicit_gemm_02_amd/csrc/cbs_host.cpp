@@ -122,9 +122,26 @@ struct Choice {
 // Tiles of a configuration for this layer.
 void tiles_of(const cbs_layer *L, int cfg, int *px_tiles, int *co_tiles) {
   const KernelConfig &c = config(cfg);
+  if (c.lds == 2) {  // halo tiles: whole TH x TW blocks of one image, all channels
+    *co_tiles = 1;
+    *px_tiles = L->d.n * ceil_div(L->oh, c.th) * ceil_div(L->ow, c.tw);
+    return;
+  }
   const int tco = c.cb * 16 * c.wco, tpx = c.pb * 16 * c.wpx;
   *co_tiles = ceil_div(L->co_blocks * 16, tco);
   *px_tiles = ceil_div(L->M, tpx);
+}
+
+// LDS bytes of a halo-tile workgroup: the input window (4-channel slots,
+// rounded up to whole waves of slots) followed by all fragment-ordered weights.
+void halo_lds(const cbs_layer *L, int cfg, int *halo_bytes, int *smem_bytes) {
+  const KernelConfig &c = config(cfg);
+  const int s = L->d.stride;
+  const int hh = (c.th - 1) * s + 3, hw = (c.tw - 1) * s + 3;
+  const int slots = hh * hw * (L->cin_pad / 4);
+  const int slot_bytes = L->d.dtype == CBS_F32 ? 16 : 4;
+  *halo_bytes = round_up(slots, 64) * slot_bytes;
+  *smem_bytes = *halo_bytes + L->co_blocks * L->steps * 1024;
 }
 
 // Rough cost model (cycles at one SIMD) used when the tile table has no entry:
@@ -155,6 +172,12 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
   const KernelConfig &c = config(cfg);
   if (splitk < 1 || splitk > 64) return false;
   if (c.lds && splitk != 1) return false;
+  if (c.lds == 2) {
+    if (L->d.k != 3 || L->co_blocks > 4) return false;
+    int hb, sb;
+    halo_lds(L, cfg, &hb, &sb);
+    if (sb > 64 * 1024) return false;
+  }
   if (splitk > 1 && L->steps < splitk * c.wk) return false;
   int pxt, cot;
   tiles_of(L, cfg, &pxt, &cot);
@@ -176,6 +199,7 @@ Choice choose(const cbs_layer *L) {
   Choice best{2, 1};
   double best_cost = 1e300;
   for (int cfg = 0; cfg < num_configs(); cfg++) {
+    if (config(cfg).lds == 2) continue;  // halo tiles are chosen by measurement only
     for (int sk : {1}) {
       if (!config_fits(L, cfg, sk)) continue;
       const double cost = model_cost(L, cfg, sk);
@@ -272,6 +296,12 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out) {
   p.co_blocks = L->co_blocks;
   p.x_bytes = (unsigned)((size_t)L->d.n * L->d.h * L->d.w * L->cin_pad * (L->d.dtype == CBS_F32 ? 4 : 1));
   p.w_bytes = (unsigned)((size_t)L->co_blocks * L->steps * 64 * 16);
+  const KernelConfig &kc = config(L->config);
+  if (kc.lds == 2) {
+    p.tiles_x = ceil_div(L->ow, kc.tw);
+    p.tiles_y = ceil_div(L->oh, kc.th);
+    halo_lds(L, L->config, &p.halo_bytes, &p.smem_bytes);
+  }
   tiles_of(L, L->config, &p.px_tiles, &p.co_tiles);
   return p;
 }

@@ -11,7 +11,9 @@ namespace cbs {
 // waves split K inside the workgroup and are reduced through LDS).
 struct KernelConfig {
   int cb, pb, wco, wpx, wk;
-  int lds;  // 0: operands straight to registers (conv_igemm); 1: LDS-staged tiles (conv_lds)
+  int lds;  // 0: operands straight to registers (conv_igemm); 1: LDS-staged tiles (conv_lds);
+            // 2: input halo tile + all weights in LDS (conv_halo, 3x3 with <= 64 output channels)
+  int th, tw;  // conv_halo: output tile of th x tw pixels
   const char *name;
 };
 
@@ -49,6 +51,9 @@ struct ConvParams {
   int px_tiles, co_tiles;// workgroup tiles along pixels and output channels
   unsigned x_bytes;      // bytes of the input buffer (buffer-load range)
   unsigned w_bytes;      // bytes of the fragment-ordered weights (buffer-load range)
+  int tiles_x, tiles_y;  // conv_halo: output tiles along a row and along the rows of one image
+  int halo_bytes;        // conv_halo: LDS bytes of the input halo tile (weights follow)
+  int smem_bytes;        // conv_halo: dynamic LDS bytes per workgroup
 };
 
 int num_configs();

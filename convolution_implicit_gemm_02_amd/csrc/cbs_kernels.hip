@@ -545,6 +545,183 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   }
 }
 
+
+// ------------------------------------------------------ halo-tile kernel --
+// For 3x3 layers with few channels (the 3-channel stem and the 8..32-channel
+// layers at 80..320 pixels) the implicit-GEMM gather re-reads every input
+// pixel up to nine times.  Here a workgroup owns a TH x TW block of output
+// pixels of one image and all (<= 64) output channels: it copies the input
+// window it needs (the halo, all channels) and the layer's fragment-ordered
+// weights straight into LDS with direct-to-LDS buffer loads (out-of-range
+// offsets supply the zero padding), then runs every tap of the convolution
+// from LDS on MFMA.  This is the direct-convolution path for the stem.
+template <int VAR, int TH, int TW>
+__global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
+  using V = Var<VAR>;
+  using Frag = typename V::Frag;
+  using Acc = typename V::Acc;
+  constexpr int NBMAX = 4;
+  constexpr int MB = TH * TW / 64;  // 16-pixel blocks per wave (4 waves)
+  static_assert(TH * TW % 64 == 0, "tile must split into 4 waves of 16-pixel blocks");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  typedef __attribute__((address_space(3))) void *lds_ptr;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (see conv_igemm)
+  const int r = lane & 15, g = lane >> 4;
+
+  const int nb_ = gridDim.x, bid = blockIdx.x;
+  const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  const int tx = logical % p.tiles_x;
+  const int rest = logical / p.tiles_x;
+  const int ty = rest % p.tiles_y;
+  const int n = rest / p.tiles_y;
+
+  const int st_ = p.stride;
+  const int HWd = (TW - 1) * st_ + 3;  // halo width in pixels
+  const int HH = (TH - 1) * st_ + 3;   // halo height
+  const int oh0 = ty * TH, ow0 = tx * TW;
+  const int iy0 = oh0 * st_ - p.pad, ix0 = ow0 * st_ - p.pad;
+  const int cq = p.cin_pad >> 2;                 // 4-channel slots per pixel
+  constexpr int SLOT = 4 * V::ESIZE;             // bytes of a 4-channel slot
+  const int halo_slots = HH * HWd * cq;
+
+  // 1) input halo and weights -> LDS (all loads in flight, no register round trip)
+  {
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
+    for (int base = wave * 64; base < halo_slots; base += 256) {
+      const int sl = base + lane;
+      const int q = sl % cq;
+      const int px = sl / cq;
+      const int hx = px % HWd, hy = px / HWd;
+      const int iy = iy0 + hy, ix = ix0 + hx;
+      const bool v = sl < halo_slots && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+      const unsigned off = v ? (unsigned)(((n * p.H + iy) * p.W + ix) * p.cin_pad + 4 * q) * (unsigned)V::ESIZE
+                             : kOutOfRange;
+      if constexpr (SLOT == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(smem + base * SLOT), 16, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(smem + base * SLOT), 4, off, 0, 0, 0);
+    }
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
+    const int wslots = (int)(p.w_bytes >> 4);
+    for (int base = wave * 64; base < wslots; base += 256)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr)(smem + p.halo_bytes + base * 16), 16,
+                                               (unsigned)(base + lane) * 16u, 0, 0, 0);
+  }
+  // epilogue operands meanwhile
+  const int nbl = p.co_blocks;  // <= NBMAX, uniform
+  f32x4 ep_bias[NBMAX], ep_dq[NBMAX];
+  {
+    const __amdgpu_buffer_rsrc_t br =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t dr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.dq, 0, V::I8 ? (int)(p.co_blocks * 64) : 0, kRsrcWord3);
+#pragma unroll
+    for (int nb = 0; nb < NBMAX; nb++) {
+      const unsigned off = (unsigned)((nb * 16 + 4 * g) * 4);
+      ep_bias[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ep_dq[nb] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (!V::RAW) ep_bias[nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0));
+      if constexpr (V::I8 && !V::RAW) ep_dq[nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, off, 0, 0));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // 2) every tap from LDS: lane (r, g) of block mb holds pixel r of that block
+  int lbase[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) {
+    const int pi = (wave * MB + mb) * 16 + r;
+    const int ly = pi / TW, lx = pi % TW;
+    lbase[mb] = (ly * st_) * HWd + lx * st_;
+  }
+  const unsigned char *wl = smem + p.halo_bytes;
+  const int pix_bytes = p.cin_pad * V::ESIZE;
+  Acc acc[NBMAX][MB];
+#pragma unroll
+  for (int nb = 0; nb < NBMAX; nb++)
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) acc[nb][mb] = Acc{};
+
+  for (int s = 0; s < p.steps; s++) {
+    Frag a[NBMAX];
+#pragma unroll
+    for (int nb = 0; nb < NBMAX; nb++)
+      a[nb] = nb < nbl ? *(const Frag *)(wl + ((nb * p.steps + s) * 64 + lane) * 16) : Frag{};
+    Frag b[MB];
+    if constexpr (V::VEC == 1) {
+      Chunk c = decode_chunk(p, s * 4 + g);
+      if (!c.ok) c.dy = c.dx = c.ci = 0;  // past K: read a valid slot, then zero it
+#pragma unroll
+      for (int mb = 0; mb < MB; mb++) {
+        const Frag v = *(const Frag *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci * V::ESIZE);
+        b[mb] = c.ok ? v : Frag{};
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; mb++) b[mb] = Frag{};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        Chunk c = decode_chunk(p, (s * 4 + g) * 4 + j);
+        if (!c.ok) c.dy = c.dx = c.ci = 0;
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) {
+          const int v = *(const int *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci);
+          b[mb][j] = c.ok ? v : 0;
+        }
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBMAX; nb++) {
+      if (nb >= nbl) break;
+      if constexpr (!V::I8) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+#pragma unroll
+          for (int mb = 0; mb < MB; mb++)
+            acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[nb][jj], b[mb][jj], acc[nb][mb], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+          acc[nb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+      }
+    }
+  }
+
+  // 3) epilogue, masked to the image and to the real channels
+#pragma unroll
+  for (int nb = 0; nb < NBMAX; nb++) {
+    if (nb >= nbl) break;
+    const int co0 = nb * 16 + 4 * g;
+    if (co0 >= p.cout_pad) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+      const int pi = (wave * MB + mb) * 16 + r;
+      const int oh = oh0 + pi / TW, ow = ow0 + pi % TW;
+      if (oh >= p.OH || ow >= p.OW) continue;
+      const size_t o = ((size_t)(n * p.OH + oh) * p.pitch + ow) * p.cout_pad + co0;
+      if constexpr (V::RAW) {
+        *(i32x4 *)((int *)p.out + o) = acc[nb][mb];
+      } else {
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float z;
+          if constexpr (V::I8)
+            z = (float)acc[nb][mb][i] * ep_dq[nb][i] + ep_bias[nb][i];
+          else
+            z = acc[nb][mb][i] + ep_bias[nb][i];
+          y[i] = silu_f(z);
+        }
+        *(f32x4 *)((float *)p.out + o) = y;
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------- config table --
 // id, CB, PB, WCO, WPX, WK, PF (prefetch depth), name
 #define CBS_CONFIG_LIST(X)                    \
@@ -576,12 +753,23 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   X(21, 4, 2, 2, 1, 2, "L.p128c32")          \
   X(22, 2, 2, 2, 1, 2, "L.p64c32")
 
+// Halo-tile configurations: id, TH, TW (output tile), name.
+#define CBS_HALO_CONFIG_LIST(X)              \
+  X(23, 4, 64, "H.t4x64")                    \
+  X(24, 2, 64, "H.t2x64")                    \
+  X(25, 8, 32, "H.t8x32")                    \
+  X(26, 4, 32, "H.t4x32")                    \
+  X(27, 2, 32, "H.t2x32")
+
 static const KernelConfig kConfigs[] = {
-#define X(id, cb, pb, wco, wpx, wk, pf, name) {cb, pb, wco, wpx, wk, 0, name},
+#define X(id, cb, pb, wco, wpx, wk, pf, name) {cb, pb, wco, wpx, wk, 0, 0, 0, name},
     CBS_CONFIG_LIST(X)
 #undef X
-#define X(id, mb, nb, wm, wn, ks, name) {nb, mb, wn, wm, 1, 1, name},
+#define X(id, mb, nb, wm, wn, ks, name) {nb, mb, wn, wm, 1, 1, 0, 0, name},
     CBS_LDS_CONFIG_LIST(X)
+#undef X
+#define X(id, th, tw, name) {4, th * tw / 64, 1, 4, 1, 2, th, tw, name},
+    CBS_HALO_CONFIG_LIST(X)
 #undef X
 };
 
@@ -604,6 +792,14 @@ static hipError_t launch_lds(const ConvParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int VAR, int TH, int TW>
+static hipError_t launch_halo(const ConvParams &p, hipStream_t stream) {
+  if (p.splitk != 1 || p.co_blocks > 4 || p.k != 3) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)p.px_tiles;
+  hipLaunchKernelGGL((conv_halo<VAR, TH, TW>), dim3(grid), dim3(256), (unsigned)p.smem_bytes, stream, p);
+  return hipGetLastError();
+}
+
 template <int VAR>
 static hipError_t launch_var(int cfg, const ConvParams &p, hipStream_t stream) {
   switch (cfg) {
@@ -616,6 +812,11 @@ static hipError_t launch_var(int cfg, const ConvParams &p, hipStream_t stream) {
   case id:                              \
     return launch_lds<VAR, mb, nb, wm, wn, ks>(p, stream);
     CBS_LDS_CONFIG_LIST(X)
+#undef X
+#define X(id, th, tw, name) \
+  case id:                  \
+    return launch_halo<VAR, th, tw>(p, stream);
+    CBS_HALO_CONFIG_LIST(X)
 #undef X
     default:
       return hipErrorInvalidValue;
