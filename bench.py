@@ -142,7 +142,10 @@ def layer_rows(bench, us):
     return rows
 
 
-KERNEL_SOURCES = ("convolution_implicit_gemm_02_amd/csrc/cbs_kernels.hip",
+KERNEL_SOURCES = ("convolution_implicit_gemm_02_amd/csrc/conv_kernels.h",
+                  "convolution_implicit_gemm_02_amd/csrc/conv_configs.h",
+                  "convolution_implicit_gemm_02_amd/csrc/cbs_variant.hip",
+                  "convolution_implicit_gemm_02_amd/csrc/cbs_kernels.hip",
                   "convolution_implicit_gemm_02_amd/csrc/cbs_host.cpp",
                   "convolution_implicit_gemm_02_amd/csrc/cbs_internal.h",
                   "convolution_implicit_gemm_02_amd/csrc/tile_table.inc")
@@ -189,13 +192,16 @@ def cpu_baseline(W, max_seconds=30.0):
             "sample": sample, "seconds": round(t_total, 3), "us_per_list": round(t_total * 1e6 * len(layers) / done, 1)}
 
 
-def profile_layer(cbs, W, torch, name, dtype, batch, launches):
+def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, splitk=0):
     """Run only one layer of the list `launches` times back to back (for a profiler
     run on exactly that kernel), then a plain device copy of known size (the
     reference for scaling the profiler's byte counters).  Prints one JSON line."""
     b = ListBench(cbs, W, torch, dtype, batch)
     i = [s.name for s in b.specs].index(name)
     layer, xin, out = b.layers[i], b.ins[i], b.outs[i]
+    if config is not None:
+        cbs.cbs_layer_set_config(layer, config, splitk)
+        b.infos[i] = cbs.cbs_layer_info(layer)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     cbs.cbs_run_layer_list([layer] * 10, [xin] * 10, [out] * 10)
     torch.cuda.synchronize()
@@ -228,6 +234,7 @@ def main():
     ap.add_argument("--dtype", default="f32", choices=["f32", "int8"], help="profile mode dtype")
     ap.add_argument("--batch", type=int, default=1, help="profile mode batch")
     ap.add_argument("--launches", type=int, default=200, help="profile mode launches")
+    ap.add_argument("--config", type=int, default=None, help="profile mode: force this kernel configuration")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the batch-16 list shards over images with no "
@@ -243,7 +250,7 @@ def main():
     log("device: %s, %d CUs" % (props.name, props.multi_processor_count))
     if args.only_layer:
         profile_layer(cbs, W, torch, args.only_layer, cbs.CBS_I8 if args.dtype == "int8" else cbs.CBS_F32,
-                      args.batch, args.launches)
+                      args.batch, args.launches, args.config)
         return
 
     results = {}

@@ -76,28 +76,54 @@ def masked_mfma_kernels(text: str, pattern: str):
     return bad
 
 
+VARIANTS = 5  # kernel variants, one translation unit each (cbs_variant.hip with -DCBS_VAR=n)
+CONV_KERNELS = r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+):"
+
+
+def _jobs() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 4
+    return max(1, min(8, n))
+
+
+def _parallel(cmds):
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=_jobs()) as ex:
+        for f in [ex.submit(_run, c) for c in cmds]:
+            f.result()
+
+
 def check_mfma_guards(hipcc: str) -> None:
     """Fail the build if any MFMA of the conv kernels may run under a partial
     EXEC mask.  MFMA ignores EXEC, so an MFMA under a per-lane condition would
     still execute for the whole wave; every MFMA guard must be a scalar
-    (wave-uniform) branch.  Scans the device assembly of this build, after
-    checking that the scan flags a known-masked probe and passes a uniform one."""
+    (wave-uniform) branch.  Scans the device assembly of every variant of this
+    build, after checking that the scan flags a known-masked probe and passes a
+    uniform one."""
+    import re
     probe_src = os.path.join(BUILD_DIR, "guard_probe.hip")
     probe_asm = os.path.join(BUILD_DIR, "guard_probe.s")
     with open(probe_src, "w") as f:
         f.write(_GUARD_PROBE)
-    _run([hipcc, "--cuda-device-only", "-S", probe_src, "-o", probe_asm, "-O3"] + COMMON + DEVICE_FLAGS)
+    cmds = [[hipcc, "--cuda-device-only", "-S", probe_src, "-o", probe_asm, "-O3"] + COMMON + DEVICE_FLAGS]
+    asms = []
+    for v in range(VARIANTS):
+        asm = os.path.join(BUILD_DIR, "cbs_variant_%d.s" % v)
+        asms.append(asm)
+        cmds.append([hipcc, "--cuda-device-only", "-S", os.path.join(CSRC, "cbs_variant.hip"), "-o", asm, "-O3",
+                     "-DCBS_VAR=%d" % v] + COMMON + DEVICE_FLAGS)
+    _parallel(cmds)
     flagged = masked_mfma_kernels(open(probe_asm).read(), r"^(_Z\d+probe_\w+):")
     if not any("probe_masked" in n for n in flagged) or any("probe_uniform" in n for n in flagged):
         raise RuntimeError("MFMA guard check failed its calibration (flagged: %s)" % flagged)
-    asm = os.path.join(BUILD_DIR, "cbs_kernels.s")
-    _run([hipcc, "--cuda-device-only", "-S", os.path.join(CSRC, "cbs_kernels.hip"), "-o", asm, "-O3"]
-         + COMMON + DEVICE_FLAGS)
-    text = open(asm).read()
-    import re
-    if len(re.findall(r"^_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+:", text, re.M)) < 3:
-        raise RuntimeError("MFMA guard check found no conv kernels in the device assembly")
-    bad = masked_mfma_kernels(text, r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+):")
+    bad = []
+    for asm in asms:
+        text = open(asm).read()
+        if len(re.findall(CONV_KERNELS, text, re.M)) < 3:
+            raise RuntimeError("MFMA guard check found no conv kernels in %s" % asm)
+        bad += masked_mfma_kernels(text, CONV_KERNELS)
     if bad:
         raise RuntimeError("MFMA inside an EXEC-masked region in: %s" % ", ".join(bad))
 
@@ -107,15 +133,23 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     hipcc = _hipcc()
     check_mfma_guards(hipcc)
+    objs, cmds = [], []
     k_obj = os.path.join(BUILD_DIR, "cbs_kernels.o")
-    h_obj = os.path.join(BUILD_DIR, "cbs_host.o")
-    # kernels: -O3, device code without packed fp32
-    _run([hipcc, "-c", os.path.join(CSRC, "cbs_kernels.hip"), "-o", k_obj, "-O3"] + COMMON + DEVICE_FLAGS)
+    cmds.append([hipcc, "-c", os.path.join(CSRC, "cbs_kernels.hip"), "-o", k_obj, "-O3"] + COMMON + DEVICE_FLAGS)
+    objs.append(k_obj)
+    for v in range(VARIANTS):
+        o = os.path.join(BUILD_DIR, "cbs_variant_%d.o" % v)
+        cmds.append([hipcc, "-c", os.path.join(CSRC, "cbs_variant.hip"), "-o", o, "-O3", "-DCBS_VAR=%d" % v]
+                    + COMMON + DEVICE_FLAGS)
+        objs.append(o)
     # host library: every double product/sum rounded as written (no FMA contraction)
-    _run([hipcc, "-c", os.path.join(CSRC, "cbs_host.cpp"), "-o", h_obj, "-O2", "-ffp-contract=off"]
-         + COMMON + DEVICE_FLAGS)
+    h_obj = os.path.join(BUILD_DIR, "cbs_host.o")
+    cmds.append([hipcc, "-c", os.path.join(CSRC, "cbs_host.cpp"), "-o", h_obj, "-O2", "-ffp-contract=off"]
+                + COMMON + DEVICE_FLAGS)
+    objs.append(h_obj)
+    _parallel(cmds)
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    _run([hipcc, "-shared", "-o", tmp, k_obj, h_obj, "--offload-arch=" + ARCH, "-fPIC"])
+    _run([hipcc, "-shared", "-o", tmp] + objs + ["--offload-arch=" + ARCH, "-fPIC"])
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

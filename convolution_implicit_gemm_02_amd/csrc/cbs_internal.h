@@ -19,11 +19,11 @@ struct KernelConfig {
 
 // Kernel-variant families (dtype x operand gathering x epilogue).
 enum Variant {
-  VAR_F32 = 0,         // fp32 activations, 4-channel chunks, SiLU epilogue
-  VAR_I8_C16 = 1,      // int8, 16-channel chunks (C_in_pad % 16 == 0), dequant+SiLU
-  VAR_I8_C4 = 2,       // int8, 4-channel chunks (any C_in_pad % 4 == 0), dequant+SiLU
-  VAR_I8_C16_RAW = 3,  // as VAR_I8_C16, stores raw int32 accumulators
-  VAR_I8_C4_RAW = 4,   // as VAR_I8_C4, stores raw int32 accumulators
+  VAR_F32 = 0,          // fp32 activations, 4-channel chunks, SiLU epilogue
+  VAR_I8_C16 = 1,       // int8, 16-channel chunks (C_in_pad % 16 == 0), dequant+SiLU
+  VAR_I8_C4 = 2,        // int8, 4-channel chunks (any C_in_pad % 4 == 0), dequant+SiLU
+  VAR_I8_C16_RAW = 3,   // as VAR_I8_C16, stores raw int32 accumulators
+  VAR_I8_C4_RAW = 4,    // as VAR_I8_C4, stores raw int32 accumulators
   VAR_COUNT = 5
 };
 
@@ -60,6 +60,13 @@ int num_configs();
 const KernelConfig &config(int i);
 // Launch variant `var` with configuration `cfg`; returns the hipError_t of the launch.
 hipError_t launch_conv(int var, int cfg, const ConvParams &p, hipStream_t stream);
+// One per variant (cbs_variant.hip compiled with -DCBS_VAR=n).
+hipError_t launch_var_0(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_1(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_2(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_3(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_4(int cfg, const ConvParams &p, hipStream_t stream);
+
 hipError_t launch_pack_nhwc_f32(const float *x, float *y, int n, int c, int hw, int c_pad,
                                 hipStream_t stream);
 hipError_t launch_quantize_nhwc_i8(const float *x, int8_t *y, float s_x, int n, int c, int hw,

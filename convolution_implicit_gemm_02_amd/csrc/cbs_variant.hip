@@ -1,0 +1,16 @@
+// cbs_variant.hip -- one kernel variant of libcbs (fp32 / int8, operand
+// gathering, epilogue), selected at compile time with -DCBS_VAR=<n>; the
+// build compiles this file once per variant, in parallel.
+#include "conv_kernels.h"
+
+#ifndef CBS_VAR
+#error "compile with -DCBS_VAR=<variant>"
+#endif
+
+namespace cbs {
+#define CBS_PASTE2(a, b) a##b
+#define CBS_PASTE(a, b) CBS_PASTE2(a, b)
+hipError_t CBS_PASTE(launch_var_, CBS_VAR)(int cfg, const ConvParams &p, hipStream_t stream) {
+  return launch_variant<CBS_VAR>(cfg, p, stream);
+}
+}  // namespace cbs

@@ -1,0 +1,35 @@
+// conv_configs.h -- kernel configurations of libcbs (shared by the kernel
+// translation units and the configuration table).  Each X-macro entry is one
+// tile shape; its id is its index in the table and in the tile sweep.
+#pragma once
+
+// Register-direct conv_igemm: id, CB, PB (16-channel / 16-pixel blocks per
+// wave), WCO, WPX, WK (waves along channels, pixels, K), PF (prefetch depth).
+#define CBS_CONFIG_LIST(X)                    \
+  X(0, 1, 4, 1, 4, 1, 4, "c16p256")           \
+  X(1, 2, 2, 1, 4, 1, 4, "c32p128")           \
+  X(2, 2, 2, 2, 2, 1, 4, "c64p64")            \
+  X(3, 4, 2, 1, 4, 1, 2, "c64p128")           \
+  X(4, 4, 2, 2, 2, 1, 2, "c128p64")           \
+  X(5, 4, 1, 1, 1, 4, 4, "c64p16k4")          \
+  X(6, 2, 1, 1, 1, 4, 4, "c32p16k4")          \
+  X(7, 1, 2, 1, 2, 2, 4, "c16p64k2")          \
+  X(8, 2, 2, 2, 1, 2, 4, "c64p32k2")          \
+  X(9, 1, 1, 1, 1, 4, 4, "c16p16k4")          \
+  X(10, 2, 1, 1, 1, 8, 4, "c32p16k8")         \
+  X(11, 2, 2, 1, 1, 4, 4, "c32p32k4")
+
+// LDS-staged conv_lds: id, MB, NB (16-blocks per wave), WM, WN (waves), KS, name.
+#define CBS_LDS_CONFIG_LIST(X)               \
+  X(12, 4, 2, 2, 2, 2, "L.p128c64")          \
+  X(13, 2, 2, 2, 2, 2, "L.p64c64")           \
+  X(14, 2, 4, 2, 2, 2, "L.p64c128")          \
+  X(15, 2, 2, 2, 1, 2, "L.p64c32")           \
+  X(16, 4, 4, 2, 2, 2, "L.p128c128")
+
+// Halo-tile conv_halo: id, TH, TW (output tile), name.
+#define CBS_HALO_CONFIG_LIST(X)              \
+  X(17, 4, 64, "H.t4x64")                    \
+  X(18, 8, 32, "H.t8x32")                    \
+  X(19, 4, 32, "H.t4x32")                    \
+  X(20, 2, 64, "H.t2x64")

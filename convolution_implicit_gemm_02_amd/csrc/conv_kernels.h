@@ -1,0 +1,784 @@
+#pragma once
+// conv_kernels.h -- gfx950 kernels of libcbs: implicit-GEMM fused Conv2d +
+// folded BN + SiLU on MFMA (fp32 and int8), as templates instantiated once
+// per variant by cbs_variant.hip.
+//
+// The convolution is computed as the implicit GEMM described on the vision-rs
+// "YOLO26N Inference Optimisation" page, section "NHWC migration -- What NHWC
+// is and why it matters": rows = output pixels (n, oh, ow), K = (kh, kw, c_in)
+// with c_in contiguous, columns = output channels.  Here the MFMA "A" operand
+// is the weights (16 output channels per block) and the "B" operand is the
+// gathered activations (16 output pixels per block), so every lane of the
+// accumulator holds 4 consecutive output channels of one pixel and the
+// epilogue stores one 16-byte NHWC vector per lane.
+//
+// K is walked in "chunks": 4 consecutive input channels of one tap (fp32 and
+// small-channel int8) or 16 (int8 with C_in_pad % 16 == 0).  At each K step,
+// lane group g = lane/16 of a wave loads chunk (4*step + g) (times 4 chunks
+// for the small-channel int8 gather); the weights were laid out at create in
+// exactly this order ("fragment order"), so each weight load is one
+// contiguous 1 KiB read per wave.  Chunks that fall in the zero padding of
+// the image, past K, or on pixels past the end of the tile are not loaded
+// and count as zeros, which is the zero padding of the definition.
+//
+// Output pixels are indexed by their logical position m = (n*OH + oh)*OW + ow
+// and stored at ((n*OH + oh)*pitch + ow), so a tail tile can never write into
+// the guard pixels of a row or into the next row: the overflow documented in
+// the same page's section "Bug fixed: TMA overflow" cannot happen by
+// construction, whatever the tile shape.
+//
+// Small-M layers (batch 1 at 20x20 or 40x40) split K across the waves of a
+// workgroup (reduced in LDS) and, optionally, across workgroups: each
+// workgroup writes its partial tile to a workspace, and the last one to
+// arrive (atomic ticket per tile) sums all partials in split order, runs the
+// epilogue and re-arms the ticket, so no memset is ever needed and the result
+// is bitwise deterministic.
+#include "cbs_internal.h"
+#include "conv_configs.h"
+
+
+namespace cbs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int VAR> struct Var;
+template <> struct Var<VAR_F32> {
+  using Frag = f32x4; using Acc = f32x4;
+  static constexpr int VEC = 1, ESIZE = 4; static constexpr bool I8 = false, RAW = false;
+};
+template <> struct Var<VAR_I8_C16> {
+  using Frag = i32x4; using Acc = i32x4;
+  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = false;
+};
+template <> struct Var<VAR_I8_C4> {
+  using Frag = i32x4; using Acc = i32x4;
+  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = false;
+};
+template <> struct Var<VAR_I8_C16_RAW> {
+  using Frag = i32x4; using Acc = i32x4;
+  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = true;
+};
+template <> struct Var<VAR_I8_C4_RAW> {
+  using Frag = i32x4; using Acc = i32x4;
+  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = true;
+};
+
+
+// Buffer resource word 3 (data format) for the gfx9 family, and an offset
+// that every buffer of this library lies below (sizes are checked < 2^31 at
+// create): loads at it return zero.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr unsigned kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ float silu_f(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
+
+// Decoded K chunk: tap offset (dy, dx) and first channel.
+struct Chunk {
+  int dy, dx, ci;
+  bool ok;
+};
+
+__device__ __forceinline__ Chunk decode_chunk(const ConvParams &p, int c) {
+  Chunk r;
+  const int tap = (int)(((unsigned)c * p.cpt_magic) >> 20);
+  r.ci = (c - tap * p.chunks_per_tap) * p.chunk_ch;
+  r.dy = (p.k == 1) ? 0 : ((tap * 11) >> 5);  // tap / 3 for tap < 9
+  r.dx = tap - r.dy * p.k;
+  r.ok = c < p.total_chunks;
+  return r;
+}
+
+template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
+__global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) {
+  using V = Var<VAR>;
+  using Frag = typename V::Frag;
+  using Acc = typename V::Acc;
+  const int lane = threadIdx.x & 63;
+  // The wave index is made explicitly wave-uniform: every condition that
+  // guards an MFMA below depends only on it, so it compiles to a scalar
+  // branch.  (MFMA ignores EXEC; an MFMA under a per-lane mask would run.)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wk = wave % WK;
+  const int wco = (wave / WK) % WCO;
+  const int wpx = wave / (WK * WCO);
+  const int slot = wco + WCO * wpx;
+  const int r = lane & 15, g = lane >> 4;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs; remap so that each
+  // XCD receives a contiguous range of logical tiles (the co tiles and K
+  // splits of one pixel tile then share that XCD's L2).
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int per = nb >> 3, rem = nb & 7, xcd = bid & 7, loc = bid >> 3;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  const int split = logical % p.splitk;
+  const int tile = logical / p.splitk;
+  const int co_tile = tile % p.co_tiles;
+  const int px_tile = tile / p.co_tiles;
+
+  // The 16-pixel blocks of this wave: lane r owns pixel r of each block.
+  int pixbase[PB], iy0[PB], ix0[PB], outpix[PB];
+  bool mval[PB];
+#pragma unroll
+  for (int b = 0; b < PB; b++) {
+    const int m = ((px_tile * WPX + wpx) * PB + b) * 16 + r;
+    mval[b] = m < p.M;
+    const int mm = mval[b] ? m : 0;
+    const int ow = mm % p.OW;
+    const int t = mm / p.OW;
+    const int oh = t % p.OH;
+    const int n = t / p.OH;
+    iy0[b] = oh * p.stride - p.pad;
+    ix0[b] = ow * p.stride - p.pad;
+    pixbase[b] = (n * p.H + iy0[b]) * p.W + ix0[b];
+    outpix[b] = (n * p.OH + oh) * p.pitch + ow;
+  }
+  const int cob0 = (co_tile * WCO + wco) * CB;
+  // Weights: a per-lane offset of the block (out of range for blocks past the
+  // end) plus a wave-uniform step offset in the scalar operand.
+  unsigned wvoff[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++)
+    wvoff[cb] = (cob0 + cb) < p.co_blocks ? ((unsigned)((cob0 + cb) * p.steps) * 64u + (unsigned)lane) * 16u
+                                          : kOutOfRange;
+  // Epilogue operands are fetched now, so their latency overlaps the main loop
+  // (out-of-range channels read as zero).
+  f32x4 ep_bias[CB], ep_dq[CB];
+  {
+    const __amdgpu_buffer_rsrc_t br =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t dr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.dq, 0, V::I8 ? (int)(p.co_blocks * 64) : 0, kRsrcWord3);
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+      const unsigned off = (unsigned)(((cob0 + cb) * 16 + 4 * g) * 4);
+      ep_bias[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ep_dq[cb] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (!V::RAW) ep_bias[cb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0));
+      if constexpr (V::I8 && !V::RAW) ep_dq[cb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, off, 0, 0));
+    }
+  }
+  const int s_begin = split * p.steps_per_split;
+  const int s_end = min(p.steps, s_begin + p.steps_per_split);
+
+  // Every operand load is a branch-free buffer load: an out-of-range byte
+  // offset returns zeros, which supplies the image's zero padding, the pixel
+  // tail, the K tail and output-channel blocks past the end without any
+  // condition around a load (so the compiler can count loads in flight and
+  // wait only for the oldest one).
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
+  auto load = [&](int s, Frag(&aa)[CB], Frag(&bb)[PB]) {
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+      aa[cb] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], s * 1024, 0));
+    if constexpr (V::VEC == 1) {
+      const Chunk c = decode_chunk(p, s * 4 + g);
+      const int doff = (c.dy * p.W + c.dx) * p.cin_pad + c.ci;
+#pragma unroll
+      for (int b = 0; b < PB; b++) {
+        const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
+        const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+        const unsigned off = v ? (unsigned)(pixbase[b] * p.cin_pad + doff) * (unsigned)V::ESIZE : kOutOfRange;
+        bb[b] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const Chunk c = decode_chunk(p, (s * 4 + g) * 4 + j);
+        const int doff = (c.dy * p.W + c.dx) * p.cin_pad + c.ci;
+#pragma unroll
+        for (int b = 0; b < PB; b++) {
+          const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
+          const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+          const unsigned off = v ? (unsigned)(pixbase[b] * p.cin_pad + doff) : kOutOfRange;
+          bb[b][j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
+        }
+      }
+    }
+  };
+
+  Acc acc[CB][PB];
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+    for (int b = 0; b < PB; b++) acc[cb][b] = Acc{};
+
+  // Independent accumulators are interleaved so consecutive MFMAs never wait
+  // on each other's result.
+  auto mma = [&](const Frag(&aa)[CB], const Frag(&bb)[PB]) {
+    if constexpr (!V::I8) {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+          for (int b = 0; b < PB; b++)
+            acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[cb][j], bb[b][j], acc[cb][b], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int b = 0; b < PB; b++)
+          acc[cb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[cb], bb[b], acc[cb][b], 0, 0, 0);
+    }
+  };
+
+  // Main loop: a ring of PF register sets keeps the loads of the next PF K
+  // steps of this wave in flight while the MFMAs of the current step run
+  // (small layers are latency-bound otherwise).  Loads past the wave's last
+  // step are clamped onto it, so every iteration issues the same loads.
+  {
+    const int s0 = s_begin + wk;
+    if (s0 < s_end) {
+      const int s_last = s0 + ((s_end - 1 - s0) / WK) * WK;
+      Frag a[PF][CB], b[PF][PB];
+#pragma unroll
+      for (int i = 0; i < PF; i++) load(min(s0 + i * WK, s_last), a[i], b[i]);
+      for (int s = s0; s < s_end; s += PF * WK) {
+#pragma unroll
+        for (int i = 0; i < PF; i++) {
+          const int si = s + i * WK;
+          if (si < s_end) mma(a[i], b[i]);
+          load(min(si + PF * WK, s_last), a[i], b[i]);
+        }
+      }
+    }
+  }
+
+  // Reduce the WK K-slices of the workgroup through LDS, in slice order.
+  if constexpr (WK > 1) {
+    __shared__ Acc red[(WK - 1) * WCO * WPX * CB * PB][64];
+    if (wk > 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int b = 0; b < PB; b++)
+          red[(((wk - 1) * WCO * WPX + slot) * CB + cb) * PB + b][lane] = acc[cb][b];
+    }
+    __syncthreads();
+    if (wk == 0) {
+      for (int w = 1; w < WK; w++)
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+          for (int b = 0; b < PB; b++)
+            acc[cb][b] += red[(((w - 1) * WCO * WPX + slot) * CB + cb) * PB + b][lane];
+    }
+  }
+
+  // Cross-workgroup split-K: publish the partial tile, take a ticket; the
+  // last workgroup of the tile sums every partial in split order.
+  if (p.splitk > 1) {
+    __shared__ int s_last;
+    constexpr int TILE_VECS = WCO * WPX * CB * PB * 64;
+    Acc *wsb = (Acc *)p.ws + (size_t)tile * p.splitk * TILE_VECS;
+    if (wk == 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int b = 0; b < PB; b++)
+          wsb[(size_t)split * TILE_VECS + ((slot * CB + cb) * PB + b) * 64 + lane] = acc[cb][b];
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned prev = atomicAdd(&p.counters[tile], 1u);
+      s_last = (prev == (unsigned)(p.splitk - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (wk == 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int b = 0; b < PB; b++) {
+          Acc sum = Acc{};
+          for (int sp = 0; sp < p.splitk; sp++) {
+            const Acc v = (sp == split)
+                              ? acc[cb][b]
+                              : __builtin_nontemporal_load(
+                                    &wsb[(size_t)sp * TILE_VECS + ((slot * CB + cb) * PB + b) * 64 + lane]);
+            sum += v;
+          }
+          acc[cb][b] = sum;
+        }
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if (wk != 0) return;
+
+  // Epilogue: bias (+ dequant) + SiLU in registers, masked 16-byte NHWC stores.
+#pragma unroll
+  for (int cb = 0; cb < CB; cb++) {
+    const int co0 = (cob0 + cb) * 16 + 4 * g;
+    if (co0 >= p.cout_pad) continue;
+    if constexpr (V::RAW) {
+#pragma unroll
+      for (int b = 0; b < PB; b++)
+        if (mval[b]) *(i32x4 *)((int *)p.out + (size_t)outpix[b] * p.cout_pad + co0) = acc[cb][b];
+    } else {
+      const f32x4 bias = ep_bias[cb];
+      const f32x4 dq = ep_dq[cb];
+#pragma unroll
+      for (int b = 0; b < PB; b++) {
+        if (!mval[b]) continue;
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float z;
+          if constexpr (V::I8)
+            z = (float)acc[cb][b][i] * dq[i] + bias[i];
+          else
+            z = acc[cb][b][i] + bias[i];
+          y[i] = silu_f(z);
+        }
+        *(f32x4 *)((float *)p.out + (size_t)outpix[b] * p.cout_pad + co0) = y;
+      }
+    }
+  }
+}
+
+
+// ------------------------------------------------------ LDS-staged kernel --
+// The workgroup stages KS K-steps of weight and activation fragments in LDS
+// (double-buffered, same fragment order and branch-free buffer loads as
+// above); its WM x WN waves split the output tile and read their operands
+// from LDS, so each fetched byte feeds several waves.  Used for the larger
+// (batch-16, 80x80 and up) layers, where the register-direct kernel is bound
+// by vector-memory issue rather than by MFMA.
+
+struct Pix {
+  int base, iy0, ix0, out;
+  bool ok;
+};
+
+__device__ __forceinline__ Pix pixel_of(const ConvParams &p, int m) {
+  Pix q;
+  q.ok = m < p.M;
+  const int mm = q.ok ? m : 0;
+  const int ow = mm % p.OW;
+  const int t = mm / p.OW;
+  const int oh = t % p.OH;
+  const int n = t / p.OH;
+  q.iy0 = oh * p.stride - p.pad;
+  q.ix0 = ow * p.stride - p.pad;
+  q.base = (n * p.H + q.iy0) * p.W + q.ix0;
+  q.out = (n * p.OH + oh) * p.pitch + ow;
+  return q;
+}
+
+// The activation fragment of one lane: pixel q, K chunk group `cg` (= 4*step + g).
+template <class V>
+__device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu_buffer_rsrc_t xr, const Pix &q,
+                                                   int cg) {
+  using Frag = typename V::Frag;
+  if constexpr (V::VEC == 1) {
+    const Chunk c = decode_chunk(p, cg);
+    const int iy = q.iy0 + c.dy, ix = q.ix0 + c.dx;
+    const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+    const unsigned off =
+        v ? (unsigned)(q.base * p.cin_pad + (c.dy * p.W + c.dx) * p.cin_pad + c.ci) * (unsigned)V::ESIZE : kOutOfRange;
+    return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+  } else {
+    Frag f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const Chunk c = decode_chunk(p, cg * 4 + j);
+      const int iy = q.iy0 + c.dy, ix = q.ix0 + c.dx;
+      const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+      const unsigned off = v ? (unsigned)(q.base * p.cin_pad + (c.dy * p.W + c.dx) * p.cin_pad + c.ci) : kOutOfRange;
+      f[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
+    }
+    return f;
+  }
+}
+
+template <int VAR, int MB, int NB, int WM, int WN, int KS>
+__global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
+  using V = Var<VAR>;
+  using Frag = typename V::Frag;
+  using Acc = typename V::Acc;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BMB = MB * WM, BNB = NB * WN;     // 16-pixel and 16-channel blocks per workgroup
+  constexpr int SB = BMB + BNB;                   // fragment blocks per K step
+  constexpr int NA = KS * BNB * 64 / NT;          // weight slots per thread per stage
+  constexpr int NX = KS * BMB * 64 / NT;          // activation slots per thread per stage
+  static_assert((KS * BNB * 64) % NT == 0 && (KS * BMB * 64) % NT == 0, "stage must split evenly over threads");
+  __shared__ Frag lds[2][KS * SB * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (see conv_igemm)
+  const int wm = wave % WM, wn = wave / WM;
+  const int r = lane & 15, g = lane >> 4;
+
+  const int nb_ = gridDim.x, bid = blockIdx.x;
+  const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  const int co_tile = logical % p.co_tiles;
+  const int px_tile = logical / p.co_tiles;
+
+  // pixels of this thread's activation slots (the same for every stage)
+  Pix xpix[NX];
+#pragma unroll
+  for (int i = 0; i < NX; i++) {
+    const int j = tid + i * NT;
+    const int pxb = (j >> 6) % BMB;
+    xpix[i] = pixel_of(p, (px_tile * BMB + pxb) * 16 + r);
+  }
+  // epilogue operands of this wave's blocks
+  f32x4 ep_bias[NB], ep_dq[NB];
+  {
+    const __amdgpu_buffer_rsrc_t br =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t dr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.dq, 0, V::I8 ? (int)(p.co_blocks * 64) : 0, kRsrcWord3);
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      const unsigned off = (unsigned)((((co_tile * BNB + wn * NB + nb) * 16) + 4 * g) * 4);
+      ep_bias[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ep_dq[nb] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (!V::RAW) ep_bias[nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0));
+      if constexpr (V::I8 && !V::RAW) ep_dq[nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, off, 0, 0));
+    }
+  }
+
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
+  const int nst = (p.steps + KS - 1) / KS;
+
+  Frag ra[NA], rx[NX];
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < NA; i++) {
+      const int j = tid + i * NT;
+      const int ks = j / (BNB * 64), blk = (j >> 6) % BNB;
+      const int s = st * KS + ks;
+      const unsigned off = s < p.steps
+                               ? ((unsigned)((co_tile * BNB + blk) * p.steps + s) * 64u + (unsigned)lane) * 16u
+                               : kOutOfRange;
+      ra[i] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < NX; i++) {
+      const int j = tid + i * NT;
+      const int ks = j / (BMB * 64);
+      const int s = st * KS + ks;
+      rx[i] = gather<V>(p, xr, xpix[i], s * 4 + g);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; i++) {
+      const int j = tid + i * NT;
+      const int ks = j / (BNB * 64), blk = (j >> 6) % BNB;
+      lds[buf][(ks * SB + blk) * 64 + lane] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NX; i++) {
+      const int j = tid + i * NT;
+      const int ks = j / (BMB * 64), pxb = (j >> 6) % BMB;
+      lds[buf][(ks * SB + BNB + pxb) * 64 + lane] = rx[i];
+    }
+  };
+
+  Acc acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) acc[nb][mb] = Acc{};
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      Frag a[NB], b[MB];
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) a[nb] = lds[buf][(ks * SB + wn * NB + nb) * 64 + lane];
+#pragma unroll
+      for (int mb = 0; mb < MB; mb++) b[mb] = lds[buf][(ks * SB + BNB + wm * MB + mb) * 64 + lane];
+      if constexpr (!V::I8) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+#pragma unroll
+          for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++)
+              acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[nb][jj], b[mb][jj], acc[nb][mb], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+          for (int mb = 0; mb < MB; mb++)
+            acc[nb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+      }
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int st = 0; st < nst; st++) {
+    const bool more = st + 1 < nst;
+    if (more) gload(st + 1);
+    compute(st & 1);
+    if (more) sstore((st + 1) & 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++) {
+    const int co0 = (co_tile * BNB + wn * NB + nb) * 16 + 4 * g;
+    if (co0 >= p.cout_pad) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+      const Pix q = pixel_of(p, (px_tile * BMB + wm * MB + mb) * 16 + r);
+      if (!q.ok) continue;
+      if constexpr (V::RAW) {
+        *(i32x4 *)((int *)p.out + (size_t)q.out * p.cout_pad + co0) = acc[nb][mb];
+      } else {
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float z;
+          if constexpr (V::I8)
+            z = (float)acc[nb][mb][i] * ep_dq[nb][i] + ep_bias[nb][i];
+          else
+            z = acc[nb][mb][i] + ep_bias[nb][i];
+          y[i] = silu_f(z);
+        }
+        *(f32x4 *)((float *)p.out + (size_t)q.out * p.cout_pad + co0) = y;
+      }
+    }
+  }
+}
+
+
+// ------------------------------------------------------ halo-tile kernel --
+// For 3x3 layers with few channels (the 3-channel stem and the 8..32-channel
+// layers at 80..320 pixels) the implicit-GEMM gather re-reads every input
+// pixel up to nine times.  Here a workgroup owns a TH x TW block of output
+// pixels of one image and all (<= 64) output channels: it copies the input
+// window it needs (the halo, all channels) and the layer's fragment-ordered
+// weights straight into LDS with direct-to-LDS buffer loads (out-of-range
+// offsets supply the zero padding), then runs every tap of the convolution
+// from LDS on MFMA.  This is the direct-convolution path for the stem.
+template <int VAR, int TH, int TW>
+__global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
+  using V = Var<VAR>;
+  using Frag = typename V::Frag;
+  using Acc = typename V::Acc;
+  constexpr int NBMAX = 4;
+  constexpr int MB = TH * TW / 64;  // 16-pixel blocks per wave (4 waves)
+  static_assert(TH * TW % 64 == 0, "tile must split into 4 waves of 16-pixel blocks");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  typedef __attribute__((address_space(3))) void *lds_ptr;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (see conv_igemm)
+  const int r = lane & 15, g = lane >> 4;
+
+  const int nb_ = gridDim.x, bid = blockIdx.x;
+  const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
+  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  const int tx = logical % p.tiles_x;
+  const int rest = logical / p.tiles_x;
+  const int ty = rest % p.tiles_y;
+  const int n = rest / p.tiles_y;
+
+  const int st_ = p.stride;
+  const int HWd = (TW - 1) * st_ + 3;  // halo width in pixels
+  const int HH = (TH - 1) * st_ + 3;   // halo height
+  const int oh0 = ty * TH, ow0 = tx * TW;
+  const int iy0 = oh0 * st_ - p.pad, ix0 = ow0 * st_ - p.pad;
+  const int cq = p.cin_pad >> 2;                 // 4-channel slots per pixel
+  constexpr int SLOT = 4 * V::ESIZE;             // bytes of a 4-channel slot
+  const int halo_slots = HH * HWd * cq;
+
+  // 1) input halo and weights -> LDS (all loads in flight, no register round trip)
+  {
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
+    for (int base = wave * 64; base < halo_slots; base += 256) {
+      const int sl = base + lane;
+      const int q = sl % cq;
+      const int px = sl / cq;
+      const int hx = px % HWd, hy = px / HWd;
+      const int iy = iy0 + hy, ix = ix0 + hx;
+      const bool v = sl < halo_slots && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+      const unsigned off = v ? (unsigned)(((n * p.H + iy) * p.W + ix) * p.cin_pad + 4 * q) * (unsigned)V::ESIZE
+                             : kOutOfRange;
+      if constexpr (SLOT == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(smem + base * SLOT), 16, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(smem + base * SLOT), 4, off, 0, 0, 0);
+    }
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
+    const int wslots = (int)(p.w_bytes >> 4);
+    for (int base = wave * 64; base < wslots; base += 256)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr)(smem + p.halo_bytes + base * 16), 16,
+                                               (unsigned)(base + lane) * 16u, 0, 0, 0);
+  }
+  // epilogue operands meanwhile
+  const int nbl = p.co_blocks;  // <= NBMAX, uniform
+  f32x4 ep_bias[NBMAX], ep_dq[NBMAX];
+  {
+    const __amdgpu_buffer_rsrc_t br =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t dr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.dq, 0, V::I8 ? (int)(p.co_blocks * 64) : 0, kRsrcWord3);
+#pragma unroll
+    for (int nb = 0; nb < NBMAX; nb++) {
+      const unsigned off = (unsigned)((nb * 16 + 4 * g) * 4);
+      ep_bias[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ep_dq[nb] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (!V::RAW) ep_bias[nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0));
+      if constexpr (V::I8 && !V::RAW) ep_dq[nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, off, 0, 0));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // 2) every tap from LDS: lane (r, g) of block mb holds pixel r of that block
+  int lbase[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) {
+    const int pi = (wave * MB + mb) * 16 + r;
+    const int ly = pi / TW, lx = pi % TW;
+    lbase[mb] = (ly * st_) * HWd + lx * st_;
+  }
+  const unsigned char *wl = smem + p.halo_bytes;
+  const int pix_bytes = p.cin_pad * V::ESIZE;
+  Acc acc[NBMAX][MB];
+#pragma unroll
+  for (int nb = 0; nb < NBMAX; nb++)
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) acc[nb][mb] = Acc{};
+
+  for (int s = 0; s < p.steps; s++) {
+    Frag a[NBMAX];
+#pragma unroll
+    for (int nb = 0; nb < NBMAX; nb++)
+      a[nb] = nb < nbl ? *(const Frag *)(wl + ((nb * p.steps + s) * 64 + lane) * 16) : Frag{};
+    Frag b[MB];
+    if constexpr (V::VEC == 1) {
+      Chunk c = decode_chunk(p, s * 4 + g);
+      if (!c.ok) c.dy = c.dx = c.ci = 0;  // past K: read a valid slot, then zero it
+#pragma unroll
+      for (int mb = 0; mb < MB; mb++) {
+        const Frag v = *(const Frag *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci * V::ESIZE);
+        b[mb] = c.ok ? v : Frag{};
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; mb++) b[mb] = Frag{};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        Chunk c = decode_chunk(p, (s * 4 + g) * 4 + j);
+        if (!c.ok) c.dy = c.dx = c.ci = 0;
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) {
+          const int v = *(const int *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci);
+          b[mb][j] = c.ok ? v : 0;
+        }
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBMAX; nb++) {
+      if (nb >= nbl) break;
+      if constexpr (!V::I8) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+#pragma unroll
+          for (int mb = 0; mb < MB; mb++)
+            acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[nb][jj], b[mb][jj], acc[nb][mb], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++)
+          acc[nb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
+      }
+    }
+  }
+
+  // 3) epilogue, masked to the image and to the real channels
+#pragma unroll
+  for (int nb = 0; nb < NBMAX; nb++) {
+    if (nb >= nbl) break;
+    const int co0 = nb * 16 + 4 * g;
+    if (co0 >= p.cout_pad) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+      const int pi = (wave * MB + mb) * 16 + r;
+      const int oh = oh0 + pi / TW, ow = ow0 + pi % TW;
+      if (oh >= p.OH || ow >= p.OW) continue;
+      const size_t o = ((size_t)(n * p.OH + oh) * p.pitch + ow) * p.cout_pad + co0;
+      if constexpr (V::RAW) {
+        *(i32x4 *)((int *)p.out + o) = acc[nb][mb];
+      } else {
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float z;
+          if constexpr (V::I8)
+            z = (float)acc[nb][mb][i] * ep_dq[nb][i] + ep_bias[nb][i];
+          else
+            z = acc[nb][mb][i] + ep_bias[nb][i];
+          y[i] = silu_f(z);
+        }
+        *(f32x4 *)((float *)p.out + o) = y;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launch --
+template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
+static hipError_t launch_one(const ConvParams &p, hipStream_t stream) {
+  const unsigned grid = (unsigned)p.px_tiles * (unsigned)p.co_tiles * (unsigned)p.splitk;
+  hipLaunchKernelGGL((conv_igemm<VAR, CB, PB, WCO, WPX, WK, PF>), dim3(grid), dim3(64 * WCO * WPX * WK), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int VAR, int MB, int NB, int WM, int WN, int KS>
+static hipError_t launch_lds(const ConvParams &p, hipStream_t stream) {
+  if (p.splitk != 1) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)p.px_tiles * (unsigned)p.co_tiles;
+  hipLaunchKernelGGL((conv_lds<VAR, MB, NB, WM, WN, KS>), dim3(grid), dim3(64 * WM * WN), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int VAR, int TH, int TW>
+static hipError_t launch_halo(const ConvParams &p, hipStream_t stream) {
+  if (p.splitk != 1 || p.co_blocks > 4 || p.k != 3) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)p.px_tiles;
+  hipLaunchKernelGGL((conv_halo<VAR, TH, TW>), dim3(grid), dim3(256), (unsigned)p.smem_bytes, stream, p);
+  return hipGetLastError();
+}
+
+// Launch configuration `cfg` of variant VAR.
+template <int VAR>
+static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t stream) {
+  switch (cfg) {
+#define X(id, cb, pb, wco, wpx, wk, pf, name) \
+  case id:                                    \
+    return launch_one<VAR, cb, pb, wco, wpx, wk, pf>(p, stream);
+    CBS_CONFIG_LIST(X)
+#undef X
+#define X(id, mb, nb, wm, wn, ks, name) \
+  case id:                              \
+    return launch_lds<VAR, mb, nb, wm, wn, ks>(p, stream);
+    CBS_LDS_CONFIG_LIST(X)
+#undef X
+#define X(id, th, tw, name) \
+  case id:                  \
+    return launch_halo<VAR, th, tw>(p, stream);
+    CBS_HALO_CONFIG_LIST(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace cbs
