@@ -13,7 +13,11 @@ Sources (the pages the method comes from):
     contraction over C_in, kH, kW).
   * "Edge optimisation of YOLO26" (edge-optimization README): "Highlights" and
     "Design notes" (per-output-channel int8 weights, symmetric scales,
-    percentile calibration of activations).
+    percentile calibration of activations; INT8 end to end).
+  * "YOLO26N Inference Optimisation", section "Improvements" #6 and #7 and
+    "NHWC migration -- Op-by-op impact across the graph": bias-only convs,
+    residual adds after the activation, channel cat / chunk (the layout side
+    of these is plain numpy slicing in the tests; the oracle sees NCHW).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against closed forms,
 invariants, numpy library routines on special cases and brute force.
@@ -92,12 +96,46 @@ def _load():
             lib.oracle_conv_bn_silu_i8_points.argtypes = [P, F, P, P, P, P, P, D, I, I, I, I, I, I, I, I,
                                                           P, L, P, P, P]
             lib.oracle_conv_bn_silu_i8_points.restype = L
+            lib.oracle_conv_bn_act_f32.argtypes = [P, P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, P, P, P]
+            lib.oracle_conv_bn_act_f32.restype = None
+            lib.oracle_conv_bn_act_f32_points.argtypes = [P, P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, P,
+                                                          P, L, P, P]
+            lib.oracle_conv_bn_act_f32_points.restype = None
+            lib.oracle_epilogue_i8_act.argtypes = [P, I, I, I, F, P, P, I, P, P, P]
+            lib.oracle_epilogue_i8_act.restype = None
+            lib.oracle_conv_bn_act_i8.argtypes = [P, F, P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, P,
+                                                  P, P, P, P, P, P]
+            lib.oracle_conv_bn_act_i8.restype = L
+            lib.oracle_conv_bn_act_i8_points.argtypes = [P, F, P, P, P, P, P, D, I, I, I, I, I, I, I, I, I,
+                                                         P, P, L, P, P, P]
+            lib.oracle_conv_bn_act_i8_points.restype = L
             _lib = lib
     return _lib
 
 
 def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+# Epilogue activations: "silu" (the block's SiLU) or "none" (identity: a plain
+# conv + bias, as the head's final convs).
+_ACT = {"silu": 0, "none": 1}
+
+
+def _act(act: str) -> int:
+    if act not in _ACT:
+        raise ValueError("activation %r not in %s" % (act, sorted(_ACT)))
+    return _ACT[act]
+
+
+def _res(residual, shape):
+    """Residual as a C-contiguous float64 array of the output's shape (or None)."""
+    if residual is None:
+        return None
+    r = np.ascontiguousarray(residual, dtype=np.float64)
+    if r.shape != tuple(shape):
+        raise ValueError("residual shape %s != output shape %s" % (r.shape, tuple(shape)))
+    return r
 
 
 def _f32(a):
@@ -169,6 +207,24 @@ def conv_bn_silu_f32(x, w, gamma, beta, mean, var, eps: float, stride: int, pad:
     return y, s
 
 
+def conv_bn_act_f32(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: int, act: str = "silu",
+                    residual=None, with_bound: bool = True):
+    """y = act(BN(conv(x, W))) + residual in double (residual NCHW like y, or None);
+    also S = sum |W' * x| per output.  Returns (y, S)."""
+    x = _f32(x)
+    w = _f32(w)
+    n, c_in, h, wd = x.shape
+    c_out, _, k, _ = w.shape
+    oh, ow = out_dim(h, k, stride, pad), out_dim(wd, k, stride, pad)
+    y = np.empty((n, c_out, oh, ow), np.float64)
+    r = _res(residual, y.shape)
+    s = np.empty_like(y) if with_bound else None
+    _load().oracle_conv_bn_act_f32(_p(x), _p(w), _p(_f32(gamma)), _p(_f32(beta)), _p(_f32(mean)),
+                                   _p(_f32(var)), float(eps), n, c_in, h, wd, c_out, k, stride, pad, _act(act),
+                                   _p(r), _p(y), _p(s))
+    return y, s
+
+
 def quantize_weights(w_folded):
     """Per-output-channel symmetric int8: returns (q int8 same shape, s_w float64 [C_out])."""
     wf = np.ascontiguousarray(w_folded, dtype=np.float64)
@@ -185,6 +241,14 @@ def quantize_activations(x, s_x: float) -> np.ndarray:
     q = np.empty(x.shape, np.int8)
     _load().oracle_quantize_activations(_p(x), x.size, float(np.float32(s_x)), _p(q))
     return q
+
+
+def requantize(y, s_y: float) -> np.ndarray:
+    """INT8 output codes of a layer: the activation quantiser applied to the
+    fp32 value of y (float64 -> float32 rounds to nearest even), i.e. the codes
+    the next INT8 layer would get from this layer's fp32 output."""
+    y32 = np.asarray(y, dtype=np.float64).astype(np.float32)
+    return quantize_activations(y32, s_y)
 
 
 def conv_i8_acc(qx, qw, stride: int, pad: int) -> np.ndarray:
@@ -224,6 +288,20 @@ def epilogue_i8(acc, s_x: float, s_w, b_folded):
     return y, f
 
 
+def epilogue_i8_act(acc, s_x: float, s_w, b_folded, act: str = "silu", residual=None):
+    """y = act(acc * fp32(s_x*s_w[co]) + b'[co]) + residual; returns (y float64, f float32 [C_out])."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    n, c_out, oh, ow = acc.shape
+    y = np.empty(acc.shape, np.float64)
+    r = _res(residual, y.shape)
+    f = np.empty((c_out,), np.float32)
+    _load().oracle_epilogue_i8_act(_p(acc), n, c_out, oh * ow, float(np.float32(s_x)),
+                                   _p(np.ascontiguousarray(s_w, dtype=np.float64)),
+                                   _p(np.ascontiguousarray(b_folded, dtype=np.float64)), _act(act), _p(r),
+                                   _p(y), _p(f))
+    return y, f
+
+
 def percentile_abs(x, q: float) -> float:
     """q-th percentile of |x| ('linear' definition)."""
     x = _f32(x).ravel()
@@ -250,6 +328,31 @@ def conv_bn_silu_i8(x, s_x: float, w, gamma, beta, mean, var, eps: float, stride
                                          _p(_f32(beta)), _p(_f32(mean)), _p(_f32(var)), float(eps),
                                          n, c_in, h, wd, c_out, k, stride, pad, _p(y), _p(acc), _p(qw),
                                          _p(sw), _p(f), _p(absacc))
+    if ovf != 0:
+        raise OverflowError("int8 oracle: %d accumulators outside int32 (or allocation failure)" % ovf)
+    return {"y": y, "acc": acc, "qw": qw, "s_w": sw, "f": f, "absacc": absacc}
+
+
+def conv_bn_act_i8(x, s_x: float, w, gamma, beta, mean, var, eps: float, stride: int, pad: int,
+                   act: str = "silu", residual=None, with_bound: bool = True) -> dict:
+    """The INT8 block with the epilogue options: y = act(acc * f + b') + residual
+    (residual float64 NCHW like y, or None).  Same dict as conv_bn_silu_i8."""
+    x = _f32(x)
+    w = _f32(w)
+    n, c_in, h, wd = x.shape
+    c_out, _, k, _ = w.shape
+    oh, ow = out_dim(h, k, stride, pad), out_dim(wd, k, stride, pad)
+    y = np.empty((n, c_out, oh, ow), np.float64)
+    r = _res(residual, y.shape)
+    acc = np.empty((n, c_out, oh, ow), np.int32)
+    qw = np.empty(w.shape, np.int8)
+    sw = np.empty((c_out,), np.float64)
+    f = np.empty((c_out,), np.float32)
+    absacc = np.empty((n, c_out, oh, ow), np.int64) if with_bound else None
+    ovf = _load().oracle_conv_bn_act_i8(_p(x), float(np.float32(s_x)), _p(w), _p(_f32(gamma)),
+                                        _p(_f32(beta)), _p(_f32(mean)), _p(_f32(var)), float(eps),
+                                        n, c_in, h, wd, c_out, k, stride, pad, _act(act), _p(r), _p(y), _p(acc),
+                                        _p(qw), _p(sw), _p(f), _p(absacc))
     if ovf != 0:
         raise OverflowError("int8 oracle: %d accumulators outside int32 (or allocation failure)" % ovf)
     return {"y": y, "acc": acc, "qw": qw, "s_w": sw, "f": f, "absacc": absacc}
@@ -290,6 +393,54 @@ def conv_bn_silu_i8_points(x, s_x: float, w, gamma, beta, mean, var, eps: float,
                                                 _p(_f32(beta)), _p(_f32(mean)), _p(_f32(var)), float(eps),
                                                 n, c_in, h, wd, c_out, k, stride, pad, _p(pts), npts,
                                                 _p(y), _p(acc), _p(absacc))
+    if ovf != 0:
+        raise OverflowError("int8 oracle points: %d accumulators outside int32 (or allocation failure)" % ovf)
+    return y, acc, absacc
+
+
+def _res_pts(res_pts, npts):
+    if res_pts is None:
+        return None
+    r = np.ascontiguousarray(res_pts, dtype=np.float64).ravel()
+    if r.size != npts:
+        raise ValueError("residual values %d != points %d" % (r.size, npts))
+    return r
+
+
+def conv_bn_act_f32_points(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: int, pts,
+                           act: str = "silu", res_pts=None):
+    """conv_bn_act_f32 at the outputs pts[i] = (b, co, oh, ow) only; res_pts[i] is the
+    residual at output i (or None).  Returns (y, S) float64 [npts]."""
+    x = _f32(x)
+    w = _f32(w)
+    n, c_in, h, wd = x.shape
+    c_out, _, k, _ = w.shape
+    pts, npts = _points(pts)
+    r = _res_pts(res_pts, npts)
+    y = np.empty((npts,), np.float64)
+    s = np.empty((npts,), np.float64)
+    _load().oracle_conv_bn_act_f32_points(_p(x), _p(w), _p(_f32(gamma)), _p(_f32(beta)), _p(_f32(mean)),
+                                          _p(_f32(var)), float(eps), n, c_in, h, wd, c_out, k, stride, pad,
+                                          _act(act), _p(r), _p(pts), npts, _p(y), _p(s))
+    return y, s
+
+
+def conv_bn_act_i8_points(x, s_x: float, w, gamma, beta, mean, var, eps: float, stride: int, pad: int, pts,
+                          act: str = "silu", res_pts=None):
+    """conv_bn_act_i8 at the outputs pts only: returns (y float64, acc int32, absacc int64), each [npts]."""
+    x = _f32(x)
+    w = _f32(w)
+    n, c_in, h, wd = x.shape
+    c_out, _, k, _ = w.shape
+    pts, npts = _points(pts)
+    r = _res_pts(res_pts, npts)
+    y = np.empty((npts,), np.float64)
+    acc = np.empty((npts,), np.int32)
+    absacc = np.empty((npts,), np.int64)
+    ovf = _load().oracle_conv_bn_act_i8_points(_p(x), float(np.float32(s_x)), _p(w), _p(_f32(gamma)),
+                                               _p(_f32(beta)), _p(_f32(mean)), _p(_f32(var)), float(eps),
+                                               n, c_in, h, wd, c_out, k, stride, pad, _act(act), _p(r), _p(pts),
+                                               npts, _p(y), _p(acc), _p(absacc))
     if ovf != 0:
         raise OverflowError("int8 oracle points: %d accumulators outside int32 (or allocation failure)" % ovf)
     return y, acc, absacc

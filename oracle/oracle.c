@@ -36,6 +36,16 @@
  *  - INT8 epilogue: y = SiLU(acc * f[co] + b'[co]) with f = fp32(s_x * s_w).
  *  - Percentile: the 'linear' definition (position q*(n-1) in the sorted
  *    sample, linear interpolation between the two neighbours).
+ *  - Fused epilogue options ("YOLO26N Inference Optimisation", section
+ *    "Improvements" #7: bias and residual adds in the conv epilogue; the
+ *    plain conv2d_forward + nchw_bias_add of section "nsys kernel-level
+ *    breakdown"): the activation is SiLU or the identity, and a residual r is
+ *    added after the activation, y = act(z) + r (the shortcut of a YOLO
+ *    bottleneck adds its input to the output of its second conv block).
+ *  - INT8 output (edge-optimization README, "Highlights": the network runs in
+ *    INT8 end to end): the output codes are the activation quantiser applied
+ *    to the fp32 value of y, q_y = clamp(rne(fp32(fp32(y) / s_y)), -127, 127);
+ *    an int8 residual contributes r = s_r * q_r.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (see build.py).
  * -ffp-contract=off keeps every multiply and add separately rounded, so the
@@ -126,6 +136,9 @@ void oracle_conv2d(const float *x, const float *wt, int n, int c_in, int h, int 
 /* SiLU(z) = z * sigmoid(z) = z / (1 + e^-z). */
 double oracle_silu1(double z) { return z / (1.0 + exp(-z)); }
 
+/* The activation of the epilogue: act 0 = SiLU, act 1 = identity. */
+static double act1(int act, double z) { return act == 1 ? z : oracle_silu1(z); }
+
 void oracle_silu(const double *z, double *y, long count) {
     for (long i = 0; i < count; i++) y[i] = oracle_silu1(z[i]);
 }
@@ -159,20 +172,25 @@ void oracle_bn_fold(const float *wt, int c_out, int per_co, const float *gamma, 
 }
 
 /*
- * The fused FP32 block, unfolded: y = SiLU(BN(conv(x, W))), computed as
- * conv -> batch norm -> SiLU in double.  Also returns, per output,
+ * The fused FP32 block, unfolded: y = act(BN(conv(x, W))) (+ residual),
+ * computed as conv -> batch norm -> activation -> residual add in double
+ * (act 0 = SiLU, 1 = identity; residual is an NCHW double tensor shaped like
+ * y, or NULL).  Also returns, per output,
  *   sabs[n,co,oh,ow] = sum |W'[co,ci,i,j] * x~[...]|   with W' the folded weights,
  * the magnitude that scales the parity tolerance.
  */
-void oracle_conv_bn_silu_f32(const float *x, const float *wt, const float *gamma,
-                             const float *beta, const float *mean, const float *var, double eps,
-                             int n, int c_in, int h, int w, int c_out, int k, int s, int p,
-                             double *y, double *sabs) {
+void oracle_conv_bn_act_f32(const float *x, const float *wt, const float *gamma,
+                            const float *beta, const float *mean, const float *var, double eps,
+                            int n, int c_in, int h, int w, int c_out, int k, int s, int p, int act,
+                            const double *residual, double *y, double *sabs) {
     int oh_n = oracle_out_dim(h, k, s, p), ow_n = oracle_out_dim(w, k, s, p);
     size_t count = (size_t)n * c_out * oh_n * ow_n;
     oracle_conv2d(x, wt, n, c_in, h, w, c_out, k, s, p, y);
     oracle_batchnorm(y, n, c_out, oh_n * ow_n, gamma, beta, mean, var, eps);
-    oracle_silu(y, y, (long)count);
+    for (size_t i = 0; i < count; i++) {
+        y[i] = act1(act, y[i]);
+        if (residual) y[i] += residual[i];
+    }
     if (sabs) {
         dims_t d = make_dims(n, c_in, h, w, c_out, k, s, p);
 #pragma omp parallel for collapse(2) schedule(static)
@@ -187,26 +205,45 @@ void oracle_conv_bn_silu_f32(const float *x, const float *wt, const float *gamma
     }
 }
 
+/* The plain block, y = SiLU(BN(conv(x, W))). */
+void oracle_conv_bn_silu_f32(const float *x, const float *wt, const float *gamma,
+                             const float *beta, const float *mean, const float *var, double eps,
+                             int n, int c_in, int h, int w, int c_out, int k, int s, int p,
+                             double *y, double *sabs) {
+    oracle_conv_bn_act_f32(x, wt, gamma, beta, mean, var, eps, n, c_in, h, w, c_out, k, s, p, 0, NULL, y,
+                           sabs);
+}
+
 /*
  * The same fused FP32 block evaluated only at the given outputs: pts holds
  * npts quadruples (b, co, oh, ow); y[i] and sabs[i] (may be NULL) receive the
  * value and the tolerance magnitude of output i.  Used to check full-size
  * layers on a sample of outputs.
  */
-void oracle_conv_bn_silu_f32_points(const float *x, const float *wt, const float *gamma,
-                                    const float *beta, const float *mean, const float *var,
-                                    double eps, int n, int c_in, int h, int w, int c_out, int k,
-                                    int s, int p, const int32_t *pts, long npts, double *y,
-                                    double *sabs) {
+void oracle_conv_bn_act_f32_points(const float *x, const float *wt, const float *gamma,
+                                   const float *beta, const float *mean, const float *var,
+                                   double eps, int n, int c_in, int h, int w, int c_out, int k,
+                                   int s, int p, int act, const double *res_pts,
+                                   const int32_t *pts, long npts, double *y, double *sabs) {
     dims_t d = make_dims(n, c_in, h, w, c_out, k, s, p);
 #pragma omp parallel for schedule(dynamic, 16)
     for (long t = 0; t < npts; t++) {
         int b = pts[4 * t], co = pts[4 * t + 1], oh = pts[4 * t + 2], ow = pts[4 * t + 3];
         double conv = conv_at(x, wt, &d, b, co, oh, ow, 0, 0.0);
         double bn = (conv - (double)mean[co]) / sqrt((double)var[co] + eps) * (double)gamma[co] + (double)beta[co];
-        y[t] = oracle_silu1(bn);
+        y[t] = act1(act, bn);
+        if (res_pts) y[t] += res_pts[t];
         if (sabs) sabs[t] = conv_at(x, wt, &d, b, co, oh, ow, 1, (double)gamma[co] / sqrt((double)var[co] + eps));
     }
+}
+
+void oracle_conv_bn_silu_f32_points(const float *x, const float *wt, const float *gamma,
+                                    const float *beta, const float *mean, const float *var,
+                                    double eps, int n, int c_in, int h, int w, int c_out, int k,
+                                    int s, int p, const int32_t *pts, long npts, double *y,
+                                    double *sabs) {
+    oracle_conv_bn_act_f32_points(x, wt, gamma, beta, mean, var, eps, n, c_in, h, w, c_out, k, s, p, 0, NULL,
+                                  pts, npts, y, sabs);
 }
 
 /* ---------------------------------------------------------------- INT8 -- */
@@ -270,21 +307,31 @@ long oracle_conv_i8_acc(const int8_t *qx, const int8_t *qw, int n, int c_in, int
 }
 
 /*
- * INT8 epilogue: dequantise, add the folded bias, SiLU, all in double:
- *   f[co] = fp32(s_x * s_w[co]),  y = SiLU(acc * f[co] + b'[co]).
+ * INT8 epilogue: dequantise, add the folded bias, activation, residual, all
+ * in double:
+ *   f[co] = fp32(s_x * s_w[co]),  y = act(acc * f[co] + b'[co]) (+ residual).
+ * act 0 = SiLU, 1 = identity; residual (NCHW double like y) may be NULL.
  * f_out (may be NULL) receives the fp32 dequantisation factors.
  */
-void oracle_epilogue_i8(const int32_t *acc, int n, int c_out, int hw, float s_x, const double *s_w,
-                        const double *b_folded, double *y, float *f_out) {
+void oracle_epilogue_i8_act(const int32_t *acc, int n, int c_out, int hw, float s_x, const double *s_w,
+                            const double *b_folded, int act, const double *residual, double *y,
+                            float *f_out) {
     for (int co = 0; co < c_out; co++) {
         float f = (float)((double)s_x * s_w[co]);
         if (f_out) f_out[co] = f;
         for (int b = 0; b < n; b++) {
             size_t base = ((size_t)b * c_out + co) * hw;
-            for (int i = 0; i < hw; i++)
-                y[base + i] = oracle_silu1((double)acc[base + i] * (double)f + b_folded[co]);
+            for (int i = 0; i < hw; i++) {
+                y[base + i] = act1(act, (double)acc[base + i] * (double)f + b_folded[co]);
+                if (residual) y[base + i] += residual[base + i];
+            }
         }
     }
+}
+
+void oracle_epilogue_i8(const int32_t *acc, int n, int c_out, int hw, float s_x, const double *s_w,
+                        const double *b_folded, double *y, float *f_out) {
+    oracle_epilogue_i8_act(acc, n, c_out, hw, s_x, s_w, b_folded, 0, NULL, y, f_out);
 }
 
 /*
@@ -342,11 +389,11 @@ double oracle_percentile_abs(const float *x, long count, double q) {
  * convolution, dequant + bias + SiLU.  Any output pointer may be NULL except y.
  * Returns the int32 overflow count of the accumulators (0 expected).
  */
-long oracle_conv_bn_silu_i8(const float *x, float s_x, const float *wt, const float *gamma,
-                            const float *beta, const float *mean, const float *var, double eps,
-                            int n, int c_in, int h, int w, int c_out, int k, int s, int p,
-                            double *y, int32_t *acc_out, int8_t *qw_out, double *sw_out,
-                            float *f_out, int64_t *absacc_out) {
+long oracle_conv_bn_act_i8(const float *x, float s_x, const float *wt, const float *gamma,
+                           const float *beta, const float *mean, const float *var, double eps,
+                           int n, int c_in, int h, int w, int c_out, int k, int s, int p, int act,
+                           const double *residual, double *y, int32_t *acc_out, int8_t *qw_out,
+                           double *sw_out, float *f_out, int64_t *absacc_out) {
     int per_co = c_in * k * k;
     int oh_n = oracle_out_dim(h, k, s, p), ow_n = oracle_out_dim(w, k, s, p);
     size_t nx = (size_t)n * c_in * h * w, ny = (size_t)n * c_out * oh_n * ow_n;
@@ -362,7 +409,7 @@ long oracle_conv_bn_silu_i8(const float *x, float s_x, const float *wt, const fl
     oracle_quantize_weights(wf, c_out, per_co, qw, sw);
     oracle_quantize_activations(x, (long)nx, s_x, qx);
     ovf = oracle_conv_i8_acc(qx, qw, n, c_in, h, w, c_out, k, s, p, acc);
-    oracle_epilogue_i8(acc, n, c_out, oh_n * ow_n, s_x, sw, bf, y, f_out);
+    oracle_epilogue_i8_act(acc, n, c_out, oh_n * ow_n, s_x, sw, bf, act, residual, y, f_out);
     if (acc_out) memcpy(acc_out, acc, sizeof(int32_t) * ny);
     if (qw_out) memcpy(qw_out, qw, (size_t)c_out * per_co);
     if (sw_out) memcpy(sw_out, sw, sizeof(double) * (size_t)c_out);
@@ -372,17 +419,26 @@ done:
     return ovf;
 }
 
+long oracle_conv_bn_silu_i8(const float *x, float s_x, const float *wt, const float *gamma,
+                            const float *beta, const float *mean, const float *var, double eps,
+                            int n, int c_in, int h, int w, int c_out, int k, int s, int p,
+                            double *y, int32_t *acc_out, int8_t *qw_out, double *sw_out,
+                            float *f_out, int64_t *absacc_out) {
+    return oracle_conv_bn_act_i8(x, s_x, wt, gamma, beta, mean, var, eps, n, c_in, h, w, c_out, k, s, p, 0,
+                                 NULL, y, acc_out, qw_out, sw_out, f_out, absacc_out);
+}
+
 /*
  * The INT8 block evaluated only at the given outputs (pts: npts quadruples
  * b, co, oh, ow): fold, quantise weights, quantise the whole input, then the
  * integer sums and the epilogue at each point.  acc_out / absacc_out may be
  * NULL.  Returns the int32 overflow count (0 expected), -1 on allocation failure.
  */
-long oracle_conv_bn_silu_i8_points(const float *x, float s_x, const float *wt, const float *gamma,
-                                   const float *beta, const float *mean, const float *var,
-                                   double eps, int n, int c_in, int h, int w, int c_out, int k,
-                                   int s, int p, const int32_t *pts, long npts, double *y,
-                                   int32_t *acc_out, int64_t *absacc_out) {
+long oracle_conv_bn_act_i8_points(const float *x, float s_x, const float *wt, const float *gamma,
+                                  const float *beta, const float *mean, const float *var,
+                                  double eps, int n, int c_in, int h, int w, int c_out, int k,
+                                  int s, int p, int act, const double *res_pts, const int32_t *pts,
+                                  long npts, double *y, int32_t *acc_out, int64_t *absacc_out) {
     dims_t d = make_dims(n, c_in, h, w, c_out, k, s, p);
     int per_co = c_in * k * k;
     size_t nx = (size_t)n * c_in * h * w;
@@ -403,11 +459,21 @@ long oracle_conv_bn_silu_i8_points(const float *x, float s_x, const float *wt, c
         int64_t acc = conv_i8_at(qx, qw, &d, b, co, oh, ow, &a);
         if (acc > INT32_MAX || acc < INT32_MIN) ovf++;
         float f = (float)((double)s_x * sw[co]);
-        y[t] = oracle_silu1((double)(int32_t)acc * (double)f + bf[co]);
+        y[t] = act1(act, (double)(int32_t)acc * (double)f + bf[co]);
+        if (res_pts) y[t] += res_pts[t];
         if (acc_out) acc_out[t] = (int32_t)acc;
         if (absacc_out) absacc_out[t] = a;
     }
 done:
     free(wf); free(bf); free(sw); free(qw); free(qx);
     return ovf;
+}
+
+long oracle_conv_bn_silu_i8_points(const float *x, float s_x, const float *wt, const float *gamma,
+                                   const float *beta, const float *mean, const float *var,
+                                   double eps, int n, int c_in, int h, int w, int c_out, int k,
+                                   int s, int p, const int32_t *pts, long npts, double *y,
+                                   int32_t *acc_out, int64_t *absacc_out) {
+    return oracle_conv_bn_act_i8_points(x, s_x, wt, gamma, beta, mean, var, eps, n, c_in, h, w, c_out, k, s, p,
+                                        0, NULL, pts, npts, y, acc_out, absacc_out);
 }
