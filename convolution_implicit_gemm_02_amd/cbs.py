@@ -30,6 +30,8 @@ CBS_EDEVICE = -4
 CBS_ELAUNCH = -5
 CBS_F32 = 0
 CBS_I8 = 1
+CBS_ACT_SILU = 0
+CBS_ACT_NONE = 1
 
 _STATUS_NAMES = {0: "CBS_OK", -1: "CBS_EINVAL", -2: "CBS_EUNSUPPORTED", -3: "CBS_ENOMEM",
                  -4: "CBS_EDEVICE", -5: "CBS_ELAUNCH"}
@@ -46,7 +48,10 @@ class cbs_conv_desc(ctypes.Structure):
                 ("w", ctypes.c_int32), ("c_out", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("stride", ctypes.c_int32), ("pad", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_row_pitch", ctypes.c_int32), ("in_scale", ctypes.c_float),
-                ("bn_eps", ctypes.c_float)]
+                ("bn_eps", ctypes.c_float), ("act", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("out_scale", ctypes.c_float), ("in_c_stride", ctypes.c_int32), ("in_c_offset", ctypes.c_int32),
+                ("out_c_stride", ctypes.c_int32), ("out_c_offset", ctypes.c_int32),
+                ("res_c_stride", ctypes.c_int32), ("res_c_offset", ctypes.c_int32), ("res_scale", ctypes.c_float)]
 
 
 class cbs_layer_info_t(ctypes.Structure):
@@ -54,7 +59,13 @@ class cbs_layer_info_t(ctypes.Structure):
                 ("ow", ctypes.c_int32), ("out_row_pitch", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("in_bytes", ctypes.c_int64), ("out_bytes", ctypes.c_int64), ("flops", ctypes.c_int64),
                 ("alg_bytes", ctypes.c_int64), ("config", ctypes.c_int32), ("splitk", ctypes.c_int32),
-                ("grid", ctypes.c_int32), ("threads", ctypes.c_int32), ("config_name", ctypes.c_char * 48)]
+                ("grid", ctypes.c_int32), ("threads", ctypes.c_int32), ("config_name", ctypes.c_char * 48),
+                ("res_bytes", ctypes.c_int64)]
+
+
+class cbs_step(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_void_p), ("in_", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("residual", ctypes.c_void_p)]
 
 
 # Every symbol the header declares, with (restype, argtypes).
@@ -65,6 +76,9 @@ _SIGNATURES = {
     "cbs_create_layer_folded": (_I, [ctypes.POINTER(cbs_conv_desc), _P, _P, _P, ctypes.POINTER(_P)]),
     "cbs_destroy_layer": (None, [_P]),
     "cbs_run_layer": (_I, [_P, _P, _P, _P]),
+    "cbs_run_layer_res": (_I, [_P, _P, _P, _P, _P]),
+    "cbs_run_steps": (_I, [ctypes.POINTER(cbs_step), _I, _P]),
+    "cbs_graph_create_steps": (_I, [ctypes.POINTER(cbs_step), _I, _P, ctypes.POINTER(_P)]),
     "cbs_run_layer_list": (_I, [ctypes.POINTER(_P), _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
     "cbs_graph_create": (_I, [ctypes.POINTER(_P), _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _P,
                               ctypes.POINTER(_P)]),
@@ -137,9 +151,11 @@ class Layer:
 
 
 def make_desc(n, c_in, h, w, c_out, k, stride, pad, dtype=CBS_F32, out_row_pitch=0, in_scale=0.0,
-              bn_eps=1e-3) -> cbs_conv_desc:
+              bn_eps=1e-3, act=CBS_ACT_SILU, out_dtype=CBS_F32, out_scale=0.0, in_c_stride=0, in_c_offset=0,
+              out_c_stride=0, out_c_offset=0, res_c_stride=0, res_c_offset=0, res_scale=0.0) -> cbs_conv_desc:
     return cbs_conv_desc(n, c_in, h, w, c_out, k, stride, pad, dtype, out_row_pitch, float(in_scale),
-                         float(bn_eps))
+                         float(bn_eps), act, out_dtype, float(out_scale), in_c_stride, in_c_offset,
+                         out_c_stride, out_c_offset, res_c_stride, res_c_offset, float(res_scale))
 
 
 def cbs_create_layer(desc: cbs_conv_desc, w_oihw, gamma, beta, mean, var) -> Layer:
@@ -165,6 +181,32 @@ def cbs_destroy_layer(layer: Layer) -> None:
 
 def cbs_run_layer(layer: Layer, inp, out, stream=None) -> None:
     _check(lib.cbs_run_layer(layer.handle, _dev_ptr(inp), _dev_ptr(out), _stream(stream)), "cbs_run_layer")
+
+
+def cbs_run_layer_res(layer: Layer, inp, out, residual, stream=None) -> None:
+    _check(lib.cbs_run_layer_res(layer.handle, _dev_ptr(inp), _dev_ptr(out), _dev_ptr(residual), _stream(stream)),
+           "cbs_run_layer_res")
+
+
+def _step_array(steps):
+    """steps: (layer, in, out) or (layer, in, out, residual) tuples."""
+    arr = (cbs_step * max(1, len(steps)))()
+    for i, st in enumerate(steps):
+        layer, inp, out = st[:3]
+        res = st[3] if len(st) > 3 else None
+        arr[i] = cbs_step(layer.handle, _dev_ptr(inp), _dev_ptr(out), _dev_ptr(res))
+    return arr
+
+
+def cbs_run_steps(steps, stream=None) -> None:
+    _check(lib.cbs_run_steps(_step_array(steps), len(steps), _stream(stream)), "cbs_run_steps")
+
+
+def cbs_graph_create_steps(steps, stream=None) -> "Graph":
+    h = _P()
+    _check(lib.cbs_graph_create_steps(_step_array(steps), len(steps), _stream(stream), ctypes.byref(h)),
+           "cbs_graph_create_steps")
+    return Graph(h.value, list(steps))
 
 
 def _ptr_array(items):

@@ -56,6 +56,7 @@ int out_dim(int in, int k, int s, int p) {
 struct cbs_layer {
   cbs_conv_desc d;
   int oh, ow, pitch, cin_pad, cout_pad, co_blocks, M;
+  int in_cs, out_cs, res_cs;  // channel strides of input, output, residual (res_cs 0: none)
   int variant;       // fused-epilogue variant
   int raw_variant;   // raw-accumulator variant (INT8), -1 for fp32
   int chunk_ch, chunks_per_tap, total_chunks, steps;
@@ -98,18 +99,51 @@ cbs_status validate(const cbs_conv_desc *d) {
     return fail(CBS_EINVAL, "INT8 layer needs a finite in_scale > 0");
   if (!(d->bn_eps >= 0.0f) || !std::isfinite(d->bn_eps)) return fail(CBS_EINVAL, "bn_eps must be finite and >= 0");
   if (d->c_in > 4096 || d->c_out > 4096) return fail(CBS_EUNSUPPORTED, "channels above 4096");
+  if (d->act != CBS_ACT_SILU && d->act != CBS_ACT_NONE) return fail(CBS_EINVAL, "act %d unknown", d->act);
+  if (d->out_dtype != CBS_F32 && d->out_dtype != CBS_I8) return fail(CBS_EINVAL, "out_dtype %d unknown", d->out_dtype);
+  if (d->out_dtype == CBS_I8 && !(d->out_scale > 0.0f && std::isfinite(d->out_scale)))
+    return fail(CBS_EINVAL, "int8 output needs a finite out_scale > 0");
   const int oh = out_dim(d->h, d->k, d->stride, d->pad), ow = out_dim(d->w, d->k, d->stride, d->pad);
   if (oh < 1 || ow < 1) return fail(CBS_EINVAL, "empty output (%dx%d)", oh, ow);
   if (d->out_row_pitch != 0 && d->out_row_pitch < ow)
     return fail(CBS_EINVAL, "out_row_pitch %d < OW %d", d->out_row_pitch, ow);
+  // channel slices: (stride 0, offset 0) is the dense layout; a slice needs
+  // 4-aligned channel counts, offsets and strides, and must fit in the pixel
+  struct Slice {
+    const char *what;
+    int stride, offset, channels;
+  } slices[3] = {{"in", d->in_c_stride, d->in_c_offset, d->c_in},
+                 {"out", d->out_c_stride, d->out_c_offset, d->c_out},
+                 {"res", d->res_c_stride, d->res_c_offset, d->c_out}};
+  for (const Slice &sl : slices) {
+    if (sl.stride < 0 || sl.offset < 0)
+      return fail(CBS_EINVAL, "%s_c_stride / %s_c_offset must be >= 0", sl.what, sl.what);
+    if (sl.stride == 0) {
+      if (sl.offset != 0) return fail(CBS_EINVAL, "%s_c_offset %d needs %s_c_stride > 0", sl.what, sl.offset, sl.what);
+      continue;
+    }
+    if (sl.channels % 4 || sl.offset % 4 || sl.stride % 4)
+      return fail(CBS_EINVAL, "%s slice: channels %d, offset %d and stride %d must be multiples of 4", sl.what,
+                  sl.channels, sl.offset, sl.stride);
+    if (sl.offset + sl.channels > sl.stride)
+      return fail(CBS_EINVAL, "%s slice: offset %d + channels %d > stride %d", sl.what, sl.offset, sl.channels,
+                  sl.stride);
+  }
+  if (d->res_c_stride > 0 && d->out_dtype == CBS_I8 && !(d->res_scale > 0.0f && std::isfinite(d->res_scale)))
+    return fail(CBS_EINVAL, "int8 residual needs a finite res_scale > 0");
   const int pitch = d->out_row_pitch ? d->out_row_pitch : ow;
-  const double in_elems = (double)d->n * d->h * d->w * round_up(d->c_in, 4);
-  const double out_elems = (double)d->n * oh * pitch * round_up(d->c_out, 4);
-  if (in_elems >= 2147483647.0 || out_elems >= 2147483647.0)
+  const int in_cs = d->in_c_stride ? d->in_c_stride : round_up(d->c_in, 4);
+  const int out_cs = d->out_c_stride ? d->out_c_stride : round_up(d->c_out, 4);
+  const double in_elems = (double)d->n * d->h * d->w * in_cs;
+  const double out_elems = (double)d->n * oh * pitch * out_cs;
+  const double res_elems = (double)d->n * oh * ow * d->res_c_stride;
+  if (in_elems >= 2147483647.0 || out_elems >= 2147483647.0 || res_elems >= 2147483647.0)
     return fail(CBS_EUNSUPPORTED, "tensor above 2^31 elements");
-  // the kernels address the input with 32-bit buffer offsets below 2^31
+  // the kernels address input and residual with 32-bit buffer offsets below 2^31
   const double in_bytes = in_elems * (d->dtype == CBS_F32 ? 4.0 : 1.0);
+  const double res_bytes = res_elems * (d->out_dtype == CBS_F32 ? 4.0 : 1.0);
   if (in_bytes >= 2147483648.0 - 64.0) return fail(CBS_EUNSUPPORTED, "input above 2^31 bytes");
+  if (res_bytes >= 2147483648.0 - 64.0) return fail(CBS_EUNSUPPORTED, "residual above 2^31 bytes");
   return CBS_OK;
 }
 
@@ -264,14 +298,35 @@ cbs_status setup_splitk(cbs_layer *L) {
   return CBS_OK;
 }
 
-ConvParams make_params(const cbs_layer *L, const void *in, void *out) {
+// Kernel arguments of one launch.  raw: the INT8 test hook, which stores
+// int32 accumulators densely ([N][OH][pitch][C_out_pad]) with no epilogue.
+ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void *res, bool raw) {
   ConvParams p;
   std::memset(&p, 0, sizeof(p));
-  p.x = in;
+  const size_t esz_in = L->d.dtype == CBS_F32 ? 4 : 1;
+  const size_t esz_out = (raw || L->d.out_dtype == CBS_F32) ? 4 : 1;
+  p.x = (const char *)in + (size_t)L->d.in_c_offset * esz_in;
+  p.x_cs = L->in_cs;
+  p.x_bytes = (unsigned)((size_t)L->d.n * L->d.h * L->d.w * L->in_cs * esz_in - (size_t)L->d.in_c_offset * esz_in);
   p.wfrag = L->d_wfrag;
   p.bias = L->d_bias;
   p.dq = L->d_dq;
-  p.out = out;
+  if (raw) {
+    p.out = out;
+    p.out_cs = L->cout_pad;
+  } else {
+    p.out = (char *)out + (size_t)L->d.out_c_offset * esz_out;
+    p.out_cs = L->out_cs;
+    p.act = L->d.act == CBS_ACT_NONE ? ACT_NONE : ACT_SILU;
+    p.out_i8 = L->d.out_dtype == CBS_I8;
+    p.out_scale = L->d.out_scale;
+    if (L->res_cs) {
+      p.res = (const char *)res + (size_t)L->d.res_c_offset * esz_out;
+      p.res_cs = L->res_cs;
+      p.res_scale = L->d.res_scale;
+      p.res_bytes = (unsigned)((size_t)L->M * L->res_cs * esz_out - (size_t)L->d.res_c_offset * esz_out);
+    }
+  }
   p.ws = L->d_ws;
   p.counters = L->d_counters;
   p.N = L->d.n;
@@ -294,7 +349,6 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out) {
   p.splitk = L->splitk;
   p.steps_per_split = ceil_div(L->steps, L->splitk);
   p.co_blocks = L->co_blocks;
-  p.x_bytes = (unsigned)((size_t)L->d.n * L->d.h * L->d.w * L->cin_pad * (L->d.dtype == CBS_F32 ? 4 : 1));
   p.w_bytes = (unsigned)((size_t)L->co_blocks * L->steps * 64 * 16);
   const KernelConfig &kc = config(L->config);
   if (kc.lds == 2) {
@@ -306,10 +360,20 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out) {
   return p;
 }
 
-cbs_status launch(const cbs_layer *L, int variant, const void *in, void *out, void *stream) {
-  ConvParams p = make_params(L, in, out);
-  hipError_t e = launch_conv(variant, L->config, p, (hipStream_t)stream);
+cbs_status launch(const cbs_layer *L, const void *in, void *out, const void *res, void *stream, bool raw = false) {
+  ConvParams p = make_params(L, in, out, res, raw);
+  hipError_t e = launch_conv(raw ? L->raw_variant : L->variant, L->config, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(CBS_ELAUNCH, "conv launch: %s", hipGetErrorString(e));
+  return CBS_OK;
+}
+
+// Argument check of one step: buffers present, residual given iff the layer has one.
+cbs_status check_step(const cbs_layer *L, const void *in, const void *out, const void *res, const char *where,
+                      int idx) {
+  if (!L || !in || !out) return fail(CBS_EINVAL, "%s: null layer or buffer (entry %d)", where, idx);
+  if (L->res_cs && !res)
+    return fail(CBS_EINVAL, "%s: layer %d was created with a residual and needs one", where, idx);
+  if (!L->res_cs && res) return fail(CBS_EINVAL, "%s: layer %d has no residual but one was given", where, idx);
   return CBS_OK;
 }
 
@@ -345,6 +409,9 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   L->pitch = d.out_row_pitch ? d.out_row_pitch : L->ow;
   L->cin_pad = round_up(d.c_in, 4);
   L->cout_pad = round_up(d.c_out, 4);
+  L->in_cs = d.in_c_stride ? d.in_c_stride : L->cin_pad;
+  L->out_cs = d.out_c_stride ? d.out_c_stride : L->cout_pad;
+  L->res_cs = d.res_c_stride;
   L->co_blocks = ceil_div(L->cout_pad, 16);
   L->M = d.n * L->oh * L->ow;
   const int taps = d.k * d.k;
@@ -353,7 +420,8 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
     L->chunk_ch = 4;
     L->variant = VAR_F32;
     L->raw_variant = -1;
-  } else if (L->cin_pad % 16 == 0) {
+  } else if (L->cin_pad % 16 == 0 && L->in_cs % 16 == 0 && d.in_c_offset % 16 == 0) {
+    // 16-channel chunks: one 16-byte load per lane, which needs 16-byte aligned pixels
     L->chunk_ch = 16;
     L->variant = VAR_I8_C16;
     L->raw_variant = VAR_I8_C16_RAW;
@@ -506,33 +574,51 @@ void cbs_destroy_layer(cbs_layer *layer) {
 }
 
 cbs_status cbs_run_layer(const cbs_layer *layer, const void *in, void *out, void *stream) {
-  if (!layer || !in || !out) return fail(CBS_EINVAL, "run_layer: null layer or buffer");
-  return launch(layer, layer->variant, in, out, stream);
+  cbs_status st = check_step(layer, in, out, nullptr, "run_layer", 0);
+  if (st != CBS_OK) return st;
+  return launch(layer, in, out, nullptr, stream);
+}
+
+cbs_status cbs_run_layer_res(const cbs_layer *layer, const void *in, void *out, const void *residual,
+                             void *stream) {
+  if (!residual) return fail(CBS_EINVAL, "run_layer_res: residual is NULL");
+  cbs_status st = check_step(layer, in, out, residual, "run_layer_res", 0);
+  if (st != CBS_OK) return st;
+  return launch(layer, in, out, residual, stream);
 }
 
 cbs_status cbs_run_layer_list(cbs_layer *const *layers, int32_t n, const void *const *ins,
                               void *const *outs, void *stream) {
   if (n < 0 || (n > 0 && (!layers || !ins || !outs))) return fail(CBS_EINVAL, "run_layer_list: bad arguments");
   for (int32_t i = 0; i < n; i++) {
-    if (!layers[i] || !ins[i] || !outs[i]) return fail(CBS_EINVAL, "run_layer_list: null entry %d", i);
-    cbs_status st = launch(layers[i], layers[i]->variant, ins[i], outs[i], stream);
+    cbs_status st = check_step(layers[i], ins[i], outs[i], nullptr, "run_layer_list", i);
+    if (st == CBS_OK) st = launch(layers[i], ins[i], outs[i], nullptr, stream);
     if (st != CBS_OK) return st;
   }
   return CBS_OK;
 }
 
-cbs_status cbs_graph_create(cbs_layer *const *layers, int32_t n, const void *const *ins, void *const *outs,
-                            void *stream, cbs_graph **out) {
-  (void)stream;
-  if (!out) return fail(CBS_EINVAL, "graph_create: out is NULL");
-  *out = nullptr;
-  if (n < 1 || !layers || !ins || !outs) return fail(CBS_EINVAL, "graph_create: bad arguments");
-  for (int32_t i = 0; i < n; i++)
-    if (!layers[i] || !ins[i] || !outs[i]) return fail(CBS_EINVAL, "graph_create: null entry %d", i);
+cbs_status cbs_run_steps(const cbs_step *steps, int32_t n, void *stream) {
+  if (n < 0 || (n > 0 && !steps)) return fail(CBS_EINVAL, "run_steps: bad arguments");
+  for (int32_t i = 0; i < n; i++) {
+    const cbs_step &t = steps[i];
+    cbs_status st = check_step(t.layer, t.in, t.out, t.residual, "run_steps", i);
+    if (st == CBS_OK) st = launch(t.layer, t.in, t.out, t.residual, stream);
+    if (st != CBS_OK) return st;
+  }
+  return CBS_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Capture a validated step list into an instantiated graph.  The capture runs
+// on a private stream (the caller's may be the null stream, which cannot be
+// captured), at default priority.
+cbs_status capture(const std::vector<cbs_step> &steps, cbs_graph **out) {
   cbs_graph *G = new (std::nothrow) cbs_graph();
   if (!G) return fail(CBS_ENOMEM, "host allocation");
-  // Capture on a private stream (the caller's may be the null stream, which
-  // cannot be captured); default priority.
   hipStream_t cs = nullptr;
   hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
   if (e != hipSuccess) {
@@ -543,8 +629,8 @@ cbs_status cbs_graph_create(cbs_layer *const *layers, int32_t n, const void *con
   cbs_status st = CBS_OK;
   if (e != hipSuccess) st = fail(CBS_EDEVICE, "begin capture: %s", hipGetErrorString(e));
   if (st == CBS_OK) {
-    for (int32_t i = 0; i < n && st == CBS_OK; i++)
-      st = launch(layers[i], layers[i]->variant, ins[i], outs[i], cs);
+    for (size_t i = 0; i < steps.size() && st == CBS_OK; i++)
+      st = launch(steps[i].layer, steps[i].in, steps[i].out, steps[i].residual, cs);
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(cs, &g);
     if (st == CBS_OK && e != hipSuccess) st = fail(CBS_EDEVICE, "end capture: %s", hipGetErrorString(e));
@@ -561,6 +647,37 @@ cbs_status cbs_graph_create(cbs_layer *const *layers, int32_t n, const void *con
   }
   *out = G;
   return CBS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cbs_status cbs_graph_create(cbs_layer *const *layers, int32_t n, const void *const *ins, void *const *outs,
+                            void *stream, cbs_graph **out) {
+  (void)stream;
+  if (!out) return fail(CBS_EINVAL, "graph_create: out is NULL");
+  *out = nullptr;
+  if (n < 1 || !layers || !ins || !outs) return fail(CBS_EINVAL, "graph_create: bad arguments");
+  std::vector<cbs_step> steps(n);
+  for (int32_t i = 0; i < n; i++) {
+    cbs_status st = check_step(layers[i], ins[i], outs[i], nullptr, "graph_create", i);
+    if (st != CBS_OK) return st;
+    steps[i] = cbs_step{layers[i], ins[i], outs[i], nullptr};
+  }
+  return capture(steps, out);
+}
+
+cbs_status cbs_graph_create_steps(const cbs_step *steps, int32_t n, void *stream, cbs_graph **out) {
+  (void)stream;
+  if (!out) return fail(CBS_EINVAL, "graph_create_steps: out is NULL");
+  *out = nullptr;
+  if (n < 1 || !steps) return fail(CBS_EINVAL, "graph_create_steps: bad arguments");
+  for (int32_t i = 0; i < n; i++) {
+    cbs_status st = check_step(steps[i].layer, steps[i].in, steps[i].out, steps[i].residual, "graph_create_steps", i);
+    if (st != CBS_OK) return st;
+  }
+  return capture(std::vector<cbs_step>(steps, steps + n), out);
 }
 
 cbs_status cbs_graph_launch(const cbs_graph *graph, void *stream) {
@@ -588,12 +705,15 @@ cbs_status cbs_layer_info(const cbs_layer *L, cbs_layer_info_t *info) {
   info->out_row_pitch = L->pitch;
   info->dtype = d.dtype;
   const int64_t esz = d.dtype == CBS_F32 ? 4 : 1;
-  info->in_bytes = (int64_t)d.n * d.h * d.w * L->cin_pad * esz;
-  info->out_bytes = (int64_t)d.n * L->oh * L->pitch * L->cout_pad * 4;
+  const int64_t osz = d.out_dtype == CBS_F32 ? 4 : 1;
+  info->in_bytes = (int64_t)d.n * d.h * d.w * L->in_cs * esz;
+  info->out_bytes = (int64_t)d.n * L->oh * L->pitch * L->out_cs * osz;
+  info->res_bytes = (int64_t)d.n * L->oh * L->ow * L->res_cs * osz;
   const int64_t kk = (int64_t)d.k * d.k;
-  info->flops = 2 * (int64_t)d.n * L->oh * L->ow * d.c_out * d.c_in * kk;
+  const int64_t out_elems = (int64_t)d.n * L->oh * L->ow * d.c_out;
+  info->flops = 2 * out_elems * d.c_in * kk;
   info->alg_bytes = (int64_t)d.n * d.h * d.w * d.c_in * esz + (int64_t)d.c_out * d.c_in * kk * esz +
-                    (int64_t)d.n * L->oh * L->ow * d.c_out * 4 + 8 * (int64_t)d.c_out;
+                    out_elems * osz * (L->res_cs ? 2 : 1) + 8 * (int64_t)d.c_out;
   info->config = L->config;
   info->splitk = L->splitk;
   int pxt, cot;
@@ -659,7 +779,7 @@ cbs_status cbs_quantize_nhwc_i8(const float *nchw, int8_t *nhwc, float s_x, int3
 cbs_status cbs_run_layer_raw_acc(const cbs_layer *L, const void *in, int32_t *acc, void *stream) {
   if (!L || !in || !acc) return fail(CBS_EINVAL, "run_layer_raw_acc: null layer or buffer");
   if (L->raw_variant < 0) return fail(CBS_EINVAL, "run_layer_raw_acc: not an INT8 layer");
-  return launch(L, L->raw_variant, in, acc, stream);
+  return launch(L, in, acc, nullptr, stream, true);
 }
 
 cbs_status cbs_get_qweights(const cbs_layer *L, int8_t *q_oihw, double *s_w) {

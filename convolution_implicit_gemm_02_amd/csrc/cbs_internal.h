@@ -28,16 +28,29 @@ enum Variant {
 };
 
 // Everything a launch needs; filled at create, passed by value.
+// Epilogue activation codes (ConvParams::act).
+enum Act { ACT_SILU = 0, ACT_NONE = 1 };
+
 struct ConvParams {
-  const void *x;         // NHWC input [N][H][W][cin_pad]
+  const void *x;         // NHWC input, first channel of the layer: pixel i at x + i*x_cs
   const void *wfrag;     // weights in MFMA fragment order [co_blocks][steps][64 lanes][16 bytes]
   const float *bias;     // folded bias [co_blocks*16] (zero beyond C_out)
   const float *dq;       // INT8 dequant factors f[co] [co_blocks*16] (null for fp32)
-  void *out;             // NHWC output [N][OH][pitch][cout_pad] (fp32, or int32 for raw)
+  void *out;             // NHWC output, first channel of the layer: pixel (n,oh,ow) at
+                         // out + ((n*OH + oh)*pitch + ow)*out_cs  (fp32, int8, or int32 for raw)
+  const void *res;       // residual, first channel: logical pixel m at res + m*res_cs (null if none)
   float *ws;             // split-K partial tiles (null when splitk == 1)
   unsigned *counters;    // split-K arrival counters, one per output tile (zero between launches)
   int N, H, W, cin_pad;
+  int x_cs;              // input elements between consecutive pixels (cin_pad when dense)
   int OH, OW, cout_pad, pitch;
+  int out_cs;            // output elements between consecutive pixels (cout_pad when dense)
+  int res_cs;            // residual elements between consecutive pixels (0: no residual)
+  int act;               // Act
+  int out_i8;            // 1: int8 output codes q = clamp(rne(fp32(y / out_scale)), +-127)
+  float out_scale;       // s_y for int8 output
+  float res_scale;       // scale of int8 residual codes
+  unsigned res_bytes;    // bytes of the residual buffer from res (buffer-load range)
   int k, stride, pad;
   int M;                 // N*OH*OW output pixels
   int chunk_ch;          // channels per chunk (4 or 16)
@@ -49,7 +62,7 @@ struct ConvParams {
   int splitk;            // workgroups per output tile along K
   int co_blocks;         // 16-channel output blocks holding real channels
   int px_tiles, co_tiles;// workgroup tiles along pixels and output channels
-  unsigned x_bytes;      // bytes of the input buffer (buffer-load range)
+  unsigned x_bytes;      // bytes of the input buffer from x (buffer-load range)
   unsigned w_bytes;      // bytes of the fragment-ordered weights (buffer-load range)
   int tiles_x, tiles_y;  // conv_halo: output tiles along a row and along the rows of one image
   int halo_bytes;        // conv_halo: LDS bytes of the input halo tile (weights follow)

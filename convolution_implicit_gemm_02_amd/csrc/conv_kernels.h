@@ -73,6 +73,54 @@ constexpr unsigned kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ float silu_f(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, kRsrcWord3);
+}
+
+// The fused epilogue of one lane: output channels co0 .. co0+3 of one pixel.
+// z holds the pre-activation values (accumulator + folded bias, dequantised
+// for int8); opix is the pixel's storage index ((n*OH + oh)*pitch + ow) and m
+// its logical index ((n*OH + oh)*OW + ow), which addresses the dense-row
+// residual.  Order: activation, then the residual add, then (int8 output) the
+// quantiser of the next layer's input, so the int8 codes are exactly those
+// the graph-entry quantiser would produce from this layer's fp32 output.
+// act, the residual and the output type are kernel arguments: every branch
+// here is wave-uniform.
+__device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buffer_rsrc_t rr, f32x4 z, int opix,
+                                               int m, int co0) {
+  f32x4 y;
+  if (p.act == ACT_NONE) {
+    y = z;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++) y[i] = silu_f(z[i]);
+  }
+  if (p.res_cs) {
+    const unsigned e = (unsigned)(m * p.res_cs + co0);
+    if (p.out_i8) {
+      const unsigned w = __builtin_amdgcn_raw_buffer_load_b32(rr, e, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; i++) y[i] += p.res_scale * (float)(int)(signed char)((w >> (8 * i)) & 0xffu);
+    } else {
+      y += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, e * 4u, 0, 0));
+    }
+  }
+  const size_t o = (size_t)opix * p.out_cs + co0;
+  if (p.out_i8) {
+    unsigned word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      // fp32 division, correctly rounded, then round half to even and clamp
+      float t = rintf(__fdiv_rn(y[i], p.out_scale));
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      word |= ((unsigned)((int)t & 0xff)) << (8 * i);
+    }
+    *(unsigned *)((signed char *)p.out + o) = word;
+  } else {
+    *(f32x4 *)((float *)p.out + o) = y;
+  }
+}
+
 // Decoded K chunk: tap offset (dy, dx) and first channel.
 struct Chunk {
   int dy, dx, ci;
@@ -174,24 +222,24 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
       aa[cb] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], s * 1024, 0));
     if constexpr (V::VEC == 1) {
       const Chunk c = decode_chunk(p, s * 4 + g);
-      const int doff = (c.dy * p.W + c.dx) * p.cin_pad + c.ci;
+      const int doff = (c.dy * p.W + c.dx) * p.x_cs + c.ci;
 #pragma unroll
       for (int b = 0; b < PB; b++) {
         const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
         const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
-        const unsigned off = v ? (unsigned)(pixbase[b] * p.cin_pad + doff) * (unsigned)V::ESIZE : kOutOfRange;
+        const unsigned off = v ? (unsigned)(pixbase[b] * p.x_cs + doff) * (unsigned)V::ESIZE : kOutOfRange;
         bb[b] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const Chunk c = decode_chunk(p, (s * 4 + g) * 4 + j);
-        const int doff = (c.dy * p.W + c.dx) * p.cin_pad + c.ci;
+        const int doff = (c.dy * p.W + c.dx) * p.x_cs + c.ci;
 #pragma unroll
         for (int b = 0; b < PB; b++) {
           const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
           const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
-          const unsigned off = v ? (unsigned)(pixbase[b] * p.cin_pad + doff) : kOutOfRange;
+          const unsigned off = v ? (unsigned)(pixbase[b] * p.x_cs + doff) : kOutOfRange;
           bb[b][j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
         }
       }
@@ -311,7 +359,9 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
 
   if (wk != 0) return;
 
-  // Epilogue: bias (+ dequant) + SiLU in registers, masked 16-byte NHWC stores.
+  // Epilogue: bias (+ dequant), activation, residual, output conversion in
+  // registers; masked NHWC stores of 4 channels per lane.
+  const __amdgpu_buffer_rsrc_t rr = rsrc(p.res, p.res_bytes);
 #pragma unroll
   for (int cb = 0; cb < CB; cb++) {
     const int co0 = (cob0 + cb) * 16 + 4 * g;
@@ -319,24 +369,22 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     if constexpr (V::RAW) {
 #pragma unroll
       for (int b = 0; b < PB; b++)
-        if (mval[b]) *(i32x4 *)((int *)p.out + (size_t)outpix[b] * p.cout_pad + co0) = acc[cb][b];
+        if (mval[b]) *(i32x4 *)((int *)p.out + (size_t)outpix[b] * p.out_cs + co0) = acc[cb][b];
     } else {
       const f32x4 bias = ep_bias[cb];
       const f32x4 dq = ep_dq[cb];
 #pragma unroll
       for (int b = 0; b < PB; b++) {
         if (!mval[b]) continue;
-        f32x4 y;
+        f32x4 z;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          float z;
           if constexpr (V::I8)
-            z = (float)acc[cb][b][i] * dq[i] + bias[i];
+            z[i] = (float)acc[cb][b][i] * dq[i] + bias[i];
           else
-            z = acc[cb][b][i] + bias[i];
-          y[i] = silu_f(z);
+            z[i] = acc[cb][b][i] + bias[i];
         }
-        *(f32x4 *)((float *)p.out + (size_t)outpix[b] * p.cout_pad + co0) = y;
+        epilogue_store(p, rr, z, outpix[b], ((px_tile * WPX + wpx) * PB + b) * 16 + r, co0);
       }
     }
   }
@@ -381,7 +429,7 @@ __device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu
     const int iy = q.iy0 + c.dy, ix = q.ix0 + c.dx;
     const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
     const unsigned off =
-        v ? (unsigned)(q.base * p.cin_pad + (c.dy * p.W + c.dx) * p.cin_pad + c.ci) * (unsigned)V::ESIZE : kOutOfRange;
+        v ? (unsigned)(q.base * p.x_cs + (c.dy * p.W + c.dx) * p.x_cs + c.ci) * (unsigned)V::ESIZE : kOutOfRange;
     return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
   } else {
     Frag f;
@@ -390,7 +438,7 @@ __device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu
       const Chunk c = decode_chunk(p, cg * 4 + j);
       const int iy = q.iy0 + c.dy, ix = q.ix0 + c.dx;
       const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
-      const unsigned off = v ? (unsigned)(q.base * p.cin_pad + (c.dy * p.W + c.dx) * p.cin_pad + c.ci) : kOutOfRange;
+      const unsigned off = v ? (unsigned)(q.base * p.x_cs + (c.dy * p.W + c.dx) * p.x_cs + c.ci) : kOutOfRange;
       f[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
     }
     return f;
@@ -528,28 +576,28 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
     __syncthreads();
   }
 
+  const __amdgpu_buffer_rsrc_t rr = rsrc(p.res, p.res_bytes);
 #pragma unroll
   for (int nb = 0; nb < NB; nb++) {
     const int co0 = (co_tile * BNB + wn * NB + nb) * 16 + 4 * g;
     if (co0 >= p.cout_pad) continue;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
-      const Pix q = pixel_of(p, (px_tile * BMB + wm * MB + mb) * 16 + r);
+      const int m = (px_tile * BMB + wm * MB + mb) * 16 + r;
+      const Pix q = pixel_of(p, m);
       if (!q.ok) continue;
       if constexpr (V::RAW) {
-        *(i32x4 *)((int *)p.out + (size_t)q.out * p.cout_pad + co0) = acc[nb][mb];
+        *(i32x4 *)((int *)p.out + (size_t)q.out * p.out_cs + co0) = acc[nb][mb];
       } else {
-        f32x4 y;
+        f32x4 z;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          float z;
           if constexpr (V::I8)
-            z = (float)acc[nb][mb][i] * ep_dq[nb][i] + ep_bias[nb][i];
+            z[i] = (float)acc[nb][mb][i] * ep_dq[nb][i] + ep_bias[nb][i];
           else
-            z = acc[nb][mb][i] + ep_bias[nb][i];
-          y[i] = silu_f(z);
+            z[i] = acc[nb][mb][i] + ep_bias[nb][i];
         }
-        *(f32x4 *)((float *)p.out + (size_t)q.out * p.cout_pad + co0) = y;
+        epilogue_store(p, rr, z, q.out, m, co0);
       }
     }
   }
@@ -607,7 +655,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
       const int hx = px % HWd, hy = px / HWd;
       const int iy = iy0 + hy, ix = ix0 + hx;
       const bool v = sl < halo_slots && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
-      const unsigned off = v ? (unsigned)(((n * p.H + iy) * p.W + ix) * p.cin_pad + 4 * q) * (unsigned)V::ESIZE
+      const unsigned off = v ? (unsigned)(((n * p.H + iy) * p.W + ix) * p.x_cs + 4 * q) * (unsigned)V::ESIZE
                              : kOutOfRange;
       if constexpr (SLOT == 16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(smem + base * SLOT), 16, off, 0, 0, 0);
@@ -702,6 +750,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   }
 
   // 3) epilogue, masked to the image and to the real channels
+  const __amdgpu_buffer_rsrc_t rr = rsrc(p.res, p.res_bytes);
 #pragma unroll
   for (int nb = 0; nb < NBMAX; nb++) {
     if (nb >= nbl) break;
@@ -712,21 +761,19 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
       const int pi = (wave * MB + mb) * 16 + r;
       const int oh = oh0 + pi / TW, ow = ow0 + pi % TW;
       if (oh >= p.OH || ow >= p.OW) continue;
-      const size_t o = ((size_t)(n * p.OH + oh) * p.pitch + ow) * p.cout_pad + co0;
+      const int opix = (n * p.OH + oh) * p.pitch + ow;
       if constexpr (V::RAW) {
-        *(i32x4 *)((int *)p.out + o) = acc[nb][mb];
+        *(i32x4 *)((int *)p.out + (size_t)opix * p.out_cs + co0) = acc[nb][mb];
       } else {
-        f32x4 y;
+        f32x4 z;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          float z;
           if constexpr (V::I8)
-            z = (float)acc[nb][mb][i] * ep_dq[nb][i] + ep_bias[nb][i];
+            z[i] = (float)acc[nb][mb][i] * ep_dq[nb][i] + ep_bias[nb][i];
           else
-            z = acc[nb][mb][i] + ep_bias[nb][i];
-          y[i] = silu_f(z);
+            z[i] = acc[nb][mb][i] + ep_bias[nb][i];
         }
-        *(f32x4 *)((float *)p.out + o) = y;
+        epilogue_store(p, rr, z, opix, (n * p.OH + oh) * p.OW + ow, co0);
       }
     }
   }

@@ -28,13 +28,41 @@
  *   acc = sum q_w * q_x                                          (exact int32)
  *   y   = SiLU(float(acc) * f[co] + b'[co]),  f[co] = fp32(s_x * s_w[co])
  *
- * Layouts (all device buffers are caller-owned and dense):
- *   input  : NHWC [N][H][W][C_in_pad]; fp32 for CBS_F32, int8 for CBS_I8.
- *            C_in_pad = round_up(C_in, 4); padded lanes must hold 0.
- *   output : NHWC fp32 [N][OH][out_row_pitch][C_out_pad],
- *            C_out_pad = round_up(C_out, 4).  Only pixels ow < OW of each row
- *            are written (padded channels get +0.0); the out_row_pitch - OW
- *            guard pixels after every row are never touched.
+ * Fused epilogue and I/O options (descriptor fields after bn_eps), from the
+ * same vision-rs page, section "Improvements" #6 (a conv reads a channel_cat
+ * result as slices of its producers, so no cat kernel runs) and #7 (bias and
+ * residual adds happen in the conv epilogue, while the results are still in
+ * registers), and section "NHWC migration -- Op-by-op impact across the
+ * graph" (bias add, cat and chunk disappear into the conv); and from the
+ * edge-optimization README ("Highlights": the network runs in INT8 end to end):
+ *   act = CBS_ACT_NONE:  y = conv + b'          (the page's plain conv2d_forward
+ *                                                 + nchw_bias_add, via create_layer_folded)
+ *   residual:            y = act(...) + r        (r fp32; for int8 output r = res_scale * q_r)
+ *   out_dtype = CBS_I8:  q_y = clamp(rne(fp32(y / s_y)), -127, 127), the quantiser of the
+ *                        next INT8 layer's input (s_y = its s_x), applied to the fp32 y.
+ *
+ * Layouts (all device buffers are caller-owned):
+ *   input  : NHWC [N][H][W][in_c_stride]; fp32 for CBS_F32, int8 for CBS_I8;
+ *            the layer reads channels in_c_offset .. in_c_offset + C_in_pad - 1.
+ *            Dense (in_c_stride = 0): the stride is C_in_pad = round_up(C_in, 4)
+ *            and padded lanes must hold 0.  Slice (in_c_stride > 0): C_in,
+ *            in_c_offset and in_c_stride are multiples of 4 and
+ *            in_c_offset + C_in <= in_c_stride (a channel_chunk / channel_cat
+ *            slice read in place).
+ *   output : NHWC [N][OH][out_row_pitch][out_c_stride], fp32 or int8
+ *            (out_dtype); the layer writes channels out_c_offset ..
+ *            out_c_offset + C_out_pad - 1 of pixels ow < OW and nothing else:
+ *            the out_row_pitch - OW guard pixels after every row and all other
+ *            channels are never touched.  Dense: stride C_out_pad, padded
+ *            channels get 0.  Slice: C_out, out_c_offset and out_c_stride are
+ *            multiples of 4 and out_c_offset + C_out <= out_c_stride (writing
+ *            into a channel_cat buffer in place).
+ *   residual (res_c_stride > 0): NHWC [N][OH][OW][res_c_stride] (dense rows,
+ *            like an input), of the output's dtype; the layer reads channels
+ *            res_c_offset .. res_c_offset + C_out - 1.  C_out, res_c_offset and
+ *            res_c_stride are multiples of 4, res_c_offset + C_out <= res_c_stride.
+ *            It may share a buffer with the output when their channel ranges
+ *            are disjoint.
  *   weights: host OIHW fp32 [C_out][C_in][k][k], copied at create.
  *
  * Execution: every cbs_run_* call only enqueues kernels on the given stream
@@ -67,6 +95,9 @@ typedef int32_t cbs_status;
 #define CBS_F32 0
 #define CBS_I8 1
 
+#define CBS_ACT_SILU 0 /* y = SiLU(z) (the default) */
+#define CBS_ACT_NONE 1 /* y = z: plain convolution + bias */
+
 typedef struct cbs_layer cbs_layer; /* opaque: one fused conv layer on one device */
 typedef struct cbs_graph cbs_graph; /* opaque: a captured layer list */
 
@@ -82,6 +113,17 @@ typedef struct cbs_conv_desc {
     int32_t out_row_pitch; /* output pixels between consecutive (n, oh) rows, >= OW; 0 means OW */
     float in_scale;        /* CBS_I8: per-tensor activation scale s_x > 0; ignored for CBS_F32 */
     float bn_eps;          /* batch-norm epsilon >= 0, used as (double)bn_eps */
+    /* ---- fused epilogue and I/O (all-zero = the plain layer described above) ---- */
+    int32_t act;           /* CBS_ACT_SILU (0) or CBS_ACT_NONE */
+    int32_t out_dtype;     /* CBS_F32 (0): fp32 output; CBS_I8: int8 codes of scale out_scale */
+    float out_scale;       /* out_dtype CBS_I8: per-tensor output scale s_y > 0 */
+    int32_t in_c_stride;   /* channels between consecutive input pixels; 0 = C_in_pad (dense) */
+    int32_t in_c_offset;   /* first input channel of this layer within a pixel (0 when dense) */
+    int32_t out_c_stride;  /* channels between consecutive output pixels; 0 = C_out_pad (dense) */
+    int32_t out_c_offset;  /* first output channel written within a pixel (0 when dense) */
+    int32_t res_c_stride;  /* residual: channels between its pixels; 0 = no residual */
+    int32_t res_c_offset;  /* residual: first channel within its pixel */
+    float res_scale;       /* out_dtype CBS_I8 with a residual: scale of its int8 codes, > 0 */
 } cbs_conv_desc;
 
 typedef struct cbs_layer_info_t {
@@ -89,16 +131,18 @@ typedef struct cbs_layer_info_t {
     int32_t oh, ow;               /* output height and width */
     int32_t out_row_pitch;        /* pixels per output row (>= ow) */
     int32_t dtype;                /* CBS_F32 or CBS_I8 */
-    int64_t in_bytes;             /* size of the input buffer run_layer reads */
+    int64_t in_bytes;             /* size of the input buffer run_layer reads (N*H*W*in_c_stride*b_in) */
     int64_t out_bytes;            /* size of the output buffer run_layer writes into
-                                     (N*OH*pitch*C_out_pad*4; guards included) */
+                                     (N*OH*pitch*out_c_stride*b_out; guards included) */
     int64_t flops;                /* 2*N*OH*OW*C_out*C_in*k*k (logical channels) */
-    int64_t alg_bytes;            /* N*H*W*C_in*b_in + C_out*C_in*k*k*b_w + N*OH*OW*C_out*4 + 8*C_out */
+    int64_t alg_bytes;            /* N*H*W*C_in*b_in + C_out*C_in*k*k*b_w + N*OH*OW*C_out*b_out
+                                     (+ the same again for a residual) + 8*C_out */
     int32_t config;               /* kernel configuration index in use */
     int32_t splitk;               /* workgroups that share one output tile along K */
     int32_t grid;                 /* workgroups per launch */
     int32_t threads;              /* threads per workgroup */
     char config_name[48];         /* human-readable configuration name */
+    int64_t res_bytes;            /* size of the residual buffer read (0 without residual) */
 } cbs_layer_info_t;
 
 /*
@@ -130,9 +174,17 @@ void cbs_destroy_layer(cbs_layer *layer);
 /*
  * Enqueue the fused layer on `stream`: in (device, layout above) -> out
  * (device, layout above).  in and out must not overlap.  Errors: CBS_EINVAL
- * (null layer or buffer), CBS_ELAUNCH.
+ * (null layer or buffer, or a layer created with a residual), CBS_ELAUNCH.
  */
 cbs_status cbs_run_layer(const cbs_layer *layer, const void *in, void *out, void *stream);
+
+/*
+ * Same for a layer created with a residual (res_c_stride > 0): residual is
+ * the device tensor added after the activation (layout above).  CBS_EINVAL if
+ * the layer has no residual or residual is NULL.
+ */
+cbs_status cbs_run_layer_res(const cbs_layer *layer, const void *in, void *out, const void *residual,
+                             void *stream);
 
 /*
  * Enqueue layers[0..n-1] in order on one stream, layer i reading ins[i] and
@@ -149,6 +201,26 @@ cbs_status cbs_run_layer_list(cbs_layer *const *layers, int32_t n, const void *c
  */
 cbs_status cbs_graph_create(cbs_layer *const *layers, int32_t n, const void *const *ins,
                             void *const *outs, void *stream, cbs_graph **out);
+/*
+ * One step of a chained block: a layer with its input, output and residual
+ * (NULL unless the layer was created with one).  Consecutive steps share
+ * buffers through channel slices, so a C3k2-style block (1x1 conv, chunk,
+ * bottleneck 3x3 pair with shortcut, cat, 1x1 conv) runs as its convolutions
+ * alone, with no cat, chunk or add kernel in between.
+ */
+typedef struct cbs_step {
+    const cbs_layer *layer;
+    const void *in;
+    void *out;
+    const void *residual;
+} cbs_step;
+
+/* Enqueue steps[0..n-1] in order on one stream; stops at the first failure. */
+cbs_status cbs_run_steps(const cbs_step *steps, int32_t n, void *stream);
+
+/* Capture the same steps into a HIP graph, as cbs_graph_create does for a list. */
+cbs_status cbs_graph_create_steps(const cbs_step *steps, int32_t n, void *stream, cbs_graph **out);
+
 /* Enqueue one replay of a captured list on `stream`. */
 cbs_status cbs_graph_launch(const cbs_graph *graph, void *stream);
 /* Release a captured list.  NULL is a no-op. */

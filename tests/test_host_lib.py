@@ -64,6 +64,22 @@ def _create_status(cbs, **kw):
     (dict(dtype=1, in_scale=0.0), "CBS_EINVAL"), (dict(dtype=1, in_scale=float("nan")), "CBS_EINVAL"),
     (dict(out_row_pitch=5), "CBS_EINVAL"), (dict(bn_eps=-1.0), "CBS_EINVAL"),
     (dict(h=1, w=1, k=3, pad=0), "CBS_EINVAL"), (dict(n=4096, h=1024, w=1024, c_in=256), "CBS_EUNSUPPORTED"),
+    # fused epilogue / slice options
+    (dict(act=2), "CBS_EINVAL"), (dict(act=-1), "CBS_EINVAL"), (dict(out_dtype=3), "CBS_EINVAL"),
+    (dict(out_dtype=1, out_scale=0.0), "CBS_EINVAL"), (dict(out_dtype=1, out_scale=float("inf")), "CBS_EINVAL"),
+    (dict(in_c_offset=4), "CBS_EINVAL"),                                   # offset without a stride
+    (dict(in_c_stride=16, in_c_offset=12), "CBS_EINVAL"),                  # slice past the pixel
+    (dict(in_c_stride=18, in_c_offset=8), "CBS_EINVAL"),                   # stride not a multiple of 4
+    (dict(in_c_stride=16, in_c_offset=2), "CBS_EINVAL"),                   # offset not a multiple of 4
+    (dict(c_in=6, in_c_stride=16), "CBS_EINVAL"),                          # sliced C_in not a multiple of 4
+    (dict(in_c_stride=-4), "CBS_EINVAL"),
+    (dict(out_c_stride=12, out_c_offset=8), "CBS_EINVAL"), (dict(out_c_offset=4), "CBS_EINVAL"),
+    (dict(c_out=6, out_c_stride=8), "CBS_EINVAL"),
+    (dict(res_c_offset=4), "CBS_EINVAL"), (dict(res_c_stride=12, res_c_offset=8), "CBS_EINVAL"),
+    (dict(c_out=6, res_c_stride=8), "CBS_EINVAL"), (dict(res_c_stride=10), "CBS_EINVAL"),
+    (dict(out_dtype=1, out_scale=0.1, res_c_stride=8, res_scale=0.0), "CBS_EINVAL"),
+    (dict(n=64, h=512, w=512, c_in=8, in_c_stride=2048), "CBS_EUNSUPPORTED"),
+    (dict(n=64, h=512, w=512, res_c_stride=2048), "CBS_EUNSUPPORTED"),
 ])
 def test_descriptor_rejected(cbs, kw, status):
     st, h, msg = _create_status(cbs, **kw)
@@ -86,6 +102,14 @@ def test_null_arguments(cbs):
     assert out.value is None
     assert cbs.lib.cbs_run_layer_list(None, -1, None, None, None) == cbs.CBS_EINVAL
     assert cbs.lib.cbs_run_layer_list(None, 0, None, None, None) == cbs.CBS_OK  # empty list: nothing to do
+    assert cbs.lib.cbs_run_layer_res(None, None, None, None, None) == cbs.CBS_EINVAL
+    assert cbs.lib.cbs_run_steps(None, -1, None) == cbs.CBS_EINVAL
+    assert cbs.lib.cbs_run_steps(None, 0, None) == cbs.CBS_OK
+    steps = (cbs.cbs_step * 1)()
+    assert cbs.lib.cbs_run_steps(steps, 1, None) == cbs.CBS_EINVAL  # null layer
+    out2 = ctypes.c_void_p(5)
+    assert cbs.lib.cbs_graph_create_steps(steps, 1, None, ctypes.byref(out2)) == cbs.CBS_EINVAL
+    assert out2.value is None
     cbs.lib.cbs_destroy_layer(None)
     cbs.lib.cbs_graph_destroy(None)
     d = cbs.make_desc(1, 8, 8, 8, 8, 3, 1, 1)
@@ -119,10 +143,29 @@ def test_last_error_is_thread_local(cbs):
     assert cbs.cbs_last_error() == mine
 
 
-def test_valid_descriptor_without_device(cbs):
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(act=1, out_dtype=1, out_scale=0.05),
+    dict(c_in=8, in_c_stride=24, in_c_offset=16, c_out=8, out_c_stride=16, out_c_offset=8),
+    dict(dtype=1, in_scale=0.1, res_c_stride=8, out_dtype=1, out_scale=0.1, res_scale=0.2),
+])
+def test_valid_descriptor_without_device(cbs, kw):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    st, h, msg = _create_status(cbs)
+    st, h, msg = _create_status(cbs, **kw)
     assert st == cbs.CBS_EDEVICE, msg
     assert not h
+
+
+def test_descriptor_layout_matches_header(cbs):
+    """The ctypes descriptor has the header's field order and size (every field 4 bytes)."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct cbs_conv_desc \{(.*?)\} cbs_conv_desc;", src, re.S).group(1)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if decl:
+            names += [t.strip() for t in decl.split(None, 1)[1].split(",")]
+    assert names == [f for f, _ in cbs.cbs_conv_desc._fields_]
+    assert ctypes.sizeof(cbs.cbs_conv_desc) == 4 * len(names)
