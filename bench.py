@@ -11,6 +11,10 @@ ms_per_step, per-layer roofline of the dominant kernel (HIP events on the
 launch stream), and the CPU oracle timed on the host cores as a baseline.
 Per-layer details go to gpurun_out/bench_layers.json when that folder exists.
 
+The line also carries INT8 with int8 output (the requantising epilogue) and
+the 25 backbone layers chained as five downsample + C3k2 stages through
+channel slices and fused residuals (chain_*).
+
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
 """
 from __future__ import annotations
@@ -38,9 +42,12 @@ def log(*a):
 
 
 class ListBench:
-    """Device-resident inputs/outputs and created layers for one (dtype, batch)."""
+    """Device-resident inputs/outputs and created layers for one (dtype, batch).
+    out_i8: INT8 layers write int8 codes (the requantising epilogue) instead of
+    fp32; the output scale is the layer's own input scale (timing does not
+    depend on the value)."""
 
-    def __init__(self, cbs, W, torch, dtype, batch, seed=0):
+    def __init__(self, cbs, W, torch, dtype, batch, seed=0, out_i8=False):
         self.cbs, self.torch = cbs, torch
         self.dtype = dtype
         self.batch = batch
@@ -58,12 +65,13 @@ class ListBench:
             else:
                 s_x = W.calibration_scale(L.x)
                 desc = cbs.make_desc(batch, sp.c_in, sp.h, sp.w, sp.c_out, sp.k, sp.stride, sp.pad, dtype, 0,
-                                     float(s_x), L.eps)
+                                     float(s_x), L.eps, out_dtype=cbs.CBS_I8 if out_i8 else cbs.CBS_F32,
+                                     out_scale=float(s_x) if out_i8 else 0.0)
                 xin = torch.empty(batch * sp.h * sp.w * cpad, dtype=torch.int8, device=dev)
                 cbs.cbs_quantize_nhwc_i8(x, xin, s_x, batch, sp.c_in, sp.h, sp.w, cpad)
             layer = cbs.cbs_create_layer(desc, L.w, L.gamma, L.beta, L.mean, L.var)
             info = cbs.cbs_layer_info(layer)
-            out = torch.empty(info["out_bytes"] // 4, dtype=torch.float32, device=dev)
+            out = torch.empty(info["out_bytes"], dtype=torch.uint8, device=dev)
             self.layers.append(layer)
             self.ins.append(xin)
             self.outs.append(out)
@@ -123,6 +131,96 @@ class ListBench:
                 ts.append(e0.elapsed_time(e1) / r)
             res.append(float(np.median(ts)) * 1e3)  # microseconds
         return res
+
+
+class ChainBench:
+    """The 25 backbone layers of the list chained as they run in the network: five
+    stages, each a 3x3 s2 downsample and a C3k2 block (cv1 1x1 into the first c
+    channels of a 1.5c-channel buffer T; the bottleneck's two 3x3 convs read the
+    second half of cv1's output in place and the second adds it back and writes
+    the last c/2 channels of T; cv2 1x1 reads T whole).  Each stage's output is
+    the next stage's input.  One step = 25 kernels, no cat / chunk / add kernel,
+    replayed as one captured graph.  INT8: every tensor is int8 codes (scales:
+    the calibration of the list layers' generated inputs; timing does not
+    depend on them)."""
+
+    def __init__(self, cbs, W, torch, int8, batch, seed=0):
+        self.cbs, self.torch, self.batch = cbs, torch, batch
+        dev = torch.device("cuda", 0)
+        gen = W.generate("yolo26n", n=batch, seed=seed)[:25]
+        DT = cbs.CBS_I8 if int8 else cbs.CBS_F32
+        tdt = torch.int8 if int8 else torch.float32
+        img = gen[0]
+        cpad = 4
+        x = torch.from_numpy(img.x).to(dev)
+        cur = torch.empty(batch * img.spec.h * img.spec.w * cpad, dtype=tdt, device=dev)
+        s_img = W.calibration_scale(img.x)
+        s_act = W.calibration_scale(gen[1].x)  # an N(0,1) feature map
+        if int8:
+            cbs.cbs_quantize_nhwc_i8(x, cur, s_img, batch, img.spec.c_in, img.spec.h, img.spec.w, cpad)
+        else:
+            cbs.cbs_pack_nhwc_f32(x, cur, batch, img.spec.c_in, img.spec.h, img.spec.w, cpad)
+        self.input = cur
+        self.layers, self.steps, self.bufs, self.flops = [], [], [], 0
+        s_in = s_img
+        for st in range(5):
+            down, cv1, b1, b2, cv2 = gen[5 * st: 5 * st + 5]
+            c, h = cv1.spec.c_out, cv1.spec.h
+            half = c // 2
+            D = torch.empty(batch * h * h * c, dtype=tdt, device=dev)
+            T = torch.empty(batch * h * h * 3 * half, dtype=tdt, device=dev)
+            U = torch.empty(batch * h * h * half, dtype=tdt, device=dev)
+            Y = torch.empty(batch * h * h * c, dtype=tdt, device=dev)
+
+            def mk(L, s_x, **kw):
+                sp = L.spec
+                d = cbs.make_desc(batch, sp.c_in, sp.h, sp.w, sp.c_out, sp.k, sp.stride, sp.pad, DT, 0,
+                                  float(s_x) if int8 else 0.0, L.eps, out_dtype=DT,
+                                  out_scale=float(s_act) if int8 else 0.0, **kw)
+                layer = cbs.cbs_create_layer(d, L.w, L.gamma, L.beta, L.mean, L.var)
+                self.layers.append(layer)
+                self.flops += cbs.cbs_layer_info(layer)["flops"]
+                return layer
+
+            ld = mk(down, s_in)
+            l1 = mk(cv1, s_act, out_c_stride=3 * half, out_c_offset=0)
+            lb1 = mk(b1, s_act, in_c_stride=3 * half, in_c_offset=half)
+            lb2 = mk(b2, s_act, out_c_stride=3 * half, out_c_offset=2 * half, res_c_stride=3 * half,
+                     res_c_offset=half, res_scale=float(s_act) if int8 else 0.0)
+            l2 = mk(cv2, s_act)
+            self.steps += [(ld, cur, D), (l1, D, T), (lb1, T, U), (lb2, U, T, T), (l2, T, Y)]
+            self.bufs += [D, T, U, Y]
+            cur, s_in = Y, s_act
+        torch.cuda.synchronize()
+        self.graph = cbs.cbs_graph_create_steps(self.steps)
+
+    def time_steps(self, steps, warmup, use_graph=True):
+        torch, cbs = self.torch, self.cbs
+        run = (lambda: cbs.cbs_graph_launch(self.graph)) if use_graph else (lambda: cbs.cbs_run_steps(self.steps))
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+
+def warm_device(torch, seconds=0.5):
+    """Keep the device busy with plain copies for a moment before the first timed
+    region, so that the first configuration is not timed while clocks ramp up."""
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def layer_rows(bench, us):
@@ -253,12 +351,15 @@ def main():
                       args.batch, args.launches, args.config)
         return
 
+    warm_device(torch)
     results = {}
-    combos = [("f32", cbs.CBS_F32, 1)] if args.quick else [("f32", cbs.CBS_F32, 1), ("int8", cbs.CBS_I8, 1),
-                                                           ("f32", cbs.CBS_F32, 16), ("int8", cbs.CBS_I8, 16)]
+    combos = [("f32", cbs.CBS_F32, 1, False)]
+    if not args.quick:
+        combos += [("int8", cbs.CBS_I8, 1, False), ("int8out", cbs.CBS_I8, 1, True), ("f32", cbs.CBS_F32, 16, False),
+                   ("int8", cbs.CBS_I8, 16, False), ("int8out", cbs.CBS_I8, 16, True)]
     layer_tables = {}
-    for name, dt, bs in combos:
-        b = ListBench(cbs, W, torch, dt, bs)
+    for name, dt, bs, out_i8 in combos:
+        b = ListBench(cbs, W, torch, dt, bs, out_i8=out_i8)
         steps = args.steps if bs == 1 else max(10, args.steps // 8)
         ms_graph, wall_graph = b.time_steps(steps, args.warmup, use_graph=True)
         ms_list, _ = b.time_steps(steps, args.warmup, use_graph=False)
@@ -276,6 +377,25 @@ def main():
                 % (r["layer"], r["c_in"], r["c_out"], r["h_in"], r["k"], r["s"], r["us"], r["tflops"], r["gbs"],
                    r["roof_us"], r["bound"], r["frac"], r["config"]))
         del b
+        torch.cuda.empty_cache()
+
+    # the 25 backbone layers chained through channel slices and fused residuals
+    chains = {}
+    for name, int8, bs in ([] if args.quick else [("f32", False, 1), ("int8", True, 1), ("f32", False, 16),
+                                                  ("int8", True, 16)]):
+        c = ChainBench(cbs, W, torch, int8, bs)
+        steps = args.steps if bs == 1 else max(10, args.steps // 8)
+        ms_graph = c.time_steps(steps, args.warmup, use_graph=True)
+        ms_plain = c.time_steps(steps, args.warmup, use_graph=False)
+        lst = results.get("%s_bs%d" % ("int8out" if int8 else "f32", bs))
+        indep = round(sum(r["us"] for r in lst["rows"][:25]), 2) if lst else None
+        key = "chain_%s_bs%d" % (name, bs)
+        chains[key] = {"value": round(c.flops / (ms_graph * 1e-3) / 1e12, 4), "unit": "TOP/s" if int8 else "TFLOP/s",
+                       "total_us": round(ms_graph * 1e3, 2), "total_us_plain_launches": round(ms_plain * 1e3, 2),
+                       "layers": len(c.layers), "sum_us_same_layers_unchained": indep}
+        log("%s: 25 chained backbone layers %.1f us (graph), %.1f us (plain); the same layers unchained, "
+            "sum of per-layer %s us" % (key, ms_graph * 1e3, ms_plain * 1e3, indep))
+        del c
         torch.cuda.empty_cache()
 
     head = results["f32_bs1"]
@@ -310,6 +430,7 @@ def main():
         line[key] = {"value": round(r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12, 4),
                      "unit": "TOP/s" if int8 else "TFLOP/s", "total_us": round(r["ms_per_step"] * 1e3, 2),
                      "total_us_plain_launches": round(r["ms_per_step_plain_launches"] * 1e3, 2)}
+    line.update(chains)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(W)
     outdir = os.path.join(ROOT, "gpurun_out")

@@ -76,7 +76,48 @@ def masked_mfma_kernels(text: str, pattern: str):
     return bad
 
 
-VARIANTS = 5  # kernel variants, one translation unit each (cbs_variant.hip with -DCBS_VAR=n)
+def late_argument_loads(text: str, pattern: str):
+    """Kernels of a device assembly whose kernel-argument reads (scalar loads:
+    the conv kernels make no other) cost more than one memory round trip:
+    loads issued after a wait for earlier ones, or after the first MFMA (a
+    dependent round trip after the main loop).  Returns (flagged names, number
+    of kernels with at least one argument load before their first MFMA)."""
+    import re
+    bad, early = [], 0
+    for name in re.findall(pattern, text, re.M):
+        i = text.index(name + ":")
+        body = [line.strip() for line in text[i:text.index(".Lfunc_end", i)].split("\n")]
+        first = next((k for k, line in enumerate(body) if line.startswith("v_mfma")), len(body))
+        rounds, pending, late = 0, False, False
+        for k, line in enumerate(body):
+            if line.startswith("s_load_"):
+                if not pending:
+                    rounds += 1
+                pending = True
+                late |= k > first
+            elif "lgkmcnt" in line:
+                pending = False
+        early += any(line.startswith("s_load_") for line in body[:first])
+        if rounds > 1 or late:
+            bad.append(name)
+    return bad, early
+
+
+def flat_memory_ops(text: str, pattern: str):
+    """Kernels that access memory through FLAT instructions (a generic pointer
+    whose global address space the compiler lost): slower than global/buffer
+    ones, and they also wait on the LDS counter."""
+    import re
+    bad = []
+    for name in re.findall(pattern, text, re.M):
+        i = text.index(name + ":")
+        body = text[i:text.index(".Lfunc_end", i)]
+        if re.search(r"^\s+flat_(load|store|atomic)", body, re.M):
+            bad.append(name)
+    return bad
+
+
+VARIANTS = 8  # kernel variants, one translation unit each (cbs_variant.hip with -DCBS_VAR=n)
 CONV_KERNELS = r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+):"
 
 
@@ -101,7 +142,8 @@ def check_mfma_guards(hipcc: str) -> None:
     still execute for the whole wave; every MFMA guard must be a scalar
     (wave-uniform) branch.  Scans the device assembly of every variant of this
     build, after checking that the scan flags a known-masked probe and passes a
-    uniform one."""
+    uniform one.  Also fails if a conv kernel reads a kernel argument after its
+    first MFMA (a memory round trip at the end of every launch)."""
     import re
     probe_src = os.path.join(BUILD_DIR, "guard_probe.hip")
     probe_asm = os.path.join(BUILD_DIR, "guard_probe.s")
@@ -118,14 +160,22 @@ def check_mfma_guards(hipcc: str) -> None:
     flagged = masked_mfma_kernels(open(probe_asm).read(), r"^(_Z\d+probe_\w+):")
     if not any("probe_masked" in n for n in flagged) or any("probe_uniform" in n for n in flagged):
         raise RuntimeError("MFMA guard check failed its calibration (flagged: %s)" % flagged)
-    bad = []
+    bad, late = [], []
     for asm in asms:
         text = open(asm).read()
-        if len(re.findall(CONV_KERNELS, text, re.M)) < 3:
+        n = len(re.findall(CONV_KERNELS, text, re.M))
+        if n < 3:
             raise RuntimeError("MFMA guard check found no conv kernels in %s" % asm)
         bad += masked_mfma_kernels(text, CONV_KERNELS)
+        flagged, early = late_argument_loads(text, CONV_KERNELS)
+        if early < n:
+            raise RuntimeError("argument-load check matched no early scalar loads in %s" % asm)
+        late += flagged
+        late += ["%s (FLAT access)" % k for k in flat_memory_ops(text, CONV_KERNELS)]
     if bad:
         raise RuntimeError("MFMA inside an EXEC-masked region in: %s" % ", ".join(bad))
+    if late:
+        raise RuntimeError("kernel argument read after the main loop, or FLAT access, in: %s" % ", ".join(late))
 
 
 def build(verbose: bool = True) -> str:

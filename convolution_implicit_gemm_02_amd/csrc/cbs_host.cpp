@@ -431,6 +431,9 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
     L->variant = VAR_I8_C4;
     L->raw_variant = VAR_I8_C4_RAW;
   }
+  // the general epilogue only when an option needs it
+  if (d.act != CBS_ACT_SILU || d.out_dtype != CBS_F32 || d.res_c_stride != 0)
+    L->variant = L->variant == VAR_F32 ? VAR_F32_X : L->variant == VAR_I8_C16 ? VAR_I8_C16_X : VAR_I8_C4_X;
   L->chunks_per_tap = L->cin_pad / L->chunk_ch;
   L->total_chunks = taps * L->chunks_per_tap;
   const int chunks_per_step = 4 * vec;

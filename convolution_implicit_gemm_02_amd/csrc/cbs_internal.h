@@ -24,7 +24,13 @@ enum Variant {
   VAR_I8_C4 = 2,        // int8, 4-channel chunks (any C_in_pad % 4 == 0), dequant+SiLU
   VAR_I8_C16_RAW = 3,   // as VAR_I8_C16, stores raw int32 accumulators
   VAR_I8_C4_RAW = 4,    // as VAR_I8_C4, stores raw int32 accumulators
-  VAR_COUNT = 5
+  // the same three with the general epilogue: identity activation, residual,
+  // int8 output (runtime, wave-uniform); the plain ones above keep the short
+  // SiLU + fp32 store, so the common case executes no extra instructions
+  VAR_F32_X = 5,
+  VAR_I8_C16_X = 6,
+  VAR_I8_C4_X = 7,
+  VAR_COUNT = 8
 };
 
 // Everything a launch needs; filled at create, passed by value.
@@ -79,6 +85,9 @@ hipError_t launch_var_1(int cfg, const ConvParams &p, hipStream_t stream);
 hipError_t launch_var_2(int cfg, const ConvParams &p, hipStream_t stream);
 hipError_t launch_var_3(int cfg, const ConvParams &p, hipStream_t stream);
 hipError_t launch_var_4(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_5(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_6(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_7(int cfg, const ConvParams &p, hipStream_t stream);
 
 hipError_t launch_pack_nhwc_f32(const float *x, float *y, int n, int c, int hw, int c_pad,
                                 hipStream_t stream);

@@ -30,6 +30,9 @@ hipError_t launch_conv(int var, int cfg, const ConvParams &p, hipStream_t stream
     case 2: return launch_var_2(cfg, p, stream);
     case 3: return launch_var_3(cfg, p, stream);
     case 4: return launch_var_4(cfg, p, stream);
+    case 5: return launch_var_5(cfg, p, stream);
+    case 6: return launch_var_6(cfg, p, stream);
+    case 7: return launch_var_7(cfg, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

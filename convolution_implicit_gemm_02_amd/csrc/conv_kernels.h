@@ -42,27 +42,33 @@ namespace cbs {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Operand and epilogue traits of a variant: VEC = 4-channel chunks per lane
+// and K step (int8 small-channel gather), ESIZE = bytes per activation, RAW =
+// store int32 accumulators, X = general epilogue (act / residual / int8 out).
 template <int VAR> struct Var;
 template <> struct Var<VAR_F32> {
   using Frag = f32x4; using Acc = f32x4;
-  static constexpr int VEC = 1, ESIZE = 4; static constexpr bool I8 = false, RAW = false;
+  static constexpr int VEC = 1, ESIZE = 4; static constexpr bool I8 = false, RAW = false, X = false;
 };
 template <> struct Var<VAR_I8_C16> {
   using Frag = i32x4; using Acc = i32x4;
-  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = false;
+  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = false, X = false;
 };
 template <> struct Var<VAR_I8_C4> {
   using Frag = i32x4; using Acc = i32x4;
-  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = false;
+  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = false, X = false;
 };
 template <> struct Var<VAR_I8_C16_RAW> {
   using Frag = i32x4; using Acc = i32x4;
-  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = true;
+  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = true, X = false;
 };
 template <> struct Var<VAR_I8_C4_RAW> {
   using Frag = i32x4; using Acc = i32x4;
-  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = true;
+  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = true, X = false;
 };
+template <> struct Var<VAR_F32_X> : Var<VAR_F32> { static constexpr bool X = true; };
+template <> struct Var<VAR_I8_C16_X> : Var<VAR_I8_C16> { static constexpr bool X = true; };
+template <> struct Var<VAR_I8_C4_X> : Var<VAR_I8_C4> { static constexpr bool X = true; };
 
 
 // Buffer resource word 3 (data format) for the gfx9 family, and an offset
@@ -72,6 +78,75 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr unsigned kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ float silu_f(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
+
+// Kernel arguments arrive through scalar loads from the argument block.  Left
+// to itself the compiler re-reads the ones that only the epilogue uses after
+// the main loop (to free SGPRs), which puts one more dependent memory round
+// trip at the end of every launch.  Pinning them at entry (an empty asm that
+// "modifies" the value, so it cannot be re-read) keeps them in SGPRs from the
+// start.  The build checks that no argument load follows the first MFMA.
+template <class T>
+__device__ __forceinline__ void pin_sgpr(T &v) {
+  asm volatile("" : "+s"(v));
+}
+
+// A pinned pointer no longer carries the compiler's knowledge that kernel
+// pointer arguments point to global memory, so every access through one names
+// the global address space explicitly (otherwise it becomes a slower FLAT
+// access, which also waits on the LDS counter).
+#define CBS_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ CBS_GLOBAL T *gmem(const void *ptr) {
+  return (CBS_GLOBAL T *)ptr;
+}
+
+// Every argument the kernels read, pinned at entry: the compiler then issues
+// all argument loads at once and waits for them once, instead of spreading
+// them over two or three dependent rounds (it sinks loads towards their first
+// use), each costing a memory round trip before the first operand load.
+__device__ __forceinline__ void pin_all_args(ConvParams &p, int &nblocks) {
+  pin_sgpr(nblocks);  // the grid size comes from the dispatch's own argument area
+  pin_sgpr(p.x);
+  pin_sgpr(p.wfrag);
+  pin_sgpr(p.bias);
+  pin_sgpr(p.dq);
+  pin_sgpr(p.H);
+  pin_sgpr(p.W);
+  pin_sgpr(p.x_cs);
+  pin_sgpr(p.k);
+  pin_sgpr(p.stride);
+  pin_sgpr(p.pad);
+  pin_sgpr(p.chunk_ch);
+  pin_sgpr(p.chunks_per_tap);
+  pin_sgpr(p.cpt_magic);
+  pin_sgpr(p.total_chunks);
+  pin_sgpr(p.steps);
+  pin_sgpr(p.steps_per_split);
+  pin_sgpr(p.co_blocks);
+  pin_sgpr(p.co_tiles);
+  pin_sgpr(p.x_bytes);
+  pin_sgpr(p.w_bytes);
+  pin_sgpr(p.out);
+  pin_sgpr(p.res);
+  pin_sgpr(p.ws);
+  pin_sgpr(p.counters);
+  pin_sgpr(p.cout_pad);
+  pin_sgpr(p.out_cs);
+  pin_sgpr(p.res_cs);
+  pin_sgpr(p.res_bytes);
+  pin_sgpr(p.act);
+  pin_sgpr(p.out_i8);
+  pin_sgpr(p.out_scale);
+  pin_sgpr(p.res_scale);
+  pin_sgpr(p.splitk);
+  pin_sgpr(p.OH);
+  pin_sgpr(p.OW);
+  pin_sgpr(p.pitch);
+  pin_sgpr(p.M);
+  pin_sgpr(p.tiles_x);
+  pin_sgpr(p.tiles_y);
+  pin_sgpr(p.halo_bytes);
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, kRsrcWord3);
@@ -86,9 +161,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, unsigne
 // the graph-entry quantiser would produce from this layer's fp32 output.
 // act, the residual and the output type are kernel arguments: every branch
 // here is wave-uniform.
+template <bool X>
 __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buffer_rsrc_t rr, f32x4 z, int opix,
                                                int m, int co0) {
   f32x4 y;
+  if constexpr (!X) {  // plain: SiLU, fp32 store
+#pragma unroll
+    for (int i = 0; i < 4; i++) y[i] = silu_f(z[i]);
+    *(gmem<f32x4>(p.out) + ((size_t)opix * p.out_cs + co0) / 4) = y;
+    return;
+  }
   if (p.act == ACT_NONE) {
     y = z;
   } else {
@@ -115,9 +197,9 @@ __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buf
       t = fminf(fmaxf(t, -127.0f), 127.0f);
       word |= ((unsigned)((int)t & 0xff)) << (8 * i);
     }
-    *(unsigned *)((signed char *)p.out + o) = word;
+    *(gmem<unsigned>(p.out) + o / 4) = word;
   } else {
-    *(f32x4 *)((float *)p.out + o) = y;
+    *(gmem<f32x4>(p.out) + o / 4) = y;
   }
 }
 
@@ -142,6 +224,8 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   using V = Var<VAR>;
   using Frag = typename V::Frag;
   using Acc = typename V::Acc;
+  int nblocks = gridDim.x;
+  pin_all_args(p, nblocks);
   const int lane = threadIdx.x & 63;
   // The wave index is made explicitly wave-uniform: every condition that
   // guards an MFMA below depends only on it, so it compiles to a scalar
@@ -156,9 +240,9 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   // Workgroups are dispatched round-robin over the 8 XCDs; remap so that each
   // XCD receives a contiguous range of logical tiles (the co tiles and K
   // splits of one pixel tile then share that XCD's L2).
-  const int nb = gridDim.x, bid = blockIdx.x;
+  const int nb = nblocks, bid = blockIdx.x;
   const int per = nb >> 3, rem = nb & 7, xcd = bid & 7, loc = bid >> 3;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
   const int split = logical % p.splitk;
   const int tile = logical / p.splitk;
   const int co_tile = tile % p.co_tiles;
@@ -320,7 +404,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   if (p.splitk > 1) {
     __shared__ int s_last;
     constexpr int TILE_VECS = WCO * WPX * CB * PB * 64;
-    Acc *wsb = (Acc *)p.ws + (size_t)tile * p.splitk * TILE_VECS;
+    CBS_GLOBAL Acc *wsb = gmem<Acc>(p.ws) + (size_t)tile * p.splitk * TILE_VECS;
     if (wk == 0) {
 #pragma unroll
       for (int cb = 0; cb < CB; cb++)
@@ -331,7 +415,8 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     __threadfence();
     __syncthreads();
     if (threadIdx.x == 0) {
-      const unsigned prev = atomicAdd(&p.counters[tile], 1u);
+      const unsigned prev =
+          __hip_atomic_fetch_add(gmem<unsigned>(p.counters) + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = (prev == (unsigned)(p.splitk - 1));
     }
     __syncthreads();
@@ -354,7 +439,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
         }
     }
     if (threadIdx.x == 0)
-      __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gmem<unsigned>(p.counters) + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   if (wk != 0) return;
@@ -369,7 +454,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     if constexpr (V::RAW) {
 #pragma unroll
       for (int b = 0; b < PB; b++)
-        if (mval[b]) *(i32x4 *)((int *)p.out + (size_t)outpix[b] * p.out_cs + co0) = acc[cb][b];
+        if (mval[b]) *(gmem<i32x4>(p.out) + ((size_t)outpix[b] * p.out_cs + co0) / 4) = acc[cb][b];
     } else {
       const f32x4 bias = ep_bias[cb];
       const f32x4 dq = ep_dq[cb];
@@ -384,7 +469,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
           else
             z[i] = acc[cb][b][i] + bias[i];
         }
-        epilogue_store(p, rr, z, outpix[b], ((px_tile * WPX + wpx) * PB + b) * 16 + r, co0);
+        epilogue_store<V::X>(p, rr, z, outpix[b], ((px_tile * WPX + wpx) * PB + b) * 16 + r, co0);
       }
     }
   }
@@ -452,6 +537,8 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   using Acc = typename V::Acc;
   constexpr int NT = 64 * WM * WN;
   constexpr int BMB = MB * WM, BNB = NB * WN;     // 16-pixel and 16-channel blocks per workgroup
+  int nblocks = gridDim.x;
+  pin_all_args(p, nblocks);
   constexpr int SB = BMB + BNB;                   // fragment blocks per K step
   constexpr int NA = KS * BNB * 64 / NT;          // weight slots per thread per stage
   constexpr int NX = KS * BMB * 64 / NT;          // activation slots per thread per stage
@@ -463,9 +550,9 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   const int wm = wave % WM, wn = wave / WM;
   const int r = lane & 15, g = lane >> 4;
 
-  const int nb_ = gridDim.x, bid = blockIdx.x;
+  const int nb_ = nblocks, bid = blockIdx.x;
   const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
   const int co_tile = logical % p.co_tiles;
   const int px_tile = logical / p.co_tiles;
 
@@ -587,7 +674,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
       const Pix q = pixel_of(p, m);
       if (!q.ok) continue;
       if constexpr (V::RAW) {
-        *(i32x4 *)((int *)p.out + (size_t)q.out * p.out_cs + co0) = acc[nb][mb];
+        *(gmem<i32x4>(p.out) + ((size_t)q.out * p.out_cs + co0) / 4) = acc[nb][mb];
       } else {
         f32x4 z;
 #pragma unroll
@@ -597,7 +684,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
           else
             z[i] = acc[nb][mb][i] + ep_bias[nb][i];
         }
-        epilogue_store(p, rr, z, q.out, m, co0);
+        epilogue_store<V::X>(p, rr, z, q.out, m, co0);
       }
     }
   }
@@ -622,15 +709,17 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   constexpr int MB = TH * TW / 64;  // 16-pixel blocks per wave (4 waves)
   static_assert(TH * TW % 64 == 0, "tile must split into 4 waves of 16-pixel blocks");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int nblocks = gridDim.x;
+  pin_all_args(p, nblocks);
   typedef __attribute__((address_space(3))) void *lds_ptr;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (see conv_igemm)
   const int r = lane & 15, g = lane >> 4;
 
-  const int nb_ = gridDim.x, bid = blockIdx.x;
+  const int nb_ = nblocks, bid = blockIdx.x;
   const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
   const int tx = logical % p.tiles_x;
   const int rest = logical / p.tiles_x;
   const int ty = rest % p.tiles_y;
@@ -763,7 +852,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
       if (oh >= p.OH || ow >= p.OW) continue;
       const int opix = (n * p.OH + oh) * p.pitch + ow;
       if constexpr (V::RAW) {
-        *(i32x4 *)((int *)p.out + (size_t)opix * p.out_cs + co0) = acc[nb][mb];
+        *(gmem<i32x4>(p.out) + ((size_t)opix * p.out_cs + co0) / 4) = acc[nb][mb];
       } else {
         f32x4 z;
 #pragma unroll
@@ -773,7 +862,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
           else
             z[i] = acc[nb][mb][i] + ep_bias[nb][i];
         }
-        epilogue_store(p, rr, z, opix, (n * p.OH + oh) * p.OW + ow, co0);
+        epilogue_store<V::X>(p, rr, z, opix, (n * p.OH + oh) * p.OW + ow, co0);
       }
     }
   }
