@@ -320,6 +320,10 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
     p.act = L->d.act == CBS_ACT_NONE ? ACT_NONE : ACT_SILU;
     p.out_i8 = L->d.out_dtype == CBS_I8;
     p.out_scale = L->d.out_scale;
+    // RN(1/s) in fp32: the double quotient rounded to float (one float of 24
+    // bits times one of 25 cannot land within 2^-53 of 1 unless both are powers
+    // of two, so the double rounding never changes the result)
+    p.out_rcp = L->d.out_dtype == CBS_I8 ? (float)(1.0 / (double)L->d.out_scale) : 0.0f;
     if (L->res_cs) {
       p.res = (const char *)res + (size_t)L->d.res_c_offset * esz_out;
       p.res_cs = L->res_cs;

@@ -55,6 +55,7 @@ struct ConvParams {
   int act;               // Act
   int out_i8;            // 1: int8 output codes q = clamp(rne(fp32(y / out_scale)), +-127)
   float out_scale;       // s_y for int8 output
+  float out_rcp;         // RN(1/s_y), the correctly rounded fp32 reciprocal
   float res_scale;       // scale of int8 residual codes
   unsigned res_bytes;    // bytes of the residual buffer from res (buffer-load range)
   int k, stride, pad;

@@ -137,6 +137,7 @@ __device__ __forceinline__ void pin_all_args(ConvParams &p, int &nblocks) {
   pin_sgpr(p.act);
   pin_sgpr(p.out_i8);
   pin_sgpr(p.out_scale);
+  pin_sgpr(p.out_rcp);
   pin_sgpr(p.res_scale);
   pin_sgpr(p.splitk);
   pin_sgpr(p.OH);
@@ -189,11 +190,19 @@ __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buf
   }
   const size_t o = (size_t)opix * p.out_cs + co0;
   if (p.out_i8) {
+    // q = clamp(rne(fp32(y / s)), +-127) with the correctly rounded quotient
+    // from Markstein's correction step: with r = RN(1/s), q0 = RN(y r),
+    // e = y - q0 s (exact in one FMA), RN(q0 + e r) = RN(y / s) for quotients
+    // in the normal range.  y is first limited to +-128 s, which changes no
+    // code (everything beyond is clamped to +-127 anyway) and keeps q0 finite.
+    const float s = p.out_scale, r = p.out_rcp, lim = 128.0f * s;
     unsigned word = 0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      // fp32 division, correctly rounded, then round half to even and clamp
-      float t = rintf(__fdiv_rn(y[i], p.out_scale));
+      const float yc = fminf(fmaxf(y[i], -lim), lim);
+      const float q0 = yc * r;
+      const float e = __builtin_fmaf(-q0, s, yc);
+      float t = rintf(__builtin_fmaf(e, r, q0));
       t = fminf(fmaxf(t, -127.0f), 127.0f);
       word |= ((unsigned)((int)t & 0xff)) << (8 * i);
     }
@@ -700,12 +709,15 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
 // weights straight into LDS with direct-to-LDS buffer loads (out-of-range
 // offsets supply the zero padding), then runs every tap of the convolution
 // from LDS on MFMA.  This is the direct-convolution path for the stem.
-template <int VAR, int TH, int TW>
+template <int VAR, int TH, int TW, int NBMAX>
 __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   using V = Var<VAR>;
   using Frag = typename V::Frag;
   using Acc = typename V::Acc;
-  constexpr int NBMAX = 4;
+  // NBMAX (1, 2 or 4) bounds the 16-channel output blocks at compile time, so
+  // accumulators and epilogue operands take registers only for blocks that can
+  // exist: a 16-channel layer keeps a quarter of the 64-channel footprint and
+  // runs at a higher occupancy.
   constexpr int MB = TH * TW / 64;  // 16-pixel blocks per wave (4 waves)
   static_assert(TH * TW % 64 == 0, "tile must split into 4 waves of 16-pixel blocks");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -887,9 +899,15 @@ static hipError_t launch_lds(const ConvParams &p, hipStream_t stream) {
 
 template <int VAR, int TH, int TW>
 static hipError_t launch_halo(const ConvParams &p, hipStream_t stream) {
-  if (p.splitk != 1 || p.co_blocks > 4 || p.k != 3) return hipErrorInvalidValue;
+  if (p.splitk != 1 || p.co_blocks < 1 || p.co_blocks > 4 || p.k != 3) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)p.px_tiles;
-  hipLaunchKernelGGL((conv_halo<VAR, TH, TW>), dim3(grid), dim3(256), (unsigned)p.smem_bytes, stream, p);
+  const unsigned smem = (unsigned)p.smem_bytes;
+  if (p.co_blocks == 1)
+    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 1>), dim3(grid), dim3(256), smem, stream, p);
+  else if (p.co_blocks == 2)
+    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 2>), dim3(grid), dim3(256), smem, stream, p);
+  else
+    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 4>), dim3(grid), dim3(256), smem, stream, p);
   return hipGetLastError();
 }
 
