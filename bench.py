@@ -82,6 +82,19 @@ class ListBench:
         self.flops = sum(i["flops"] for i in self.infos)
         self.graph = cbs.cbs_graph_create(self.layers, self.ins, self.outs)
 
+    def autotune(self, iters=20):
+        """Create-time tuning of every layer on its own buffers (cbs_layer_autotune), then
+        re-capture the graph.  Returns the number of layers whose configuration changed."""
+        changed = 0
+        for i, (layer, xin, out) in enumerate(zip(self.layers, self.ins, self.outs)):
+            before = (self.infos[i]["config"], self.infos[i]["splitk"])
+            after = self.cbs.cbs_layer_autotune(layer, xin, out, iters=iters)
+            changed += after != before
+            self.infos[i] = self.cbs.cbs_layer_info(layer)
+        self.torch.cuda.synchronize()
+        self.graph = self.cbs.cbs_graph_create(self.layers, self.ins, self.outs)
+        return changed
+
     def time_steps(self, steps, warmup, use_graph=True):
         torch, cbs = self.torch, self.cbs
         for _ in range(warmup):
@@ -379,6 +392,24 @@ def main():
         del b
         torch.cuda.empty_cache()
 
+    # create-time tuning (cbs_layer_autotune) against the compiled-in table, batch 1
+    tuned = {}
+    for name, dt in ([] if args.quick else [("f32", cbs.CBS_F32), ("int8", cbs.CBS_I8)]):
+        b = ListBench(cbs, W, torch, dt, 1)
+        t0 = time.perf_counter()
+        changed = b.autotune()
+        t_tune = time.perf_counter() - t0
+        steps = args.steps
+        ms_graph, _ = b.time_steps(steps, args.warmup, use_graph=True)
+        key = "%s_bs1_autotuned" % name
+        tuned[key] = {"value": round(b.flops / (ms_graph * 1e-3) / 1e12, 4),
+                      "unit": "TOP/s" if dt == cbs.CBS_I8 else "TFLOP/s", "total_us": round(ms_graph * 1e3, 2),
+                      "layers_changed": changed, "tune_seconds": round(t_tune, 2)}
+        log("%s: list %.1f us (graph) after create-time tuning (%d of %d layers changed configuration, %.1f s)"
+            % (key, ms_graph * 1e3, changed, len(b.layers), t_tune))
+        del b
+        torch.cuda.empty_cache()
+
     # the 25 backbone layers chained through channel slices and fused residuals
     chains = {}
     for name, int8, bs in ([] if args.quick else [("f32", False, 1), ("int8", True, 1), ("f32", False, 16),
@@ -430,6 +461,7 @@ def main():
         line[key] = {"value": round(r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12, 4),
                      "unit": "TOP/s" if int8 else "TFLOP/s", "total_us": round(r["ms_per_step"] * 1e3, 2),
                      "total_us_plain_launches": round(r["ms_per_step_plain_launches"] * 1e3, 2)}
+    line.update(tuned)
     line.update(chains)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(W)

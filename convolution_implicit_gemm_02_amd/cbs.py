@@ -32,6 +32,7 @@ CBS_F32 = 0
 CBS_I8 = 1
 CBS_ACT_SILU = 0
 CBS_ACT_NONE = 1
+CBS_TUNE_FORCE = 1
 
 _STATUS_NAMES = {0: "CBS_OK", -1: "CBS_EINVAL", -2: "CBS_EUNSUPPORTED", -3: "CBS_ENOMEM",
                  -4: "CBS_EDEVICE", -5: "CBS_ELAUNCH"}
@@ -87,6 +88,8 @@ _SIGNATURES = {
     "cbs_layer_info": (_I, [_P, ctypes.POINTER(cbs_layer_info_t)]),
     "cbs_layer_set_config": (_I, [_P, _I, _I]),
     "cbs_num_configs": (_I, []),
+    "cbs_layer_autotune": (_I, [_P, _P, _P, _P, _I, _I, _P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "cbs_autotune_clear_cache": (None, []),
     "cbs_config_name": (ctypes.c_char_p, [_I]),
     "cbs_last_error": (ctypes.c_char_p, []),
     "cbs_pack_nhwc_f32": (_I, [_P, _P, _I, _I, _I, _I, _I, _P]),
@@ -266,6 +269,19 @@ def cbs_layer_info(layer: Layer) -> dict:
 
 def cbs_layer_set_config(layer: Layer, config: int, splitk: int = 0) -> None:
     _check(lib.cbs_layer_set_config(layer.handle, int(config), int(splitk)), "cbs_layer_set_config")
+
+
+def cbs_layer_autotune(layer: Layer, inp, out, residual=None, iters=0, flags=0, stream=None):
+    """Time every configuration on these buffers and keep the fastest; returns (config, splitk)."""
+    c, k = _I(), _I()
+    _check(lib.cbs_layer_autotune(layer.handle, _dev_ptr(inp), _dev_ptr(out), _dev_ptr(residual), int(iters),
+                                  int(flags), _stream(stream), ctypes.byref(c), ctypes.byref(k)),
+           "cbs_layer_autotune")
+    return c.value, k.value
+
+
+def cbs_autotune_clear_cache() -> None:
+    lib.cbs_autotune_clear_cache()
 
 
 def cbs_num_configs() -> int:

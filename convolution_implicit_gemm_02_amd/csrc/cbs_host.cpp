@@ -18,8 +18,11 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/cbs.h"
@@ -752,6 +755,118 @@ cbs_status cbs_layer_set_config(cbs_layer *L, int32_t cfg, int32_t splitk) {
 }
 
 int32_t cbs_num_configs(void) { return num_configs(); }
+
+}  // extern "C"
+
+namespace {
+
+// Create-time tuning results, per device and per everything that changes a
+// kernel's timing: shape, dtype, epilogue variant and channel strides.
+using TuneKey = std::tuple<int, int, int, int, int, int, int, int, int, int, int, int, int, int>;
+std::mutex g_tune_mu;
+std::map<TuneKey, Choice> g_tune_cache;
+
+TuneKey tune_key(const cbs_layer *L) {
+  const cbs_conv_desc &d = L->d;
+  return TuneKey{L->device, d.n, d.c_in, d.c_out, d.h, d.w, d.k, d.stride, d.pad, d.dtype, L->variant, L->in_cs,
+                 L->out_cs, L->res_cs};
+}
+
+// Mean time of `iters` back-to-back launches (after two warm-ups), in ms.
+cbs_status time_config(cbs_layer *L, const void *in, void *out, const void *res, int iters, hipStream_t st,
+                       hipEvent_t e0, hipEvent_t e1, float *ms) {
+  for (int i = 0; i < 2; i++) {
+    cbs_status s = launch(L, in, out, res, st);
+    if (s != CBS_OK) return s;
+  }
+  if (hipEventRecord(e0, st) != hipSuccess) return fail(CBS_EDEVICE, "autotune: event record failed");
+  for (int i = 0; i < iters; i++) {
+    cbs_status s = launch(L, in, out, res, st);
+    if (s != CBS_OK) return s;
+  }
+  if (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess)
+    return fail(CBS_EDEVICE, "autotune: event wait failed");
+  if (hipEventElapsedTime(ms, e0, e1) != hipSuccess) return fail(CBS_EDEVICE, "autotune: elapsed time failed");
+  *ms /= (float)iters;
+  return CBS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cbs_status cbs_layer_autotune(cbs_layer *L, const void *in, void *out, const void *residual, int32_t iters,
+                              int32_t flags, void *stream, int32_t *config_out, int32_t *splitk_out) {
+  cbs_status st = check_step(L, in, out, residual, "layer_autotune", 0);
+  if (st != CBS_OK) return st;
+  if (iters < 0 || iters > 100000) return fail(CBS_EINVAL, "layer_autotune: iters %d out of range", iters);
+  if (flags & ~CBS_TUNE_FORCE) return fail(CBS_EINVAL, "layer_autotune: unknown flags 0x%x", flags);
+  if (iters == 0) iters = 20;
+  const TuneKey key = tune_key(L);
+  Choice best{L->config, L->splitk};
+  bool cached = false;
+  if (!(flags & CBS_TUNE_FORCE)) {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    auto it = g_tune_cache.find(key);
+    if (it != g_tune_cache.end()) {
+      best = it->second;
+      cached = true;
+    }
+  }
+  if (!cached) {
+    hipStream_t hs = (hipStream_t)stream;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+      if (e0) (void)hipEventDestroy(e0);
+      return fail(CBS_EDEVICE, "layer_autotune: event creation failed");
+    }
+    const int old_cfg = L->config, old_sk = L->splitk;
+    float best_ms = 1e30f;
+    st = CBS_OK;
+    for (int cfg = 0; cfg < num_configs() && st == CBS_OK; cfg++) {
+      for (int sk : {1, 2, 4}) {
+        if (!config_fits(L, cfg, sk)) continue;
+        if (sk > 1) {  // cross-workgroup split-K only for grids that leave CUs idle
+          int pxt, cot;
+          tiles_of(L, cfg, &pxt, &cot);
+          if ((long)pxt * cot >= 256) continue;
+        }
+        L->config = cfg;
+        L->splitk = sk;
+        st = setup_splitk(L);
+        float ms = 0.f;
+        if (st == CBS_OK) st = time_config(L, in, out, residual, iters, hs, e0, e1, &ms);
+        if (st != CBS_OK) break;
+        if (ms < best_ms) {
+          best_ms = ms;
+          best = {cfg, sk};
+        }
+      }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != CBS_OK) {
+      L->config = old_cfg;
+      L->splitk = old_sk;
+      (void)setup_splitk(L);
+      return st;
+    }
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_tune_cache[key] = best;
+  }
+  L->config = best.config;
+  L->splitk = best.splitk;
+  st = setup_splitk(L);
+  if (st != CBS_OK) return st;
+  if (config_out) *config_out = best.config;
+  if (splitk_out) *splitk_out = best.splitk;
+  return CBS_OK;
+}
+
+void cbs_autotune_clear_cache(void) {
+  std::lock_guard<std::mutex> lk(g_tune_mu);
+  g_tune_cache.clear();
+}
 
 const char *cbs_config_name(int32_t cfg) {
   if (cfg < 0 || cfg >= num_configs()) return nullptr;

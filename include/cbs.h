@@ -238,6 +238,31 @@ cbs_status cbs_layer_info(const cbs_layer *layer, cbs_layer_info_t *info);
  */
 cbs_status cbs_layer_set_config(cbs_layer *layer, int32_t config, int32_t splitk);
 int32_t cbs_num_configs(void);
+
+/*
+ * Create-time tuning: the vision-rs page's improvement #1 in its intended
+ * form ("Improvements" #1: benchmark candidate tiles per unique layer shape,
+ * since one fixed tile spans 5 to 556 us across call sites).  Times every
+ * kernel configuration that can run this layer (split-K 1, plus 2 and 4 for
+ * register-direct configurations whose grid is below 256 workgroups) with
+ * `iters` launches each (0 = 20) after two warm-ups, with HIP events on
+ * `stream`, on the caller's buffers, and keeps the fastest.  The choice is
+ * cached in the process per device, shape, dtype, epilogue and channel
+ * strides: a later call for the same key takes it without timing, unless
+ * flags has CBS_TUNE_FORCE.  Blocks until the timing is done, may allocate
+ * (split-K workspaces), writes `out` as a run does; not for use under graph
+ * capture.  The compiled-in tile table (an offline sweep of the same kind)
+ * stays the default at create; this call replaces it for one layer.
+ * *config_out / *splitk_out (may be NULL) receive the choice.  Errors:
+ * CBS_EINVAL (null layer or buffer, residual mismatch, bad iters or flags),
+ * CBS_ELAUNCH / CBS_EDEVICE (the layer keeps its previous configuration).
+ */
+#define CBS_TUNE_FORCE 1
+cbs_status cbs_layer_autotune(cbs_layer *layer, const void *in, void *out, const void *residual,
+                              int32_t iters, int32_t flags, void *stream, int32_t *config_out,
+                              int32_t *splitk_out);
+/* Forget every cached tuning result (all devices). */
+void cbs_autotune_clear_cache(void);
 /* Name of configuration i, or NULL when i is out of range.  Static storage. */
 const char *cbs_config_name(int32_t config);
 

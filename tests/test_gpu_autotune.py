@@ -1,0 +1,80 @@
+"""GPU tests of the create-time autotuner (cbs_layer_autotune): it picks a
+configuration that can run the layer, the layer then still matches the
+oracle, the choice is cached per shape, and CBS_TUNE_FORCE re-times.
+
+The vision-rs page ranks per-shape tile autotuning first among its
+improvements (section "Improvements", #1); the compiled-in table is the
+offline form of it, this is the create-time form."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from convolution_implicit_gemm_02_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from convolution_implicit_gemm_02_amd import cbs
+    from gpu_helpers import (alloc_out, assert_f32_parity, assert_i8_parity, check_guards, create, pack_input,
+                             run_f32, run_i8)
+
+SHAPES = [
+    W.LayerSpec("t.single", 32, 32, 40, 40, 3, 1, 1),
+    W.LayerSpec("t.untabled", 24, 40, 19, 23, 3, 2, 1),      # no tile-table entry: cost model at create
+    W.LayerSpec("t.1x1", 96, 48, 17, 17, 1, 1, 0),
+    W.LayerSpec("t.stem", 3, 16, 64, 48, 3, 2, 1, "uniform"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "i8"])
+@pytest.mark.parametrize("idx", range(len(SHAPES)))
+def test_autotune_keeps_parity(idx, dtype):
+    cbs.cbs_autotune_clear_cache()
+    L = W.draw_layer(np.random.default_rng(70 + idx), SHAPES[idx], 2)
+    s_x = W.calibration_scale(L.x) if dtype == "i8" else None
+    layer = create(L, cbs.CBS_F32 if dtype == "f32" else cbs.CBS_I8, s_x=s_x)
+    xin = pack_input(L, cbs.CBS_F32 if dtype == "f32" else cbs.CBS_I8, s_x=s_x)
+    out, _ = alloc_out(L, layer)
+    cfg, sk = cbs.cbs_layer_autotune(layer, xin, out, iters=5)
+    info = cbs.cbs_layer_info(layer)
+    assert (info["config"], info["splitk"]) == (cfg, sk)
+    assert 0 <= cfg < cbs.cbs_num_configs() and sk in (1, 2, 4)
+    if dtype == "f32":
+        r = run_f32(L, layer=layer)
+        y, s = oracle.conv_bn_silu_f32(L.x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride, L.spec.pad)
+        assert_f32_parity(r["y"], y, s, "%s autotuned %s" % (L.spec.name, info["config_name"]))
+    else:
+        r = run_i8(L, s_x, layer=layer)
+        ref = oracle.conv_bn_silu_i8(L.x, s_x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride,
+                                     L.spec.pad)
+        assert np.array_equal(r["acc"], ref["acc"])
+        assert_i8_parity(r["y"], ref["y"], ref["f"], ref["absacc"], "%s autotuned int8" % L.spec.name)
+    assert check_guards(r["host"], L, r["info"]) == 0
+
+
+def test_autotune_cache_and_force():
+    cbs.cbs_autotune_clear_cache()
+    L = W.draw_layer(np.random.default_rng(80), SHAPES[1], 1)
+    a = create(L, cbs.CBS_F32)
+    b = create(L, cbs.CBS_F32)
+    xin = pack_input(L, cbs.CBS_F32)
+    out, _ = alloc_out(L, a)
+    t0 = time.perf_counter()
+    first = cbs.cbs_layer_autotune(a, xin, out, iters=10)
+    t_first = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    second = cbs.cbs_layer_autotune(b, xin, out, iters=10)
+    t_second = time.perf_counter() - t0
+    assert second == first, "same shape must take the cached choice"
+    assert t_second < t_first, "a cached choice must not re-time every configuration"
+    forced = cbs.cbs_layer_autotune(b, xin, out, iters=3, flags=cbs.CBS_TUNE_FORCE)
+    assert cbs.cbs_layer_info(b)["config"] == forced[0]
+    with pytest.raises(cbs.CbsError):
+        cbs.cbs_layer_autotune(b, xin, out, iters=-1)
+    with pytest.raises(cbs.CbsError):
+        cbs.cbs_layer_autotune(b, xin, out, flags=8)
+    with pytest.raises(cbs.CbsError):
+        cbs.cbs_layer_autotune(b, xin, out, residual=xin)  # the layer has no residual

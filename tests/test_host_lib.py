@@ -103,6 +103,8 @@ def test_null_arguments(cbs):
     assert cbs.lib.cbs_run_layer_list(None, -1, None, None, None) == cbs.CBS_EINVAL
     assert cbs.lib.cbs_run_layer_list(None, 0, None, None, None) == cbs.CBS_OK  # empty list: nothing to do
     assert cbs.lib.cbs_run_layer_res(None, None, None, None, None) == cbs.CBS_EINVAL
+    assert cbs.lib.cbs_layer_autotune(None, None, None, None, 0, 0, None, None, None) == cbs.CBS_EINVAL
+    cbs.lib.cbs_autotune_clear_cache()
     assert cbs.lib.cbs_run_steps(None, -1, None) == cbs.CBS_EINVAL
     assert cbs.lib.cbs_run_steps(None, 0, None) == cbs.CBS_OK
     steps = (cbs.cbs_step * 1)()
