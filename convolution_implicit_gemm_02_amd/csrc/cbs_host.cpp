@@ -303,6 +303,17 @@ cbs_status setup_splitk(cbs_layer *L) {
 
 // Kernel arguments of one launch.  raw: the INT8 test hook, which stores
 // int32 accumulators densely ([N][OH][pitch][C_out_pad]) with no epilogue.
+// Multiply-shift divisor for d >= 1 (numerators below 2^31; see FastDiv).
+FastDiv make_fastdiv(int d) {
+  if (d < 1) d = 1;
+  int l = 0;
+  while ((1ull << l) < (unsigned long long)d) l++;
+  FastDiv f;
+  f.magic = (unsigned)(((1ull << 32) * ((1ull << l) - (unsigned long long)d)) / (unsigned long long)d + 1ull);
+  f.shift = l;
+  return f;
+}
+
 ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void *res, bool raw) {
   ConvParams p;
   std::memset(&p, 0, sizeof(p));
@@ -364,6 +375,12 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
     halo_lds(L, L->config, &p.halo_bytes, &p.smem_bytes);
   }
   tiles_of(L, L->config, &p.px_tiles, &p.co_tiles);
+  p.div_ow = make_fastdiv(p.OW);
+  p.div_oh = make_fastdiv(p.OH);
+  p.div_cot = make_fastdiv(p.co_tiles);
+  p.div_sk = make_fastdiv(p.splitk);
+  p.div_tx = make_fastdiv(p.tiles_x);
+  p.div_ty = make_fastdiv(p.tiles_y);
   return p;
 }
 

@@ -37,6 +37,17 @@ enum Variant {
 // Epilogue activation codes (ConvParams::act).
 enum Act { ACT_SILU = 0, ACT_NONE = 1 };
 
+// Division by a run-time constant d >= 1, for numerators below 2^31, with one
+// multiply-high, an add and a shift (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994, Figure 4.1): with
+// l = ceil(log2 d) and magic = floor(2^32 (2^l - d) / d) + 1,
+//   n / d = (mulhi(n, magic) + n) >> l,
+// where the sum stays below 2^32 because n < 2^31.  Set up on the host.
+struct FastDiv {
+  unsigned magic;
+  int shift;
+};
+
 struct ConvParams {
   const void *x;         // NHWC input, first channel of the layer: pixel i at x + i*x_cs
   const void *wfrag;     // weights in MFMA fragment order [co_blocks][steps][64 lanes][16 bytes]
@@ -72,6 +83,9 @@ struct ConvParams {
   unsigned x_bytes;      // bytes of the input buffer from x (buffer-load range)
   unsigned w_bytes;      // bytes of the fragment-ordered weights (buffer-load range)
   int tiles_x, tiles_y;  // conv_halo: output tiles along a row and along the rows of one image
+  FastDiv div_ow, div_oh;    // by OW and OH: pixel index -> (n, oh, ow)
+  FastDiv div_cot, div_sk;   // by co_tiles and splitk: workgroup -> tile
+  FastDiv div_tx, div_ty;    // by tiles_x and tiles_y (conv_halo)
   int halo_bytes;        // conv_halo: LDS bytes of the input halo tile (weights follow)
   int smem_bytes;        // conv_halo: dynamic LDS bytes per workgroup
 };

@@ -146,7 +146,23 @@ __device__ __forceinline__ void pin_all_args(ConvParams &p, int &nblocks) {
   pin_sgpr(p.M);
   pin_sgpr(p.tiles_x);
   pin_sgpr(p.tiles_y);
+  pin_sgpr(p.div_ow.magic);
+  pin_sgpr(p.div_ow.shift);
+  pin_sgpr(p.div_oh.magic);
+  pin_sgpr(p.div_oh.shift);
+  pin_sgpr(p.div_cot.magic);
+  pin_sgpr(p.div_cot.shift);
+  pin_sgpr(p.div_sk.magic);
+  pin_sgpr(p.div_sk.shift);
+  pin_sgpr(p.div_tx.magic);
+  pin_sgpr(p.div_tx.shift);
+  pin_sgpr(p.div_ty.magic);
+  pin_sgpr(p.div_ty.shift);
   pin_sgpr(p.halo_bytes);
+}
+
+__device__ __forceinline__ int fdiv(int n, FastDiv f) {
+  return (int)((__umulhi((unsigned)n, f.magic) + (unsigned)n) >> f.shift);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, unsigned bytes) {
@@ -252,10 +268,10 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   const int nb = nblocks, bid = blockIdx.x;
   const int per = nb >> 3, rem = nb & 7, xcd = bid & 7, loc = bid >> 3;
   const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
-  const int split = logical % p.splitk;
-  const int tile = logical / p.splitk;
-  const int co_tile = tile % p.co_tiles;
-  const int px_tile = tile / p.co_tiles;
+  const int tile = fdiv(logical, p.div_sk);
+  const int split = logical - tile * p.splitk;
+  const int px_tile = fdiv(tile, p.div_cot);
+  const int co_tile = tile - px_tile * p.co_tiles;
 
   // The 16-pixel blocks of this wave: lane r owns pixel r of each block.
   int pixbase[PB], iy0[PB], ix0[PB], outpix[PB];
@@ -265,10 +281,10 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     const int m = ((px_tile * WPX + wpx) * PB + b) * 16 + r;
     mval[b] = m < p.M;
     const int mm = mval[b] ? m : 0;
-    const int ow = mm % p.OW;
-    const int t = mm / p.OW;
-    const int oh = t % p.OH;
-    const int n = t / p.OH;
+    const int t = fdiv(mm, p.div_ow);
+    const int ow = mm - t * p.OW;
+    const int n = fdiv(t, p.div_oh);
+    const int oh = t - n * p.OH;
     iy0[b] = oh * p.stride - p.pad;
     ix0[b] = ow * p.stride - p.pad;
     pixbase[b] = (n * p.H + iy0[b]) * p.W + ix0[b];
@@ -502,10 +518,10 @@ __device__ __forceinline__ Pix pixel_of(const ConvParams &p, int m) {
   Pix q;
   q.ok = m < p.M;
   const int mm = q.ok ? m : 0;
-  const int ow = mm % p.OW;
-  const int t = mm / p.OW;
-  const int oh = t % p.OH;
-  const int n = t / p.OH;
+  const int t = fdiv(mm, p.div_ow);
+  const int ow = mm - t * p.OW;
+  const int n = fdiv(t, p.div_oh);
+  const int oh = t - n * p.OH;
   q.iy0 = oh * p.stride - p.pad;
   q.ix0 = ow * p.stride - p.pad;
   q.base = (n * p.H + q.iy0) * p.W + q.ix0;
@@ -562,8 +578,8 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   const int nb_ = nblocks, bid = blockIdx.x;
   const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
   const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
-  const int co_tile = logical % p.co_tiles;
-  const int px_tile = logical / p.co_tiles;
+  const int px_tile = fdiv(logical, p.div_cot);
+  const int co_tile = logical - px_tile * p.co_tiles;
 
   // pixels of this thread's activation slots (the same for every stage)
   Pix xpix[NX];
@@ -732,10 +748,10 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   const int nb_ = nblocks, bid = blockIdx.x;
   const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
   const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
-  const int tx = logical % p.tiles_x;
-  const int rest = logical / p.tiles_x;
-  const int ty = rest % p.tiles_y;
-  const int n = rest / p.tiles_y;
+  const int rest = fdiv(logical, p.div_tx);
+  const int tx = logical - rest * p.tiles_x;
+  const int n = fdiv(rest, p.div_ty);
+  const int ty = rest - n * p.tiles_y;
 
   const int st_ = p.stride;
   const int HWd = (TW - 1) * st_ + 3;  // halo width in pixels
