@@ -77,7 +77,12 @@ template <> struct Var<VAR_I8_C4_X> : Var<VAR_I8_C4> { static constexpr bool X =
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr unsigned kOutOfRange = 0x80000000u;
 
-__device__ __forceinline__ float silu_f(float z) { return __fdividef(z, 1.0f + __expf(-z)); }
+// SiLU(z) = z / (1 + e^-z), with the hardware exponential and reciprocal
+// (each within about one ulp): a correctly rounded division costs ten
+// instructions per value, which made the epilogue of the small layers the
+// largest VALU cost of the kernel.  For z < -88, e^-z is +inf, the reciprocal
+// 0 and y = -0 (the true value is below 1e-36 in magnitude).
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Kernel arguments arrive through scalar loads from the argument block.  Left
 // to itself the compiler re-reads the ones that only the epilogue uses after
