@@ -171,11 +171,20 @@ void tiles_of(const cbs_layer *L, int cfg, int *px_tiles, int *co_tiles) {
 
 // LDS bytes of a halo-tile workgroup: the input window (4-channel slots,
 // rounded up to whole waves of slots) followed by all fragment-ordered weights.
+// 4-channel slots per halo pixel in LDS: fp32 pixels of an even number of
+// 16-byte slots get one zero slot more, so that the 16 pixels a fragment read
+// touches (consecutive, or every other one for stride 2) fall on distinct LDS
+// banks.
+int halo_cq(const cbs_layer *L) {
+  const int cq = L->cin_pad / 4;
+  return (L->d.dtype == CBS_F32 && cq % 2 == 0) ? cq + 1 : cq;
+}
+
 void halo_lds(const cbs_layer *L, int cfg, int *halo_bytes, int *smem_bytes) {
   const KernelConfig &c = config(cfg);
   const int s = L->d.stride;
   const int hh = (c.th - 1) * s + 3, hw = (c.tw - 1) * s + 3;
-  const int slots = hh * hw * (L->cin_pad / 4);
+  const int slots = hh * hw * halo_cq(L);
   const int slot_bytes = L->d.dtype == CBS_F32 ? 16 : 4;
   *halo_bytes = round_up(slots, 64) * slot_bytes;
   *smem_bytes = *halo_bytes + L->co_blocks * L->steps * 1024;
@@ -372,6 +381,9 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
   if (kc.lds == 2) {
     p.tiles_x = ceil_div(L->ow, kc.tw);
     p.tiles_y = ceil_div(L->oh, kc.th);
+    p.halo_cq = halo_cq(L);
+    p.div_hcq = make_fastdiv(p.halo_cq);
+    p.div_hwd = make_fastdiv((kc.tw - 1) * L->d.stride + 3);
     halo_lds(L, L->config, &p.halo_bytes, &p.smem_bytes);
   }
   tiles_of(L, L->config, &p.px_tiles, &p.co_tiles);

@@ -48,7 +48,11 @@ struct FastDiv {
   int shift;
 };
 
+// Fields are grouped by the kernels that read them (all kernels, then the
+// pixel-tiled ones, split-K, the halo kernel, host-only), so the kernels'
+// wide scalar loads of the argument block fetch few unused words.
 struct ConvParams {
+  // ---- every kernel
   const void *x;         // NHWC input, first channel of the layer: pixel i at x + i*x_cs
   const void *wfrag;     // weights in MFMA fragment order [co_blocks][steps][64 lanes][16 bytes]
   const float *bias;     // folded bias [co_blocks*16] (zero beyond C_out)
@@ -56,37 +60,47 @@ struct ConvParams {
   void *out;             // NHWC output, first channel of the layer: pixel (n,oh,ow) at
                          // out + ((n*OH + oh)*pitch + ow)*out_cs  (fp32, int8, or int32 for raw)
   const void *res;       // residual, first channel: logical pixel m at res + m*res_cs (null if none)
-  float *ws;             // split-K partial tiles (null when splitk == 1)
-  unsigned *counters;    // split-K arrival counters, one per output tile (zero between launches)
-  int N, H, W, cin_pad;
+  int H, W;
   int x_cs;              // input elements between consecutive pixels (cin_pad when dense)
-  int OH, OW, cout_pad, pitch;
-  int out_cs;            // output elements between consecutive pixels (cout_pad when dense)
-  int res_cs;            // residual elements between consecutive pixels (0: no residual)
-  int act;               // Act
-  int out_i8;            // 1: int8 output codes q = clamp(rne(fp32(y / out_scale)), +-127)
-  float out_scale;       // s_y for int8 output
-  float out_rcp;         // RN(1/s_y), the correctly rounded fp32 reciprocal
-  float res_scale;       // scale of int8 residual codes
-  unsigned res_bytes;    // bytes of the residual buffer from res (buffer-load range)
   int k, stride, pad;
-  int M;                 // N*OH*OW output pixels
   int chunk_ch;          // channels per chunk (4 or 16)
   int chunks_per_tap;    // cin_pad / chunk_ch
   unsigned cpt_magic;    // chunk / chunks_per_tap == (chunk * cpt_magic) >> 20 for the chunks in use
   int total_chunks;      // k*k*chunks_per_tap
   int steps;             // K steps (each 16 fp32 or 64 int8 channels of K)
-  int steps_per_split;   // K steps per split-K workgroup
-  int splitk;            // workgroups per output tile along K
   int co_blocks;         // 16-channel output blocks holding real channels
-  int px_tiles, co_tiles;// workgroup tiles along pixels and output channels
   unsigned x_bytes;      // bytes of the input buffer from x (buffer-load range)
   unsigned w_bytes;      // bytes of the fragment-ordered weights (buffer-load range)
-  int tiles_x, tiles_y;  // conv_halo: output tiles along a row and along the rows of one image
+  int OH, OW, cout_pad, pitch;
+  int out_cs;            // output elements between consecutive pixels (cout_pad when dense)
+  int res_cs;            // residual elements between consecutive pixels (0: no residual)
+  unsigned res_bytes;    // bytes of the residual buffer from res (buffer-load range)
+  int act;               // Act
+  int out_i8;            // 1: int8 output codes q = clamp(rne(fp32(y / out_scale)), +-127)
+  float out_scale;       // s_y for int8 output
+  float out_rcp;         // RN(1/s_y), the correctly rounded fp32 reciprocal
+  float res_scale;       // scale of int8 residual codes
+  // ---- pixel-tiled kernels (conv_igemm, conv_lds)
+  int M;                 // N*OH*OW output pixels
+  int co_tiles;          // workgroup tiles along output channels
   FastDiv div_ow, div_oh;    // by OW and OH: pixel index -> (n, oh, ow)
-  FastDiv div_cot, div_sk;   // by co_tiles and splitk: workgroup -> tile
-  FastDiv div_tx, div_ty;    // by tiles_x and tiles_y (conv_halo)
-  int halo_bytes;        // conv_halo: LDS bytes of the input halo tile (weights follow)
+  FastDiv div_cot;           // by co_tiles: workgroup -> (pixel tile, channel tile)
+  // ---- cross-workgroup split-K (conv_igemm)
+  float *ws;             // split-K partial tiles (null when splitk == 1)
+  unsigned *counters;    // split-K arrival counters, one per output tile (zero between launches)
+  int splitk;            // workgroups per output tile along K
+  int steps_per_split;   // K steps per split-K workgroup
+  FastDiv div_sk;            // by splitk
+  // ---- conv_halo
+  int cin_pad;
+  int tiles_x, tiles_y;  // output tiles along a row and along the rows of one image
+  int halo_bytes;        // LDS bytes of the input halo tile (weights follow)
+  int halo_cq;           // 4-channel slots per pixel in LDS (padded, see halo_lds)
+  FastDiv div_tx, div_ty;    // by tiles_x and tiles_y
+  FastDiv div_hcq, div_hwd;  // by halo_cq and by the halo width in pixels
+  // ---- host only
+  int N;
+  int px_tiles;          // workgroup tiles along pixels
   int smem_bytes;        // conv_halo: dynamic LDS bytes per workgroup
 };
 

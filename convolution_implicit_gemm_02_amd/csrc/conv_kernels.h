@@ -109,12 +109,14 @@ __device__ __forceinline__ CBS_GLOBAL T *gmem(const void *ptr) {
 // all argument loads at once and waits for them once, instead of spreading
 // them over two or three dependent rounds (it sinks loads towards their first
 // use), each costing a memory round trip before the first operand load.
-__device__ __forceinline__ void pin_all_args(ConvParams &p, int &nblocks) {
+__device__ __forceinline__ void pin_common_args(ConvParams &p, int &nblocks) {
   pin_sgpr(nblocks);  // the grid size comes from the dispatch's own argument area
   pin_sgpr(p.x);
   pin_sgpr(p.wfrag);
   pin_sgpr(p.bias);
   pin_sgpr(p.dq);
+  pin_sgpr(p.out);
+  pin_sgpr(p.res);
   pin_sgpr(p.H);
   pin_sgpr(p.W);
   pin_sgpr(p.x_cs);
@@ -126,15 +128,9 @@ __device__ __forceinline__ void pin_all_args(ConvParams &p, int &nblocks) {
   pin_sgpr(p.cpt_magic);
   pin_sgpr(p.total_chunks);
   pin_sgpr(p.steps);
-  pin_sgpr(p.steps_per_split);
   pin_sgpr(p.co_blocks);
-  pin_sgpr(p.co_tiles);
   pin_sgpr(p.x_bytes);
   pin_sgpr(p.w_bytes);
-  pin_sgpr(p.out);
-  pin_sgpr(p.res);
-  pin_sgpr(p.ws);
-  pin_sgpr(p.counters);
   pin_sgpr(p.cout_pad);
   pin_sgpr(p.out_cs);
   pin_sgpr(p.res_cs);
@@ -144,26 +140,49 @@ __device__ __forceinline__ void pin_all_args(ConvParams &p, int &nblocks) {
   pin_sgpr(p.out_scale);
   pin_sgpr(p.out_rcp);
   pin_sgpr(p.res_scale);
-  pin_sgpr(p.splitk);
   pin_sgpr(p.OH);
   pin_sgpr(p.OW);
   pin_sgpr(p.pitch);
+}
+
+// The pixel-tiled kernels (conv_igemm, conv_lds) also decompose pixel and
+// workgroup indices; conv_igemm alone reduces split-K partial tiles.
+__device__ __forceinline__ void pin_tiled_args(ConvParams &p, int &nblocks, bool splitk_args) {
+  pin_common_args(p, nblocks);
   pin_sgpr(p.M);
-  pin_sgpr(p.tiles_x);
-  pin_sgpr(p.tiles_y);
+  pin_sgpr(p.co_tiles);
   pin_sgpr(p.div_ow.magic);
   pin_sgpr(p.div_ow.shift);
   pin_sgpr(p.div_oh.magic);
   pin_sgpr(p.div_oh.shift);
   pin_sgpr(p.div_cot.magic);
   pin_sgpr(p.div_cot.shift);
-  pin_sgpr(p.div_sk.magic);
-  pin_sgpr(p.div_sk.shift);
+  if (splitk_args) {
+    pin_sgpr(p.ws);
+    pin_sgpr(p.counters);
+    pin_sgpr(p.splitk);
+    pin_sgpr(p.steps_per_split);
+    pin_sgpr(p.div_sk.magic);
+    pin_sgpr(p.div_sk.shift);
+  }
+}
+
+// conv_halo: the tile grid and the LDS halo layout.
+__device__ __forceinline__ void pin_halo_args(ConvParams &p, int &nblocks) {
+  pin_sgpr(p.cin_pad);
+  pin_sgpr(p.tiles_x);
+  pin_sgpr(p.tiles_y);
+  pin_sgpr(p.halo_bytes);
   pin_sgpr(p.div_tx.magic);
   pin_sgpr(p.div_tx.shift);
   pin_sgpr(p.div_ty.magic);
   pin_sgpr(p.div_ty.shift);
-  pin_sgpr(p.halo_bytes);
+  pin_sgpr(p.halo_cq);
+  pin_sgpr(p.div_hcq.magic);
+  pin_sgpr(p.div_hcq.shift);
+  pin_sgpr(p.div_hwd.magic);
+  pin_sgpr(p.div_hwd.shift);
+  pin_common_args(p, nblocks);
 }
 
 __device__ __forceinline__ int fdiv(int n, FastDiv f) {
@@ -255,7 +274,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   using Frag = typename V::Frag;
   using Acc = typename V::Acc;
   int nblocks = gridDim.x;
-  pin_all_args(p, nblocks);
+  pin_tiled_args(p, nblocks, true);
   const int lane = threadIdx.x & 63;
   // The wave index is made explicitly wave-uniform: every condition that
   // guards an MFMA below depends only on it, so it compiles to a scalar
@@ -568,7 +587,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int BMB = MB * WM, BNB = NB * WN;     // 16-pixel and 16-channel blocks per workgroup
   int nblocks = gridDim.x;
-  pin_all_args(p, nblocks);
+  pin_tiled_args(p, nblocks, false);
   constexpr int SB = BMB + BNB;                   // fragment blocks per K step
   constexpr int NA = KS * BNB * 64 / NT;          // weight slots per thread per stage
   constexpr int NX = KS * BMB * 64 / NT;          // activation slots per thread per stage
@@ -743,7 +762,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   static_assert(TH * TW % 64 == 0, "tile must split into 4 waves of 16-pixel blocks");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int nblocks = gridDim.x;
-  pin_all_args(p, nblocks);
+  pin_halo_args(p, nblocks);
   typedef __attribute__((address_space(3))) void *lds_ptr;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -764,19 +783,21 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   const int oh0 = ty * TH, ow0 = tx * TW;
   const int iy0 = oh0 * st_ - p.pad, ix0 = ow0 * st_ - p.pad;
   const int cq = p.cin_pad >> 2;                 // 4-channel slots per pixel
+  const int cql = p.halo_cq;                     // slots per pixel in LDS (cq, or cq + 1: see below)
   constexpr int SLOT = 4 * V::ESIZE;             // bytes of a 4-channel slot
-  const int halo_slots = HH * HWd * cq;
+  const int halo_slots = HH * HWd * cql;
 
   // 1) input halo and weights -> LDS (all loads in flight, no register round trip)
   {
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
     for (int base = wave * 64; base < halo_slots; base += 256) {
       const int sl = base + lane;
-      const int q = sl % cq;
-      const int px = sl / cq;
-      const int hx = px % HWd, hy = px / HWd;
+      const int px = fdiv(sl, p.div_hcq);
+      const int q = sl - px * cql;  // q == cq: the padding slot, loaded as zeros
+      const int hy = fdiv(px, p.div_hwd);
+      const int hx = px - hy * HWd;
       const int iy = iy0 + hy, ix = ix0 + hx;
-      const bool v = sl < halo_slots && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+      const bool v = sl < halo_slots && q < cq && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
       const unsigned off = v ? (unsigned)(((n * p.H + iy) * p.W + ix) * p.x_cs + 4 * q) * (unsigned)V::ESIZE
                              : kOutOfRange;
       if constexpr (SLOT == 16)
@@ -819,7 +840,10 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
     lbase[mb] = (ly * st_) * HWd + lx * st_;
   }
   const unsigned char *wl = smem + p.halo_bytes;
-  const int pix_bytes = p.cin_pad * V::ESIZE;
+  // An fp32 pixel of an even number of 16-byte slots would put the 16
+  // pixels of a fragment read on repeating LDS banks; the host pads it to an
+  // odd number of slots (a zero slot), which makes those reads conflict-free.
+  const int pix_bytes = cql * SLOT;
   Acc acc[NBMAX][MB];
 #pragma unroll
   for (int nb = 0; nb < NBMAX; nb++)
