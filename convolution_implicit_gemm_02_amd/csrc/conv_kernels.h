@@ -427,25 +427,31 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     }
   }
 
-  // Reduce the WK K-slices of the workgroup through LDS, in slice order.
+  // The WK waves of a workgroup hold partial sums of the same output blocks.
+  // After the exchange below, block (cb, b) is finished -- reduced, split-K
+  // combined and stored -- by wave (cb * PB + b) % WK, so the reduction and the
+  // epilogue are spread over all WK waves instead of serialised on one.
+  auto mine = [&](int cb, int b) { return WK == 1 || (cb * PB + b) % WK == wk; };
+
+  // Reduce the WK K-slices through LDS, in slice order (the same order for
+  // every block, so the result does not depend on which wave sums it).
   if constexpr (WK > 1) {
-    __shared__ Acc red[(WK - 1) * WCO * WPX * CB * PB][64];
-    if (wk > 0) {
+    __shared__ Acc red[WK * WCO * WPX * CB * PB][64];
 #pragma unroll
-      for (int cb = 0; cb < CB; cb++)
+    for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-        for (int b = 0; b < PB; b++)
-          red[(((wk - 1) * WCO * WPX + slot) * CB + cb) * PB + b][lane] = acc[cb][b];
-    }
+      for (int b = 0; b < PB; b++)
+        red[((wk * WCO * WPX + slot) * CB + cb) * PB + b][lane] = acc[cb][b];
     __syncthreads();
-    if (wk == 0) {
-      for (int w = 1; w < WK; w++)
 #pragma unroll
-        for (int cb = 0; cb < CB; cb++)
+    for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-          for (int b = 0; b < PB; b++)
-            acc[cb][b] += red[(((w - 1) * WCO * WPX + slot) * CB + cb) * PB + b][lane];
-    }
+      for (int b = 0; b < PB; b++) {
+        if (!mine(cb, b)) continue;
+        Acc sum = red[(slot * CB + cb) * PB + b][lane];
+        for (int w = 1; w < WK; w++) sum += red[((w * WCO * WPX + slot) * CB + cb) * PB + b][lane];
+        acc[cb][b] = sum;
+      }
   }
 
   // Cross-workgroup split-K: publish the partial tile, take a ticket; the
@@ -454,13 +460,11 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     __shared__ int s_last;
     constexpr int TILE_VECS = WCO * WPX * CB * PB * 64;
     CBS_GLOBAL Acc *wsb = gmem<Acc>(p.ws) + (size_t)tile * p.splitk * TILE_VECS;
-    if (wk == 0) {
 #pragma unroll
-      for (int cb = 0; cb < CB; cb++)
+    for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-        for (int b = 0; b < PB; b++)
-          wsb[(size_t)split * TILE_VECS + ((slot * CB + cb) * PB + b) * 64 + lane] = acc[cb][b];
-    }
+      for (int b = 0; b < PB; b++)
+        if (mine(cb, b)) wsb[(size_t)split * TILE_VECS + ((slot * CB + cb) * PB + b) * 64 + lane] = acc[cb][b];
     __threadfence();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -471,27 +475,24 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     __syncthreads();
     if (!s_last) return;
     __threadfence();
-    if (wk == 0) {
 #pragma unroll
-      for (int cb = 0; cb < CB; cb++)
+    for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-        for (int b = 0; b < PB; b++) {
-          Acc sum = Acc{};
-          for (int sp = 0; sp < p.splitk; sp++) {
-            const Acc v = (sp == split)
-                              ? acc[cb][b]
-                              : __builtin_nontemporal_load(
-                                    &wsb[(size_t)sp * TILE_VECS + ((slot * CB + cb) * PB + b) * 64 + lane]);
-            sum += v;
-          }
-          acc[cb][b] = sum;
+      for (int b = 0; b < PB; b++) {
+        if (!mine(cb, b)) continue;
+        Acc sum = Acc{};
+        for (int sp = 0; sp < p.splitk; sp++) {
+          const Acc v = (sp == split)
+                            ? acc[cb][b]
+                            : __builtin_nontemporal_load(
+                                  &wsb[(size_t)sp * TILE_VECS + ((slot * CB + cb) * PB + b) * 64 + lane]);
+          sum += v;
         }
-    }
+        acc[cb][b] = sum;
+      }
     if (threadIdx.x == 0)
       __hip_atomic_store(gmem<unsigned>(p.counters) + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-
-  if (wk != 0) return;
 
   // Epilogue: bias (+ dequant), activation, residual, output conversion in
   // registers; masked NHWC stores of 4 channels per lane.
@@ -503,13 +504,13 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     if constexpr (V::RAW) {
 #pragma unroll
       for (int b = 0; b < PB; b++)
-        if (mval[b]) *(gmem<i32x4>(p.out) + ((size_t)outpix[b] * p.out_cs + co0) / 4) = acc[cb][b];
+        if (mine(cb, b) && mval[b]) *(gmem<i32x4>(p.out) + ((size_t)outpix[b] * p.out_cs + co0) / 4) = acc[cb][b];
     } else {
       const f32x4 bias = ep_bias[cb];
       const f32x4 dq = ep_dq[cb];
 #pragma unroll
       for (int b = 0; b < PB; b++) {
-        if (!mval[b]) continue;
+        if (!mine(cb, b) || !mval[b]) continue;
         f32x4 z;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
