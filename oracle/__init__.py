@@ -109,6 +109,13 @@ def _load():
             lib.oracle_conv_bn_act_i8_points.argtypes = [P, F, P, P, P, P, P, D, I, I, I, I, I, I, I, I, I,
                                                          P, P, L, P, P, P]
             lib.oracle_conv_bn_act_i8_points.restype = L
+            lib.oracle_quantize_activations_u8.argtypes = [P, L, F, I, P]
+            lib.oracle_quantize_activations_u8.restype = None
+            lib.oracle_conv_u8_acc.argtypes = [P, I, P, I, I, I, I, I, I, I, I, P, P]
+            lib.oracle_conv_u8_acc.restype = L
+            lib.oracle_conv_bn_act_u8.argtypes = [P, F, I, P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, P,
+                                                  P, P, P, P, P, P]
+            lib.oracle_conv_bn_act_u8.restype = L
             _lib = lib
     return _lib
 
@@ -251,6 +258,35 @@ def requantize(y, s_y: float) -> np.ndarray:
     return quantize_activations(y32, s_y)
 
 
+def quantize_activations_u8(x, s_x: float, z: int) -> np.ndarray:
+    """Asymmetric uint8: q = clamp(rne(fp32(x / s_x)) + z, 0, 255)."""
+    x = _f32(x)
+    q = np.empty(x.shape, np.uint8)
+    _load().oracle_quantize_activations_u8(_p(x), x.size, float(np.float32(s_x)), int(z), _p(q))
+    return q
+
+
+def requantize_u8(y, s_y: float, z: int) -> np.ndarray:
+    """Asymmetric uint8 output codes: the u8 quantiser applied to the fp32 value of y."""
+    return quantize_activations_u8(np.asarray(y, dtype=np.float64).astype(np.float32), s_y, z)
+
+
+def conv_u8_acc(qx, z: int, qw, stride: int, pad: int, with_abs: bool = False):
+    """sum q_w (q - z) over the taps inside the image (int32); with_abs also returns sum |.| (int64)."""
+    qx = np.ascontiguousarray(qx, dtype=np.uint8)
+    qw = np.ascontiguousarray(qw, dtype=np.int8)
+    n, c_in, h, wd = qx.shape
+    c_out, _, k, _ = qw.shape
+    oh, ow = out_dim(h, k, stride, pad), out_dim(wd, k, stride, pad)
+    acc = np.empty((n, c_out, oh, ow), np.int32)
+    absacc = np.empty((n, c_out, oh, ow), np.int64) if with_abs else None
+    ovf = _load().oracle_conv_u8_acc(_p(qx), int(z), _p(qw), n, c_in, h, wd, c_out, k, stride, pad, _p(acc),
+                                     _p(absacc))
+    if ovf:
+        raise OverflowError("%d accumulators outside int32" % ovf)
+    return (acc, absacc) if with_abs else acc
+
+
 def conv_i8_acc(qx, qw, stride: int, pad: int) -> np.ndarray:
     """Exact integer convolution (int32 result; raises if any sum leaves int32)."""
     qx = np.ascontiguousarray(qx, dtype=np.int8)
@@ -355,6 +391,31 @@ def conv_bn_act_i8(x, s_x: float, w, gamma, beta, mean, var, eps: float, stride:
                                         _p(qw), _p(sw), _p(f), _p(absacc))
     if ovf != 0:
         raise OverflowError("int8 oracle: %d accumulators outside int32 (or allocation failure)" % ovf)
+    return {"y": y, "acc": acc, "qw": qw, "s_w": sw, "f": f, "absacc": absacc}
+
+
+def conv_bn_act_u8(x, s_x: float, z_x: int, w, gamma, beta, mean, var, eps: float, stride: int, pad: int,
+                   act: str = "silu", residual=None, with_bound: bool = True) -> dict:
+    """The block with asymmetric uint8 activations (zero point z_x).  Same dict as
+    conv_bn_act_i8 (absacc = sum |q_w (q - z_x)|)."""
+    x = _f32(x)
+    w = _f32(w)
+    n, c_in, h, wd = x.shape
+    c_out, _, k, _ = w.shape
+    oh, ow = out_dim(h, k, stride, pad), out_dim(wd, k, stride, pad)
+    y = np.empty((n, c_out, oh, ow), np.float64)
+    r = _res(residual, y.shape)
+    acc = np.empty((n, c_out, oh, ow), np.int32)
+    qw = np.empty(w.shape, np.int8)
+    sw = np.empty((c_out,), np.float64)
+    f = np.empty((c_out,), np.float32)
+    absacc = np.empty((n, c_out, oh, ow), np.int64) if with_bound else None
+    ovf = _load().oracle_conv_bn_act_u8(_p(x), float(np.float32(s_x)), int(z_x), _p(w), _p(_f32(gamma)),
+                                        _p(_f32(beta)), _p(_f32(mean)), _p(_f32(var)), float(eps), n, c_in, h, wd,
+                                        c_out, k, stride, pad, _act(act), _p(r), _p(y), _p(acc), _p(qw), _p(sw),
+                                        _p(f), _p(absacc))
+    if ovf != 0:
+        raise OverflowError("u8 oracle: %d accumulators outside int32 (or allocation failure)" % ovf)
     return {"y": y, "acc": acc, "qw": qw, "s_w": sw, "f": f, "absacc": absacc}
 
 

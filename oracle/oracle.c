@@ -42,6 +42,13 @@
  *    breakdown"): the activation is SiLU or the identity, and a residual r is
  *    added after the activation, y = act(z) + r (the shortcut of a YOLO
  *    bottleneck adds its input to the output of its second conv block).
+ *  - Asymmetric activations (edge-optimization README, "Design notes": ONNX
+ *    Runtime's default is asymmetric uint8 activations with symmetric
+ *    weights, because activations after SiLU are mostly positive):
+ *    q = clamp(rne(fp32(x / s_x)) + z_x, 0, 255) with an integer zero point
+ *    z_x in [0, 255], so x ~ s_x (q - z_x).  The convolution sums
+ *    q_w (q - z_x) over the taps inside the image: zero padding is a real
+ *    zero, i.e. the code z_x, and contributes nothing.
  *  - INT8 output (edge-optimization README, "Highlights": the network runs in
  *    INT8 end to end): the output codes are the activation quantiser applied
  *    to the fp32 value of y, q_y = clamp(rne(fp32(fp32(y) / s_y)), -127, 127);
@@ -285,6 +292,63 @@ void oracle_quantize_activations(const float *x, long count, float s_x, int8_t *
 }
 
 /*
+ * Per-tensor asymmetric uint8 activation quantisation:
+ *   q = clamp(rne(fp32(x / s_x)) + z, 0, 255), the division in fp32.
+ */
+void oracle_quantize_activations_u8(const float *x, long count, float s_x, int z, uint8_t *q) {
+    for (long i = 0; i < count; i++) {
+        volatile float r = x[i] / s_x; /* one correctly rounded fp32 division */
+        double v = nearbyint((double)r) + (double)z;
+        if (v < 0.0) v = 0.0;
+        if (v > 255.0) v = 255.0;
+        q[i] = (uint8_t)v;
+    }
+}
+
+/* One output of the asymmetric integer convolution: sum over the taps inside
+ * the image of q_w * (q - z); *absacc (if not NULL) gets sum |q_w (q - z)|. */
+static int64_t conv_u8_at(const uint8_t *qx, int z, const int8_t *qw, const dims_t *d, int b, int co, int oh,
+                          int ow, int64_t *absacc) {
+    int64_t acc = 0, aacc = 0;
+    for (int ci = 0; ci < d->c_in; ci++)
+        for (int i = 0; i < d->k; i++)
+            for (int j = 0; j < d->k; j++) {
+                int iy = oh * d->s - d->p + i, ix = ow * d->s - d->p + j;
+                if (iy < 0 || iy >= d->h || ix < 0 || ix >= d->w) continue;
+                int64_t t = (int64_t)qw[(((size_t)co * d->c_in + ci) * d->k + i) * d->k + j] *
+                            ((int64_t)qx[(((size_t)b * d->c_in + ci) * d->h + iy) * d->w + ix] - (int64_t)z);
+                acc += t;
+                aacc += t < 0 ? -t : t;
+            }
+    if (absacc) *absacc = aacc;
+    return acc;
+}
+
+/*
+ * Asymmetric integer convolution: acc = sum q_w (q - z) over the taps inside
+ * the image (padding is the real value 0), exact in int64, stored as int32.
+ * Returns the number of sums outside the int32 range (0 expected).
+ */
+long oracle_conv_u8_acc(const uint8_t *qx, int z, const int8_t *qw, int n, int c_in, int h, int w, int c_out,
+                        int k, int s, int p, int32_t *acc_out, int64_t *absacc_out) {
+    dims_t d = make_dims(n, c_in, h, w, c_out, k, s, p);
+    long overflow = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(+ : overflow)
+    for (int b = 0; b < n; b++)
+        for (int co = 0; co < c_out; co++)
+            for (int oh = 0; oh < d.oh; oh++)
+                for (int ow = 0; ow < d.ow; ow++) {
+                    int64_t a;
+                    int64_t acc = conv_u8_at(qx, z, qw, &d, b, co, oh, ow, &a);
+                    if (acc > INT32_MAX || acc < INT32_MIN) overflow++;
+                    size_t o = (((size_t)b * c_out + co) * d.oh + oh) * d.ow + ow;
+                    acc_out[o] = (int32_t)acc;
+                    if (absacc_out) absacc_out[o] = a;
+                }
+    return overflow;
+}
+
+/*
  * Integer convolution with zero padding, accumulated exactly (int64) and
  * stored as int32: acc[n,co,oh,ow] = sum_{ci,i,j} q_w[co,ci,i,j] * q_x~[...].
  * Returns the number of accumulators outside the int32 range (0 expected:
@@ -476,4 +540,40 @@ long oracle_conv_bn_silu_i8_points(const float *x, float s_x, const float *wt, c
                                    int32_t *acc_out, int64_t *absacc_out) {
     return oracle_conv_bn_act_i8_points(x, s_x, wt, gamma, beta, mean, var, eps, n, c_in, h, w, c_out, k, s, p,
                                         0, NULL, pts, npts, y, acc_out, absacc_out);
+}
+
+/*
+ * The whole block with asymmetric uint8 activations: fold BN, quantise the
+ * weights per channel (symmetric), quantise the activations with (s_x, z_x),
+ * asymmetric integer convolution, then the same epilogue as the symmetric
+ * block: y = act(acc * f[co] + b'[co]) (+ residual), f = fp32(s_x * s_w[co]).
+ * Any output pointer may be NULL except y.  Returns the int32 overflow count.
+ */
+long oracle_conv_bn_act_u8(const float *x, float s_x, int z_x, const float *wt, const float *gamma,
+                           const float *beta, const float *mean, const float *var, double eps, int n,
+                           int c_in, int h, int w, int c_out, int k, int s, int p, int act,
+                           const double *residual, double *y, int32_t *acc_out, int8_t *qw_out,
+                           double *sw_out, float *f_out, int64_t *absacc_out) {
+    int per_co = c_in * k * k;
+    int oh_n = oracle_out_dim(h, k, s, p), ow_n = oracle_out_dim(w, k, s, p);
+    size_t nx = (size_t)n * c_in * h * w, ny = (size_t)n * c_out * oh_n * ow_n;
+    double *wf = (double *)malloc(sizeof(double) * (size_t)c_out * per_co);
+    double *bf = (double *)malloc(sizeof(double) * (size_t)c_out);
+    double *sw = (double *)malloc(sizeof(double) * (size_t)c_out);
+    int8_t *qw = (int8_t *)malloc((size_t)c_out * per_co);
+    uint8_t *qx = (uint8_t *)malloc(nx ? nx : 1);
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (ny ? ny : 1));
+    long ovf = -1;
+    if (!wf || !bf || !sw || !qw || !qx || !acc) goto done;
+    oracle_bn_fold(wt, c_out, per_co, gamma, beta, mean, var, eps, wf, bf);
+    oracle_quantize_weights(wf, c_out, per_co, qw, sw);
+    oracle_quantize_activations_u8(x, (long)nx, s_x, z_x, qx);
+    ovf = oracle_conv_u8_acc(qx, z_x, qw, n, c_in, h, w, c_out, k, s, p, acc, absacc_out);
+    oracle_epilogue_i8_act(acc, n, c_out, oh_n * ow_n, s_x, sw, bf, act, residual, y, f_out);
+    if (acc_out) memcpy(acc_out, acc, sizeof(int32_t) * ny);
+    if (qw_out) memcpy(qw_out, qw, (size_t)c_out * per_co);
+    if (sw_out) memcpy(sw_out, sw, sizeof(double) * (size_t)c_out);
+done:
+    free(wf); free(bf); free(sw); free(qw); free(qx); free(acc);
+    return ovf;
 }
