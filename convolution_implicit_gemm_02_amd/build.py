@@ -117,7 +117,7 @@ def flat_memory_ops(text: str, pattern: str):
     return bad
 
 
-VARIANTS = 8  # kernel variants, one translation unit each (cbs_variant.hip with -DCBS_VAR=n)
+VARIANTS = 12  # kernel variants, one translation unit each (cbs_variant.hip with -DCBS_VAR=n)
 CONV_KERNELS = r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+):"
 
 

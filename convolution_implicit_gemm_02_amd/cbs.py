@@ -30,6 +30,7 @@ CBS_EDEVICE = -4
 CBS_ELAUNCH = -5
 CBS_F32 = 0
 CBS_I8 = 1
+CBS_U8 = 2
 CBS_ACT_SILU = 0
 CBS_ACT_NONE = 1
 CBS_TUNE_FORCE = 1
@@ -52,7 +53,9 @@ class cbs_conv_desc(ctypes.Structure):
                 ("bn_eps", ctypes.c_float), ("act", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("out_scale", ctypes.c_float), ("in_c_stride", ctypes.c_int32), ("in_c_offset", ctypes.c_int32),
                 ("out_c_stride", ctypes.c_int32), ("out_c_offset", ctypes.c_int32),
-                ("res_c_stride", ctypes.c_int32), ("res_c_offset", ctypes.c_int32), ("res_scale", ctypes.c_float)]
+                ("res_c_stride", ctypes.c_int32), ("res_c_offset", ctypes.c_int32), ("res_scale", ctypes.c_float),
+                ("in_zero_point", ctypes.c_int32), ("out_zero_point", ctypes.c_int32),
+                ("res_zero_point", ctypes.c_int32)]
 
 
 class cbs_layer_info_t(ctypes.Structure):
@@ -94,6 +97,7 @@ _SIGNATURES = {
     "cbs_last_error": (ctypes.c_char_p, []),
     "cbs_pack_nhwc_f32": (_I, [_P, _P, _I, _I, _I, _I, _I, _P]),
     "cbs_quantize_nhwc_i8": (_I, [_P, _P, ctypes.c_float, _I, _I, _I, _I, _I, _P]),
+    "cbs_quantize_nhwc_u8": (_I, [_P, _P, ctypes.c_float, _I, _I, _I, _I, _I, _I, _P]),
     "cbs_run_layer_raw_acc": (_I, [_P, _P, _P, _P]),
     "cbs_get_qweights": (_I, [_P, _P, _P]),
     "cbs_get_folded": (_I, [_P, _P, _P]),
@@ -155,10 +159,12 @@ class Layer:
 
 def make_desc(n, c_in, h, w, c_out, k, stride, pad, dtype=CBS_F32, out_row_pitch=0, in_scale=0.0,
               bn_eps=1e-3, act=CBS_ACT_SILU, out_dtype=CBS_F32, out_scale=0.0, in_c_stride=0, in_c_offset=0,
-              out_c_stride=0, out_c_offset=0, res_c_stride=0, res_c_offset=0, res_scale=0.0) -> cbs_conv_desc:
+              out_c_stride=0, out_c_offset=0, res_c_stride=0, res_c_offset=0, res_scale=0.0, in_zero_point=0,
+              out_zero_point=0, res_zero_point=0) -> cbs_conv_desc:
     return cbs_conv_desc(n, c_in, h, w, c_out, k, stride, pad, dtype, out_row_pitch, float(in_scale),
                          float(bn_eps), act, out_dtype, float(out_scale), in_c_stride, in_c_offset,
-                         out_c_stride, out_c_offset, res_c_stride, res_c_offset, float(res_scale))
+                         out_c_stride, out_c_offset, res_c_stride, res_c_offset, float(res_scale),
+                         int(in_zero_point), int(out_zero_point), int(res_zero_point))
 
 
 def cbs_create_layer(desc: cbs_conv_desc, w_oihw, gamma, beta, mean, var) -> Layer:
@@ -306,6 +312,11 @@ def cbs_pack_nhwc_f32(nchw, nhwc, n, c, h, w, c_pad, stream=None) -> None:
 def cbs_quantize_nhwc_i8(nchw, nhwc, s_x, n, c, h, w, c_pad, stream=None) -> None:
     _check(lib.cbs_quantize_nhwc_i8(_dev_ptr(nchw), _dev_ptr(nhwc), float(s_x), n, c, h, w, c_pad,
                                     _stream(stream)), "cbs_quantize_nhwc_i8")
+
+
+def cbs_quantize_nhwc_u8(nchw, nhwc, s_x, z, n, c, h, w, c_pad, stream=None) -> None:
+    _check(lib.cbs_quantize_nhwc_u8(_dev_ptr(nchw), _dev_ptr(nhwc), float(s_x), int(z), n, c, h, w, c_pad,
+                                    _stream(stream)), "cbs_quantize_nhwc_u8")
 
 
 def cbs_run_layer_raw_acc(layer: Layer, inp, acc, stream=None) -> None:

@@ -70,6 +70,7 @@ struct cbs_layer {
   void *d_wfrag = nullptr;
   float *d_bias = nullptr;
   float *d_dq = nullptr;
+  int *d_corr = nullptr;   // uint8 input: accumulator start values [64][co_blocks*16]
   float *d_ws = nullptr;
   unsigned *d_counters = nullptr;
   size_t ws_bytes = 0, counters_len = 0;
@@ -97,15 +98,29 @@ cbs_status validate(const cbs_conv_desc *d) {
   if (d->k != 1 && d->k != 3) return fail(CBS_EUNSUPPORTED, "kernel size %d not in {1,3}", d->k);
   if (d->stride != 1 && d->stride != 2) return fail(CBS_EUNSUPPORTED, "stride %d not in {1,2}", d->stride);
   if (d->pad < 0 || d->pad > d->k / 2) return fail(CBS_EUNSUPPORTED, "pad %d not in [0, k/2]", d->pad);
-  if (d->dtype != CBS_F32 && d->dtype != CBS_I8) return fail(CBS_EINVAL, "dtype %d unknown", d->dtype);
-  if (d->dtype == CBS_I8 && !(d->in_scale > 0.0f && std::isfinite(d->in_scale)))
+  if (d->dtype != CBS_F32 && d->dtype != CBS_I8 && d->dtype != CBS_U8)
+    return fail(CBS_EINVAL, "dtype %d unknown", d->dtype);
+  if (d->dtype != CBS_F32 && !(d->in_scale > 0.0f && std::isfinite(d->in_scale)))
     return fail(CBS_EINVAL, "INT8 layer needs a finite in_scale > 0");
   if (!(d->bn_eps >= 0.0f) || !std::isfinite(d->bn_eps)) return fail(CBS_EINVAL, "bn_eps must be finite and >= 0");
   if (d->c_in > 4096 || d->c_out > 4096) return fail(CBS_EUNSUPPORTED, "channels above 4096");
   if (d->act != CBS_ACT_SILU && d->act != CBS_ACT_NONE) return fail(CBS_EINVAL, "act %d unknown", d->act);
-  if (d->out_dtype != CBS_F32 && d->out_dtype != CBS_I8) return fail(CBS_EINVAL, "out_dtype %d unknown", d->out_dtype);
-  if (d->out_dtype == CBS_I8 && !(d->out_scale > 0.0f && std::isfinite(d->out_scale)))
-    return fail(CBS_EINVAL, "int8 output needs a finite out_scale > 0");
+  if (d->out_dtype != CBS_F32 && d->out_dtype != CBS_I8 && d->out_dtype != CBS_U8)
+    return fail(CBS_EINVAL, "out_dtype %d unknown", d->out_dtype);
+  if (d->out_dtype != CBS_F32 && !(d->out_scale > 0.0f && std::isfinite(d->out_scale)))
+    return fail(CBS_EINVAL, "byte output needs a finite out_scale > 0");
+  // zero points: in [0, 255] for uint8 tensors, 0 for every other dtype
+  struct Zp {
+    const char *what;
+    int value;
+    bool u8;
+  } zps[3] = {{"in_zero_point", d->in_zero_point, d->dtype == CBS_U8},
+              {"out_zero_point", d->out_zero_point, d->out_dtype == CBS_U8},
+              {"res_zero_point", d->res_zero_point, d->out_dtype == CBS_U8 && d->res_c_stride > 0}};
+  for (const Zp &z : zps) {
+    if (z.u8 && (z.value < 0 || z.value > 255)) return fail(CBS_EINVAL, "%s %d not in [0, 255]", z.what, z.value);
+    if (!z.u8 && z.value != 0) return fail(CBS_EINVAL, "%s %d set for a tensor that is not uint8", z.what, z.value);
+  }
   const int oh = out_dim(d->h, d->k, d->stride, d->pad), ow = out_dim(d->w, d->k, d->stride, d->pad);
   if (oh < 1 || ow < 1) return fail(CBS_EINVAL, "empty output (%dx%d)", oh, ow);
   if (d->out_row_pitch != 0 && d->out_row_pitch < ow)
@@ -132,8 +147,8 @@ cbs_status validate(const cbs_conv_desc *d) {
       return fail(CBS_EINVAL, "%s slice: offset %d + channels %d > stride %d", sl.what, sl.offset, sl.channels,
                   sl.stride);
   }
-  if (d->res_c_stride > 0 && d->out_dtype == CBS_I8 && !(d->res_scale > 0.0f && std::isfinite(d->res_scale)))
-    return fail(CBS_EINVAL, "int8 residual needs a finite res_scale > 0");
+  if (d->res_c_stride > 0 && d->out_dtype != CBS_F32 && !(d->res_scale > 0.0f && std::isfinite(d->res_scale)))
+    return fail(CBS_EINVAL, "byte residual needs a finite res_scale > 0");
   const int pitch = d->out_row_pitch ? d->out_row_pitch : ow;
   const int in_cs = d->in_c_stride ? d->in_c_stride : round_up(d->c_in, 4);
   const int out_cs = d->out_c_stride ? d->out_c_stride : round_up(d->c_out, 4);
@@ -232,10 +247,12 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
 }
 
 Choice choose(const cbs_layer *L) {
-  // 1) the offline-tuned table
+  // 1) the offline-tuned table (uint8 layers run the int8 kernels with a
+  // different gather and start value, and take the int8 entries)
+  const int tdtype = L->d.dtype == CBS_U8 ? CBS_I8 : L->d.dtype;
   for (const TileEntry &e : kTileTable) {
     if (e.n == L->d.n && e.c_in == L->d.c_in && e.c_out == L->d.c_out && e.h == L->d.h &&
-        e.w == L->d.w && e.k == L->d.k && e.s == L->d.stride && e.dtype == L->d.dtype &&
+        e.w == L->d.w && e.k == L->d.k && e.s == L->d.stride && e.dtype == tdtype &&
         e.config < num_configs() && config_fits(L, e.config, e.splitk))
       return {e.config, e.splitk};
   }
@@ -276,10 +293,12 @@ void release(cbs_layer *L) {
   if (L->d_wfrag) (void)hipFree(L->d_wfrag);
   if (L->d_bias) (void)hipFree(L->d_bias);
   if (L->d_dq) (void)hipFree(L->d_dq);
+  if (L->d_corr) (void)hipFree(L->d_corr);
   if (L->d_ws) (void)hipFree(L->d_ws);
   if (L->d_counters) (void)hipFree(L->d_counters);
   L->d_wfrag = nullptr;
   L->d_bias = L->d_dq = L->d_ws = nullptr;
+  L->d_corr = nullptr;
   L->d_counters = nullptr;
 }
 
@@ -334,6 +353,7 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
   p.wfrag = L->d_wfrag;
   p.bias = L->d_bias;
   p.dq = L->d_dq;
+  p.corr = L->d_corr;
   if (raw) {
     p.out = out;
     p.out_cs = L->cout_pad;
@@ -341,16 +361,22 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
     p.out = (char *)out + (size_t)L->d.out_c_offset * esz_out;
     p.out_cs = L->out_cs;
     p.act = L->d.act == CBS_ACT_NONE ? ACT_NONE : ACT_SILU;
-    p.out_i8 = L->d.out_dtype == CBS_I8;
+    const bool u8_out = L->d.out_dtype == CBS_U8;
+    p.out_q = L->d.out_dtype != CBS_F32;
     p.out_scale = L->d.out_scale;
     // RN(1/s) in fp32: the double quotient rounded to float (one float of 24
     // bits times one of 25 cannot land within 2^-53 of 1 unless both are powers
     // of two, so the double rounding never changes the result)
-    p.out_rcp = L->d.out_dtype == CBS_I8 ? (float)(1.0 / (double)L->d.out_scale) : 0.0f;
+    p.out_rcp = p.out_q ? (float)(1.0 / (double)L->d.out_scale) : 0.0f;
+    p.out_zp = u8_out ? (float)L->d.out_zero_point : 0.0f;
+    p.out_lo = u8_out ? 0.0f : -127.0f;
+    p.out_hi = u8_out ? 255.0f : 127.0f;
     if (L->res_cs) {
       p.res = (const char *)res + (size_t)L->d.res_c_offset * esz_out;
       p.res_cs = L->res_cs;
       p.res_scale = L->d.res_scale;
+      p.res_xor = u8_out ? 0u : 0x80808080u;
+      p.res_zp = u8_out ? (float)L->d.res_zero_point : 128.0f;
       p.res_bytes = (unsigned)((size_t)L->M * L->res_cs * esz_out - (size_t)L->d.res_c_offset * esz_out);
     }
   }
@@ -459,17 +485,20 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   } else if (L->cin_pad % 16 == 0 && L->in_cs % 16 == 0 && d.in_c_offset % 16 == 0) {
     // 16-channel chunks: one 16-byte load per lane, which needs 16-byte aligned pixels
     L->chunk_ch = 16;
-    L->variant = VAR_I8_C16;
-    L->raw_variant = VAR_I8_C16_RAW;
+    L->variant = d.dtype == CBS_U8 ? VAR_U8_C16_X : VAR_I8_C16;
+    L->raw_variant = d.dtype == CBS_U8 ? VAR_U8_C16_RAW : VAR_I8_C16_RAW;
   } else {
     L->chunk_ch = 4;
     vec = 4;
-    L->variant = VAR_I8_C4;
-    L->raw_variant = VAR_I8_C4_RAW;
+    L->variant = d.dtype == CBS_U8 ? VAR_U8_C4_X : VAR_I8_C4;
+    L->raw_variant = d.dtype == CBS_U8 ? VAR_U8_C4_RAW : VAR_I8_C4_RAW;
   }
-  // the general epilogue only when an option needs it
-  if (d.act != CBS_ACT_SILU || d.out_dtype != CBS_F32 || d.res_c_stride != 0)
-    L->variant = L->variant == VAR_F32 ? VAR_F32_X : L->variant == VAR_I8_C16 ? VAR_I8_C16_X : VAR_I8_C4_X;
+  // the general epilogue only when an option needs it (uint8 layers always have it)
+  if (d.act != CBS_ACT_SILU || d.out_dtype != CBS_F32 || d.res_c_stride != 0) {
+    if (L->variant == VAR_F32) L->variant = VAR_F32_X;
+    if (L->variant == VAR_I8_C16) L->variant = VAR_I8_C16_X;
+    if (L->variant == VAR_I8_C4) L->variant = VAR_I8_C4_X;
+  }
   L->chunks_per_tap = L->cin_pad / L->chunk_ch;
   L->total_chunks = taps * L->chunks_per_tap;
   const int chunks_per_step = 4 * vec;
@@ -503,7 +532,7 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
 
   // ---- per-output-channel int8 quantisation (double)
   std::vector<float> dq;
-  if (d.dtype == CBS_I8) {
+  if (d.dtype != CBS_F32) {
     L->h_qw.assign((size_t)d.c_out * per_co, 0);
     L->h_sw.assign(d.c_out, 1.0);
     dq.assign((size_t)L->co_blocks * 16, 0.f);
@@ -558,6 +587,37 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
         }
       }
 
+  // ---- uint8 input: accumulator start values per border class (see
+  // border_class in conv_kernels.h).  With T[co][tap] the sum of the channel's
+  // int8 weights at a tap, Wsum[co] = sum_tap T and Win the sum over the taps
+  // whose row (bit of rm) and column (bit of cm) lie inside the image, the
+  // kernel's sum over q - 128 (and -128 on padding taps) plus
+  // 128 Wsum - z Win is the sum over q - z on the taps inside the image.
+  std::vector<int> corr;
+  if (d.dtype == CBS_U8) {
+    const int cpad16 = L->co_blocks * 16;
+    corr.assign((size_t)64 * cpad16, 0);
+    for (int co = 0; co < d.c_out; co++) {
+      long long T[9] = {0}, wsum = 0;
+      for (int ci = 0; ci < d.c_in; ci++)
+        for (int t = 0; t < taps; t++) T[t] += L->h_qw[((size_t)co * d.c_in + ci) * taps + t];
+      for (int t = 0; t < taps; t++) wsum += T[t];
+      for (int rm = 0; rm < 8; rm++)
+        for (int cm = 0; cm < 8; cm++) {
+          long long win = 0;
+          for (int i = 0; i < d.k; i++)
+            for (int j = 0; j < d.k; j++)
+              if (((rm >> i) & 1) && ((cm >> j) & 1)) win += T[i * d.k + j];
+          const long long c = 128 * wsum - (long long)d.in_zero_point * win;
+          if (c < INT32_MIN || c > INT32_MAX) {
+            delete L;
+            return fail(CBS_EUNSUPPORTED, "uint8 zero-point correction outside int32");
+          }
+          corr[(size_t)(rm * 8 + cm) * cpad16 + co] = (int)c;
+        }
+    }
+  }
+
   // ---- kernel configuration
   const Choice ch = choose(L);
   L->config = ch.config;
@@ -568,13 +628,16 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   for (int co = 0; co < d.c_out; co++) biasv[co] = L->h_bias[co];
   st = dev_alloc(&L->d_wfrag, frag_bytes);
   if (st == CBS_OK) st = dev_alloc((void **)&L->d_bias, biasv.size() * sizeof(float));
-  if (st == CBS_OK && d.dtype == CBS_I8) st = dev_alloc((void **)&L->d_dq, dq.size() * sizeof(float));
+  if (st == CBS_OK && d.dtype != CBS_F32) st = dev_alloc((void **)&L->d_dq, dq.size() * sizeof(float));
+  if (st == CBS_OK && d.dtype == CBS_U8) st = dev_alloc((void **)&L->d_corr, corr.size() * sizeof(int));
   if (st == CBS_OK) st = setup_splitk(L);
   if (st == CBS_OK) {
     hipError_t e = hipMemcpy(L->d_wfrag, frag.data(), frag_bytes, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(L->d_bias, biasv.data(), biasv.size() * sizeof(float), hipMemcpyHostToDevice);
-    if (e == hipSuccess && d.dtype == CBS_I8)
+    if (e == hipSuccess && d.dtype != CBS_F32)
       e = hipMemcpy(L->d_dq, dq.data(), dq.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess && d.dtype == CBS_U8)
+      e = hipMemcpy(L->d_corr, corr.data(), corr.size() * sizeof(int), hipMemcpyHostToDevice);
     if (e != hipSuccess) st = fail(CBS_EDEVICE, "weight upload: %s", hipGetErrorString(e));
   }
   if (st != CBS_OK) {
@@ -927,6 +990,20 @@ cbs_status cbs_quantize_nhwc_i8(const float *nchw, int8_t *nhwc, float s_x, int3
   return CBS_OK;
 }
 
+cbs_status cbs_quantize_nhwc_u8(const float *nchw, uint8_t *nhwc, float s_x, int32_t z, int32_t n, int32_t c,
+                                int32_t h, int32_t w, int32_t c_pad, void *stream) {
+  if (!nchw || !nhwc) return fail(CBS_EINVAL, "quantize_u8: null buffer");
+  if (!(s_x > 0.0f) || !std::isfinite(s_x)) return fail(CBS_EINVAL, "quantize_u8: s_x must be finite and > 0");
+  if (z < 0 || z > 255) return fail(CBS_EINVAL, "quantize_u8: zero point %d not in [0, 255]", z);
+  if (n < 0 || c < 1 || h < 0 || w < 0 || c_pad < c || c_pad % 4 != 0)
+    return fail(CBS_EINVAL, "quantize_u8: bad sizes");
+  if ((double)n * h * w * c_pad >= 2147483647.0)
+    return fail(CBS_EUNSUPPORTED, "quantize_u8: tensor above 2^31 elements");
+  hipError_t e = launch_quantize_nhwc_u8(nchw, nhwc, s_x, z, n, c, h * w, c_pad, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CBS_ELAUNCH, "quantize_u8 launch: %s", hipGetErrorString(e));
+  return CBS_OK;
+}
+
 cbs_status cbs_run_layer_raw_acc(const cbs_layer *L, const void *in, int32_t *acc, void *stream) {
   if (!L || !in || !acc) return fail(CBS_EINVAL, "run_layer_raw_acc: null layer or buffer");
   if (L->raw_variant < 0) return fail(CBS_EINVAL, "run_layer_raw_acc: not an INT8 layer");
@@ -935,7 +1012,7 @@ cbs_status cbs_run_layer_raw_acc(const cbs_layer *L, const void *in, int32_t *ac
 
 cbs_status cbs_get_qweights(const cbs_layer *L, int8_t *q_oihw, double *s_w) {
   if (!L) return fail(CBS_EINVAL, "get_qweights: null layer");
-  if (L->d.dtype != CBS_I8) return fail(CBS_EINVAL, "get_qweights: not an INT8 layer");
+  if (L->d.dtype == CBS_F32) return fail(CBS_EINVAL, "get_qweights: not an INT8 layer");
   if (q_oihw) std::memcpy(q_oihw, L->h_qw.data(), L->h_qw.size());
   if (s_w) std::memcpy(s_w, L->h_sw.data(), L->h_sw.size() * sizeof(double));
   return CBS_OK;

@@ -30,7 +30,14 @@ enum Variant {
   VAR_F32_X = 5,
   VAR_I8_C16_X = 6,
   VAR_I8_C4_X = 7,
-  VAR_COUNT = 8
+  // asymmetric uint8 activations: codes are gathered as q ^ 0x80 = q - 128
+  // (signed) and every accumulator starts at the zero-point correction of its
+  // pixel's border class; general epilogue, or raw int32 accumulators
+  VAR_U8_C16_X = 8,
+  VAR_U8_C4_X = 9,
+  VAR_U8_C16_RAW = 10,
+  VAR_U8_C4_RAW = 11,
+  VAR_COUNT = 12
 };
 
 // Everything a launch needs; filled at create, passed by value.
@@ -60,6 +67,7 @@ struct ConvParams {
   void *out;             // NHWC output, first channel of the layer: pixel (n,oh,ow) at
                          // out + ((n*OH + oh)*pitch + ow)*out_cs  (fp32, int8, or int32 for raw)
   const void *res;       // residual, first channel: logical pixel m at res + m*res_cs (null if none)
+  const int *corr;       // uint8 input: accumulator start values [64 border classes][co_blocks*16]
   int H, W;
   int x_cs;              // input elements between consecutive pixels (cin_pad when dense)
   int k, stride, pad;
@@ -76,10 +84,14 @@ struct ConvParams {
   int res_cs;            // residual elements between consecutive pixels (0: no residual)
   unsigned res_bytes;    // bytes of the residual buffer from res (buffer-load range)
   int act;               // Act
-  int out_i8;            // 1: int8 output codes q = clamp(rne(fp32(y / out_scale)), +-127)
-  float out_scale;       // s_y for int8 output
+  int out_q;             // 1: byte output codes q = clamp(rne(fp32(y / out_scale)) + out_zp, out_lo, out_hi)
+  float out_scale;       // s_y for byte output
   float out_rcp;         // RN(1/s_y), the correctly rounded fp32 reciprocal
-  float res_scale;       // scale of int8 residual codes
+  float out_zp;          // output zero point (0 for int8 codes)
+  float out_lo, out_hi;  // code range: -127, 127 (int8) or 0, 255 (uint8)
+  float res_scale;       // scale of byte residual codes
+  unsigned res_xor;      // byte residual decode, per byte: value = float(byte ^ res_xor) - res_zp,
+  float res_zp;          //   with 0x80808080 and 128 for int8 codes, 0 and the zero point for uint8
   // ---- pixel-tiled kernels (conv_igemm, conv_lds)
   int M;                 // N*OH*OW output pixels
   int co_tiles;          // workgroup tiles along output channels
@@ -117,10 +129,16 @@ hipError_t launch_var_4(int cfg, const ConvParams &p, hipStream_t stream);
 hipError_t launch_var_5(int cfg, const ConvParams &p, hipStream_t stream);
 hipError_t launch_var_6(int cfg, const ConvParams &p, hipStream_t stream);
 hipError_t launch_var_7(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_8(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_9(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_10(int cfg, const ConvParams &p, hipStream_t stream);
+hipError_t launch_var_11(int cfg, const ConvParams &p, hipStream_t stream);
 
 hipError_t launch_pack_nhwc_f32(const float *x, float *y, int n, int c, int hw, int c_pad,
                                 hipStream_t stream);
 hipError_t launch_quantize_nhwc_i8(const float *x, int8_t *y, float s_x, int n, int c, int hw,
+                                   int c_pad, hipStream_t stream);
+hipError_t launch_quantize_nhwc_u8(const float *x, uint8_t *y, float s_x, int z, int n, int c, int hw,
                                    int c_pad, hipStream_t stream);
 
 }  // namespace cbs

@@ -33,6 +33,10 @@ hipError_t launch_conv(int var, int cfg, const ConvParams &p, hipStream_t stream
     case 5: return launch_var_5(cfg, p, stream);
     case 6: return launch_var_6(cfg, p, stream);
     case 7: return launch_var_7(cfg, p, stream);
+    case 8: return launch_var_8(cfg, p, stream);
+    case 9: return launch_var_9(cfg, p, stream);
+    case 10: return launch_var_10(cfg, p, stream);
+    case 11: return launch_var_11(cfg, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -88,6 +92,36 @@ __global__ __launch_bounds__(256) void quantize_nhwc_i8_kernel(const float *__re
   *(unsigned *)(y + pix * c_pad + 4 * q) = word;
 }
 
+// Asymmetric uint8: q = clamp(rne(fp32(x / s_x)) + z, 0, 255); padded lanes
+// get z, the code of a real zero.
+__global__ __launch_bounds__(256) void quantize_nhwc_u8_kernel(const float *__restrict__ x,
+                                                               uint8_t *__restrict__ y, float s_x, int z, int n,
+                                                               int c, int hw, int c_pad) {
+  const long total = (long)n * hw * (c_pad >> 2);
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const long npix = (long)n * hw;
+  const int q = (int)(idx / npix);
+  const long pix = idx - (long)q * npix;
+  const int b = (int)(pix / hw);
+  const int i = (int)(pix - (long)b * hw);
+  const float zf = (float)z;
+  unsigned word = 0;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int ch = 4 * q + e;
+    int qv = z;
+    if (ch < c) {
+      // fp32 division, correctly rounded, round half to even, then the zero point and the clamp
+      const float t = __fdiv_rn(x[((long)b * c + ch) * hw + i], s_x);
+      const float rr = fminf(fmaxf(rintf(t) + zf, 0.0f), 255.0f);
+      qv = (int)rr;
+    }
+    word |= ((unsigned)(qv & 0xff)) << (8 * e);
+  }
+  *(unsigned *)(y + pix * c_pad + 4 * q) = word;
+}
+
 hipError_t launch_pack_nhwc_f32(const float *x, float *y, int n, int c, int hw, int c_pad,
                                 hipStream_t stream) {
   const long total = (long)n * hw * (c_pad >> 2);
@@ -104,6 +138,15 @@ hipError_t launch_quantize_nhwc_i8(const float *x, int8_t *y, float s_x, int n, 
   const unsigned grid = (unsigned)((total + 255) / 256);
   hipLaunchKernelGGL(quantize_nhwc_i8_kernel, dim3(grid), dim3(256), 0, stream, x, y, s_x, n, c, hw,
                      c_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_nhwc_u8(const float *x, uint8_t *y, float s_x, int z, int n, int c, int hw,
+                                   int c_pad, hipStream_t stream) {
+  const long total = (long)n * hw * (c_pad >> 2);
+  if (total == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(quantize_nhwc_u8_kernel, dim3(grid), dim3(256), 0, stream, x, y, s_x, z, n, c, hw, c_pad);
   return hipGetLastError();
 }
 

@@ -44,31 +44,36 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Operand and epilogue traits of a variant: VEC = 4-channel chunks per lane
 // and K step (int8 small-channel gather), ESIZE = bytes per activation, RAW =
-// store int32 accumulators, X = general epilogue (act / residual / int8 out).
+// store int32 accumulators, X = general epilogue (act / residual / byte out),
+// U8 = asymmetric uint8 activations.
 template <int VAR> struct Var;
 template <> struct Var<VAR_F32> {
   using Frag = f32x4; using Acc = f32x4;
-  static constexpr int VEC = 1, ESIZE = 4; static constexpr bool I8 = false, RAW = false, X = false;
+  static constexpr int VEC = 1, ESIZE = 4;
+  static constexpr bool I8 = false, RAW = false, X = false, U8 = false;
 };
 template <> struct Var<VAR_I8_C16> {
   using Frag = i32x4; using Acc = i32x4;
-  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = false, X = false;
+  static constexpr int VEC = 1, ESIZE = 1;
+  static constexpr bool I8 = true, RAW = false, X = false, U8 = false;
 };
 template <> struct Var<VAR_I8_C4> {
   using Frag = i32x4; using Acc = i32x4;
-  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = false, X = false;
+  static constexpr int VEC = 4, ESIZE = 1;
+  static constexpr bool I8 = true, RAW = false, X = false, U8 = false;
 };
-template <> struct Var<VAR_I8_C16_RAW> {
-  using Frag = i32x4; using Acc = i32x4;
-  static constexpr int VEC = 1, ESIZE = 1; static constexpr bool I8 = true, RAW = true, X = false;
-};
-template <> struct Var<VAR_I8_C4_RAW> {
-  using Frag = i32x4; using Acc = i32x4;
-  static constexpr int VEC = 4, ESIZE = 1; static constexpr bool I8 = true, RAW = true, X = false;
-};
+template <> struct Var<VAR_I8_C16_RAW> : Var<VAR_I8_C16> { static constexpr bool RAW = true; };
+template <> struct Var<VAR_I8_C4_RAW> : Var<VAR_I8_C4> { static constexpr bool RAW = true; };
 template <> struct Var<VAR_F32_X> : Var<VAR_F32> { static constexpr bool X = true; };
 template <> struct Var<VAR_I8_C16_X> : Var<VAR_I8_C16> { static constexpr bool X = true; };
 template <> struct Var<VAR_I8_C4_X> : Var<VAR_I8_C4> { static constexpr bool X = true; };
+template <> struct Var<VAR_U8_C16_X> : Var<VAR_I8_C16> { static constexpr bool X = true, U8 = true; };
+template <> struct Var<VAR_U8_C4_X> : Var<VAR_I8_C4> { static constexpr bool X = true, U8 = true; };
+template <> struct Var<VAR_U8_C16_RAW> : Var<VAR_I8_C16> { static constexpr bool RAW = true, U8 = true; };
+template <> struct Var<VAR_U8_C4_RAW> : Var<VAR_I8_C4> { static constexpr bool RAW = true, U8 = true; };
+
+// uint8 codes q enter the signed int8 MFMA as q ^ 0x80 = q - 128.
+constexpr int kU8Flip = (int)0x80808080u;
 
 
 // Buffer resource word 3 (data format) for the gfx9 family, and an offset
@@ -109,6 +114,7 @@ __device__ __forceinline__ CBS_GLOBAL T *gmem(const void *ptr) {
 // all argument loads at once and waits for them once, instead of spreading
 // them over two or three dependent rounds (it sinks loads towards their first
 // use), each costing a memory round trip before the first operand load.
+template <bool U8>
 __device__ __forceinline__ void pin_common_args(ConvParams &p, int &nblocks) {
   pin_sgpr(nblocks);  // the grid size comes from the dispatch's own argument area
   pin_sgpr(p.x);
@@ -117,6 +123,7 @@ __device__ __forceinline__ void pin_common_args(ConvParams &p, int &nblocks) {
   pin_sgpr(p.dq);
   pin_sgpr(p.out);
   pin_sgpr(p.res);
+  if (U8) pin_sgpr(p.corr);
   pin_sgpr(p.H);
   pin_sgpr(p.W);
   pin_sgpr(p.x_cs);
@@ -136,10 +143,15 @@ __device__ __forceinline__ void pin_common_args(ConvParams &p, int &nblocks) {
   pin_sgpr(p.res_cs);
   pin_sgpr(p.res_bytes);
   pin_sgpr(p.act);
-  pin_sgpr(p.out_i8);
+  pin_sgpr(p.out_q);
   pin_sgpr(p.out_scale);
   pin_sgpr(p.out_rcp);
+  pin_sgpr(p.out_zp);
+  pin_sgpr(p.out_lo);
+  pin_sgpr(p.out_hi);
   pin_sgpr(p.res_scale);
+  pin_sgpr(p.res_xor);
+  pin_sgpr(p.res_zp);
   pin_sgpr(p.OH);
   pin_sgpr(p.OW);
   pin_sgpr(p.pitch);
@@ -147,8 +159,9 @@ __device__ __forceinline__ void pin_common_args(ConvParams &p, int &nblocks) {
 
 // The pixel-tiled kernels (conv_igemm, conv_lds) also decompose pixel and
 // workgroup indices; conv_igemm alone reduces split-K partial tiles.
+template <bool U8>
 __device__ __forceinline__ void pin_tiled_args(ConvParams &p, int &nblocks, bool splitk_args) {
-  pin_common_args(p, nblocks);
+  pin_common_args<U8>(p, nblocks);
   pin_sgpr(p.M);
   pin_sgpr(p.co_tiles);
   pin_sgpr(p.div_ow.magic);
@@ -168,6 +181,7 @@ __device__ __forceinline__ void pin_tiled_args(ConvParams &p, int &nblocks, bool
 }
 
 // conv_halo: the tile grid and the LDS halo layout.
+template <bool U8>
 __device__ __forceinline__ void pin_halo_args(ConvParams &p, int &nblocks) {
   pin_sgpr(p.cin_pad);
   pin_sgpr(p.tiles_x);
@@ -182,7 +196,7 @@ __device__ __forceinline__ void pin_halo_args(ConvParams &p, int &nblocks) {
   pin_sgpr(p.div_hcq.shift);
   pin_sgpr(p.div_hwd.magic);
   pin_sgpr(p.div_hwd.shift);
-  pin_common_args(p, nblocks);
+  pin_common_args<U8>(p, nblocks);
 }
 
 __device__ __forceinline__ int fdiv(int n, FastDiv f) {
@@ -197,11 +211,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, unsigne
 // z holds the pre-activation values (accumulator + folded bias, dequantised
 // for int8); opix is the pixel's storage index ((n*OH + oh)*pitch + ow) and m
 // its logical index ((n*OH + oh)*OW + ow), which addresses the dense-row
-// residual.  Order: activation, then the residual add, then (int8 output) the
-// quantiser of the next layer's input, so the int8 codes are exactly those
-// the graph-entry quantiser would produce from this layer's fp32 output.
-// act, the residual and the output type are kernel arguments: every branch
-// here is wave-uniform.
+// residual.  Order: activation, then the residual add, then (byte output) the
+// quantiser of the next layer's input, so the codes are exactly those the
+// graph-entry quantiser would produce from this layer's fp32 output.  act, the
+// residual and the output type are kernel arguments: every branch here is
+// wave-uniform.
 template <bool X>
 __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buffer_rsrc_t rr, f32x4 z, int opix,
                                                int m, int co0) {
@@ -220,35 +234,71 @@ __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buf
   }
   if (p.res_cs) {
     const unsigned e = (unsigned)(m * p.res_cs + co0);
-    if (p.out_i8) {
-      const unsigned w = __builtin_amdgcn_raw_buffer_load_b32(rr, e, 0, 0);
+    if (p.out_q) {
+      // byte codes: int8 as (b ^ 0x80) - 128, uint8 as b - z_r (both exact in fp32)
+      const unsigned w = __builtin_amdgcn_raw_buffer_load_b32(rr, e, 0, 0) ^ p.res_xor;
 #pragma unroll
-      for (int i = 0; i < 4; i++) y[i] += p.res_scale * (float)(int)(signed char)((w >> (8 * i)) & 0xffu);
+      for (int i = 0; i < 4; i++) y[i] += p.res_scale * ((float)((w >> (8 * i)) & 0xffu) - p.res_zp);
     } else {
       y += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, e * 4u, 0, 0));
     }
   }
   const size_t o = (size_t)opix * p.out_cs + co0;
-  if (p.out_i8) {
-    // q = clamp(rne(fp32(y / s)), +-127) with the correctly rounded quotient
-    // from Markstein's correction step: with r = RN(1/s), q0 = RN(y r),
+  if (p.out_q) {
+    // q = clamp(rne(fp32(y / s)) + z_y, lo, hi) with the correctly rounded
+    // quotient from Markstein's correction step: with r = RN(1/s), q0 = RN(y r),
     // e = y - q0 s (exact in one FMA), RN(q0 + e r) = RN(y / s) for quotients
-    // in the normal range.  y is first limited to +-128 s, which changes no
-    // code (everything beyond is clamped to +-127 anyway) and keeps q0 finite.
-    const float s = p.out_scale, r = p.out_rcp, lim = 128.0f * s;
+    // in the normal range.  y is first limited to +-256 s, which changes no
+    // code (beyond it every code is clamped to an end of the range anyway) and
+    // keeps q0 finite.
+    const float s = p.out_scale, r = p.out_rcp, lim = 256.0f * s;
     unsigned word = 0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const float yc = fminf(fmaxf(y[i], -lim), lim);
       const float q0 = yc * r;
       const float e = __builtin_fmaf(-q0, s, yc);
-      float t = rintf(__builtin_fmaf(e, r, q0));
-      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      float t = rintf(__builtin_fmaf(e, r, q0)) + p.out_zp;
+      t = fminf(fmaxf(t, p.out_lo), p.out_hi);
       word |= ((unsigned)((int)t & 0xff)) << (8 * i);
     }
     *(gmem<unsigned>(p.out) + o / 4) = word;
   } else {
     *(gmem<f32x4>(p.out) + o / 4) = y;
+  }
+}
+
+// uint8 input: the accumulators start at a correction that turns the sum the
+// MFMAs form into the one of the definition.  The gathered operand is q - 128
+// inside the image and -128 on the padding taps (out-of-range loads read 0,
+// flipped like every other byte), so with Wsum[co] the sum of the channel's
+// int8 weights and Win[co] the sum of its weights on the taps inside the image,
+//   sum_in q_w (q - z) = MFMA sum + 128 Wsum[co] - z Win[co].
+// Win depends on the pixel only through which window rows and columns lie
+// inside the image: bit i of the row mask says row i does, likewise for the
+// columns, and the class rows * 8 + cols indexes a [64][co_blocks*16] table
+// set up at create.
+__device__ __forceinline__ int border_class(const ConvParams &p, int iy0, int ix0) {
+  const unsigned kmask = (1u << p.k) - 1u;
+  unsigned rm = 0, cm = 0;
+#pragma unroll
+  for (int i = 0; i < 3; i++) {
+    rm |= (unsigned)((unsigned)(iy0 + i) < (unsigned)p.H) << i;
+    cm |= (unsigned)((unsigned)(ix0 + i) < (unsigned)p.W) << i;
+  }
+  return (int)((rm & kmask) * 8u + (cm & kmask));
+}
+
+// Start value of the accumulator of output channels co0 .. co0+3 at a pixel of
+// border class cls (zero unless the variant has uint8 input).
+template <class V>
+__device__ __forceinline__ typename V::Acc acc_start(const ConvParams &p, int cls, int co0) {
+  if constexpr (V::U8) {
+    const __amdgpu_buffer_rsrc_t cr = rsrc(p.corr, (unsigned)(64 * p.co_blocks * 64));
+    return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         cr, (unsigned)((cls * p.co_blocks * 16 + co0) * 4), 0, 0));
+  } else {
+    return typename V::Acc{};
   }
 }
 
@@ -274,7 +324,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   using Frag = typename V::Frag;
   using Acc = typename V::Acc;
   int nblocks = gridDim.x;
-  pin_tiled_args(p, nblocks, true);
+  pin_tiled_args<V::U8>(p, nblocks, true);
   const int lane = threadIdx.x & 63;
   // The wave index is made explicitly wave-uniform: every condition that
   // guards an MFMA below depends only on it, so it compiles to a scalar
@@ -362,6 +412,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
         const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
         const unsigned off = v ? (unsigned)(pixbase[b] * p.x_cs + doff) * (unsigned)V::ESIZE : kOutOfRange;
         bb[b] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+        if constexpr (V::U8) bb[b] ^= kU8Flip;
       }
     } else {
 #pragma unroll
@@ -374,16 +425,29 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
           const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
           const unsigned off = v ? (unsigned)(pixbase[b] * p.x_cs + doff) : kOutOfRange;
           bb[b][j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
+          if constexpr (V::U8) bb[b][j] ^= kU8Flip;
         }
       }
     }
   };
 
+  // Accumulators start at zero, or (uint8 input) at the zero-point correction
+  // in the first K slice of the tile only (the others are summed onto it).
   Acc acc[CB][PB];
 #pragma unroll
   for (int cb = 0; cb < CB; cb++)
 #pragma unroll
     for (int b = 0; b < PB; b++) acc[cb][b] = Acc{};
+  if constexpr (V::U8) {
+    if (wk == 0 && split == 0) {
+#pragma unroll
+      for (int b = 0; b < PB; b++) {
+        const int cls = border_class(p, iy0[b], ix0[b]);
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++) acc[cb][b] = acc_start<V>(p, cls, (cob0 + cb) * 16 + 4 * g);
+      }
+    }
+  }
 
   // Independent accumulators are interleaved so consecutive MFMAs never wait
   // on each other's result.
@@ -565,7 +629,9 @@ __device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu
     const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
     const unsigned off =
         v ? (unsigned)(q.base * p.x_cs + (c.dy * p.W + c.dx) * p.x_cs + c.ci) * (unsigned)V::ESIZE : kOutOfRange;
-    return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    Frag f = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    if constexpr (V::U8) f ^= kU8Flip;
+    return f;
   } else {
     Frag f;
 #pragma unroll
@@ -575,6 +641,7 @@ __device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu
       const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
       const unsigned off = v ? (unsigned)(q.base * p.x_cs + (c.dy * p.W + c.dx) * p.x_cs + c.ci) : kOutOfRange;
       f[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
+      if constexpr (V::U8) f[j] ^= kU8Flip;
     }
     return f;
   }
@@ -588,7 +655,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int BMB = MB * WM, BNB = NB * WN;     // 16-pixel and 16-channel blocks per workgroup
   int nblocks = gridDim.x;
-  pin_tiled_args(p, nblocks, false);
+  pin_tiled_args<V::U8>(p, nblocks, false);
   constexpr int SB = BMB + BNB;                   // fragment blocks per K step
   constexpr int NA = KS * BNB * 64 / NT;          // weight slots per thread per stage
   constexpr int NX = KS * BMB * 64 / NT;          // activation slots per thread per stage
@@ -672,9 +739,15 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
 
   Acc acc[NB][MB];
 #pragma unroll
-  for (int nb = 0; nb < NB; nb++)
+  for (int mb = 0; mb < MB; mb++) {
+    int cls = 0;
+    if constexpr (V::U8) {
+      const Pix q = pixel_of(p, (px_tile * BMB + wm * MB + mb) * 16 + r);
+      cls = border_class(p, q.iy0, q.ix0);
+    }
 #pragma unroll
-    for (int mb = 0; mb < MB; mb++) acc[nb][mb] = Acc{};
+    for (int nb = 0; nb < NB; nb++) acc[nb][mb] = acc_start<V>(p, cls, (co_tile * BNB + wn * NB + nb) * 16 + 4 * g);
+  }
 
   auto compute = [&](int buf) {
 #pragma unroll
@@ -763,7 +836,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   static_assert(TH * TW % 64 == 0, "tile must split into 4 waves of 16-pixel blocks");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int nblocks = gridDim.x;
-  pin_halo_args(p, nblocks);
+  pin_halo_args<V::U8>(p, nblocks);
   typedef __attribute__((address_space(3))) void *lds_ptr;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -829,6 +902,18 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
       if constexpr (V::I8 && !V::RAW) ep_dq[nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, off, 0, 0));
     }
   }
+  Acc acc[NBMAX][MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) {
+    int cls = 0;
+    if constexpr (V::U8) {
+      const int pi = (wave * MB + mb) * 16 + r;
+      cls = border_class(p, (oh0 + pi / TW) * st_ - p.pad, (ow0 + pi % TW) * st_ - p.pad);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBMAX; nb++) acc[nb][mb] = nb < nbl ? acc_start<V>(p, cls, nb * 16 + 4 * g) : Acc{};
+  }
+
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -845,12 +930,6 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   // pixels of a fragment read on repeating LDS banks; the host pads it to an
   // odd number of slots (a zero slot), which makes those reads conflict-free.
   const int pix_bytes = cql * SLOT;
-  Acc acc[NBMAX][MB];
-#pragma unroll
-  for (int nb = 0; nb < NBMAX; nb++)
-#pragma unroll
-    for (int mb = 0; mb < MB; mb++) acc[nb][mb] = Acc{};
-
   for (int s = 0; s < p.steps; s++) {
     Frag a[NBMAX];
 #pragma unroll
@@ -862,7 +941,8 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
       if (!c.ok) c.dy = c.dx = c.ci = 0;  // past K: read a valid slot, then zero it
 #pragma unroll
       for (int mb = 0; mb < MB; mb++) {
-        const Frag v = *(const Frag *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci * V::ESIZE);
+        Frag v = *(const Frag *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci * V::ESIZE);
+        if constexpr (V::U8) v ^= kU8Flip;  // zero-filled padding becomes -128, as in conv_igemm
         b[mb] = c.ok ? v : Frag{};
       }
     } else {
@@ -874,7 +954,8 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
         if (!c.ok) c.dy = c.dx = c.ci = 0;
 #pragma unroll
         for (int mb = 0; mb < MB; mb++) {
-          const int v = *(const int *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci);
+          int v = *(const int *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci);
+          if constexpr (V::U8) v ^= kU8Flip;
           b[mb][j] = c.ok ? v : 0;
         }
       }

@@ -164,6 +164,18 @@ def calibration_scale(x: np.ndarray, percentile: float = CALIB_PERCENTILE) -> np
     return np.float32(p / 127.0)
 
 
+def calibration_u8(x: np.ndarray):
+    """The asymmetric uint8 calibration input (min/max, range widened to hold
+    0): s = fp32((hi - lo) / 255) and z = clamp(rne(-lo / s), 0, 255), so that
+    lo and hi map onto the ends of the code range and 0.0 onto the code z."""
+    a = np.asarray(x, dtype=np.float64)
+    lo, hi = min(float(a.min()), 0.0), max(float(a.max()), 0.0)
+    if hi == lo:
+        return np.float32(1.0), 0
+    s = np.float32((hi - lo) / 255.0)
+    return s, int(min(255, max(0, int(np.rint(-lo / float(s))))))
+
+
 def random_case(rng: np.random.Generator, max_hw: int = 24, max_c: int = 40, n_max: int = 2):
     """A random small layer shape for property sweeps (k in {1,3}, s in {1,2})."""
     k = int(rng.choice([1, 3]))

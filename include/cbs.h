@@ -41,11 +41,22 @@
  *   out_dtype = CBS_I8:  q_y = clamp(rne(fp32(y / s_y)), -127, 127), the quantiser of the
  *                        next INT8 layer's input (s_y = its s_x), applied to the fp32 y.
  *
+ * Asymmetric activations (edge-optimization README, "Design notes": ONNX
+ * Runtime quantises activations asymmetrically to uint8, with symmetric
+ * per-channel weights, since activations after SiLU are mostly positive):
+ *   dtype = CBS_U8:      q_x = clamp(rne(fp32(x / s_x)) + z_x, 0, 255), z_x = in_zero_point;
+ *                        acc = sum over the taps inside the image of q_w * (q_x - z_x)
+ *                        (exact int32: zero padding is a real zero, the code z_x), then
+ *                        the INT8 epilogue above.  Weights are quantised as for CBS_I8.
+ *   out_dtype = CBS_U8:  q_y = clamp(rne(fp32(y / s_y)) + z_y, 0, 255), z_y = out_zero_point.
+ *   residual of a CBS_U8 output: r = res_scale * (q_r - res_zero_point).
+ *
  * Layouts (all device buffers are caller-owned):
- *   input  : NHWC [N][H][W][in_c_stride]; fp32 for CBS_F32, int8 for CBS_I8;
- *            the layer reads channels in_c_offset .. in_c_offset + C_in_pad - 1.
- *            Dense (in_c_stride = 0): the stride is C_in_pad = round_up(C_in, 4)
- *            and padded lanes must hold 0.  Slice (in_c_stride > 0): C_in,
+ *   input  : NHWC [N][H][W][in_c_stride]; fp32 for CBS_F32, int8 for CBS_I8,
+ *            uint8 for CBS_U8; the layer reads channels in_c_offset ..
+ *            in_c_offset + C_in_pad - 1.  Dense (in_c_stride = 0): the stride is
+ *            C_in_pad = round_up(C_in, 4) and padded lanes must hold 0 (any code
+ *            for CBS_U8, whose padded lanes meet zero weights).  Slice (in_c_stride > 0): C_in,
  *            in_c_offset and in_c_stride are multiples of 4 and
  *            in_c_offset + C_in <= in_c_stride (a channel_chunk / channel_cat
  *            slice read in place).
@@ -94,6 +105,7 @@ typedef int32_t cbs_status;
 
 #define CBS_F32 0
 #define CBS_I8 1
+#define CBS_U8 2 /* asymmetric uint8 codes with a zero point */
 
 #define CBS_ACT_SILU 0 /* y = SiLU(z) (the default) */
 #define CBS_ACT_NONE 1 /* y = z: plain convolution + bias */
@@ -109,28 +121,32 @@ typedef struct cbs_conv_desc {
     int32_t k;             /* kernel size: 1 or 3 */
     int32_t stride;        /* 1 or 2 */
     int32_t pad;           /* zero padding, 0 <= pad <= k/2 */
-    int32_t dtype;         /* CBS_F32 or CBS_I8 */
+    int32_t dtype;         /* CBS_F32, CBS_I8 or CBS_U8 */
     int32_t out_row_pitch; /* output pixels between consecutive (n, oh) rows, >= OW; 0 means OW */
-    float in_scale;        /* CBS_I8: per-tensor activation scale s_x > 0; ignored for CBS_F32 */
+    float in_scale;        /* CBS_I8 / CBS_U8: per-tensor activation scale s_x > 0; ignored for CBS_F32 */
     float bn_eps;          /* batch-norm epsilon >= 0, used as (double)bn_eps */
     /* ---- fused epilogue and I/O (all-zero = the plain layer described above) ---- */
     int32_t act;           /* CBS_ACT_SILU (0) or CBS_ACT_NONE */
-    int32_t out_dtype;     /* CBS_F32 (0): fp32 output; CBS_I8: int8 codes of scale out_scale */
-    float out_scale;       /* out_dtype CBS_I8: per-tensor output scale s_y > 0 */
+    int32_t out_dtype;     /* CBS_F32 (0): fp32 output; CBS_I8 / CBS_U8: codes of scale out_scale */
+    float out_scale;       /* out_dtype CBS_I8 / CBS_U8: per-tensor output scale s_y > 0 */
     int32_t in_c_stride;   /* channels between consecutive input pixels; 0 = C_in_pad (dense) */
     int32_t in_c_offset;   /* first input channel of this layer within a pixel (0 when dense) */
     int32_t out_c_stride;  /* channels between consecutive output pixels; 0 = C_out_pad (dense) */
     int32_t out_c_offset;  /* first output channel written within a pixel (0 when dense) */
     int32_t res_c_stride;  /* residual: channels between its pixels; 0 = no residual */
     int32_t res_c_offset;  /* residual: first channel within its pixel */
-    float res_scale;       /* out_dtype CBS_I8 with a residual: scale of its int8 codes, > 0 */
+    float res_scale;       /* out_dtype CBS_I8 / CBS_U8 with a residual: scale of its codes, > 0 */
+    /* ---- zero points of uint8 tensors, in [0, 255]; must be 0 for other dtypes ---- */
+    int32_t in_zero_point;  /* dtype CBS_U8: z_x */
+    int32_t out_zero_point; /* out_dtype CBS_U8: z_y */
+    int32_t res_zero_point; /* out_dtype CBS_U8 with a residual: zero point of its codes */
 } cbs_conv_desc;
 
 typedef struct cbs_layer_info_t {
     int32_t c_in_pad, c_out_pad;  /* padded channel counts of input and output */
     int32_t oh, ow;               /* output height and width */
     int32_t out_row_pitch;        /* pixels per output row (>= ow) */
-    int32_t dtype;                /* CBS_F32 or CBS_I8 */
+    int32_t dtype;                /* CBS_F32, CBS_I8 or CBS_U8 */
     int64_t in_bytes;             /* size of the input buffer run_layer reads (N*H*W*in_c_stride*b_in) */
     int64_t out_bytes;            /* size of the output buffer run_layer writes into
                                      (N*OH*pitch*out_c_stride*b_out; guards included) */
@@ -149,7 +165,8 @@ typedef struct cbs_layer_info_t {
  * Create a layer: validate the descriptor, fold batch norm (double), re-lay
  * the weights into MFMA fragment order, quantise them for CBS_I8, pick the
  * kernel configuration for this shape from the tile table, and copy
- * everything to the current HIP device.  Host arrays: w_oihw has
+ * everything to the current HIP device (for CBS_U8 also the zero-point
+ * correction of the accumulators: 64 * round_up(C_out, 16) int32).  Host arrays: w_oihw has
  * C_out*C_in*k*k floats; gamma, beta, mean, var have C_out floats each; all
  * are copied and may be freed afterwards.  On success *out owns device memory
  * until cbs_destroy_layer.  Errors: CBS_EINVAL, CBS_EUNSUPPORTED, CBS_ENOMEM,
@@ -285,16 +302,24 @@ cbs_status cbs_quantize_nhwc_i8(const float *nchw, int8_t *nhwc, float s_x, int3
                                 int32_t h, int32_t w, int32_t c_pad, void *stream);
 
 /*
- * Test hook (CBS_I8 layers only): run the integer part of the layer and store
- * the raw int32 accumulators, NHWC [N][OH][out_row_pitch][C_out_pad], instead
+ * The same with asymmetric uint8 quantisation (edge-optimization README,
+ * "Design notes"): q = clamp(rne(fp32(x / s_x)) + z, 0, 255), padded lanes get
+ * z (a real zero).  s_x > 0, 0 <= z <= 255, c_pad >= c, c_pad % 4 == 0.
+ */
+cbs_status cbs_quantize_nhwc_u8(const float *nchw, uint8_t *nhwc, float s_x, int32_t z, int32_t n, int32_t c,
+                                int32_t h, int32_t w, int32_t c_pad, void *stream);
+
+/*
+ * Test hook (CBS_I8 and CBS_U8 layers): run the integer part of the layer and
+ * store the raw int32 accumulators (for CBS_U8 the zero-point corrected sum), NHWC [N][OH][out_row_pitch][C_out_pad], instead
  * of the fp32 epilogue.  Same guard-pixel rule as cbs_run_layer.
  */
 cbs_status cbs_run_layer_raw_acc(const cbs_layer *layer, const void *in, int32_t *acc, void *stream);
 
 /*
- * Test hook: copy the layer's host-side quantised weights (CBS_I8) as OIHW
- * int8 [C_out][C_in][k][k] and the per-channel scales s_w (double [C_out]).
- * Either pointer may be NULL.  CBS_EINVAL for a CBS_F32 layer.
+ * Test hook: copy the layer's host-side quantised weights (CBS_I8, CBS_U8) as
+ * OIHW int8 [C_out][C_in][k][k] and the per-channel scales s_w (double
+ * [C_out]).  Either pointer may be NULL.  CBS_EINVAL for a CBS_F32 layer.
  */
 cbs_status cbs_get_qweights(const cbs_layer *layer, int8_t *q_oihw, double *s_w);
 

@@ -7,11 +7,13 @@
   * channel slices of input and output (chunk / cat read and written in
     place) and a residual added after the activation;
   * a C3k2-style block chained through slices with no cat, chunk or add
-    kernel, in FP32 and fully in INT8.
+    kernel, in FP32 and fully in INT8;
+  * asymmetric uint8 activations with a zero point (input, output and
+    residual codes), against the oracle's asymmetric path.
 
 Tolerances.  FP32 outputs: |err| <= 1e-4 * sum|W' x| + 1e-6 (+ 2^-22 |r| for
 the residual add, one fp32 rounding).  INT8 fp32 outputs: 1e-4 * f * sum|q_w
-q_x| + 1e-6 (+ the same residual term).  INT8 output codes: the integer
+q_x| + 1e-6 (+ the same residual term), with q_x - z_x for uint8 input.  Byte output codes: the integer
 accumulators are exact, so the codes must equal the oracle's except where the
 oracle's y lies within eps of a rounding boundary of the quantiser, where
 either neighbour is correct; eps is the error bound of the kernel's fp32
@@ -34,6 +36,7 @@ if torch.cuda.is_available():
 
 SENT_F32 = np.uint32(0x7FA5A5A5).view(np.int32)  # NaN payload no kernel writes
 SENT_I8 = np.int8(-91)                              # 0xA5
+SENT_U8 = np.uint8(0xA5)
 RES_TERM = 2.0 ** -22
 I8_BAND = 2.0 ** -18
 
@@ -58,27 +61,37 @@ def _wide(rng, base_nhwc, stride, off, kind):
     n, h, w, c = base_nhwc.shape
     if kind == "f32":
         buf = (3 * rng.standard_normal((n, h, w, stride))).astype(np.float32)
+    elif kind == "u8":
+        buf = rng.integers(0, 256, (n, h, w, stride)).astype(np.uint8)
     else:
         buf = rng.integers(-127, 128, (n, h, w, stride)).astype(np.int8)
     buf[..., off:off + c] = base_nhwc
     return buf
 
 
-def _dense(base_nhwc, kind):
-    """Dense layout: channels padded to a multiple of 4 with zeros."""
+def _dense(base_nhwc, kind, rng=None):
+    """Dense layout: channels padded to a multiple of 4 with zeros (uint8: with random
+    codes, which the layer must ignore since their weights are zero)."""
     n, h, w, c = base_nhwc.shape
     cp = -(-c // 4) * 4
-    buf = np.zeros((n, h, w, cp), np.float32 if kind == "f32" else np.int8)
+    if kind == "u8":
+        buf = rng.integers(0, 256, (n, h, w, cp)).astype(np.uint8)
+    else:
+        buf = np.zeros((n, h, w, cp), np.float32 if kind == "f32" else np.int8)
     buf[..., :c] = base_nhwc
     return buf
+
+
+DTYPES = {"f32": 0, "i8": 1, "u8": 2}  # cbs.CBS_F32, CBS_I8, CBS_U8
 
 
 class Case:
     """One fused layer: spec, batch, compute dtype, epilogue and I/O options."""
 
     def __init__(self, spec, n=1, dtype="f32", act="silu", out="f32", in_sl=None, out_sl=None, res_sl=None,
-                 extra=16, folded=False, seed=0):
+                 extra=16, folded=False, seed=0, zx=None):
         self.spec, self.n, self.dtype, self.act, self.out = spec, n, dtype, act, out
+        self.zx = zx  # uint8 input: zero point override (None: the calibration's)
         self.in_sl, self.out_sl, self.res_sl = in_sl, out_sl, res_sl  # (stride, offset) or None
         self.extra, self.folded, self.seed = extra, folded, seed
 
@@ -101,32 +114,51 @@ def prepare(case):
         bn = _folded_as_bn(scale, bias)
     else:
         bn = (L.gamma, L.beta, L.mean, L.var, L.eps)
-    s_x = W.calibration_scale(L.x) if case.dtype == "i8" else np.float32(0)
-    # residual: fp32 values for fp32 output, int8 codes (with their scale) for int8 output
+    s_x, z_x = np.float32(0), 0
+    if case.dtype == "i8":
+        s_x = W.calibration_scale(L.x)
+    elif case.dtype == "u8":
+        s_x, z_x = W.calibration_u8(L.x) if case.zx is None else (W.calibration_u8(L.x)[0], case.zx)
+    # residual: fp32 values for fp32 output, byte codes (with their scale) for byte output
     res_nchw = res_codes = None
-    res_scale = np.float32(0)
+    res_scale, res_zp = np.float32(0), 0
     if case.res_sl is not None:
         if case.out == "f32":
             res_nchw = rng.standard_normal((case.n, sp.c_out, oh, ow)).astype(np.float32)
-        else:
+        elif case.out == "i8":
             res_codes = rng.integers(-127, 128, (case.n, sp.c_out, oh, ow)).astype(np.int8)
             res_scale = np.float32(0.03)
             res_nchw = res_codes.astype(np.float64) * np.float64(res_scale)
+        else:
+            res_codes = rng.integers(0, 256, (case.n, sp.c_out, oh, ow)).astype(np.uint8)
+            res_scale, res_zp = np.float32(0.02), 100
+            res_nchw = (res_codes.astype(np.float64) - res_zp) * np.float64(res_scale)
     res64 = None if res_nchw is None else np.asarray(res_nchw, np.float64)
     if case.dtype == "f32":
         y, S = oracle.conv_bn_act_f32(L.x, L.w, *bn, sp.stride, sp.pad, act=case.act, residual=res64)
         ref = {"y": y, "S": S}
     else:
-        ref = oracle.conv_bn_act_i8(L.x, s_x, L.w, *bn, sp.stride, sp.pad, act=case.act, residual=res64)
+        if case.dtype == "i8":
+            ref = oracle.conv_bn_act_i8(L.x, s_x, L.w, *bn, sp.stride, sp.pad, act=case.act, residual=res64)
+        else:
+            ref = oracle.conv_bn_act_u8(L.x, s_x, z_x, L.w, *bn, sp.stride, sp.pad, act=case.act, residual=res64)
         ref["S"] = ref["f"].astype(np.float64)[None, :, None, None] * ref["absacc"]
         _, bf = oracle.bn_fold(L.w, *bn)
         ref["bias"] = bf
     ref["res"] = res64
-    s_y = W.calibration_scale(ref["y"].astype(np.float32)) if case.out == "i8" else np.float32(0)
+    s_y, z_y = np.float32(0), 0
+    if case.out == "i8":
+        s_y = W.calibration_scale(ref["y"].astype(np.float32))
+    elif case.out == "u8":
+        s_y, z_y = W.calibration_u8(ref["y"].astype(np.float32))
     # device input
-    kind_in = "f32" if case.dtype == "f32" else "i8"
-    base = _nhwc(L.x) if case.dtype == "f32" else _nhwc(oracle.quantize_activations(L.x, s_x))
-    xin = _wide(rng, base, *case.in_sl, kind_in) if case.in_sl else _dense(base, kind_in)
+    if case.dtype == "f32":
+        base = _nhwc(L.x)
+    elif case.dtype == "i8":
+        base = _nhwc(oracle.quantize_activations(L.x, s_x))
+    else:
+        base = _nhwc(oracle.quantize_activations_u8(L.x, s_x, z_x))
+    xin = _wide(rng, base, *case.in_sl, case.dtype) if case.in_sl else _dense(base, case.dtype, rng)
     # residual buffer (dense rows)
     rbuf = None
     if case.res_sl is not None:
@@ -134,18 +166,19 @@ def prepare(case):
         rbuf = _wide(rng, rb.astype(np.float32) if case.out == "f32" else rb, *case.res_sl, case.out)
     desc = cbs.make_desc(
         case.n, sp.c_in, sp.h, sp.w, sp.c_out, sp.k, sp.stride, sp.pad,
-        cbs.CBS_F32 if case.dtype == "f32" else cbs.CBS_I8, ow + case.extra, float(s_x), bn[4],
+        DTYPES[case.dtype], ow + case.extra, float(s_x), bn[4],
         act=cbs.CBS_ACT_SILU if case.act == "silu" else cbs.CBS_ACT_NONE,
-        out_dtype=cbs.CBS_F32 if case.out == "f32" else cbs.CBS_I8, out_scale=float(s_y),
+        out_dtype=DTYPES[case.out], out_scale=float(s_y),
         in_c_stride=case.in_sl[0] if case.in_sl else 0, in_c_offset=case.in_sl[1] if case.in_sl else 0,
         out_c_stride=case.out_sl[0] if case.out_sl else 0, out_c_offset=case.out_sl[1] if case.out_sl else 0,
         res_c_stride=case.res_sl[0] if case.res_sl else 0, res_c_offset=case.res_sl[1] if case.res_sl else 0,
-        res_scale=float(res_scale))
+        res_scale=float(res_scale), in_zero_point=z_x, out_zero_point=z_y, res_zero_point=res_zp)
     if case.folded:
         layer = cbs.cbs_create_layer_folded(desc, L.w, bn[0], bn[1])
     else:
         layer = cbs.cbs_create_layer(desc, L.w, *bn[:4])
-    return {"L": L, "ref": ref, "s_y": s_y, "xin": xin, "rbuf": rbuf, "layer": layer, "desc": desc}
+    return {"L": L, "ref": ref, "s_x": s_x, "z_x": z_x, "s_y": s_y, "z_y": z_y, "xin": xin, "rbuf": rbuf,
+            "layer": layer, "desc": desc}
 
 
 def out_geometry(case, info):
@@ -165,10 +198,8 @@ def run(case, prep, config=None, splitk=0, stream=None):
     pitch = info["out_row_pitch"]
     ostride, ooff, (c0, c1) = out_geometry(case, info)
     shape = (case.n * sp.oh + 1, pitch, ostride)  # one guard row after the tensor
-    if case.out == "f32":
-        host = np.full(shape, SENT_F32, np.int32)
-    else:
-        host = np.full(shape, SENT_I8, np.int8)
+    fill = {"f32": SENT_F32, "i8": SENT_I8, "u8": SENT_U8}[case.out]
+    host = np.full(shape, fill)
     obuf = torch.from_numpy(host.copy()).to(dev())
     xin = torch.from_numpy(prep["xin"]).to(dev())
     if prep["rbuf"] is not None:
@@ -181,14 +212,13 @@ def run(case, prep, config=None, splitk=0, stream=None):
     # everything outside [rows < N*OH, pixels < OW, channels c0..c1) is untouched
     mask = np.ones(shape, bool)
     mask[: case.n * sp.oh, : sp.ow, c0:c1] = False
-    fill = SENT_F32 if case.out == "f32" else SENT_I8
     bad = int(np.count_nonzero(got[mask] != fill))
     assert bad == 0, "%r: %d elements outside the output slice were written" % (case, bad)
     region = got[: case.n * sp.oh, : sp.ow, c0:c1].reshape(case.n, sp.oh, sp.ow, c1 - c0)
     if case.out == "f32":
         region = region.view(np.float32)
-    if not case.out_sl and c1 - c0 > sp.c_out:  # dense padded channels must be zero
-        assert np.all(region[..., sp.c_out:] == 0), "%r: padded channels not zero" % case
+    if not case.out_sl and c1 - c0 > sp.c_out:  # dense padded channels hold 0 (its code for uint8)
+        assert np.all(region[..., sp.c_out:] == prep["z_y"]), "%r: padded channels not zero" % case
     return region[..., : sp.c_out].transpose(0, 3, 1, 2), got
 
 
@@ -213,14 +243,18 @@ def check(case, prep, got):
         assert not bad.any(), "%r: %d/%d outside tolerance (max err %.3g, worst ratio %.3g)" % (
             case, int(bad.sum()), bad.size, float(err.max()), float((err / eps).max()))
         return 0
-    lo = oracle.requantize(ref["y"] - eps, prep["s_y"]).astype(np.int32)
-    hi = oracle.requantize(ref["y"] + eps, prep["s_y"]).astype(np.int32)
+    if case.out == "i8":
+        lo = oracle.requantize(ref["y"] - eps, prep["s_y"]).astype(np.int32)
+        hi = oracle.requantize(ref["y"] + eps, prep["s_y"]).astype(np.int32)
+    else:
+        lo = oracle.requantize_u8(ref["y"] - eps, prep["s_y"], prep["z_y"]).astype(np.int32)
+        hi = oracle.requantize_u8(ref["y"] + eps, prep["s_y"], prep["z_y"]).astype(np.int32)
     g = got.astype(np.int32)
     bad = (g < lo) | (g > hi)
     assert not bad.any(), "%r: %d/%d codes outside the accepted interval (e.g. got %s want %s..%s)" % (
         case, int(bad.sum()), bad.size, g[bad][:5], lo[bad][:5], hi[bad][:5])
     ambiguous = int(np.count_nonzero(lo != hi))
-    limit = 0.02 if case.dtype == "i8" else 0.5
+    limit = 0.5 if case.dtype == "f32" else 0.02
     assert ambiguous <= limit * g.size, "%r: %d/%d codes within the band: the check is too weak" % (
         case, ambiguous, g.size)
     return ambiguous
@@ -275,6 +309,91 @@ def test_int8_output_equals_quantised_fp32_output():
         assert np.array_equal(qh, codes), "%r: %d codes differ" % (c8, int(np.count_nonzero(qh != codes)))
 
 
+# ------------------------------------------ f2: asymmetric uint8 ----
+
+U8_SHAPES = SHAPES + [W.LayerSpec("f", 3, 16, 34, 30, 3, 2, 1, "uniform"), spec(40, 24, 9, 13, 3, 1),
+                      spec(12, 20, 6, 5, 3, 1)]
+SENT_ACC = np.int32(np.uint32(0xA5A5A5A5).view(np.int32))
+
+
+def run_raw(case, prep):
+    """Raw int32 accumulators [N][OH][pitch][C_out_pad] (plus a guard row); checks the guards."""
+    info = cbs.cbs_layer_info(prep["layer"])
+    sp = case.spec
+    pitch, cpad = info["out_row_pitch"], info["c_out_pad"]
+    shape = (case.n * sp.oh + 1, pitch, cpad)
+    abuf = torch.from_numpy(np.full(shape, SENT_ACC, np.int32)).to(dev())
+    cbs.cbs_run_layer_raw_acc(prep["layer"], torch.from_numpy(prep["xin"]).to(dev()), abuf)
+    torch.cuda.synchronize()
+    got = abuf.cpu().numpy()
+    mask = np.ones(shape, bool)
+    mask[: case.n * sp.oh, : sp.ow, :] = False
+    assert not np.count_nonzero(got[mask] != SENT_ACC), "%r: guard pixels written" % case
+    region = got[: case.n * sp.oh, : sp.ow].reshape(case.n, sp.oh, sp.ow, cpad)
+    assert np.all(region[..., sp.c_out:] == 0), "%r: padded channels not 0" % case
+    return region[..., : sp.c_out].transpose(0, 3, 1, 2)
+
+
+@pytest.mark.parametrize("zx", [None, 0, 255])
+@pytest.mark.parametrize("sp", U8_SHAPES, ids=lambda s: "%d-%d-%dx%d-k%ds%d" % (s.c_in, s.c_out, s.h, s.w, s.k, s.stride))
+def test_u8_accumulators_exact_on_every_config(sp, zx):
+    """The zero-point corrected int32 sums over q - z equal the oracle's bit for bit, border
+    pixels included, through every kernel configuration and split-K 1 and 2."""
+    case = Case(sp, n=2, dtype="u8", seed=40, zx=zx)
+    prep = prepare(case)
+    ran = 0
+    for cfg in range(cbs.cbs_num_configs()):
+        for sk in (1, 2):
+            try:
+                cbs.cbs_layer_set_config(prep["layer"], cfg, sk)
+            except cbs.CbsError as e:
+                assert e.status == cbs.CBS_EUNSUPPORTED
+                continue
+            acc = run_raw(case, prep)
+            bad = acc != prep["ref"]["acc"]
+            assert not bad.any(), "%r config %s sk %d: %d/%d sums differ" % (
+                case, cbs.cbs_config_name(cfg), sk, int(bad.sum()), bad.size)
+            ran += 1
+    assert ran >= 12
+
+
+@pytest.mark.parametrize("act", ["silu", "none"])
+@pytest.mark.parametrize("sp", U8_SHAPES, ids=lambda s: "%d-%d-%dx%d-k%ds%d" % (s.c_in, s.c_out, s.h, s.w, s.k, s.stride))
+def test_u8_input_fp32_output(sp, act):
+    case = Case(sp, n=2, dtype="u8", act=act, seed=41)
+    prep = prepare(case)
+    got, _ = run(case, prep)
+    check(case, prep, got)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "i8", "u8"])
+@pytest.mark.parametrize("sp", U8_SHAPES, ids=lambda s: "%d-%d-%dx%d-k%ds%d" % (s.c_in, s.c_out, s.h, s.w, s.k, s.stride))
+def test_u8_output_codes(sp, dtype):
+    case = Case(sp, n=2, dtype=dtype, out="u8", extra=32, seed=42)
+    prep = prepare(case)
+    got, _ = run(case, prep)
+    check(case, prep, got)
+
+
+def test_u8_output_equals_quantised_fp32_output():
+    """uint8 output codes are exactly the graph-entry uint8 quantiser applied to the same
+    layer's fp32 output (same scale and zero point)."""
+    for sp in U8_SHAPES:
+        c8 = Case(sp, n=1, dtype="u8", out="u8", extra=0, seed=43)
+        p8 = prepare(c8)
+        codes, _ = run(c8, p8)
+        c32 = Case(sp, n=1, dtype="u8", out="f32", extra=0, seed=43)
+        p32 = prepare(c32)
+        y32, _ = run(c32, p32)
+        cp = -(-sp.c_out // 4) * 4
+        yd = torch.from_numpy(np.ascontiguousarray(y32)).to(dev())
+        q = torch.empty(sp.oh * sp.ow * cp, dtype=torch.uint8, device=dev())
+        cbs.cbs_quantize_nhwc_u8(yd, q, float(p8["s_y"]), p8["z_y"], 1, sp.c_out, sp.oh, sp.ow, cp)
+        torch.cuda.synchronize()
+        qh = q.cpu().numpy().reshape(1, sp.oh, sp.ow, -1)[..., : sp.c_out].transpose(0, 3, 1, 2)
+        assert np.array_equal(qh, codes), "%r: %d codes differ" % (c8, int(np.count_nonzero(qh != codes)))
+
+
 # ------------------------------------------------ f1: slices + residual ----
 
 SLICE_CASES = [
@@ -287,7 +406,8 @@ SLICE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode", [("f32", "f32"), ("i8", "f32"), ("i8", "i8"), ("f32", "i8")])
+@pytest.mark.parametrize("mode", [("f32", "f32"), ("i8", "f32"), ("i8", "i8"), ("f32", "i8"), ("u8", "u8"),
+                                  ("u8", "f32"), ("i8", "u8")])
 @pytest.mark.parametrize("idx", range(len(SLICE_CASES)))
 def test_slices_and_residual(idx, mode):
     sp, ins, outs, res = SLICE_CASES[idx]
@@ -297,7 +417,7 @@ def test_slices_and_residual(idx, mode):
     check(case, prep, got)
 
 
-@pytest.mark.parametrize("mode", [("f32", "f32"), ("i8", "i8")])
+@pytest.mark.parametrize("mode", [("f32", "f32"), ("i8", "i8"), ("u8", "u8")])
 def test_fused_options_on_every_config(mode):
     """Input slice + output slice + residual (+ int8 output) through every kernel configuration
     (register-direct, LDS-staged, halo) and, for the direct ones, cross-workgroup split-K."""

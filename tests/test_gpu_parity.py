@@ -98,6 +98,32 @@ def test_quantize_nhwc_i8_bit_exact():
     assert list(out.cpu().numpy()[:10]) == [0, 2, 2, 0, -2, -2, 126, 127, -127, 127]
 
 
+def test_quantize_nhwc_u8_bit_exact():
+    """Asymmetric uint8 graph-entry quantiser: the oracle's codes bit for bit, padded
+    lanes set to the zero point, ties to even before the zero point is added."""
+    rng = np.random.default_rng(2)
+    for n, c, h, w, dist in ((1, 3, 31, 7, "uniform"), (2, 24, 5, 6, "normal"), (1, 64, 9, 9, "normal")):
+        cpad = -(-c // 4) * 4
+        x = (rng.random((n, c, h, w)) if dist == "uniform" else 2 * rng.standard_normal((n, c, h, w)))
+        x = x.astype(np.float32)
+        x.flat[:6] = [1e9, -1e9, 0.0, -0.0, 3.0, -3.0]
+        s_x, z = W.calibration_u8(x)
+        xd = torch.from_numpy(x).to(dev())
+        out = torch.full((n * h * w * cpad,), 77, dtype=torch.uint8, device=dev())
+        cbs.cbs_quantize_nhwc_u8(xd, out, s_x, z, n, c, h, w, cpad)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().reshape(n, h, w, cpad)
+        ref = oracle.quantize_activations_u8(x, s_x, z).transpose(0, 2, 3, 1)
+        assert np.array_equal(got[..., :c], ref), "%d codes differ" % int(np.count_nonzero(got[..., :c] != ref))
+        assert np.all(got[..., c:] == z)
+    # exact ties with s_x = 1 and z = 10: x.5 rounds to even, then + 10, clamped to 0..255
+    x = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -10.5, -11.0, 244.5, 245.5, 300.0], np.float32).reshape(1, 10, 1, 1)
+    out = torch.zeros(12, dtype=torch.uint8, device=dev())
+    cbs.cbs_quantize_nhwc_u8(torch.from_numpy(x).to(dev()), out, 1.0, 10, 1, 10, 1, 1, 12)
+    torch.cuda.synchronize()
+    assert list(out.cpu().numpy()[:10]) == [10, 12, 12, 10, 8, 0, 0, 254, 255, 255]
+
+
 # ----------------------------------------------------------------- FP32 --
 
 @pytest.mark.parametrize("workload", ["single", "ragged", "stem"])

@@ -80,6 +80,16 @@ def _create_status(cbs, **kw):
     (dict(out_dtype=1, out_scale=0.1, res_c_stride=8, res_scale=0.0), "CBS_EINVAL"),
     (dict(n=64, h=512, w=512, c_in=8, in_c_stride=2048), "CBS_EUNSUPPORTED"),
     (dict(n=64, h=512, w=512, res_c_stride=2048), "CBS_EUNSUPPORTED"),
+    # uint8 tensors and zero points
+    (dict(dtype=2, in_scale=0.0), "CBS_EINVAL"), (dict(dtype=2, in_scale=0.1, in_zero_point=256), "CBS_EINVAL"),
+    (dict(dtype=2, in_scale=0.1, in_zero_point=-1), "CBS_EINVAL"),
+    (dict(dtype=1, in_scale=0.1, in_zero_point=3), "CBS_EINVAL"),          # zero point on an int8 input
+    (dict(in_zero_point=3), "CBS_EINVAL"),                                 # ... and on an fp32 input
+    (dict(out_dtype=2, out_scale=0.0), "CBS_EINVAL"), (dict(out_dtype=2, out_scale=0.1, out_zero_point=300), "CBS_EINVAL"),
+    (dict(out_dtype=1, out_scale=0.1, out_zero_point=5), "CBS_EINVAL"),    # zero point on int8 output
+    (dict(out_dtype=2, out_scale=0.1, res_c_stride=8, res_scale=0.1, res_zero_point=256), "CBS_EINVAL"),
+    (dict(out_dtype=2, out_scale=0.1, res_zero_point=4), "CBS_EINVAL"),    # residual zero point, no residual
+    (dict(out_dtype=2, out_scale=0.1, res_c_stride=8, res_scale=0.0), "CBS_EINVAL"),
 ])
 def test_descriptor_rejected(cbs, kw, status):
     st, h, msg = _create_status(cbs, **kw)
@@ -125,6 +135,11 @@ def test_pack_argument_checks(cbs):
     assert cbs.lib.cbs_pack_nhwc_f32(p, p, 1, 3, 4, 4, 6, None) == cbs.CBS_EINVAL    # c_pad % 4
     assert cbs.lib.cbs_quantize_nhwc_i8(p, p, 0.0, 1, 3, 4, 4, 4, None) == cbs.CBS_EINVAL
     assert cbs.lib.cbs_quantize_nhwc_i8(p, p, -1.0, 1, 3, 4, 4, 4, None) == cbs.CBS_EINVAL
+    assert cbs.lib.cbs_quantize_nhwc_u8(p, p, 0.0, 0, 1, 3, 4, 4, 4, None) == cbs.CBS_EINVAL
+    assert cbs.lib.cbs_quantize_nhwc_u8(p, p, 0.1, 256, 1, 3, 4, 4, 4, None) == cbs.CBS_EINVAL
+    assert cbs.lib.cbs_quantize_nhwc_u8(p, p, 0.1, -1, 1, 3, 4, 4, 4, None) == cbs.CBS_EINVAL
+    assert cbs.lib.cbs_quantize_nhwc_u8(None, p, 0.1, 5, 1, 3, 4, 4, 4, None) == cbs.CBS_EINVAL
+    assert cbs.lib.cbs_quantize_nhwc_u8(p, p, 0.1, 5, 1, 3, 4, 4, 2, None) == cbs.CBS_EINVAL
 
 
 def test_last_error_is_thread_local(cbs):
@@ -150,6 +165,9 @@ def test_last_error_is_thread_local(cbs):
     dict(act=1, out_dtype=1, out_scale=0.05),
     dict(c_in=8, in_c_stride=24, in_c_offset=16, c_out=8, out_c_stride=16, out_c_offset=8),
     dict(dtype=1, in_scale=0.1, res_c_stride=8, out_dtype=1, out_scale=0.1, res_scale=0.2),
+    dict(dtype=2, in_scale=0.1, in_zero_point=255, out_dtype=2, out_scale=0.1, out_zero_point=0,
+         res_c_stride=8, res_scale=0.2, res_zero_point=128),
+    dict(dtype=2, in_scale=0.1, in_zero_point=0, out_dtype=1, out_scale=0.1),
 ])
 def test_valid_descriptor_without_device(cbs, kw):
     import torch
