@@ -160,7 +160,9 @@ cbs_status validate(const cbs_conv_desc *d) {
   // the kernels address input and residual with 32-bit buffer offsets below 2^31
   const double in_bytes = in_elems * (d->dtype == CBS_F32 ? 4.0 : 1.0);
   const double res_bytes = res_elems * (d->out_dtype == CBS_F32 ? 4.0 : 1.0);
+  const double out_bytes = out_elems * (d->out_dtype == CBS_F32 ? 4.0 : 1.0);
   if (in_bytes >= 2147483648.0 - 64.0) return fail(CBS_EUNSUPPORTED, "input above 2^31 bytes");
+  if (out_bytes >= 2147483648.0 - 64.0) return fail(CBS_EUNSUPPORTED, "output above 2^31 bytes");
   if (res_bytes >= 2147483648.0 - 64.0) return fail(CBS_EUNSUPPORTED, "residual above 2^31 bytes");
   return CBS_OK;
 }
@@ -357,9 +359,11 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
   if (raw) {
     p.out = out;
     p.out_cs = L->cout_pad;
+    p.out_bytes = (unsigned)((size_t)L->d.n * L->oh * L->pitch * L->cout_pad * 4);
   } else {
     p.out = (char *)out + (size_t)L->d.out_c_offset * esz_out;
     p.out_cs = L->out_cs;
+    p.out_bytes = (unsigned)(((size_t)L->d.n * L->oh * L->pitch * L->out_cs - (size_t)L->d.out_c_offset) * esz_out);
     p.act = L->d.act == CBS_ACT_NONE ? ACT_NONE : ACT_SILU;
     const bool u8_out = L->d.out_dtype == CBS_U8;
     p.out_q = L->d.out_dtype != CBS_F32;
@@ -1007,6 +1011,8 @@ cbs_status cbs_quantize_nhwc_u8(const float *nchw, uint8_t *nhwc, float s_x, int
 cbs_status cbs_run_layer_raw_acc(const cbs_layer *L, const void *in, int32_t *acc, void *stream) {
   if (!L || !in || !acc) return fail(CBS_EINVAL, "run_layer_raw_acc: null layer or buffer");
   if (L->raw_variant < 0) return fail(CBS_EINVAL, "run_layer_raw_acc: not an INT8 layer");
+  if ((double)L->d.n * L->oh * L->pitch * L->cout_pad * 4.0 >= 2147483648.0 - 64.0)
+    return fail(CBS_EUNSUPPORTED, "run_layer_raw_acc: accumulator buffer above 2^31 bytes");
   return launch(L, in, acc, nullptr, stream, true);
 }
 

@@ -83,6 +83,7 @@ struct ConvParams {
   int out_cs;            // output elements between consecutive pixels (cout_pad when dense)
   int res_cs;            // residual elements between consecutive pixels (0: no residual)
   unsigned res_bytes;    // bytes of the residual buffer from res (buffer-load range)
+  unsigned out_bytes;    // bytes of the output buffer from out (buffer-store range)
   int act;               // Act
   int out_q;             // 1: byte output codes q = clamp(rne(fp32(y / out_scale)) + out_zp, out_lo, out_hi)
   float out_scale;       // s_y for byte output
