@@ -417,9 +417,15 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
     halo_lds(L, L->config, &p.halo_bytes, &p.smem_bytes);
   }
   tiles_of(L, L->config, &p.px_tiles, &p.co_tiles);
+  // Workgroup order (see tile_of in conv_kernels.h): pixel tiles inner when
+  // the weights are larger than the input, so that each XCD's L2 fetches only
+  // the weights of its own channel tiles.
+  const double w_total = (double)p.w_bytes, x_total = (double)L->d.n * L->d.h * L->d.w * L->cin_pad * esz_in;
+  p.px_inner = (w_total > x_total && p.co_tiles > 1) ? 1 : 0;
+  p.inner_tiles = p.px_inner ? p.px_tiles : p.co_tiles;
   p.div_ow = make_fastdiv(p.OW);
   p.div_oh = make_fastdiv(p.OH);
-  p.div_cot = make_fastdiv(p.co_tiles);
+  p.div_inner = make_fastdiv(p.inner_tiles);
   p.div_sk = make_fastdiv(p.splitk);
   p.div_tx = make_fastdiv(p.tiles_x);
   p.div_ty = make_fastdiv(p.tiles_y);

@@ -95,9 +95,10 @@ struct ConvParams {
   float res_zp;          //   with 0x80808080 and 128 for int8 codes, 0 and the zero point for uint8
   // ---- pixel-tiled kernels (conv_igemm, conv_lds)
   int M;                 // N*OH*OW output pixels
-  int co_tiles;          // workgroup tiles along output channels
+  int inner_tiles;       // tiles along the inner dimension of the workgroup order
+  int px_inner;          // 1: pixel tiles inner (channel-major order), 0: channel tiles inner
   FastDiv div_ow, div_oh;    // by OW and OH: pixel index -> (n, oh, ow)
-  FastDiv div_cot;           // by co_tiles: workgroup -> (pixel tile, channel tile)
+  FastDiv div_inner;         // by inner_tiles: workgroup -> (outer tile, inner tile)
   // ---- cross-workgroup split-K (conv_igemm)
   float *ws;             // split-K partial tiles (null when splitk == 1)
   unsigned *counters;    // split-K arrival counters, one per output tile (zero between launches)
@@ -114,6 +115,7 @@ struct ConvParams {
   // ---- host only
   int N;
   int px_tiles;          // workgroup tiles along pixels
+  int co_tiles;          // workgroup tiles along output channels
   int smem_bytes;        // conv_halo: dynamic LDS bytes per workgroup
 };
 

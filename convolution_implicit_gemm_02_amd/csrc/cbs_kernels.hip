@@ -18,7 +18,24 @@ static const KernelConfig kConfigs[] = {
 #define X(id, th, tw, name) {4, th * tw / 64, 1, 4, 1, 2, th, tw, name},
     CBS_HALO_CONFIG_LIST(X)
 #undef X
+#define X(id, cb, pb, wco, wpx, wk, pf, name) {cb, pb, wco, wpx, wk, 0, 0, 0, name},
+    CBS_CONFIG_LIST_EXT(X)
+#undef X
 };
+
+// A configuration's id is its index in kConfigs (the launch switch and the
+// tile table refer to it by number): the lists must stay in id order.
+constexpr int kConfigIds[] = {
+#define X(id, ...) id,
+    CBS_CONFIG_LIST(X) CBS_LDS_CONFIG_LIST(X) CBS_HALO_CONFIG_LIST(X) CBS_CONFIG_LIST_EXT(X)
+#undef X
+};
+constexpr bool config_ids_in_order() {
+  for (int i = 0; i < (int)(sizeof(kConfigIds) / sizeof(kConfigIds[0])); i++)
+    if (kConfigIds[i] != i) return false;
+  return sizeof(kConfigIds) == sizeof(kConfigs) / sizeof(kConfigs[0]) * sizeof(int);
+}
+static_assert(config_ids_in_order(), "configuration ids must equal their index in kConfigs");
 
 int num_configs() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
 const KernelConfig &config(int i) { return kConfigs[i]; }

@@ -33,3 +33,13 @@
   X(18, 8, 32, "H.t8x32")                    \
   X(19, 4, 32, "H.t4x32")                    \
   X(20, 2, 64, "H.t2x64")
+
+// More register-direct conv_igemm tiles (ids continue after the halo list, so
+// earlier ids stay valid): 64- and 32-channel x 32-pixel wave tiles and 8-way
+// K splits, for the batch-1 3x3 layers, where every pixel tile re-reads all
+// weights and a wider pixel tile halves that traffic.
+#define CBS_CONFIG_LIST_EXT(X)                \
+  X(21, 4, 2, 1, 1, 4, 4, "c64p32k4")         \
+  X(22, 4, 2, 1, 1, 8, 4, "c64p32k8")         \
+  X(23, 2, 2, 1, 1, 8, 4, "c32p32k8")         \
+  X(24, 4, 1, 1, 1, 8, 4, "c64p16k8")

@@ -164,13 +164,14 @@ template <bool U8>
 __device__ __forceinline__ void pin_tiled_args(ConvParams &p, int &nblocks, bool splitk_args) {
   pin_common_args<U8>(p, nblocks);
   pin_sgpr(p.M);
-  pin_sgpr(p.co_tiles);
+  pin_sgpr(p.inner_tiles);
+  pin_sgpr(p.px_inner);
   pin_sgpr(p.div_ow.magic);
   pin_sgpr(p.div_ow.shift);
   pin_sgpr(p.div_oh.magic);
   pin_sgpr(p.div_oh.shift);
-  pin_sgpr(p.div_cot.magic);
-  pin_sgpr(p.div_cot.shift);
+  pin_sgpr(p.div_inner.magic);
+  pin_sgpr(p.div_inner.shift);
   if (splitk_args) {
     pin_sgpr(p.ws);
     pin_sgpr(p.counters);
@@ -202,6 +203,20 @@ __device__ __forceinline__ void pin_halo_args(ConvParams &p, int &nblocks) {
 
 __device__ __forceinline__ int fdiv(int n, FastDiv f) {
   return (int)((__umulhi((unsigned)n, f.magic) + (unsigned)n) >> f.shift);
+}
+
+// Output tile of a logical workgroup index.  Each XCD runs a contiguous range
+// of logical indices (see the remap in the kernels), so the inner dimension
+// decides what one XCD's L2 shares: with channel tiles inner (the default)
+// an XCD takes a few pixel tiles with all their channel tiles and fetches the
+// whole weight array; with pixel tiles inner it takes a few channel tiles
+// with all pixels and fetches only their weights.  The host picks pixel tiles
+// inner when the weights outweigh the input.
+__device__ __forceinline__ void tile_of(const ConvParams &p, int t, int &px_tile, int &co_tile) {
+  const int outer = fdiv(t, p.div_inner);
+  const int inner = t - outer * p.inner_tiles;
+  px_tile = p.px_inner ? inner : outer;
+  co_tile = p.px_inner ? outer : inner;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, unsigned bytes) {
@@ -363,8 +378,8 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
   const int tile = fdiv(logical, p.div_sk);
   const int split = logical - tile * p.splitk;
-  const int px_tile = fdiv(tile, p.div_cot);
-  const int co_tile = tile - px_tile * p.co_tiles;
+  int px_tile, co_tile;
+  tile_of(p, tile, px_tile, co_tile);
 
   // The 16-pixel blocks of this wave: lane r owns pixel r of each block.
   int pixbase[PB], iy0[PB], ix0[PB], outpix[PB];
@@ -689,8 +704,8 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   const int nb_ = nblocks, bid = blockIdx.x;
   const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
   const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
-  const int px_tile = fdiv(logical, p.div_cot);
-  const int co_tile = logical - px_tile * p.co_tiles;
+  int px_tile, co_tile;
+  tile_of(p, logical, px_tile, co_tile);
 
   // pixels of this thread's activation slots (the same for every stage)
   Pix xpix[NX];
@@ -1075,6 +1090,11 @@ static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t strea
   case id:                  \
     return launch_halo<VAR, th, tw>(p, stream);
     CBS_HALO_CONFIG_LIST(X)
+#undef X
+#define X(id, cb, pb, wco, wpx, wk, pf, name) \
+  case id:                                    \
+    return launch_one<VAR, cb, pb, wco, wpx, wk, pf>(p, stream);
+    CBS_CONFIG_LIST_EXT(X)
 #undef X
     default:
       return hipErrorInvalidValue;
