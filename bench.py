@@ -45,7 +45,8 @@ class ListBench:
     """Device-resident inputs/outputs and created layers for one (dtype, batch).
     out_i8: INT8 layers write int8 codes (the requantising epilogue) instead of
     fp32; the output scale is the layer's own input scale (timing does not
-    depend on the value)."""
+    depend on the value).  CBS_U8: asymmetric uint8 input codes (min/max
+    calibration of each layer's input), fp32 output."""
 
     def __init__(self, cbs, W, torch, dtype, batch, seed=0, out_i8=False):
         self.cbs, self.torch = cbs, torch
@@ -62,6 +63,12 @@ class ListBench:
                                      L.eps)
                 xin = torch.empty(batch * sp.h * sp.w * cpad, dtype=torch.float32, device=dev)
                 cbs.cbs_pack_nhwc_f32(x, xin, batch, sp.c_in, sp.h, sp.w, cpad)
+            elif dtype == cbs.CBS_U8:
+                s_x, z_x = W.calibration_u8(L.x)
+                desc = cbs.make_desc(batch, sp.c_in, sp.h, sp.w, sp.c_out, sp.k, sp.stride, sp.pad, dtype, 0,
+                                     float(s_x), L.eps, in_zero_point=z_x)
+                xin = torch.empty(batch * sp.h * sp.w * cpad, dtype=torch.uint8, device=dev)
+                cbs.cbs_quantize_nhwc_u8(x, xin, s_x, z_x, batch, sp.c_in, sp.h, sp.w, cpad)
             else:
                 s_x = W.calibration_scale(L.x)
                 desc = cbs.make_desc(batch, sp.c_in, sp.h, sp.w, sp.c_out, sp.k, sp.stride, sp.pad, dtype, 0,
@@ -144,6 +151,35 @@ class ListBench:
                 ts.append(e0.elapsed_time(e1) / r)
             res.append(float(np.median(ts)) * 1e3)  # microseconds
         return res
+
+
+    def time_layers_single(self, scratch, reps=9):
+        """Per layer, one launch between two events: the median over `reps` with warm
+        caches (the launch right after the same one), and the median over `reps`
+        with the caches flushed first (a write of the whole `scratch` buffer,
+        larger than the L2 and the 256 MB MALL, outside the events)."""
+        torch, cbs = self.torch, self.cbs
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        warm, cold = [], []
+        for layer, xin, out in zip(self.layers, self.ins, self.outs):
+            tw, tc = [], []
+            for _ in range(reps):
+                cbs.cbs_run_layer(layer, xin, out)
+                e0.record()
+                cbs.cbs_run_layer(layer, xin, out)
+                e1.record()
+                torch.cuda.synchronize()
+                tw.append(e0.elapsed_time(e1))
+                scratch.fill_(1)
+                torch.cuda.synchronize()
+                e0.record()
+                cbs.cbs_run_layer(layer, xin, out)
+                e1.record()
+                torch.cuda.synchronize()
+                tc.append(e0.elapsed_time(e1))
+            warm.append(float(np.median(tw)) * 1e3)
+            cold.append(float(np.median(tc)) * 1e3)
+        return warm, cold
 
 
 class ChainBench:
@@ -236,11 +272,13 @@ def warm_device(torch, seconds=0.5):
     torch.cuda.empty_cache()
 
 
-def layer_rows(bench, us):
-    int8 = bench.dtype == bench.cbs.CBS_I8
+def layer_rows(bench, us, single=None, flushed=None):
+    int8 = bench.dtype != bench.cbs.CBS_F32
     peak = PEAK_INT8 if int8 else PEAK_FP32
     rows = []
-    for sp, info, t in zip(bench.specs, bench.infos, us):
+    single = single or [None] * len(us)
+    flushed = flushed or [None] * len(us)
+    for sp, info, t, t1, tf in zip(bench.specs, bench.infos, us, single, flushed):
         fl, by = info["flops"], info["alg_bytes"]
         t_mfma, t_hbm = fl / peak, by / PEAK_HBM
         bound = "mfma" if t_mfma >= t_hbm else "hbm"
@@ -249,7 +287,8 @@ def layer_rows(bench, us):
                      "us": round(t, 3), "tflops": round(fl / (t * 1e-6) / 1e12, 3),
                      "gbs": round(by / (t * 1e-6) / 1e9, 1), "flops": fl, "alg_bytes": by, "bound": bound,
                      "roof_us": round(roof_us, 3), "frac": round(roof_us / t, 4), "config": info["config_name"],
-                     "grid": info["grid"]})
+                     "grid": info["grid"], "us_single": None if t1 is None else round(t1, 3),
+                     "us_flushed": None if tf is None else round(tf, 3)})
     return rows
 
 
@@ -280,27 +319,70 @@ def measured_traffic(layer):
     return rec["traffic_bytes"]
 
 
-def cpu_baseline(W, max_seconds=30.0):
-    """The oracle (plain C, double accumulation, OpenMP) on the batch-1 FP32 list:
-    every layer in list order until the whole list is done or the time budget
-    runs out; returns TFLOP/s over the layers done."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _time_oracle_list(W, int8, max_seconds):
+    """The oracle on the batch-1 list, layer by layer in list order, until the list is
+    done or the time budget runs out: (layers done, layers, FLOPs done, seconds,
+    seconds per whole list extrapolated by FLOPs)."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
-    done_flops, t_total, done = 0, 0.0, 0
     layers = W.generate("yolo26n", n=1, seed=0)
+    done_flops, t_total, done = 0, 0.0, 0
     for L in layers:
-        t0 = time.perf_counter()
-        oracle.conv_bn_silu_f32(L.x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride, L.spec.pad,
-                                with_bound=False)
+        if int8:
+            s_x = W.calibration_scale(L.x)
+            t0 = time.perf_counter()
+            oracle.conv_bn_act_i8(L.x, s_x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride, L.spec.pad,
+                                  with_bound=False)
+        else:
+            t0 = time.perf_counter()
+            oracle.conv_bn_silu_f32(L.x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride, L.spec.pad,
+                                    with_bound=False)
         t_total += time.perf_counter() - t0
         done_flops += L.spec.flops(1)
         done += 1
         if t_total > max_seconds:
             break
+    list_flops = sum(L.spec.flops(1) for L in layers)
+    return done, len(layers), done_flops, t_total, t_total * list_flops / done_flops
+
+
+def cpu_baseline(W, max_seconds=20.0):
+    """The oracle as it stands (plain C, double accumulation for FP32, exact int32
+    sums for INT8, OpenMP) on the batch-1 list: FP32 with every host core (the
+    reported value), then FP32 with one thread and INT8 with every core, each
+    bounded to `max_seconds` (layers in list order until the list is done)."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env:
+        threads = min(threads, int(env))
+    oracle.set_threads(threads)
+    done, total, flops, sec, per_list = _time_oracle_list(W, False, max_seconds)
     sample = ("yolo26n list, batch 1, FP32, %d of %d layers (%.3f GFLOP), oracle conv+BN+SiLU in double"
-              % (done, len(layers), done_flops / 1e9))
-    return {"value": round(done_flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(t_total, 3), "us_per_list": round(t_total * 1e6 * len(layers) / done, 1)}
+              % (done, total, flops / 1e9))
+    res = {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.get_threads(), "kind": "oracle",
+           "sample": sample, "seconds": round(sec, 3), "us_per_list": round(per_list * 1e6, 1),
+           "cpu_model": cpu_model()}
+    oracle.set_threads(1)
+    done, total, flops, sec, per_list = _time_oracle_list(W, False, max_seconds)
+    res["single_thread"] = {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                            "sample": "FP32, %d of %d layers" % (done, total), "seconds": round(sec, 3),
+                            "us_per_list": round(per_list * 1e6, 1)}
+    oracle.set_threads(threads)
+    done, total, flops, sec, per_list = _time_oracle_list(W, True, max_seconds)
+    res["int8"] = {"value": round(flops / sec / 1e12, 6), "unit": "TOP/s", "cores": oracle.get_threads(),
+                   "sample": "INT8 (exact int32 sums, fp32 output), %d of %d layers" % (done, total),
+                   "seconds": round(sec, 3), "us_per_list": round(per_list * 1e6, 1)}
+    return res
 
 
 def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, splitk=0):
@@ -365,10 +447,13 @@ def main():
         return
 
     warm_device(torch)
+    # written between single launches to flush the L2s and the 256 MB MALL
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     results = {}
     combos = [("f32", cbs.CBS_F32, 1, False)]
     if not args.quick:
-        combos += [("int8", cbs.CBS_I8, 1, False), ("int8out", cbs.CBS_I8, 1, True), ("f32", cbs.CBS_F32, 16, False),
+        combos += [("int8", cbs.CBS_I8, 1, False), ("int8out", cbs.CBS_I8, 1, True), ("uint8", cbs.CBS_U8, 1, False),
+                   ("f32", cbs.CBS_F32, 16, False),
                    ("int8", cbs.CBS_I8, 16, False), ("int8out", cbs.CBS_I8, 16, True)]
     layer_tables = {}
     for name, dt, bs, out_i8 in combos:
@@ -377,18 +462,22 @@ def main():
         ms_graph, wall_graph = b.time_steps(steps, args.warmup, use_graph=True)
         ms_list, _ = b.time_steps(steps, args.warmup, use_graph=False)
         us_layers = b.time_layers()
-        rows = layer_rows(b, us_layers)
+        us_single, us_flushed = b.time_layers_single(scratch)
+        rows = layer_rows(b, us_layers, us_single, us_flushed)
         key = "%s_bs%d" % (name, bs)
         layer_tables[key] = rows
         results[key] = {"ms_per_step": ms_graph, "wall_ms_per_step": wall_graph, "ms_per_step_plain_launches": ms_list,
-                        "flops": b.flops, "rows": rows}
-        log("%s: list %.1f us (graph), %.1f us (plain launches), %.2f T(FL)OP/s, sum of per-layer %.1f us, "
-            "roofline sum %.1f us" % (key, ms_graph * 1e3, ms_list * 1e3, b.flops / (ms_graph * 1e-3) / 1e12,
-                                      sum(us_layers), sum(r["roof_us"] for r in rows)))
+                        "flops": b.flops, "rows": rows, "sum_us_single_launch": round(sum(us_single), 2),
+                        "sum_us_flushed": round(sum(us_flushed), 2)}
+        log("%s: list %.1f us (graph), %.1f us (plain launches), %.2f T(FL)OP/s, sum of per-layer %.1f us "
+            "(single launches %.1f warm, %.1f flushed), roofline sum %.1f us"
+            % (key, ms_graph * 1e3, ms_list * 1e3, b.flops / (ms_graph * 1e-3) / 1e12, sum(us_layers), sum(us_single),
+               sum(us_flushed), sum(r["roof_us"] for r in rows)))
         for r in rows:
-            log("  %-13s %4d->%-4d %4d k%d s%d  %8.2f us  %7.2f TF/s  %7.1f GB/s  roof %6.2f us (%s)  frac %.3f  %s"
-                % (r["layer"], r["c_in"], r["c_out"], r["h_in"], r["k"], r["s"], r["us"], r["tflops"], r["gbs"],
-                   r["roof_us"], r["bound"], r["frac"], r["config"]))
+            log("  %-13s %4d->%-4d %4d k%d s%d  %8.2f us (single %6.2f, flushed %6.2f)  %7.2f TF/s  %7.1f GB/s  "
+                "roof %6.2f us (%s)  frac %.3f  %s"
+                % (r["layer"], r["c_in"], r["c_out"], r["h_in"], r["k"], r["s"], r["us"], r["us_single"],
+                   r["us_flushed"], r["tflops"], r["gbs"], r["roof_us"], r["bound"], r["frac"], r["config"]))
         del b
         torch.cuda.empty_cache()
 
@@ -453,14 +542,16 @@ def main():
                        "gflop_per_step": round(head["flops"] / 1e9, 4)},
             "total_us": round(head["ms_per_step"] * 1e3, 2),
             "total_us_plain_launches": round(head["ms_per_step_plain_launches"] * 1e3, 2),
+            "sum_us_single_launch": head["sum_us_single_launch"], "sum_us_flushed": head["sum_us_flushed"],
             "roofline": roof}
     for key, r in results.items():
         if key == "f32_bs1":
             continue
-        int8 = key.startswith("int8")
+        int8 = key.startswith("int8") or key.startswith("uint8")
         line[key] = {"value": round(r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12, 4),
                      "unit": "TOP/s" if int8 else "TFLOP/s", "total_us": round(r["ms_per_step"] * 1e3, 2),
-                     "total_us_plain_launches": round(r["ms_per_step_plain_launches"] * 1e3, 2)}
+                     "total_us_plain_launches": round(r["ms_per_step_plain_launches"] * 1e3, 2),
+                     "sum_us_single_launch": r["sum_us_single_launch"], "sum_us_flushed": r["sum_us_flushed"]}
     line.update(tuned)
     line.update(chains)
     if not args.no_cpu:

@@ -254,7 +254,8 @@ template <bool X>
 __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buffer_rsrc_t rr, f32x4 z, int opix,
                                                int m, int co0) {
   f32x4 y;
-  if constexpr (!X) {  // plain: SiLU, fp32 store
+  // plain: SiLU, fp32 store (also the general variant's path when no option is set)
+  if (!X || (p.act == ACT_SILU && !p.res_cs && !p.out_q)) {
 #pragma unroll
     for (int i = 0; i < 4; i++) y[i] = silu_f(z[i]);
     store16(p, (unsigned)(opix * p.out_cs + co0) * 4u, y);
@@ -446,7 +447,6 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
         const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
         const unsigned off = v ? (unsigned)(pixbase[b] * p.x_cs + doff) * (unsigned)V::ESIZE : kOutOfRange;
         bb[b] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-        if constexpr (V::U8) bb[b] ^= kU8Flip;
       }
     } else {
 #pragma unroll
@@ -459,7 +459,6 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
           const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
           const unsigned off = v ? (unsigned)(pixbase[b] * p.x_cs + doff) : kOutOfRange;
           bb[b][j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
-          if constexpr (V::U8) bb[b][j] ^= kU8Flip;
         }
       }
     }
@@ -467,25 +466,36 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
 
   // Accumulators start at zero, or (uint8 input) at the zero-point correction
   // in the first K slice of the tile only (the others are summed onto it).
+  // Every wave loads the correction and the others mask it to zero: under a
+  // branch the compiler could no longer count the loads in flight and would
+  // wait for all prefetched steps before the first MFMA.
   Acc acc[CB][PB];
 #pragma unroll
   for (int cb = 0; cb < CB; cb++)
 #pragma unroll
     for (int b = 0; b < PB; b++) acc[cb][b] = Acc{};
   if constexpr (V::U8) {
-    if (wk == 0 && split == 0) {
+    const int keep = (wk == 0 && split == 0) ? -1 : 0;  // wave-uniform
 #pragma unroll
-      for (int b = 0; b < PB; b++) {
-        const int cls = border_class(p, iy0[b], ix0[b]);
+    for (int b = 0; b < PB; b++) {
+      const int cls = border_class(p, iy0[b], ix0[b]);
 #pragma unroll
-        for (int cb = 0; cb < CB; cb++) acc[cb][b] = acc_start<V>(p, cls, (cob0 + cb) * 16 + 4 * g);
-      }
+      for (int cb = 0; cb < CB; cb++) acc[cb][b] = acc_start<V>(p, cls, (cob0 + cb) * 16 + 4 * g) & keep;
     }
   }
 
   // Independent accumulators are interleaved so consecutive MFMAs never wait
-  // on each other's result.
-  auto mma = [&](const Frag(&aa)[CB], const Frag(&bb)[PB]) {
+  // on each other's result.  uint8 codes are flipped here, at their use: a
+  // flip next to the prefetching load would make the wave wait for it there.
+  auto mma = [&](const Frag(&aa)[CB], const Frag(&bb_in)[PB]) {
+    Frag bb[PB];
+#pragma unroll
+    for (int b = 0; b < PB; b++) {
+      if constexpr (V::U8)
+        bb[b] = bb_in[b] ^ kU8Flip;
+      else
+        bb[b] = bb_in[b];
+    }
     if constexpr (!V::I8) {
 #pragma unroll
       for (int j = 0; j < 4; j++)
@@ -663,9 +673,7 @@ __device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu
     const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
     const unsigned off =
         v ? (unsigned)(q.base * p.x_cs + (c.dy * p.W + c.dx) * p.x_cs + c.ci) * (unsigned)V::ESIZE : kOutOfRange;
-    Frag f = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-    if constexpr (V::U8) f ^= kU8Flip;
-    return f;
+    return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
   } else {
     Frag f;
 #pragma unroll
@@ -675,7 +683,6 @@ __device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu
       const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
       const unsigned off = v ? (unsigned)(q.base * p.x_cs + (c.dy * p.W + c.dx) * p.x_cs + c.ci) : kOutOfRange;
       f[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
-      if constexpr (V::U8) f[j] ^= kU8Flip;
     }
     return f;
   }
@@ -767,7 +774,12 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
     for (int i = 0; i < NX; i++) {
       const int j = tid + i * NT;
       const int ks = j / (BMB * 64), pxb = (j >> 6) % BMB;
-      lds[buf][(ks * SB + BNB + pxb) * 64 + lane] = rx[i];
+      // uint8 codes are flipped here, when the stage is written to LDS, not
+      // next to the loads, which are still in flight during the MFMAs
+      if constexpr (V::U8)
+        lds[buf][(ks * SB + BNB + pxb) * 64 + lane] = rx[i] ^ kU8Flip;
+      else
+        lds[buf][(ks * SB + BNB + pxb) * 64 + lane] = rx[i];
     }
   };
 

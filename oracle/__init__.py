@@ -116,6 +116,10 @@ def _load():
             lib.oracle_conv_bn_act_u8.argtypes = [P, F, I, P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, P,
                                                   P, P, P, P, P, P]
             lib.oracle_conv_bn_act_u8.restype = L
+            lib.oracle_set_threads.argtypes = [I]
+            lib.oracle_set_threads.restype = None
+            lib.oracle_get_threads.argtypes = []
+            lib.oracle_get_threads.restype = I
             _lib = lib
     return _lib
 
@@ -256,6 +260,15 @@ def requantize(y, s_y: float) -> np.ndarray:
     the next INT8 layer would get from this layer's fp32 output."""
     y32 = np.asarray(y, dtype=np.float64).astype(np.float32)
     return quantize_activations(y32, s_y)
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (n <= 0: unchanged)."""
+    _load().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().oracle_get_threads())
 
 
 def quantize_activations_u8(x, s_x: float, z: int) -> np.ndarray:

@@ -59,6 +59,7 @@
  * double results follow the written expressions exactly.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -577,3 +578,11 @@ done:
     free(wf); free(bf); free(sw); free(qw); free(qx); free(acc);
     return ovf;
 }
+
+/* Threads used by the parallel loops (for the harness that times the oracle
+ * with all cores and with one); n <= 0 leaves the setting unchanged. */
+void oracle_set_threads(int n) {
+    if (n > 0) omp_set_num_threads(n);
+}
+
+int oracle_get_threads(void) { return omp_get_max_threads(); }
