@@ -303,8 +303,8 @@ __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buf
   }
 }
 
-// uint8 input: the accumulators start at a correction that turns the sum the
-// MFMAs form into the one of the definition.  The gathered operand is q - 128
+// uint8 input: a correction, added to each block's sum over K, turns the sum
+// the MFMAs form into the one of the definition.  The gathered operand is q - 128
 // inside the image and -128 on the padding taps (out-of-range loads read 0,
 // flipped like every other byte), so with Wsum[co] the sum of the channel's
 // int8 weights and Win[co] the sum of its weights on the taps inside the image,
@@ -324,10 +324,12 @@ __device__ __forceinline__ int border_class(const ConvParams &p, int iy0, int ix
   return (int)((rm & kmask) * 8u + (cm & kmask));
 }
 
-// Start value of the accumulator of output channels co0 .. co0+3 at a pixel of
-// border class cls (zero unless the variant has uint8 input).
+// Correction of the accumulator of output channels co0 .. co0+3 at a pixel of
+// border class cls (zero unless the variant has uint8 input).  The kernels
+// fetch it with the epilogue operands and add it once the K slices of the block
+// are summed, so that no MFMA waits for it.
 template <class V>
-__device__ __forceinline__ typename V::Acc acc_start(const ConvParams &p, int cls, int co0) {
+__device__ __forceinline__ typename V::Acc zp_correction(const ConvParams &p, int cls, int co0) {
   if constexpr (V::U8) {
     const __amdgpu_buffer_rsrc_t cr = rsrc(p.corr, (unsigned)(64 * p.co_blocks * 64));
     return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -410,6 +412,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   // Epilogue operands are fetched now, so their latency overlaps the main loop
   // (out-of-range channels read as zero).
   f32x4 ep_bias[CB], ep_dq[CB];
+  Acc ep_corr[CB][PB];  // uint8 input: the zero-point correction of each block
   {
     const __amdgpu_buffer_rsrc_t br =
         __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
@@ -422,6 +425,12 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
       ep_dq[cb] = f32x4{1.f, 1.f, 1.f, 1.f};
       if constexpr (!V::RAW) ep_bias[cb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, off, 0, 0));
       if constexpr (V::I8 && !V::RAW) ep_dq[cb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, off, 0, 0));
+    }
+#pragma unroll
+    for (int b = 0; b < PB; b++) {
+      const int cls = V::U8 ? border_class(p, iy0[b], ix0[b]) : 0;
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++) ep_corr[cb][b] = zp_correction<V>(p, cls, (cob0 + cb) * 16 + 4 * g);
     }
   }
   const int s_begin = split * p.steps_per_split;
@@ -464,25 +473,11 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
     }
   };
 
-  // Accumulators start at zero, or (uint8 input) at the zero-point correction
-  // in the first K slice of the tile only (the others are summed onto it).
-  // Every wave loads the correction and the others mask it to zero: under a
-  // branch the compiler could no longer count the loads in flight and would
-  // wait for all prefetched steps before the first MFMA.
   Acc acc[CB][PB];
 #pragma unroll
   for (int cb = 0; cb < CB; cb++)
 #pragma unroll
     for (int b = 0; b < PB; b++) acc[cb][b] = Acc{};
-  if constexpr (V::U8) {
-    const int keep = (wk == 0 && split == 0) ? -1 : 0;  // wave-uniform
-#pragma unroll
-    for (int b = 0; b < PB; b++) {
-      const int cls = border_class(p, iy0[b], ix0[b]);
-#pragma unroll
-      for (int cb = 0; cb < CB; cb++) acc[cb][b] = acc_start<V>(p, cls, (cob0 + cb) * 16 + 4 * g) & keep;
-    }
-  }
 
   // Independent accumulators are interleaved so consecutive MFMAs never wait
   // on each other's result.  uint8 codes are flipped here, at their use: a
@@ -600,6 +595,15 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
       }
     if (threadIdx.x == 0)
       __hip_atomic_store(gmem<unsigned>(p.counters) + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // uint8 input: the block's sum over all K is complete here (and held by the
+  // wave that finishes it), so the zero-point correction is added once.
+  if constexpr (V::U8) {
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+      for (int b = 0; b < PB; b++) acc[cb][b] += ep_corr[cb][b];
   }
 
   // Epilogue: bias (+ dequant), activation, residual, output conversion in
@@ -785,6 +789,12 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
 
   Acc acc[NB][MB];
 #pragma unroll
+  for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) acc[nb][mb] = Acc{};
+  // uint8 input: zero-point corrections, fetched now and added after the loop
+  Acc ep_corr[NB][MB];
+#pragma unroll
   for (int mb = 0; mb < MB; mb++) {
     int cls = 0;
     if constexpr (V::U8) {
@@ -792,7 +802,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
       cls = border_class(p, q.iy0, q.ix0);
     }
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) acc[nb][mb] = acc_start<V>(p, cls, (co_tile * BNB + wn * NB + nb) * 16 + 4 * g);
+    for (int nb = 0; nb < NB; nb++) ep_corr[nb][mb] = zp_correction<V>(p, cls, (co_tile * BNB + wn * NB + nb) * 16 + 4 * g);
   }
 
   auto compute = [&](int buf) {
@@ -832,6 +842,12 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
     __syncthreads();
   }
 
+  if constexpr (V::U8) {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+      for (int mb = 0; mb < MB; mb++) acc[nb][mb] += ep_corr[nb][mb];
+  }
   const __amdgpu_buffer_rsrc_t rr = rsrc(p.res, p.res_bytes);
 #pragma unroll
   for (int nb = 0; nb < NB; nb++) {
@@ -957,7 +973,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
       cls = border_class(p, (oh0 + pi / TW) * st_ - p.pad, (ow0 + pi % TW) * st_ - p.pad);
     }
 #pragma unroll
-    for (int nb = 0; nb < NBMAX; nb++) acc[nb][mb] = nb < nbl ? acc_start<V>(p, cls, nb * 16 + 4 * g) : Acc{};
+    for (int nb = 0; nb < NBMAX; nb++) acc[nb][mb] = nb < nbl ? zp_correction<V>(p, cls, nb * 16 + 4 * g) : Acc{};
   }
 
   __builtin_amdgcn_s_waitcnt(0);
