@@ -37,9 +37,13 @@
 // More register-direct conv_igemm tiles (ids continue after the halo list, so
 // earlier ids stay valid): 64- and 32-channel x 32-pixel wave tiles and 8-way
 // K splits, for the batch-1 3x3 layers, where every pixel tile re-reads all
-// weights and a wider pixel tile halves that traffic.
+// weights and a wider pixel tile halves that traffic; and 8-step prefetch
+// rings for tiles that run one wave per SIMD, whose loop is bound by the
+// latency of the loads in flight.
 #define CBS_CONFIG_LIST_EXT(X)                \
   X(21, 4, 2, 1, 1, 4, 4, "c64p32k4")         \
   X(22, 4, 2, 1, 1, 8, 4, "c64p32k8")         \
   X(23, 2, 2, 1, 1, 8, 4, "c32p32k8")         \
-  X(24, 4, 1, 1, 1, 8, 4, "c64p16k8")
+  X(24, 4, 1, 1, 1, 8, 4, "c64p16k8")         \
+  X(25, 2, 1, 1, 1, 4, 8, "c32p16k4f8")       \
+  X(26, 4, 1, 1, 1, 4, 8, "c64p16k4f8")

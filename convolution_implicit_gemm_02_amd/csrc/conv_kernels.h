@@ -511,7 +511,12 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   // Main loop: a ring of PF register sets keeps the loads of the next PF K
   // steps of this wave in flight while the MFMAs of the current step run
   // (small layers are latency-bound otherwise).  Loads past the wave's last
-  // step are clamped onto it, so every iteration issues the same loads.
+  // step are clamped onto it, so every round issues the same loads.  The
+  // rounds in which all PF slots hold real steps run their MFMAs with no
+  // condition, and the last, partial round is peeled off: a branch around
+  // each slot's MFMAs stops the compiler from interleaving them with the next
+  // step's loads and address arithmetic, which a lone wave on a SIMD needs to
+  // keep the matrix unit busy (8-12% on the batch-1 3x3 layers).
   {
     const int s0 = s_begin + wk;
     if (s0 < s_end) {
@@ -519,14 +524,17 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
       Frag a[PF][CB], b[PF][PB];
 #pragma unroll
       for (int i = 0; i < PF; i++) load(min(s0 + i * WK, s_last), a[i], b[i]);
-      for (int s = s0; s < s_end; s += PF * WK) {
+      int s = s0;
+      for (; s + (PF - 1) * WK < s_end; s += PF * WK) {
 #pragma unroll
         for (int i = 0; i < PF; i++) {
-          const int si = s + i * WK;
-          if (si < s_end) mma(a[i], b[i]);
-          load(min(si + PF * WK, s_last), a[i], b[i]);
+          mma(a[i], b[i]);
+          load(min(s + (i + PF) * WK, s_last), a[i], b[i]);
         }
       }
+#pragma unroll
+      for (int i = 0; i < PF; i++)
+        if (s + i * WK < s_end) mma(a[i], b[i]);
     }
   }
 
