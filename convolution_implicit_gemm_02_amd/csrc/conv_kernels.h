@@ -842,13 +842,17 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   gload(0);
   sstore(0);
   __syncthreads();
-  for (int st = 0; st < nst; st++) {
-    const bool more = st + 1 < nst;
-    if (more) gload(st + 1);
+  // Every stage but the last fetches the next one while its MFMAs run, with
+  // no condition around the loads (a branch would keep the compiler from
+  // overlapping them, as in conv_igemm); the last stage is peeled off.
+  int st = 0;
+  for (; st + 1 < nst; st++) {
+    gload(st + 1);
     compute(st & 1);
-    if (more) sstore((st + 1) & 1);
+    sstore((st + 1) & 1);
     __syncthreads();
   }
+  compute(st & 1);
 
   if constexpr (V::U8) {
 #pragma unroll
@@ -893,7 +897,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
 // weights straight into LDS with direct-to-LDS buffer loads (out-of-range
 // offsets supply the zero padding), then runs every tap of the convolution
 // from LDS on MFMA.  This is the direct-convolution path for the stem.
-template <int VAR, int TH, int TW, int NBMAX>
+template <int VAR, int TH, int TW, int NBMAX, bool EXACT>
 __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   using V = Var<VAR>;
   using Frag = typename V::Frag;
@@ -901,7 +905,9 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   // NBMAX (1, 2 or 4) bounds the 16-channel output blocks at compile time, so
   // accumulators and epilogue operands take registers only for blocks that can
   // exist: a 16-channel layer keeps a quarter of the 64-channel footprint and
-  // runs at a higher occupancy.
+  // runs at a higher occupancy.  EXACT: the layer has exactly NBMAX blocks, so
+  // the block loops need no run-time bound (a branch in the tap loop would keep
+  // the compiler from overlapping the LDS reads with the MFMAs).
   constexpr int MB = TH * TW / 64;  // 16-pixel blocks per wave (4 waves)
   static_assert(TH * TW % 64 == 0, "tile must split into 4 waves of 16-pixel blocks");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -956,7 +962,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
                                                (unsigned)(base + lane) * 16u, 0, 0, 0);
   }
   // epilogue operands meanwhile
-  const int nbl = p.co_blocks;  // <= NBMAX, uniform
+  const int nbl = EXACT ? NBMAX : p.co_blocks;  // <= NBMAX, uniform
   f32x4 ep_bias[NBMAX], ep_dq[NBMAX];
   {
     const __amdgpu_buffer_rsrc_t br =
@@ -1100,11 +1106,13 @@ static hipError_t launch_halo(const ConvParams &p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.px_tiles;
   const unsigned smem = (unsigned)p.smem_bytes;
   if (p.co_blocks == 1)
-    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 1>), dim3(grid), dim3(256), smem, stream, p);
+    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 1, true>), dim3(grid), dim3(256), smem, stream, p);
   else if (p.co_blocks == 2)
-    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 2>), dim3(grid), dim3(256), smem, stream, p);
+    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 2, true>), dim3(grid), dim3(256), smem, stream, p);
+  else if (p.co_blocks == 4)
+    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 4, true>), dim3(grid), dim3(256), smem, stream, p);
   else
-    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 4>), dim3(grid), dim3(256), smem, stream, p);
+    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 4, false>), dim3(grid), dim3(256), smem, stream, p);
   return hipGetLastError();
 }
 

@@ -312,7 +312,7 @@ def test_int8_output_equals_quantised_fp32_output():
 # ------------------------------------------ f2: asymmetric uint8 ----
 
 U8_SHAPES = SHAPES + [W.LayerSpec("f", 3, 16, 34, 30, 3, 2, 1, "uniform"), spec(40, 24, 9, 13, 3, 1),
-                      spec(12, 20, 6, 5, 3, 1)]
+                      spec(12, 20, 6, 5, 3, 1), spec(20, 36, 10, 9, 3, 1)]  # 36: three 16-channel blocks
 SENT_ACC = np.int32(np.uint32(0xA5A5A5A5).view(np.int32))
 
 
