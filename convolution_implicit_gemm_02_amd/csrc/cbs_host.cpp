@@ -259,8 +259,9 @@ Choice choose(const cbs_layer *L) {
       return {e.config, e.splitk};
   }
   // 2) the cost model.  Cross-workgroup split-K is never picked here: its
-  // agent-scope release (an L2 write-back on a multi-XCD part) costs more than
-  // it saves; only the measured table may select it.
+  // partial-tile round trip through memory costs about a microsecond per
+  // launch, which only a measurement can weigh against the better balance;
+  // only the measured table (or the create-time tuner) may select it.
   Choice best{2, 1};
   double best_cost = 1e300;
   for (int cfg = 0; cfg < num_configs(); cfg++) {
@@ -926,7 +927,7 @@ cbs_status cbs_layer_autotune(cbs_layer *L, const void *in, void *out, const voi
     float best_ms = 1e30f;
     st = CBS_OK;
     for (int cfg = 0; cfg < num_configs() && st == CBS_OK; cfg++) {
-      for (int sk : {1, 2, 4}) {
+      for (int sk : {1, 2, 3, 4}) {
         if (!config_fits(L, cfg, sk)) continue;
         if (sk > 1) {  // cross-workgroup split-K only for grids that leave CUs idle
           int pxt, cot;

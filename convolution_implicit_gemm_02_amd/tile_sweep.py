@@ -24,7 +24,7 @@ DEFAULT_OUT = os.path.join(PKG_DIR, "csrc", "tile_table.inc")
 
 HEADER = """// tile_table.inc -- per-shape kernel configuration chosen by measurement.
 // Written by convolution_implicit_gemm_02_amd/tile_sweep.py from a sweep of
-// every configuration (split-K 1, and 2/4 for the smallest grids) on %s;
+// every configuration (split-K 1, and 2-4 for grids below 256 workgroups) on %s;
 // shapes not listed fall back to the cost model in cbs_host.cpp.
 // Key: (n, c_in, c_out, h, w, k, stride, dtype) -> (config, splitk).
 struct TileEntry {
@@ -102,8 +102,8 @@ def main():
             out = torch.empty(info["out_bytes"] // 4, dtype=torch.float32, device=dev)
             results = []
             for cfg in range(cbs.cbs_num_configs()):
-                for sk in (1, 2, 4):
-                    if sk > 1 and info["grid"] >= 128:
+                for sk in (1, 2, 3, 4):
+                    if sk > 1 and info["grid"] >= 256:
                         continue
                     try:
                         cbs.cbs_layer_set_config(layer, cfg, sk)

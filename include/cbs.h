@@ -260,7 +260,7 @@ int32_t cbs_num_configs(void);
  * Create-time tuning: the vision-rs page's improvement #1 in its intended
  * form ("Improvements" #1: benchmark candidate tiles per unique layer shape,
  * since one fixed tile spans 5 to 556 us across call sites).  Times every
- * kernel configuration that can run this layer (split-K 1, plus 2 and 4 for
+ * kernel configuration that can run this layer (split-K 1, plus 2, 3 and 4 for
  * register-direct configurations whose grid is below 256 workgroups) with
  * `iters` launches each (0 = 20) after two warm-ups, with HIP events on
  * `stream`, on the caller's buffers, and keeps the fastest.  The choice is
