@@ -7,7 +7,7 @@
   * channel slices of input and output (chunk / cat read and written in
     place) and a residual added after the activation;
   * a C3k2-style block chained through slices with no cat, chunk or add
-    kernel, in FP32 and fully in INT8;
+    kernel, in FP32, fully in INT8 and fully in asymmetric uint8;
   * asymmetric uint8 activations with a zero point (input, output and
     residual codes), against the oracle's asymmetric path.
 
@@ -508,18 +508,22 @@ def _build_chain(c, h, n, dtype, seed):
         t2 = f32_layer("b2", u, res=t01[:, half:].astype(np.float64)).astype(np.float32)
         f32_layer("cv2", np.concatenate([t01, t2], axis=1))
         return specs, params, ora, x0, None
-    # INT8 end to end: every tensor is int8 codes; scales calibrated on the oracle's fp32 chain
-    scales = {"x0": W.calibration_scale(x0)}
+    # INT8 (or uint8) end to end: every tensor is codes; scales (and zero points)
+    # calibrated on the oracle's fp32 chain
+    cal = W.calibration_scale if dtype == "i8" else W.calibration_u8
+    scales = {"x0": cal(x0)}
     d = f32_layer("down", x0).astype(np.float32)
-    scales["d"] = W.calibration_scale(d)
+    scales["d"] = cal(d)
     t01 = f32_layer("cv1", d).astype(np.float32)
-    scales["t"] = W.calibration_scale(t01)
+    scales["t"] = cal(t01)
     u = f32_layer("b1", t01[:, half:]).astype(np.float32)
-    scales["u"] = W.calibration_scale(u)
+    scales["u"] = cal(u)
     t2 = f32_layer("b2", u, res=t01[:, half:].astype(np.float64)).astype(np.float32)
     scales["t2"] = scales["t"]  # the cat buffer holds one scale
     y = f32_layer("cv2", np.concatenate([t01, t2], axis=1)).astype(np.float32)
-    scales["y"] = W.calibration_scale(y)
+    scales["y"] = cal(y)
+    if dtype == "u8":
+        return _u8_chain(specs, params, x0, scales, half)
     # the oracle's int8 chain: dequantised codes are the next layer's input
     ora = {}
 
@@ -547,31 +551,68 @@ def _build_chain(c, h, n, dtype, seed):
     return specs, params, ora, x0, scales
 
 
+def _u8_chain(specs, params, x0, scales, half):
+    """The oracle's uint8 chain: scales are (s, z) pairs; dequantised codes are the next
+    layer's input, and the residual is decoded with its own zero point."""
+    ora = {}
+
+    def u8_layer(name, codes, sz_in, sz_out, res_codes=None, sz_res=None):
+        P, sp = params[name], specs[name]
+        s_in, z_in = sz_in
+        xf = ((codes.astype(np.int32) - z_in).astype(np.float32) * np.float32(s_in)).astype(np.float32)
+        res = None
+        if res_codes is not None:
+            res = (res_codes.astype(np.float64) - sz_res[1]) * np.float64(np.float32(sz_res[0]))
+        r = oracle.conv_bn_act_u8(xf, s_in, z_in, P.w, P.gamma, P.beta, P.mean, P.var, P.eps, sp.stride, sp.pad,
+                                  residual=res)
+        assert np.array_equal(oracle.quantize_activations_u8(xf, s_in, z_in), codes)
+        _, bf = oracle.bn_fold(P.w, P.gamma, P.beta, P.mean, P.var, P.eps)
+        r["bias"], r["res"], r["s_y"], r["z_y"] = bf, res, sz_out[0], sz_out[1]
+        r["codes"] = oracle.requantize_u8(r["y"], sz_out[0], sz_out[1])
+        ora[name] = r
+        return r["codes"]
+
+    q0 = oracle.quantize_activations_u8(x0, *scales["x0"])
+    qd = u8_layer("down", q0, scales["x0"], scales["d"])
+    qt01 = u8_layer("cv1", qd, scales["d"], scales["t"])
+    qu = u8_layer("b1", qt01[:, half:], scales["t"], scales["u"])
+    qt2 = u8_layer("b2", qu, scales["u"], scales["t"], res_codes=qt01[:, half:], sz_res=scales["t"])
+    u8_layer("cv2", np.concatenate([qt01, qt2], axis=1), scales["t"], scales["y"])
+    ora["q0"] = q0
+    return specs, params, ora, x0, scales
+
+
 def _create_chain(specs, params, n, dtype, scales, c):
     half = c // 2
-    i8 = dtype == "i8"
-    DT = cbs.CBS_I8 if i8 else cbs.CBS_F32
+    DT = DTYPES[dtype]
     sc = scales or {}
 
-    def mk(name, s_in=0.0, s_out=0.0, **kw):
+    def sz(key):  # (scale, zero point) of a tensor; fp32 tensors have neither
+        v = sc.get(key, (0.0, 0))
+        return v if isinstance(v, tuple) else (v, 0)
+
+    def mk(name, key_in, key_out, res_key=None, **kw):
         sp, P = specs[name], params[name]
+        (s_in, z_in), (s_out, z_out) = sz(key_in), sz(key_out)
+        if res_key is not None:
+            kw.update(res_scale=float(sz(res_key)[0]), res_zero_point=sz(res_key)[1])
         d = cbs.make_desc(n, sp.c_in, sp.h, sp.w, sp.c_out, sp.k, sp.stride, sp.pad, DT, 0, float(s_in), P.eps,
-                          out_dtype=DT, out_scale=float(s_out), **kw)
+                          out_dtype=DT, out_scale=float(s_out), in_zero_point=z_in, out_zero_point=z_out, **kw)
         return cbs.cbs_create_layer(d, P.w, P.gamma, P.beta, P.mean, P.var)
 
     return {
-        "down": mk("down", sc.get("x0", 0), sc.get("d", 0)),
-        "cv1": mk("cv1", sc.get("d", 0), sc.get("t", 0), out_c_stride=3 * half, out_c_offset=0),
-        "b1": mk("b1", sc.get("t", 0), sc.get("u", 0), in_c_stride=3 * half, in_c_offset=half),
-        "b2": mk("b2", sc.get("u", 0), sc.get("t", 0), out_c_stride=3 * half, out_c_offset=2 * half,
-                 res_c_stride=3 * half, res_c_offset=half, res_scale=float(sc.get("t", 0))),
-        "cv2": mk("cv2", sc.get("t", 0), sc.get("y", 0)),
+        "down": mk("down", "x0", "d"),
+        "cv1": mk("cv1", "d", "t", out_c_stride=3 * half, out_c_offset=0),
+        "b1": mk("b1", "t", "u", in_c_stride=3 * half, in_c_offset=half),
+        "b2": mk("b2", "u", "t", res_key="t", out_c_stride=3 * half, out_c_offset=2 * half,
+                 res_c_stride=3 * half, res_c_offset=half),
+        "cv2": mk("cv2", "t", "y"),
     }
 
 
 def _run_chain(layers, x0_dev, n, c, h, dtype, graph_replays=0):
     half = c // 2
-    tdt = torch.int8 if dtype == "i8" else torch.float32
+    tdt = {"f32": torch.float32, "i8": torch.int8, "u8": torch.uint8}[dtype]
     D = torch.empty(n * h * h * c, dtype=tdt, device=dev())
     T = torch.empty(n * h * h * 3 * half, dtype=tdt, device=dev())
     U = torch.empty(n * h * h * half, dtype=tdt, device=dev())
@@ -644,10 +685,21 @@ def test_c3k2_block_int8(c, h, n):
     kernel's code must be the oracle's (up to the rounding-boundary band); elsewhere an
     earlier boundary decision legitimately differs and the output is not compared.  The
     compared fraction must stay high, and the graph replays must equal the eager run."""
-    specs, params, ora, x0, scales = _build_chain(c, h, n, "i8", seed=50 + c)
-    layers = _create_chain(specs, params, n, "i8", scales, c)
+    _check_code_chain(c, h, n, "i8", seed=50 + c)
+
+
+@pytest.mark.parametrize("c,h,n", [(32, 20, 2), (64, 40, 1)])
+def test_c3k2_block_uint8(c, h, n):
+    """The same chain with every tensor asymmetric uint8 codes (own scale and zero
+    point), the residual decoded with the cat buffer's zero point."""
+    _check_code_chain(c, h, n, "u8", seed=60 + c)
+
+
+def _check_code_chain(c, h, n, dtype, seed):
+    specs, params, ora, x0, scales = _build_chain(c, h, n, dtype, seed=seed)
+    layers = _create_chain(specs, params, n, dtype, scales, c)
     q0 = torch.from_numpy(_nhwc(ora["q0"])).to(dev())
-    runs = _run_chain(layers, q0, n, c, h, "i8") + _run_chain(layers, q0, n, c, h, "i8", graph_replays=3)
+    runs = _run_chain(layers, q0, n, c, h, dtype) + _run_chain(layers, q0, n, c, h, dtype, graph_replays=3)
     for out in runs[1:]:
         assert all(np.array_equal(runs[0][k], out[k]) for k in "DTUY"), "graph replay differs from eager steps"
     got = _chain_nchw(runs[0], n, c, h)
@@ -673,8 +725,12 @@ def test_c3k2_block_int8(c, h, n):
         eps = I8_BAND * (np.abs(r["acc"] * r["f"].astype(np.float64)[None, :, None, None]) +
                          np.abs(r["bias"])[None, :, None, None] + np.abs(r["y"]) +
                          (np.abs(r["res"]) if r["res"] is not None else 0)) + 1e-30
-        lo = oracle.requantize(r["y"] - eps, r["s_y"]).astype(np.int32)
-        hi = oracle.requantize(r["y"] + eps, r["s_y"]).astype(np.int32)
+        if dtype == "i8":
+            lo = oracle.requantize(r["y"] - eps, r["s_y"]).astype(np.int32)
+            hi = oracle.requantize(r["y"] + eps, r["s_y"]).astype(np.int32)
+        else:
+            lo = oracle.requantize_u8(r["y"] - eps, r["s_y"], r["z_y"]).astype(np.int32)
+            hi = oracle.requantize_u8(r["y"] + eps, r["s_y"], r["z_y"]).astype(np.int32)
         g = got[name].astype(np.int32)
         cmp = ~touched
         bad = cmp & ((g < lo) | (g > hi))
