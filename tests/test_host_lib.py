@@ -90,6 +90,11 @@ def _create_status(cbs, **kw):
     (dict(out_dtype=2, out_scale=0.1, res_c_stride=8, res_scale=0.1, res_zero_point=256), "CBS_EINVAL"),
     (dict(out_dtype=2, out_scale=0.1, res_zero_point=4), "CBS_EINVAL"),    # residual zero point, no residual
     (dict(out_dtype=2, out_scale=0.1, res_c_stride=8, res_scale=0.0), "CBS_EINVAL"),
+    # one past each limit: 4096 channels, 2^31 - 64 bytes per tensor
+    (dict(c_in=4100, k=1, pad=0), "CBS_EUNSUPPORTED"), (dict(c_out=4100, k=1, pad=0), "CBS_EUNSUPPORTED"),
+    (dict(c_in=16, c_out=16, h=5793, w=5793), "CBS_EUNSUPPORTED"),       # 2147640336 bytes in and out
+    (dict(c_in=16, c_out=16, h=5700, w=5700, out_row_pitch=5888), "CBS_EUNSUPPORTED"),  # output only
+    (dict(c_in=64, c_out=4, h=5793, w=5793, dtype=1, in_scale=0.1), "CBS_EUNSUPPORTED"),  # int8 input bytes
 ])
 def test_descriptor_rejected(cbs, kw, status):
     st, h, msg = _create_status(cbs, **kw)
@@ -168,6 +173,10 @@ def test_last_error_is_thread_local(cbs):
     dict(dtype=2, in_scale=0.1, in_zero_point=255, out_dtype=2, out_scale=0.1, out_zero_point=0,
          res_c_stride=8, res_scale=0.2, res_zero_point=128),
     dict(dtype=2, in_scale=0.1, in_zero_point=0, out_dtype=1, out_scale=0.1),
+    # the limits themselves
+    dict(c_in=4096, c_out=4096, k=1, pad=0), dict(c_in=1024, c_out=64, k=3, pad=1),
+    dict(c_in=16, c_out=16, h=5700, w=5700),                                # 2079360000 bytes in and out
+    dict(c_in=64, c_out=4, h=5792, w=5792, dtype=1, in_scale=0.1),         # 2147024896 int8 input bytes
 ])
 def test_valid_descriptor_without_device(cbs, kw):
     import torch
