@@ -386,34 +386,38 @@ def cpu_baseline(W, max_seconds=20.0):
 
 
 def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, splitk=0):
-    """Run only one layer of the list `launches` times back to back (for a profiler
-    run on exactly that kernel), then a plain device copy of known size (the
-    reference for scaling the profiler's byte counters).  Prints one JSON line."""
+    """Run only one layer of the list (or, for name "all", every layer in list
+    order) `launches` times back to back after 10 warm-up launches, for a
+    profiler run on exactly those kernels; then a plain device copy of known
+    size (the reference for scaling the profiler's byte counters).  Prints one
+    JSON line per layer."""
     b = ListBench(cbs, W, torch, dtype, batch)
-    i = [s.name for s in b.specs].index(name)
-    layer, xin, out = b.layers[i], b.ins[i], b.outs[i]
-    if config is not None:
-        cbs.cbs_layer_set_config(layer, config, splitk)
-        b.infos[i] = cbs.cbs_layer_info(layer)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    cbs.cbs_run_layer_list([layer] * 10, [xin] * 10, [out] * 10)
-    torch.cuda.synchronize()
-    e0.record()
-    cbs.cbs_run_layer_list([layer] * launches, [xin] * launches, [out] * launches)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / launches * 1e3
+    names = [s.name for s in b.specs]
+    for i in range(len(names)) if name == "all" else [names.index(name)]:
+        layer, xin, out = b.layers[i], b.ins[i], b.outs[i]
+        if config is not None:
+            cbs.cbs_layer_set_config(layer, config, splitk)
+            b.infos[i] = cbs.cbs_layer_info(layer)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cbs.cbs_run_layer_list([layer] * 10, [xin] * 10, [out] * 10)
+        torch.cuda.synchronize()
+        e0.record()
+        cbs.cbs_run_layer_list([layer] * launches, [xin] * launches, [out] * launches)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / launches * 1e3
+        info = b.infos[i]
+        print(json.dumps({"layer": names[i], "batch": batch, "dtype": "int8" if dtype else "f32",
+                          "launches": launches, "warmup_launches": 10, "us_per_launch": round(us, 3),
+                          "config": info["config_name"], "grid": info["grid"], "flops": info["flops"],
+                          "alg_bytes": info["alg_bytes"]}), flush=True)
     copy_bytes = 256 << 20
     src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    info = b.infos[i]
-    print(json.dumps({"layer": name, "batch": batch, "dtype": "int8" if dtype else "f32", "launches": launches,
-                      "us_per_launch": round(us, 3), "config": info["config_name"], "grid": info["grid"],
-                      "flops": info["flops"], "alg_bytes": info["alg_bytes"], "copy_bytes_each": copy_bytes,
-                      "copies": 5}), flush=True)
+    print(json.dumps({"copy_bytes_each": copy_bytes, "copies": 5}), flush=True)
 
 
 def main():
@@ -423,7 +427,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true", help="batch-1 FP32 only")
-    ap.add_argument("--only-layer", default=None, help="profile mode: run only this layer of the list")
+    ap.add_argument("--only-layer", default=None, help="profile mode: run only this layer of the list (\"all\": each layer in turn)")
     ap.add_argument("--dtype", default="f32", choices=["f32", "int8"], help="profile mode dtype")
     ap.add_argument("--batch", type=int, default=1, help="profile mode batch")
     ap.add_argument("--launches", type=int, default=200, help="profile mode launches")
