@@ -21,13 +21,16 @@ static const KernelConfig kConfigs[] = {
 #define X(id, cb, pb, wco, wpx, wk, pf, name) {cb, pb, wco, wpx, wk, 0, 0, 0, name},
     CBS_CONFIG_LIST_EXT(X)
 #undef X
+#define X(id, mb, nb, wm, wn, ks, name) {nb, mb, wn, wm, 1, 1, 0, 0, name},
+    CBS_LDS_CONFIG_LIST_EXT(X)
+#undef X
 };
 
 // A configuration's id is its index in kConfigs (the launch switch and the
 // tile table refer to it by number): the lists must stay in id order.
 constexpr int kConfigIds[] = {
 #define X(id, ...) id,
-    CBS_CONFIG_LIST(X) CBS_LDS_CONFIG_LIST(X) CBS_HALO_CONFIG_LIST(X) CBS_CONFIG_LIST_EXT(X)
+    CBS_CONFIG_LIST(X) CBS_LDS_CONFIG_LIST(X) CBS_HALO_CONFIG_LIST(X) CBS_CONFIG_LIST_EXT(X) CBS_LDS_CONFIG_LIST_EXT(X)
 #undef X
 };
 constexpr bool config_ids_in_order() {

@@ -47,3 +47,13 @@
   X(24, 4, 1, 1, 1, 8, 4, "c64p16k8")         \
   X(25, 2, 1, 1, 1, 4, 8, "c32p16k4f8")       \
   X(26, 4, 1, 1, 1, 4, 8, "c64p16k4f8")
+
+// One more LDS-staged tile with a deeper K stage (4 fragment steps per stage
+// instead of 2).  Deeper stages were measured for the int8 batch-16 3x3
+// layers, where a 2-step stage of a 64 x 64 tile is only 128 cycles of MFMA
+// work per wave: 4- and 8-step stages (the latter in 128 KB of LDS) take the
+// same time per K step, so those layers are bound by operand throughput, not
+// by the wait at each stage.  Only the 4-step 64 x 64 tile wins on some shapes
+// (batch-1 and int8 1x1 layers, by up to 4%).
+#define CBS_LDS_CONFIG_LIST_EXT(X)           \
+  X(27, 2, 2, 2, 2, 4, "L.p64c64k4")

@@ -1152,6 +1152,11 @@ static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t strea
     return launch_one<VAR, cb, pb, wco, wpx, wk, pf>(p, stream);
     CBS_CONFIG_LIST_EXT(X)
 #undef X
+#define X(id, mb, nb, wm, wn, ks, name) \
+  case id:                              \
+    return launch_lds<VAR, mb, nb, wm, wn, ks>(p, stream);
+    CBS_LDS_CONFIG_LIST_EXT(X)
+#undef X
     default:
       return hipErrorInvalidValue;
   }
