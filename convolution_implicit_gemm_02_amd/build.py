@@ -76,7 +76,7 @@ def masked_mfma_kernels(text: str, pattern: str):
     return bad
 
 
-def late_argument_loads(text: str, pattern: str):
+def late_argument_loads(text: str, pattern: str, max_rounds: int = 1):
     """Kernels of a device assembly whose kernel-argument reads (scalar loads:
     the conv kernels make no other) cost more than one memory round trip:
     loads issued after a wait for earlier ones, or after the first MFMA (a
@@ -98,7 +98,7 @@ def late_argument_loads(text: str, pattern: str):
             elif "lgkmcnt" in line:
                 pending = False
         early += any(line.startswith("s_load_") for line in body[:first])
-        if rounds > 1 or late:
+        if rounds > max_rounds or late:
             bad.append(name)
     return bad, early
 
@@ -119,6 +119,10 @@ def flat_memory_ops(text: str, pattern: str):
 
 VARIANTS = 12  # kernel variants, one translation unit each (cbs_variant.hip with -DCBS_VAR=n)
 CONV_KERNELS = r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+):"
+# grouped launches read their member's arguments in a second round, at an
+# offset that depends on the first (the group's workgroup ranges)
+GROUP_KERNELS = r"^(_ZN3cbs16conv_igemm_group\w+):"
+GROUP_VARIANTS = (0, 1, 2, 5, 6, 7, 8, 9)  # variants with grouped kernels (not the raw-accumulator hooks)
 
 
 def _jobs() -> int:
@@ -172,6 +176,12 @@ def check_mfma_guards(hipcc: str) -> None:
             raise RuntimeError("argument-load check matched no early scalar loads in %s" % asm)
         late += flagged
         late += ["%s (FLAT access)" % k for k in flat_memory_ops(text, CONV_KERNELS)]
+        ng = len(re.findall(GROUP_KERNELS, text, re.M))
+        if (ng > 0) != (asms.index(asm) in GROUP_VARIANTS):
+            raise RuntimeError("grouped kernels expected exactly in variants %s (%s has %d)" % (GROUP_VARIANTS, asm, ng))
+        bad += masked_mfma_kernels(text, GROUP_KERNELS)
+        late += late_argument_loads(text, GROUP_KERNELS, max_rounds=2)[0]
+        late += ["%s (FLAT access)" % k for k in flat_memory_ops(text, GROUP_KERNELS)]
     if bad:
         raise RuntimeError("MFMA inside an EXEC-masked region in: %s" % ", ".join(bad))
     if late:

@@ -88,6 +88,10 @@ _SIGNATURES = {
                               ctypes.POINTER(_P)]),
     "cbs_graph_launch": (_I, [_P, _P]),
     "cbs_graph_destroy": (None, [_P]),
+    "cbs_group_create": (_I, [ctypes.POINTER(_P), _I, _I, ctypes.POINTER(_P)]),
+    "cbs_group_run": (_I, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
+    "cbs_group_config": (_I, [_P]),
+    "cbs_group_destroy": (None, [_P]),
     "cbs_layer_info": (_I, [_P, ctypes.POINTER(cbs_layer_info_t)]),
     "cbs_layer_set_config": (_I, [_P, _I, _I]),
     "cbs_num_configs": (_I, []),
@@ -152,7 +156,7 @@ class Layer:
     desc: cbs_conv_desc
 
     def __del__(self):
-        if getattr(self, "handle", 0):
+        if getattr(self, "handle", 0) and lib is not None:
             lib.cbs_destroy_layer(self.handle)
             self.handle = 0
 
@@ -241,7 +245,7 @@ class Graph:
         self._keep = keep  # layers and buffers must outlive the graph
 
     def __del__(self):
-        if getattr(self, "handle", 0):
+        if getattr(self, "handle", 0) and lib is not None:
             lib.cbs_graph_destroy(self.handle)
             self.handle = 0
 
@@ -263,6 +267,38 @@ def cbs_graph_destroy(graph: Graph) -> None:
     if graph.handle:
         lib.cbs_graph_destroy(graph.handle)
         graph.handle = 0
+
+
+CBS_GROUP_MAX = 4
+
+
+class Group:
+    """Independent layers run by one launch (a cbs_group*), destroyed on garbage collection."""
+
+    def __init__(self, handle: int, layers):
+        self.handle = handle
+        self._layers = layers  # the layers must outlive the group
+
+    def __del__(self):
+        if getattr(self, "handle", 0) and lib is not None:
+            lib.cbs_group_destroy(self.handle)
+            self.handle = 0
+
+
+def cbs_group_create(layers, config: int = -1) -> Group:
+    h = _P()
+    _check(lib.cbs_group_create(_ptr_array([l.handle for l in layers]), len(layers), config, ctypes.byref(h)),
+           "cbs_group_create")
+    return Group(h.value, list(layers))
+
+
+def cbs_group_run(group: Group, ins, outs, stream=None) -> None:
+    _check(lib.cbs_group_run(group.handle, _ptr_array([_dev_ptr(b) for b in ins]),
+                             _ptr_array([_dev_ptr(b) for b in outs]), _stream(stream)), "cbs_group_run")
+
+
+def cbs_group_config(group: Group) -> int:
+    return lib.cbs_group_config(group.handle)
 
 
 def cbs_layer_info(layer: Layer) -> dict:

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -84,6 +85,24 @@ struct cbs_layer {
 struct cbs_graph {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+};
+
+// Independent layers run by one grouped launch.  The members are kept in
+// grid order (the caller's index of each in `slot`); all share one kernel
+// variant and one register-direct configuration.  Each member has its own
+// cross-workgroup split-K factor, which evens out the K depth of the
+// members' workgroups, with the group's own partial-tile workspace and
+// arrival counters.
+static_assert(cbs::kGroupMax == CBS_GROUP_MAX, "group size limit differs from the header's");
+struct cbs_group {
+  int n = 0;
+  int config = 0;
+  int variant = 0;
+  const cbs_layer *member[cbs::kGroupMax] = {};
+  int slot[cbs::kGroupMax] = {};
+  int splitk[cbs::kGroupMax] = {};
+  float *d_ws[cbs::kGroupMax] = {};
+  unsigned *d_counters[cbs::kGroupMax] = {};
 };
 
 namespace {
@@ -345,7 +364,10 @@ FastDiv make_fastdiv(int d) {
   return f;
 }
 
-ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void *res, bool raw) {
+// Kernel arguments of one launch of layer L with configuration cfg and split-K
+// factor splitk (the layer's own, or a group's).
+ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void *res, bool raw, int cfg,
+                       int splitk) {
   ConvParams p;
   std::memset(&p, 0, sizeof(p));
   const size_t esz_in = L->d.dtype == CBS_F32 ? 4 : 1;
@@ -385,8 +407,8 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
       p.res_bytes = (unsigned)((size_t)L->M * L->res_cs * esz_out - (size_t)L->d.res_c_offset * esz_out);
     }
   }
-  p.ws = L->d_ws;
-  p.counters = L->d_counters;
+  p.ws = splitk > 1 ? L->d_ws : nullptr;
+  p.counters = splitk > 1 ? L->d_counters : nullptr;
   p.N = L->d.n;
   p.H = L->d.h;
   p.W = L->d.w;
@@ -404,20 +426,20 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
   p.cpt_magic = L->cpt_magic;
   p.total_chunks = L->total_chunks;
   p.steps = L->steps;
-  p.splitk = L->splitk;
-  p.steps_per_split = ceil_div(L->steps, L->splitk);
+  p.splitk = splitk;
+  p.steps_per_split = ceil_div(L->steps, splitk);
   p.co_blocks = L->co_blocks;
   p.w_bytes = (unsigned)((size_t)L->co_blocks * L->steps * 64 * 16);
-  const KernelConfig &kc = config(L->config);
+  const KernelConfig &kc = config(cfg);
   if (kc.lds == 2) {
     p.tiles_x = ceil_div(L->ow, kc.tw);
     p.tiles_y = ceil_div(L->oh, kc.th);
     p.halo_cq = halo_cq(L);
     p.div_hcq = make_fastdiv(p.halo_cq);
     p.div_hwd = make_fastdiv((kc.tw - 1) * L->d.stride + 3);
-    halo_lds(L, L->config, &p.halo_bytes, &p.smem_bytes);
+    halo_lds(L, cfg, &p.halo_bytes, &p.smem_bytes);
   }
-  tiles_of(L, L->config, &p.px_tiles, &p.co_tiles);
+  tiles_of(L, cfg, &p.px_tiles, &p.co_tiles);
   // Workgroup order (see tile_of in conv_kernels.h): pixel tiles inner when
   // the weights are larger than the input, so that each XCD's L2 fetches only
   // the weights of its own channel tiles.
@@ -433,8 +455,86 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
   return p;
 }
 
+// Split-K factors of a group's members under configuration cfg: the member
+// with the shallowest K per wave keeps split-K 1, and each deeper member is
+// split (up to 4 ways) towards that depth, so that no member's workgroups run
+// several times longer than the others'.
+void group_splits(const cbs_layer *const *m, int n, int cfg, int *sk) {
+  const KernelConfig &c = config(cfg);
+  double shallowest = 1e300;
+  for (int i = 0; i < n; i++) shallowest = std::min(shallowest, std::ceil((double)m[i]->steps / c.wk));
+  for (int i = 0; i < n; i++) {
+    const double depth = std::ceil((double)m[i]->steps / c.wk);
+    int s = (int)std::lround(depth / shallowest);
+    s = std::max(1, std::min(4, s));
+    while (s > 1 && !config_fits(m[i], cfg, s)) s--;
+    sk[i] = s;
+  }
+}
+
+// Cost of a grouped launch (the model_cost terms): the members' waves share
+// the 1024 SIMDs, and no member's wave can finish before its own K slice.
+double group_cost(const cbs_layer *const *m, int n, int cfg, const int *sk) {
+  const KernelConfig &c = config(cfg);
+  double total = 0.0, longest = 0.0, split_cost = 0.0;
+  for (int i = 0; i < n; i++) {
+    const cbs_layer *L = m[i];
+    int pxt, cot;
+    tiles_of(L, cfg, &pxt, &cot);
+    const double steps_per_wave = std::ceil((double)L->steps / (c.wk * sk[i]));
+    const double mfma_step = L->d.dtype == CBS_F32 ? 4 * 32.0 : 16.0;
+    const double load_step = 40.0 * (c.cb + c.pb);
+    const double per_wave = steps_per_wave * std::max(mfma_step * c.cb * c.pb, load_step) + 1500.0;
+    total += (double)pxt * cot * sk[i] * c.wco * c.wpx * c.wk * per_wave;
+    longest = std::max(longest, per_wave);
+    if (sk[i] > 1) split_cost = 2500.0;
+  }
+  return std::max(total / 1024.0, longest) + split_cost;
+}
+
+// Whether configuration cfg (with split-K factors sk) can run every member of a group.
+bool group_config_fits(const cbs_layer *const *m, int n, int cfg, const int *sk) {
+  if (cfg < 0 || cfg >= num_configs() || config(cfg).lds != 0) return false;
+  double grid = 0.0;
+  for (int i = 0; i < n; i++) {
+    if (!config_fits(m[i], cfg, sk[i])) return false;
+    int pxt, cot;
+    tiles_of(m[i], cfg, &pxt, &cot);
+    grid += (double)pxt * cot * sk[i];
+  }
+  return grid < 2147483647.0;
+}
+
+void group_release(cbs_group *g) {
+  for (int i = 0; i < cbs::kGroupMax; i++) {
+    if (g->d_ws[i]) (void)hipFree(g->d_ws[i]);
+    if (g->d_counters[i]) (void)hipFree(g->d_counters[i]);
+    g->d_ws[i] = nullptr;
+    g->d_counters[i] = nullptr;
+  }
+}
+
+// The partial-tile workspace and zeroed arrival counters of the split members.
+cbs_status group_setup_splitk(cbs_group *g) {
+  const KernelConfig &c = config(g->config);
+  for (int i = 0; i < g->n; i++) {
+    if (g->splitk[i] <= 1) continue;
+    int pxt, cot;
+    tiles_of(g->member[i], g->config, &pxt, &cot);
+    const size_t tiles = (size_t)pxt * cot;
+    const size_t tile_vecs = (size_t)c.wco * c.wpx * c.cb * c.pb * 64;
+    cbs_status st = dev_alloc((void **)&g->d_ws[i], tiles * g->splitk[i] * tile_vecs * 16);
+    if (st == CBS_OK) st = dev_alloc((void **)&g->d_counters[i], tiles * sizeof(unsigned));
+    if (st != CBS_OK) return st;
+    hipError_t e = hipMemset(g->d_counters[i], 0, tiles * sizeof(unsigned));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(CBS_EDEVICE, "group counter init: %s", hipGetErrorString(e));
+  }
+  return CBS_OK;
+}
+
 cbs_status launch(const cbs_layer *L, const void *in, void *out, const void *res, void *stream, bool raw = false) {
-  ConvParams p = make_params(L, in, out, res, raw);
+  ConvParams p = make_params(L, in, out, res, raw, L->config, L->splitk);
   hipError_t e = launch_conv(raw ? L->raw_variant : L->variant, L->config, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(CBS_ELAUNCH, "conv launch: %s", hipGetErrorString(e));
   return CBS_OK;
@@ -709,6 +809,95 @@ cbs_status cbs_run_layer_list(cbs_layer *const *layers, int32_t n, const void *c
     if (st != CBS_OK) return st;
   }
   return CBS_OK;
+}
+
+cbs_status cbs_group_create(cbs_layer *const *layers, int32_t n, int32_t config_id, cbs_group **out) {
+  if (!out) return fail(CBS_EINVAL, "group_create: out is NULL");
+  *out = nullptr;
+  if (!layers || n < 1 || n > kGroupMax)
+    return fail(CBS_EINVAL, "group_create: needs 1 to %d layers (got %d)", kGroupMax, (int)n);
+  for (int32_t i = 0; i < n; i++) {
+    const cbs_layer *L = layers[i];
+    if (!L) return fail(CBS_EINVAL, "group_create: layer %d is NULL", (int)i);
+    if (L->res_cs) return fail(CBS_EUNSUPPORTED, "group_create: layer %d has a residual", (int)i);
+    if (L->variant != layers[0]->variant || L->device != layers[0]->device)
+      return fail(CBS_EUNSUPPORTED, "group_create: layer %d differs from layer 0 in kernel variant (dtype, "
+                                    "input chunking or epilogue) or device", (int)i);
+  }
+  cbs_group *g = new cbs_group;
+  g->n = n;
+  g->variant = layers[0]->variant;
+  // grid order: deepest K first, so that the longest workgroups start first
+  for (int32_t i = 0; i < n; i++) g->slot[i] = i;
+  std::stable_sort(g->slot, g->slot + n, [&](int a, int b) { return layers[a]->steps > layers[b]->steps; });
+  for (int32_t i = 0; i < n; i++) g->member[i] = layers[g->slot[i]];
+  int sk[kGroupMax];
+  if (config_id >= 0) {
+    const bool direct = config_id < num_configs() && config(config_id).lds == 0;
+    if (direct) group_splits(g->member, n, config_id, sk);
+    if (!direct || !group_config_fits(g->member, n, config_id, sk)) {
+      delete g;
+      return fail(CBS_EUNSUPPORTED, "group_create: configuration %d is not a register-direct configuration "
+                                    "that fits every layer", (int)config_id);
+    }
+    g->config = config_id;
+  } else {
+    double best = 1e300;
+    g->config = -1;
+    for (int cfg = 0; cfg < num_configs(); cfg++) {
+      if (config(cfg).lds != 0) continue;
+      group_splits(g->member, n, cfg, sk);
+      if (!group_config_fits(g->member, n, cfg, sk)) continue;
+      const double c = group_cost(g->member, n, cfg, sk);
+      if (c < best * 0.999) {
+        best = c;
+        g->config = cfg;
+      }
+    }
+    if (g->config < 0) {
+      delete g;
+      return fail(CBS_EUNSUPPORTED, "group_create: no register-direct configuration fits every layer");
+    }
+  }
+  group_splits(g->member, n, g->config, g->splitk);
+  cbs_status st = group_setup_splitk(g);
+  if (st != CBS_OK) {
+    group_release(g);
+    delete g;
+    return st;
+  }
+  *out = g;
+  return CBS_OK;
+}
+
+cbs_status cbs_group_run(const cbs_group *group, const void *const *ins, void *const *outs, void *stream) {
+  if (!group || !ins || !outs) return fail(CBS_EINVAL, "group_run: null group or buffer list");
+  GroupArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  long long grid = 0;
+  for (int j = 0; j < kGroupMax; j++) ga.first[j] = INT_MAX;
+  for (int j = 0; j < group->n; j++) {
+    const int i = group->slot[j];
+    const cbs_layer *L = group->member[j];
+    cbs_status st = check_step(L, ins[i], outs[i], nullptr, "group_run", i);
+    if (st != CBS_OK) return st;
+    ga.p[j] = make_params(L, ins[i], outs[i], nullptr, false, group->config, group->splitk[j]);
+    ga.p[j].ws = group->d_ws[j];
+    ga.p[j].counters = group->d_counters[j];
+    ga.first[j] = (int)grid;
+    grid += (long long)ga.p[j].px_tiles * ga.p[j].co_tiles * group->splitk[j];
+  }
+  hipError_t e = launch_conv_group(group->variant, group->config, ga, (unsigned)grid, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(CBS_ELAUNCH, "group launch: %s", hipGetErrorString(e));
+  return CBS_OK;
+}
+
+int32_t cbs_group_config(const cbs_group *group) { return group ? group->config : -1; }
+
+void cbs_group_destroy(cbs_group *group) {
+  if (!group) return;
+  group_release(group);
+  delete group;
 }
 
 cbs_status cbs_run_steps(const cbs_step *steps, int32_t n, void *stream) {

@@ -1,6 +1,7 @@
 // cbs_internal.h -- shared between the host library (cbs_host.cpp) and the
 // kernels (cbs_kernels.hip) of libcbs.  Not part of the public C ABI.
 #pragma once
+#include <cstddef>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -119,6 +120,18 @@ struct ConvParams {
   int smem_bytes;        // conv_halo: dynamic LDS bytes per workgroup
 };
 
+// Arguments of one grouped launch (conv_igemm_group): up to kGroupMax
+// independent layers of one kernel variant, run with one register-direct
+// configuration.  p must stay the first member: the kernel reads p[i] from the
+// start of its argument segment.
+constexpr int kGroupMax = 4;
+struct GroupArgs {
+  ConvParams p[kGroupMax];
+  int first[kGroupMax];  // first logical workgroup of each member (first[0] = 0; INT_MAX for unused slots)
+};
+static_assert(offsetof(GroupArgs, p) == 0, "member parameters must start the argument segment");
+static_assert(sizeof(GroupArgs) <= 4096, "kernel arguments above 4 KB");
+
 int num_configs();
 const KernelConfig &config(int i);
 // Launch variant `var` with configuration `cfg`; returns the hipError_t of the launch.
@@ -136,6 +149,17 @@ hipError_t launch_var_8(int cfg, const ConvParams &p, hipStream_t stream);
 hipError_t launch_var_9(int cfg, const ConvParams &p, hipStream_t stream);
 hipError_t launch_var_10(int cfg, const ConvParams &p, hipStream_t stream);
 hipError_t launch_var_11(int cfg, const ConvParams &p, hipStream_t stream);
+// Grouped launch of variant `var` with register-direct configuration `cfg` over
+// `grid` workgroups (the members' grids end to end).  RAW variants have none.
+hipError_t launch_conv_group(int var, int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream);
+hipError_t launch_group_var_0(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream);
+hipError_t launch_group_var_1(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream);
+hipError_t launch_group_var_2(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream);
+hipError_t launch_group_var_5(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream);
+hipError_t launch_group_var_6(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream);
+hipError_t launch_group_var_7(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream);
+hipError_t launch_group_var_8(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream);
+hipError_t launch_group_var_9(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream);
 
 hipError_t launch_pack_nhwc_f32(const float *x, float *y, int n, int c, int hw, int c_pad,
                                 hipStream_t stream);

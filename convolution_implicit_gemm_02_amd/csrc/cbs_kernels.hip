@@ -61,6 +61,20 @@ hipError_t launch_conv(int var, int cfg, const ConvParams &p, hipStream_t stream
   }
 }
 
+hipError_t launch_conv_group(int var, int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream) {
+  switch (var) {
+    case 0: return launch_group_var_0(cfg, g, grid, stream);
+    case 1: return launch_group_var_1(cfg, g, grid, stream);
+    case 2: return launch_group_var_2(cfg, g, grid, stream);
+    case 5: return launch_group_var_5(cfg, g, grid, stream);
+    case 6: return launch_group_var_6(cfg, g, grid, stream);
+    case 7: return launch_group_var_7(cfg, g, grid, stream);
+    case 8: return launch_group_var_8(cfg, g, grid, stream);
+    case 9: return launch_group_var_9(cfg, g, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // ------------------------------------------------------ graph-entry packs --
 // One thread per (pixel, 4-channel group); consecutive threads take
 // consecutive pixels so the NCHW plane reads are coalesced.

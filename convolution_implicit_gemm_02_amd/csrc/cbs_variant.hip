@@ -13,4 +13,9 @@ namespace cbs {
 hipError_t CBS_PASTE(launch_var_, CBS_VAR)(int cfg, const ConvParams &p, hipStream_t stream) {
   return launch_variant<CBS_VAR>(cfg, p, stream);
 }
+#if CBS_VAR != 3 && CBS_VAR != 4 && CBS_VAR != 10 && CBS_VAR != 11  // not the raw-accumulator test hooks
+hipError_t CBS_PASTE(launch_group_var_, CBS_VAR)(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream) {
+  return launch_group_variant<CBS_VAR>(cfg, g, grid, stream);
+}
+#endif
 }  // namespace cbs

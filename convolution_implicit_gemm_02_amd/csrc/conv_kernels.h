@@ -356,13 +356,25 @@ __device__ __forceinline__ Chunk decode_chunk(const ConvParams &p, int c) {
   return r;
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs; this remaps a
+// workgroup id to a logical tile so that each XCD receives a contiguous range
+// of logical tiles (the co tiles and K splits of one pixel tile then share
+// that XCD's L2).
+__device__ __forceinline__ int xcd_major(int nblocks, int bid) {
+  const int per = nblocks >> 3, rem = nblocks & 7, xcd = bid & 7, loc = bid >> 3;
+  return xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
+}
+
+// Workgroup `bid` of a grid of nblocks runs logical tile
+// xcd_major(nblocks, bid) - first of the layer described by p (its pixel
+// tile, channel tile and K split); first is the layer's first logical tile
+// in a grouped launch, 0 otherwise.
 template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
-__global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) {
+__device__ __forceinline__ void igemm_workgroup(const ConvParams &p, const int nblocks, const int bid,
+                                                const int first) {
   using V = Var<VAR>;
   using Frag = typename V::Frag;
   using Acc = typename V::Acc;
-  int nblocks = gridDim.x;
-  pin_tiled_args<V::U8>(p, nblocks, true);
   const int lane = threadIdx.x & 63;
   // The wave index is made explicitly wave-uniform: every condition that
   // guards an MFMA below depends only on it, so it compiles to a scalar
@@ -374,12 +386,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
   const int slot = wco + WCO * wpx;
   const int r = lane & 15, g = lane >> 4;
 
-  // Workgroups are dispatched round-robin over the 8 XCDs; remap so that each
-  // XCD receives a contiguous range of logical tiles (the co tiles and K
-  // splits of one pixel tile then share that XCD's L2).
-  const int nb = nblocks, bid = blockIdx.x;
-  const int per = nb >> 3, rem = nb & 7, xcd = bid & 7, loc = bid >> 3;
-  const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
+  const int logical = xcd_major(nblocks, bid) - first;
   const int tile = fdiv(logical, p.div_sk);
   const int split = logical - tile * p.splitk;
   int px_tile, co_tile;
@@ -655,6 +662,48 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) 
       }
     }
   }
+}
+
+template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
+__global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm(ConvParams p) {
+  int nblocks = gridDim.x;
+  pin_tiled_args<Var<VAR>::U8>(p, nblocks, true);
+  igemm_workgroup<VAR, CB, PB, WCO, WPX, WK, PF>(p, nblocks, blockIdx.x, 0);
+}
+
+// The parameters of group member i, read from the kernel-argument segment
+// (GroupArgs::p starts it) with scalar loads at a wave-uniform offset.
+__device__ __forceinline__ ConvParams group_member(int i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef const __attribute__((address_space(4))) ConvParams *kernarg_params;
+  return ((kernarg_params)__builtin_amdgcn_kernarg_segment_ptr())[i];
+#else
+  (void)i;  // the host pass of the kernel sources has no kernel-argument segment
+  return ConvParams{};
+#endif
+}
+
+// Several independent layers of one kernel variant in one launch: the grid
+// is the members' grids laid end to end (in the XCD-major logical order), and
+// each workgroup runs the tile of the member its logical index falls in.  The
+// member's parameters are read from the kernel-argument segment at a
+// wave-uniform offset (scalar loads, a second round after ga.first).
+template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
+__global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm_group(GroupArgs ga) {
+  int nblocks = gridDim.x;
+  const int logical = xcd_major(nblocks, blockIdx.x);
+  int member = 0, first = 0;
+#pragma unroll
+  for (int j = 1; j < kGroupMax; j++) {
+    const bool in_later = logical >= ga.first[j];  // unused slots hold INT_MAX
+    member += in_later ? 1 : 0;
+    first = in_later ? ga.first[j] : first;
+  }
+  member = __builtin_amdgcn_readfirstlane(member);
+  first = __builtin_amdgcn_readfirstlane(first);
+  ConvParams p = group_member(member);
+  pin_tiled_args<Var<VAR>::U8>(p, nblocks, true);
+  igemm_workgroup<VAR, CB, PB, WCO, WPX, WK, PF>(p, nblocks, blockIdx.x, first);
 }
 
 
@@ -1126,6 +1175,28 @@ static hipError_t launch_halo(const ConvParams &p, hipStream_t stream) {
   else
     hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 4, false>), dim3(grid), dim3(256), smem, stream, p);
   return hipGetLastError();
+}
+
+template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
+static hipError_t launch_group_one(const GroupArgs &g, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((conv_igemm_group<VAR, CB, PB, WCO, WPX, WK, PF>), dim3(grid), dim3(64 * WCO * WPX * WK), 0,
+                     stream, g);
+  return hipGetLastError();
+}
+
+// Grouped launch of variant VAR with register-direct configuration `cfg`.
+template <int VAR>
+static hipError_t launch_group_variant(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream) {
+  switch (cfg) {
+#define X(id, cb, pb, wco, wpx, wk, pf, name) \
+  case id:                                    \
+    return launch_group_one<VAR, cb, pb, wco, wpx, wk, pf>(g, grid, stream);
+    CBS_CONFIG_LIST(X)
+    CBS_CONFIG_LIST_EXT(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 // Launch configuration `cfg` of variant VAR.

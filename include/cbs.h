@@ -112,6 +112,7 @@ typedef int32_t cbs_status;
 
 typedef struct cbs_layer cbs_layer; /* opaque: one fused conv layer on one device */
 typedef struct cbs_graph cbs_graph; /* opaque: a captured layer list */
+typedef struct cbs_group cbs_group; /* opaque: independent layers run by one launch */
 
 typedef struct cbs_conv_desc {
     int32_t n;             /* batch, >= 1 */
@@ -242,6 +243,46 @@ cbs_status cbs_graph_create_steps(const cbs_step *steps, int32_t n, void *stream
 cbs_status cbs_graph_launch(const cbs_graph *graph, void *stream);
 /* Release a captured list.  NULL is a no-op. */
 void cbs_graph_destroy(cbs_graph *graph);
+
+/*
+ * Grouped launch.  A small layer leaves most of the GPU idle, and every launch
+ * pays a fixed few-microsecond cost that serialised small kernels add up
+ * (vision-rs "YOLO26N Inference Optimisation", "Key observations" 1 and 4).
+ * A group runs up to CBS_GROUP_MAX independent layers -- none reads another's
+ * output, as with the three scales of a detection head -- as one kernel whose
+ * grid is the members' grids end to end, so the small members fill the CUs
+ * the large one leaves idle.
+ *
+ * cbs_group_create: layers[0..n-1], 1 <= n <= CBS_GROUP_MAX, must run the same
+ * kernel variant on the same device: the same dtype; for int8 and uint8 the
+ * same input chunking (C_in_pad, the input channel stride and offset all
+ * multiples of 16, or not); and all with, or all without, an option of the
+ * general epilogue (identity activation, byte output).  No member may have a
+ * residual.  config is a register-direct configuration id (one whose
+ * cbs_config_name starts with "c"), or -1 to let a cost model choose.  Each
+ * member gets its own cross-workgroup split-K factor (1 to 4), which evens out
+ * the K depth of the members' workgroups; the group allocates its own split-K
+ * workspace here, so one group runs from one stream at a time.  The group
+ * keeps pointers to the layers, which must outlive it; their own
+ * configurations are not changed.  Errors: CBS_EINVAL (NULL out or layers, n
+ * out of range, a NULL layer), CBS_EUNSUPPORTED (mixed variants or devices, a
+ * residual, a configuration that is not register-direct or does not fit
+ * every member), CBS_ENOMEM, CBS_EDEVICE.
+ *
+ * cbs_group_run: enqueue the group on `stream`; member i reads ins[i] and
+ * writes outs[i], with the layouts of cbs_run_layer.  No output may overlap
+ * another member's input or output.  It enqueues one kernel and nothing else
+ * (no allocation, copy or synchronisation), so it can be captured into a HIP
+ * graph with the caller's own stream capture.  Errors: CBS_EINVAL (NULL
+ * group or buffers), CBS_ELAUNCH.
+ */
+#define CBS_GROUP_MAX 4
+cbs_status cbs_group_create(cbs_layer *const *layers, int32_t n, int32_t config, cbs_group **out);
+cbs_status cbs_group_run(const cbs_group *group, const void *const *ins, void *const *outs, void *stream);
+/* The configuration id the group runs with (-1 for NULL). */
+int32_t cbs_group_config(const cbs_group *group);
+/* Release a group and its workspace (not its layers).  NULL is a no-op. */
+void cbs_group_destroy(cbs_group *group);
 
 /* Fill *info with the layer's shapes, buffer sizes, work and configuration. */
 cbs_status cbs_layer_info(const cbs_layer *layer, cbs_layer_info_t *info);

@@ -133,6 +133,25 @@ def test_null_arguments(cbs):
     assert cbs.lib.cbs_create_layer(ctypes.byref(d), None, None, None, None, None, None) == cbs.CBS_EINVAL
 
 
+def test_group_argument_checks(cbs):
+    """Grouped launches reject bad arguments before looking at any layer's device."""
+    out = ctypes.c_void_p(5)
+    assert cbs.lib.cbs_group_create(None, 1, -1, ctypes.byref(out)) == cbs.CBS_EINVAL
+    assert out.value is None
+    layers = (ctypes.c_void_p * 5)()
+    assert cbs.lib.cbs_group_create(layers, 1, -1, None) == cbs.CBS_EINVAL          # no out
+    for n in (0, -1, cbs.CBS_GROUP_MAX + 1):
+        assert cbs.lib.cbs_group_create(layers, n, -1, ctypes.byref(out)) == cbs.CBS_EINVAL
+        assert "1 to %d layers" % cbs.CBS_GROUP_MAX in cbs.cbs_last_error()
+    assert cbs.lib.cbs_group_create(layers, 2, -1, ctypes.byref(out)) == cbs.CBS_EINVAL  # NULL layers
+    assert "NULL" in cbs.cbs_last_error()
+    assert out.value is None
+    p = (ctypes.c_void_p * 1)()
+    assert cbs.lib.cbs_group_run(None, p, p, None) == cbs.CBS_EINVAL
+    assert cbs.lib.cbs_group_config(None) == -1
+    cbs.lib.cbs_group_destroy(None)
+
+
 def test_pack_argument_checks(cbs):
     p = ctypes.c_void_p(0x1000)
     assert cbs.lib.cbs_pack_nhwc_f32(None, p, 1, 3, 4, 4, 4, None) == cbs.CBS_EINVAL
