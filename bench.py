@@ -481,58 +481,67 @@ def cpu_model():
     return "unknown"
 
 
-def _time_oracle_list(W, int8, max_seconds):
-    """The oracle on the batch-1 list, layer by layer in list order, until the list is
-    done or the time budget runs out: (layers done, layers, FLOPs done, seconds,
-    seconds per whole list extrapolated by FLOPs)."""
+def _time_oracle_list(W, int8, min_seconds, max_seconds):
+    """The oracle on the batch-1 list, layer by layer in list order, repeated until
+    at least min_seconds of oracle time, or cut short once max_seconds is passed:
+    (layers done, layers per list, FLOPs done, seconds, seconds per whole list
+    extrapolated by FLOPs)."""
     import oracle
     layers = W.generate("yolo26n", n=1, seed=0)
+    scales = [W.calibration_scale(L.x) for L in layers] if int8 else None
     done_flops, t_total, done = 0, 0.0, 0
-    for L in layers:
-        if int8:
-            s_x = W.calibration_scale(L.x)
+    while t_total < min_seconds:
+        for i, L in enumerate(layers):
             t0 = time.perf_counter()
-            oracle.conv_bn_act_i8(L.x, s_x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride, L.spec.pad,
-                                  with_bound=False)
-        else:
-            t0 = time.perf_counter()
-            oracle.conv_bn_silu_f32(L.x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride, L.spec.pad,
-                                    with_bound=False)
-        t_total += time.perf_counter() - t0
-        done_flops += L.spec.flops(1)
-        done += 1
+            if int8:
+                oracle.conv_bn_act_i8(L.x, scales[i], L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride,
+                                      L.spec.pad, with_bound=False)
+            else:
+                oracle.conv_bn_silu_f32(L.x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride, L.spec.pad,
+                                        with_bound=False)
+            t_total += time.perf_counter() - t0
+            done_flops += L.spec.flops(1)
+            done += 1
+            if t_total > max_seconds:
+                break
         if t_total > max_seconds:
             break
     list_flops = sum(L.spec.flops(1) for L in layers)
     return done, len(layers), done_flops, t_total, t_total * list_flops / done_flops
 
 
-def cpu_baseline(W, max_seconds=20.0):
+def _sample(done, total, flops):
+    if done >= total:
+        return "%.1f passes of the %d-layer list (%.2f GFLOP)" % (done / total, total, flops / 1e9)
+    return "%d of %d layers (%.3f GFLOP)" % (done, total, flops / 1e9)
+
+
+def cpu_baseline(W, min_seconds=10.0, max_seconds=20.0):
     """The oracle as it stands (plain C, double accumulation for FP32, exact int32
     sums for INT8, OpenMP) on the batch-1 list: FP32 with every host core (the
-    reported value), then FP32 with one thread and INT8 with every core, each
-    bounded to `max_seconds` (layers in list order until the list is done)."""
+    reported value), then FP32 with one thread and INT8 with every core.  Each
+    leg repeats the list for at least `min_seconds` of oracle time and stops
+    once it passes `max_seconds` (mid-list if need be; a partial list is
+    extrapolated by FLOPs)."""
     import oracle
     threads = len(os.sched_getaffinity(0))
     env = os.environ.get("OMP_NUM_THREADS")
     if env:
         threads = min(threads, int(env))
     oracle.set_threads(threads)
-    done, total, flops, sec, per_list = _time_oracle_list(W, False, max_seconds)
-    sample = ("yolo26n list, batch 1, FP32, %d of %d layers (%.3f GFLOP), oracle conv+BN+SiLU in double"
-              % (done, total, flops / 1e9))
+    done, total, flops, sec, per_list = _time_oracle_list(W, False, min_seconds, max_seconds)
     res = {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.get_threads(), "kind": "oracle",
-           "sample": sample, "seconds": round(sec, 3), "us_per_list": round(per_list * 1e6, 1),
-           "cpu_model": cpu_model()}
+           "sample": "yolo26n list, batch 1, FP32, oracle conv+BN+SiLU in double: " + _sample(done, total, flops),
+           "seconds": round(sec, 3), "us_per_list": round(per_list * 1e6, 1), "cpu_model": cpu_model()}
     oracle.set_threads(1)
-    done, total, flops, sec, per_list = _time_oracle_list(W, False, max_seconds)
+    done, total, flops, sec, per_list = _time_oracle_list(W, False, min_seconds, max_seconds)
     res["single_thread"] = {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-                            "sample": "FP32, %d of %d layers" % (done, total), "seconds": round(sec, 3),
+                            "sample": "FP32: " + _sample(done, total, flops), "seconds": round(sec, 3),
                             "us_per_list": round(per_list * 1e6, 1)}
     oracle.set_threads(threads)
-    done, total, flops, sec, per_list = _time_oracle_list(W, True, max_seconds)
+    done, total, flops, sec, per_list = _time_oracle_list(W, True, min_seconds, max_seconds)
     res["int8"] = {"value": round(flops / sec / 1e12, 6), "unit": "TOP/s", "cores": oracle.get_threads(),
-                   "sample": "INT8 (exact int32 sums, fp32 output), %d of %d layers" % (done, total),
+                   "sample": "INT8 (exact int32 sums, fp32 output): " + _sample(done, total, flops),
                    "seconds": round(sec, 3), "us_per_list": round(per_list * 1e6, 1)}
     return res
 
