@@ -1078,7 +1078,12 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
       if (!c.ok) c.dy = c.dx = c.ci = 0;  // past K: read a valid slot, then zero it
 #pragma unroll
       for (int mb = 0; mb < MB; mb++) {
-        Frag v = *(const Frag *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci * V::ESIZE);
+        // 16-byte aligned (pixels are whole 16-byte slots and a chunk starts a
+        // slot): said explicitly, so the read is one ds_read_b128, whose lanes
+        // the slot padding spreads over distinct banks, and not two 8-byte
+        // reads, which it does not
+        Frag v = *(const Frag *)__builtin_assume_aligned(
+            smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci * V::ESIZE, 16);
         if constexpr (V::U8) v ^= kU8Flip;  // zero-filled padding becomes -128, as in conv_igemm
         b[mb] = c.ok ? v : Frag{};
       }
