@@ -96,19 +96,24 @@ def make_members(specs, dtype, out, n=1, seed=80):
     return [Member(Case(sp, n=n, dtype=dtype, out=out, extra=5, seed=seed + i)) for i, sp in enumerate(specs)]
 
 
+@pytest.mark.parametrize("n", [1, 16])
 @pytest.mark.parametrize("dtype,out", [("f32", "f32"), ("i8", "f32"), ("i8", "i8"), ("u8", "u8")])
 @pytest.mark.parametrize("which", ["head3x3", "head1x1"])
-def test_detection_head_group(which, dtype, out):
+def test_detection_head_group(which, dtype, out, n):
+    """The head's three scales at full size, batch 1 and 16 (the shapes the list step groups),
+    with the cost model's configuration and with c64p128, which the batch-16 list picks."""
     specs = HEAD_3X3 if which == "head3x3" else HEAD_1X1
-    members = make_members(specs, dtype, out)
+    members = make_members(specs, dtype, out, n=n)
     singles = [m.single() for m in members]
-    group = cbs.cbs_group_create([m.layer for m in members])
-    assert cbs.cbs_config_name(cbs.cbs_group_config(group)).startswith("c")
-    got = run_group(group, members)
-    for m, g, s in zip(members, got, singles):
-        check(m.case, m.prep, g)
-        if dtype != "f32":
-            assert np.array_equal(g, s), "%r: group output differs from the single launch" % m.case
+    names = [cbs.cbs_config_name(i) for i in range(cbs.cbs_num_configs())]
+    for cfg in (-1, names.index("c64p128")):
+        group = cbs.cbs_group_create([m.layer for m in members], cfg)
+        assert cbs.cbs_config_name(cbs.cbs_group_config(group)).startswith("c")
+        got = run_group(group, members)
+        for m, g, s in zip(members, got, singles):
+            check(m.case, m.prep, g)
+            if dtype != "f32":
+                assert np.array_equal(g, s), "%r: group output differs from the single launch" % m.case
 
 
 @pytest.mark.parametrize("dtype", ["f32", "i8", "u8"])
