@@ -34,6 +34,25 @@ def test_header_symbols_exported(cbs):
     assert set(names) <= set(cbs._SIGNATURES)
 
 
+@pytest.mark.parametrize("lang,std", [("c", "c99"), ("c++", "c++11")])
+def test_header_compiles_standalone(tmp_path, lang, std):
+    """include/cbs.h is a self-contained C99 / C++11 header (no HIP or torch types)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "cbs.h"\n'
+                   "int main(void) {\n"
+                   "  cbs_conv_desc d = {0}; cbs_layer_info_t i; cbs_step s = {0};\n"
+                   "  (void)d; (void)i; (void)s;\n"
+                   "  return CBS_GROUP_MAX == 4 ? 0 : 1;\n"
+                   "}\n")
+    subprocess.run([cc, "-std=" + std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only", "-x", lang,
+                    "-I", os.path.dirname(HEADER), str(src)], check=True)
+
+
 def test_configs_listed(cbs):
     n = cbs.cbs_num_configs()
     assert n >= 4
