@@ -44,10 +44,11 @@ def test_header_compiles_standalone(tmp_path, lang, std):
         pytest.skip("no host compiler")
     src = tmp_path / "use_header.c"
     src.write_text('#include "cbs.h"\n'
+                   "#include <string.h>\n"
                    "int main(void) {\n"
-                   "  cbs_conv_desc d = {0}; cbs_layer_info_t i; cbs_step s = {0};\n"
-                   "  (void)d; (void)i; (void)s;\n"
-                   "  return CBS_GROUP_MAX == 4 ? 0 : 1;\n"
+                   "  cbs_conv_desc d; cbs_layer_info_t i; cbs_step s;\n"
+                   "  memset(&d, 0, sizeof d); memset(&i, 0, sizeof i); memset(&s, 0, sizeof s);\n"
+                   "  return CBS_GROUP_MAX == 4 && d.n == 0 && i.grid == 0 && s.layer == NULL ? 0 : 1;\n"
                    "}\n")
     subprocess.run([cc, "-std=" + std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only", "-x", lang,
                     "-I", os.path.dirname(HEADER), str(src)], check=True)
