@@ -57,3 +57,13 @@
 // (batch-1 and int8 1x1 layers, by up to 4%).
 #define CBS_LDS_CONFIG_LIST_EXT(X)           \
   X(27, 2, 2, 2, 2, 4, "L.p64c64k4")
+
+// LDS-staged tiles filled by direct-to-LDS loads through a ring of NS stage
+// buffers (NS - 1 stages in flight): id, MB, NB, WM, WN, KS, NS, name.
+#define CBS_LDS_RING_CONFIG_LIST(X)             \
+  X(28, 2, 2, 2, 2, 2, 3, "R.p64c64k2s3")       \
+  X(29, 2, 2, 2, 2, 2, 4, "R.p64c64k2s4")       \
+  X(30, 2, 2, 2, 2, 1, 4, "R.p64c64k1s4")       \
+  X(31, 2, 4, 2, 2, 1, 4, "R.p64c128k1s4")      \
+  X(32, 4, 2, 2, 2, 1, 4, "R.p128c64k1s4")      \
+  X(33, 2, 2, 2, 1, 2, 4, "R.p64c32k2s4")

@@ -709,11 +709,26 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm_group(GroupArg
 
 // ------------------------------------------------------ LDS-staged kernel --
 // The workgroup stages KS K-steps of weight and activation fragments in LDS
-// (double-buffered, same fragment order and branch-free buffer loads as
-// above); its WM x WN waves split the output tile and read their operands
-// from LDS, so each fetched byte feeds several waves.  Used for the larger
-// (batch-16, 80x80 and up) layers, where the register-direct kernel is bound
-// by vector-memory issue rather than by MFMA.
+// (same fragment order and branch-free buffer loads as above); its WM x WN
+// waves split the output tile and read their operands from LDS, so each
+// fetched byte feeds several waves.  Used for the larger (batch-16, 80x80 and
+// up) layers, where the register-direct kernel is bound by vector-memory issue
+// rather than by MFMA.
+//
+// Two ways to fill a stage:
+//   NS == 0: loads into registers, written to the other of two LDS buffers
+//            after the current stage's MFMAs (the loads of one stage ahead are
+//            in flight during the MFMAs);
+//   NS >= 2: direct-to-LDS buffer loads into a ring of NS buffers, NS - 1
+//            stages ahead.  A fragment of one wave is 64 lanes x 16 bytes laid
+//            out lane after lane, which is exactly what a 16-byte load to LDS
+//            writes, so the data never passes through registers: no staging
+//            registers, no LDS writes, and the loads of several stages are in
+//            flight at once.  Out-of-range offsets write zeros, as the
+//            register loads read them.  Only variants with one 16-byte chunk
+//            per lane can do this (the 4-byte gather of the small-channel
+//            int8 variants needs a lane stride of 16 bytes in LDS); the others
+//            take the register path whatever NS says.
 
 struct Pix {
   int base, iy0, ix0, out;
@@ -735,18 +750,24 @@ __device__ __forceinline__ Pix pixel_of(const ConvParams &p, int m) {
   return q;
 }
 
+// Byte offset of the 16-byte activation fragment of one lane (one chunk per
+// lane, VEC == 1): pixel q, K chunk `cg` (= 4*step + g); out of range (read as
+// zeros) in the image's zero padding, past K and past the last pixel.
+template <class V>
+__device__ __forceinline__ unsigned gather_off(const ConvParams &p, const Pix &q, int cg) {
+  const Chunk c = decode_chunk(p, cg);
+  const int iy = q.iy0 + c.dy, ix = q.ix0 + c.dx;
+  const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
+  return v ? (unsigned)(q.base * p.x_cs + (c.dy * p.W + c.dx) * p.x_cs + c.ci) * (unsigned)V::ESIZE : kOutOfRange;
+}
+
 // The activation fragment of one lane: pixel q, K chunk group `cg` (= 4*step + g).
 template <class V>
 __device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu_buffer_rsrc_t xr, const Pix &q,
                                                    int cg) {
   using Frag = typename V::Frag;
   if constexpr (V::VEC == 1) {
-    const Chunk c = decode_chunk(p, cg);
-    const int iy = q.iy0 + c.dy, ix = q.ix0 + c.dx;
-    const bool v = c.ok && q.ok && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
-    const unsigned off =
-        v ? (unsigned)(q.base * p.x_cs + (c.dy * p.W + c.dx) * p.x_cs + c.ci) * (unsigned)V::ESIZE : kOutOfRange;
-    return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, gather_off<V>(p, q, cg), 0, 0));
   } else {
     Frag f;
 #pragma unroll
@@ -761,7 +782,33 @@ __device__ __forceinline__ typename V::Frag gather(const ConvParams &p, __amdgpu
   }
 }
 
-template <int VAR, int MB, int NB, int WM, int WN, int KS>
+// s_waitcnt with vmcnt = n and the LDS/scalar counter at 0 (expcnt left
+// alone), in the gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier that waits only for what the caller waited for: a
+// __syncthreads() would also wait for every vector-memory load of the wave,
+// including the direct-to-LDS loads of the stages still in flight.  The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 16-byte direct-to-LDS buffer load per lane: lane l's 16 bytes land at
+// dst + 16 l (dst wave-uniform).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void *dst, unsigned off) {
+  typedef __attribute__((address_space(3))) void *lds_ptr;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, off, 0, 0, 0);
+}
+
+template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS>
 __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   using V = Var<VAR>;
   using Frag = typename V::Frag;
@@ -774,7 +821,9 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   constexpr int NA = KS * BNB * 64 / NT;          // weight slots per thread per stage
   constexpr int NX = KS * BMB * 64 / NT;          // activation slots per thread per stage
   static_assert((KS * BNB * 64) % NT == 0 && (KS * BMB * 64) % NT == 0, "stage must split evenly over threads");
-  __shared__ Frag lds[2][KS * SB * 64];
+  constexpr bool DMA = NS >= 2 && V::VEC == 1;    // direct-to-LDS ring (see above)
+  constexpr int NBUF = DMA ? NS : 2;
+  __shared__ Frag lds[NBUF][KS * SB * 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (see conv_igemm)
@@ -816,7 +865,33 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
   const int nst = (p.steps + KS - 1) / KS;
 
-  Frag ra[NA], rx[NX];
+  // Direct-to-LDS issue of stage st into buffer buf: every thread issues
+  // exactly NA + NX loads (stages past the end load zeros), so the number of
+  // loads in flight per stage is a compile-time constant.  Slot i of a
+  // thread is fragment block (j >> 6) of the stage, j = tid + i * NT, which is
+  // wave-uniform: the LDS destination of each load is one wave-uniform base,
+  // to which the hardware adds lane * 16.
+  auto dma_issue = [&](int st, int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; i++) {
+      const int jw = wave + i * (NT / 64);
+      const int ks = jw / BNB, blk = jw % BNB;
+      const int s = st * KS + ks;
+      const unsigned off = s < p.steps
+                               ? ((unsigned)((co_tile * BNB + blk) * p.steps + s) * 64u + (unsigned)lane) * 16u
+                               : kOutOfRange;
+      load_lds16(wr, &lds[buf][(ks * SB + blk) * 64], off);
+    }
+#pragma unroll
+    for (int i = 0; i < NX; i++) {
+      const int jw = wave + i * (NT / 64);
+      const int ks = jw / BMB, pxb = jw % BMB;
+      const int s = st * KS + ks;
+      load_lds16(xr, &lds[buf][(ks * SB + BNB + pxb) * 64], gather_off<V>(p, xpix[i], s * 4 + g));
+    }
+  };
+
+  Frag ra[DMA ? 1 : NA], rx[DMA ? 1 : NX];
   auto gload = [&](int st) {
 #pragma unroll
     for (int i = 0; i < NA; i++) {
@@ -881,7 +956,12 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) a[nb] = lds[buf][(ks * SB + wn * NB + nb) * 64 + lane];
 #pragma unroll
-      for (int mb = 0; mb < MB; mb++) b[mb] = lds[buf][(ks * SB + BNB + wm * MB + mb) * 64 + lane];
+      for (int mb = 0; mb < MB; mb++) {
+        b[mb] = lds[buf][(ks * SB + BNB + wm * MB + mb) * 64 + lane];
+        // uint8 codes reach the direct-to-LDS ring unflipped (zeros where the
+        // loads were out of range, which become -128 like every padding code)
+        if constexpr (DMA && V::U8) b[mb] ^= kU8Flip;
+      }
       if constexpr (!V::I8) {
 #pragma unroll
         for (int jj = 0; jj < 4; jj++)
@@ -900,20 +980,48 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
     }
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  // Every stage but the last fetches the next one while its MFMAs run, with
-  // no condition around the loads (a branch would keep the compiler from
-  // overlapping them, as in conv_igemm); the last stage is peeled off.
-  int st = 0;
-  for (; st + 1 < nst; st++) {
-    gload(st + 1);
-    compute(st & 1);
-    sstore((st + 1) & 1);
+  if constexpr (DMA) {
+    // Ring of NS buffers: stages st + 1 .. st + NS - 2 stay in flight while
+    // stage st is waited for.  Per iteration: wait until at most (NS - 2)
+    // stages of this thread's loads are outstanding (loads complete in
+    // order, so stage st has landed) and until this wave's LDS reads are done,
+    // then a barrier (every wave's part of stage st has landed, and every wave
+    // has finished reading the buffer the next issue overwrites, which held
+    // stage st - 1), then issue stage st + NS - 1, then the MFMAs of stage st.
+    constexpr int L = NA + NX;
+#pragma unroll
+    for (int i = 0; i < NS - 1; i++) dma_issue(i, i);
+    int st = 0, buf = 0;
+    for (; st + NS - 1 < nst; st++) {
+      wait_vm_lgkm0<(NS - 2) * L>();
+      lds_barrier();
+      dma_issue(st + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+      compute(buf);
+      buf = buf == NS - 1 ? 0 : buf + 1;
+    }
+    // the last NS - 1 stages (or all, for short K): nothing more is issued
+    wait_vm_lgkm0<0>();
+    lds_barrier();
+    for (; st < nst; st++) {
+      compute(buf);
+      buf = buf == NS - 1 ? 0 : buf + 1;
+    }
+  } else {
+    gload(0);
+    sstore(0);
     __syncthreads();
+    // Every stage but the last fetches the next one while its MFMAs run, with
+    // no condition around the loads (a branch would keep the compiler from
+    // overlapping them, as in conv_igemm); the last stage is peeled off.
+    int st = 0;
+    for (; st + 1 < nst; st++) {
+      gload(st + 1);
+      compute(st & 1);
+      sstore((st + 1) & 1);
+      __syncthreads();
+    }
+    compute(st & 1);
   }
-  compute(st & 1);
 
   if constexpr (V::U8) {
 #pragma unroll
@@ -1158,11 +1266,11 @@ static hipError_t launch_one(const ConvParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int VAR, int MB, int NB, int WM, int WN, int KS>
+template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS = 0>
 static hipError_t launch_lds(const ConvParams &p, hipStream_t stream) {
   if (p.splitk != 1) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)p.px_tiles * (unsigned)p.co_tiles;
-  hipLaunchKernelGGL((conv_lds<VAR, MB, NB, WM, WN, KS>), dim3(grid), dim3(64 * WM * WN), 0, stream, p);
+  hipLaunchKernelGGL((conv_lds<VAR, MB, NB, WM, WN, KS, NS>), dim3(grid), dim3(64 * WM * WN), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1232,6 +1340,11 @@ static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t strea
   case id:                              \
     return launch_lds<VAR, mb, nb, wm, wn, ks>(p, stream);
     CBS_LDS_CONFIG_LIST_EXT(X)
+#undef X
+#define X(id, mb, nb, wm, wn, ks, ns, name) \
+  case id:                                  \
+    return launch_lds<VAR, mb, nb, wm, wn, ks, ns>(p, stream);
+    CBS_LDS_RING_CONFIG_LIST(X)
 #undef X
     default:
       return hipErrorInvalidValue;

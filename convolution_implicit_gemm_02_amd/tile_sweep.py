@@ -8,6 +8,12 @@ fixed tile spans 5 to 556 us across the call sites.  This is that step, done
 once per device generation, offline, with the result compiled into the library.
 
 usage: python -m convolution_implicit_gemm_02_amd.tile_sweep [--out PATH] [--json PATH] [--quick]
+                                                            [--merge NAME_PREFIX]
+
+--merge times, per shape, only the configuration the current table (or the
+cost model) picks and the configurations whose names start with NAME_PREFIX,
+and keeps the faster: a way to fold a new kernel family into the table without
+re-timing every configuration.
 """
 from __future__ import annotations
 
@@ -74,6 +80,8 @@ def main():
     ap.add_argument("--out", default=DEFAULT_OUT)
     ap.add_argument("--json", default=None)
     ap.add_argument("--quick", action="store_true", help="batch-1 shapes only")
+    ap.add_argument("--merge", default=None, metavar="NAME_PREFIX",
+                    help="time only the current choice and the configurations named NAME_PREFIX*")
     args = ap.parse_args()
 
     import torch
@@ -101,7 +109,12 @@ def main():
             xin = torch.zeros(info["in_bytes"], dtype=torch.int8, device=dev)
             out = torch.empty(info["out_bytes"] // 4, dtype=torch.float32, device=dev)
             results = []
-            for cfg in range(cbs.cbs_num_configs()):
+            candidates = range(cbs.cbs_num_configs())
+            if args.merge is not None:
+                cur = (info["config"], info["splitk"])
+                results.append((time_layer(cbs, torch, layer, xin, out), cur[0], cur[1]))
+                candidates = [c for c in candidates if cbs.cbs_config_name(c).startswith(args.merge)]
+            for cfg in candidates:
                 for sk in (1, 2, 3, 4):
                     if sk > 1 and info["grid"] >= 256:
                         continue
@@ -110,8 +123,11 @@ def main():
                     except cbs.CbsError:
                         continue
                     results.append((time_layer(cbs, torch, layer, xin, out), cfg, sk))
+            current = results[0]
             results.sort()
             best_us, best_cfg, best_sk = results[0]
+            if args.merge is not None and best_us > 0.98 * current[0]:
+                best_us, best_cfg, best_sk = current  # within noise of the current choice: keep it
             entries.append((n, spec.c_in, spec.c_out, spec.h, spec.w, spec.k, spec.stride, dtype, best_cfg, best_sk,
                             best_us, spec.name))
             report.append({"layer": spec.name, "n": n, "dtype": "int8" if dtype else "f32", "best_us": best_us,
