@@ -66,4 +66,8 @@
   X(30, 2, 2, 2, 2, 1, 4, "R.p64c64k1s4")       \
   X(31, 2, 4, 2, 2, 1, 4, "R.p64c128k1s4")      \
   X(32, 4, 2, 2, 2, 1, 4, "R.p128c64k1s4")      \
-  X(33, 2, 2, 2, 1, 2, 4, "R.p64c32k2s4")
+  X(33, 2, 2, 2, 1, 2, 4, "R.p64c32k2s4")       \
+  X(34, 2, 2, 2, 2, 1, 8, "R.p64c64k1s8")       \
+  X(35, 4, 4, 2, 2, 1, 4, "R.p128c128k1s4")     \
+  X(36, 4, 2, 2, 2, 1, 5, "R.p128c64k1s5")      \
+  X(37, 2, 2, 2, 1, 1, 8, "R.p64c32k1s8")
