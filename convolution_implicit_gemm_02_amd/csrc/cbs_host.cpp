@@ -72,6 +72,13 @@ struct cbs_layer {
   float *d_bias = nullptr;
   float *d_dq = nullptr;
   int *d_corr = nullptr;   // uint8 input: accumulator start values [64][co_blocks*16]
+  // column-pair halo tiles (3x3 stride 1, <= 8 output channels; see conv_halo):
+  // weights over the 3 x 4 window of a pixel pair and a 16-row bias/dequant
+  bool pair = false;
+  int pair_total_chunks = 0, pair_steps = 0;
+  void *d_wfrag_pair = nullptr;
+  float *d_bias_pair = nullptr;
+  float *d_dq_pair = nullptr;
   float *d_ws = nullptr;
   unsigned *d_counters = nullptr;
   size_t ws_bytes = 0, counters_len = 0;
@@ -195,9 +202,9 @@ struct Choice {
 // Tiles of a configuration for this layer.
 void tiles_of(const cbs_layer *L, int cfg, int *px_tiles, int *co_tiles) {
   const KernelConfig &c = config(cfg);
-  if (c.lds == 2) {  // halo tiles: whole TH x TW blocks of one image, all channels
+  if (c.lds == 2 || c.lds == 3) {  // halo tiles: whole TH x TW blocks of one image, all channels
     *co_tiles = 1;
-    *px_tiles = L->d.n * ceil_div(L->oh, c.th) * ceil_div(L->ow, c.tw);
+    *px_tiles = L->d.n * ceil_div(L->oh, c.th) * ceil_div(L->ow, c.lds == 3 ? 2 * c.tw : c.tw);
     return;
   }
   const int tco = c.cb * 16 * c.wco, tpx = c.pb * 16 * c.wpx;
@@ -216,14 +223,20 @@ int halo_cq(const cbs_layer *L) {
   return (L->d.dtype == CBS_F32 && cq % 2 == 0) ? cq + 1 : cq;
 }
 
+// Halo width in pixels of a halo configuration (column pairs: 2*tw pixels
+// at stride 1 plus the 3x3 border).
+int halo_width(const cbs_layer *L, const KernelConfig &c) {
+  return c.lds == 3 ? 2 * c.tw + 2 : (c.tw - 1) * L->d.stride + 3;
+}
+
 void halo_lds(const cbs_layer *L, int cfg, int *halo_bytes, int *smem_bytes) {
   const KernelConfig &c = config(cfg);
   const int s = L->d.stride;
-  const int hh = (c.th - 1) * s + 3, hw = (c.tw - 1) * s + 3;
+  const int hh = (c.th - 1) * s + 3, hw = halo_width(L, c);
   const int slots = hh * hw * halo_cq(L);
   const int slot_bytes = L->d.dtype == CBS_F32 ? 16 : 4;
   *halo_bytes = round_up(slots, 64) * slot_bytes;
-  *smem_bytes = *halo_bytes + L->co_blocks * L->steps * 1024;
+  *smem_bytes = *halo_bytes + (c.lds == 3 ? L->pair_steps : L->co_blocks * L->steps) * 1024;
 }
 
 // Rough cost model (cycles at one SIMD) used when the tile table has no entry:
@@ -254,8 +267,9 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
   const KernelConfig &c = config(cfg);
   if (splitk < 1 || splitk > 64) return false;
   if (c.lds && splitk != 1) return false;
-  if (c.lds == 2) {
+  if (c.lds == 2 || c.lds == 3) {
     if (L->d.k != 3 || L->co_blocks > 4) return false;
+    if (c.lds == 3 && !L->pair) return false;
     int hb, sb;
     halo_lds(L, cfg, &hb, &sb);
     if (sb > 64 * 1024) return false;
@@ -284,7 +298,7 @@ Choice choose(const cbs_layer *L) {
   Choice best{2, 1};
   double best_cost = 1e300;
   for (int cfg = 0; cfg < num_configs(); cfg++) {
-    if (config(cfg).lds == 2) continue;  // halo tiles are chosen by measurement only
+    if (config(cfg).lds >= 2) continue;  // halo tiles are chosen by measurement only
     for (int sk : {1}) {
       if (!config_fits(L, cfg, sk)) continue;
       const double cost = model_cost(L, cfg, sk);
@@ -316,6 +330,11 @@ void release(cbs_layer *L) {
   if (L->d_bias) (void)hipFree(L->d_bias);
   if (L->d_dq) (void)hipFree(L->d_dq);
   if (L->d_corr) (void)hipFree(L->d_corr);
+  if (L->d_wfrag_pair) (void)hipFree(L->d_wfrag_pair);
+  if (L->d_bias_pair) (void)hipFree(L->d_bias_pair);
+  if (L->d_dq_pair) (void)hipFree(L->d_dq_pair);
+  L->d_wfrag_pair = nullptr;
+  L->d_bias_pair = L->d_dq_pair = nullptr;
   if (L->d_ws) (void)hipFree(L->d_ws);
   if (L->d_counters) (void)hipFree(L->d_counters);
   L->d_wfrag = nullptr;
@@ -431,13 +450,23 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
   p.co_blocks = L->co_blocks;
   p.w_bytes = (unsigned)((size_t)L->co_blocks * L->steps * 64 * 16);
   const KernelConfig &kc = config(cfg);
-  if (kc.lds == 2) {
-    p.tiles_x = ceil_div(L->ow, kc.tw);
+  if (kc.lds == 2 || kc.lds == 3) {
+    p.tiles_x = ceil_div(L->ow, kc.lds == 3 ? 2 * kc.tw : kc.tw);
     p.tiles_y = ceil_div(L->oh, kc.th);
     p.halo_cq = halo_cq(L);
     p.div_hcq = make_fastdiv(p.halo_cq);
-    p.div_hwd = make_fastdiv((kc.tw - 1) * L->d.stride + 3);
+    p.div_hwd = make_fastdiv(halo_width(L, kc));
     halo_lds(L, cfg, &p.halo_bytes, &p.smem_bytes);
+  }
+  if (kc.lds == 3) {  // column pairs: their own weights, K geometry and 16-row bias / dequant
+    p.wfrag = L->d_wfrag_pair;
+    p.bias = L->d_bias_pair;
+    p.dq = L->d_dq_pair;
+    p.total_chunks = L->pair_total_chunks;
+    p.steps = L->pair_steps;
+    p.steps_per_split = L->pair_steps;
+    p.co_blocks = 1;
+    p.w_bytes = (unsigned)((size_t)L->pair_steps * 64 * 16);
   }
   tiles_of(L, cfg, &p.px_tiles, &p.co_tiles);
   // Workgroup order (see tile_of in conv_kernels.h): pixel tiles inner when
@@ -698,6 +727,57 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
         }
       }
 
+  // ---- column pairs (conv_halo with PAIR): for 3x3 stride-1 layers with at
+  // most 8 output channels, row 8*h + co of one 16-row block is channel co of
+  // pixel 2*j + h of the pair j, over the pair's 3 x 4 input window: the
+  // weight of window tap (dy, dx) is W'[co, ci, dy, dx - h], zero where
+  // dx - h is outside 0..2.  Same chunk order as above, 12 taps instead of 9.
+  std::vector<unsigned char> frag_pair;
+  std::vector<float> bias_pair, dq_pair;
+  L->pair = d.k == 3 && d.stride == 1 && d.pad == 1 && L->cout_pad <= 8 && d.dtype != CBS_U8;
+  if (L->pair) {
+    L->pair_total_chunks = 12 * L->chunks_per_tap;
+    L->pair_steps = ceil_div(L->pair_total_chunks, chunks_per_step);
+    for (int c = 0; c < L->pair_steps * chunks_per_step; c++)
+      if ((int)(((unsigned)c * L->cpt_magic) >> 20) != c / L->chunks_per_tap) L->pair = false;
+  }
+  if (L->pair) {
+    frag_pair.assign((size_t)L->pair_steps * 64 * 16, 0);
+    for (int s = 0; s < L->pair_steps; s++)
+      for (int lane = 0; lane < 64; lane++) {
+        const int r = lane & 15, g = lane >> 4, h = r >> 3, co = r & 7;
+        unsigned char *dst = &frag_pair[((size_t)s * 64 + lane) * 16];
+        if (co >= d.c_out) continue;
+        for (int j = 0; j < vec; j++) {
+          const int c = (4 * s + g) * vec + j;
+          if (c >= L->pair_total_chunks) continue;
+          const int tap = c / L->chunks_per_tap;
+          const int ci0 = (c % L->chunks_per_tap) * L->chunk_ch;
+          const int kh = tap >> 2, kw = (tap & 3) - h;
+          if (kw < 0 || kw > 2) continue;
+          for (int e = 0; e < L->chunk_ch; e++) {
+            const int ci = ci0 + e;
+            if (ci >= d.c_in) continue;
+            const size_t src = (((size_t)co * d.c_in + ci) * 3 + kh) * 3 + kw;
+            if (d.dtype == CBS_F32) {
+              const float v = L->h_wfold[src];
+              std::memcpy(dst + 4 * e, &v, 4);
+            } else {
+              dst[j * 4 + e] = (unsigned char)L->h_qw[src];
+            }
+          }
+        }
+      }
+    bias_pair.assign(16, 0.f);
+    dq_pair.assign(16, 0.f);
+    for (int r = 0; r < 16; r++) {
+      const int co = r & 7;
+      if (co >= d.c_out) continue;
+      bias_pair[r] = L->h_bias[co];
+      if (d.dtype != CBS_F32) dq_pair[r] = dq[co];
+    }
+  }
+
   // ---- uint8 input: accumulator start values per border class (see
   // border_class in conv_kernels.h).  With T[co][tap] the sum of the channel's
   // int8 weights at a tap, Wsum[co] = sum_tap T and Win the sum over the taps
@@ -741,6 +821,10 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   if (st == CBS_OK) st = dev_alloc((void **)&L->d_bias, biasv.size() * sizeof(float));
   if (st == CBS_OK && d.dtype != CBS_F32) st = dev_alloc((void **)&L->d_dq, dq.size() * sizeof(float));
   if (st == CBS_OK && d.dtype == CBS_U8) st = dev_alloc((void **)&L->d_corr, corr.size() * sizeof(int));
+  if (st == CBS_OK && L->pair) st = dev_alloc(&L->d_wfrag_pair, frag_pair.size());
+  if (st == CBS_OK && L->pair) st = dev_alloc((void **)&L->d_bias_pair, bias_pair.size() * sizeof(float));
+  if (st == CBS_OK && L->pair && d.dtype != CBS_F32)
+    st = dev_alloc((void **)&L->d_dq_pair, dq_pair.size() * sizeof(float));
   if (st == CBS_OK) st = setup_splitk(L);
   if (st == CBS_OK) {
     hipError_t e = hipMemcpy(L->d_wfrag, frag.data(), frag_bytes, hipMemcpyHostToDevice);
@@ -749,6 +833,12 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
       e = hipMemcpy(L->d_dq, dq.data(), dq.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess && d.dtype == CBS_U8)
       e = hipMemcpy(L->d_corr, corr.data(), corr.size() * sizeof(int), hipMemcpyHostToDevice);
+    if (e == hipSuccess && L->pair)
+      e = hipMemcpy(L->d_wfrag_pair, frag_pair.data(), frag_pair.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess && L->pair)
+      e = hipMemcpy(L->d_bias_pair, bias_pair.data(), bias_pair.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess && L->pair && d.dtype != CBS_F32)
+      e = hipMemcpy(L->d_dq_pair, dq_pair.data(), dq_pair.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) st = fail(CBS_EDEVICE, "weight upload: %s", hipGetErrorString(e));
   }
   if (st != CBS_OK) {

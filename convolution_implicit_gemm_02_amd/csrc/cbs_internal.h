@@ -13,7 +13,8 @@ namespace cbs {
 struct KernelConfig {
   int cb, pb, wco, wpx, wk;
   int lds;  // 0: operands straight to registers (conv_igemm); 1: LDS-staged tiles (conv_lds);
-            // 2: input halo tile + all weights in LDS (conv_halo, 3x3 with <= 64 output channels)
+            // 2: input halo tile + all weights in LDS (conv_halo, 3x3 with <= 64 output channels);
+            // 3: conv_halo on column pairs (3x3 stride 1 with <= 8 output channels; th x tw pairs)
   int th, tw;  // conv_halo: output tile of th x tw pixels
   const char *name;
 };

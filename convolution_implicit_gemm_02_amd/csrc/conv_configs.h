@@ -71,3 +71,14 @@
   X(35, 4, 4, 2, 2, 1, 4, "R.p128c128k1s4")     \
   X(36, 4, 2, 2, 2, 1, 5, "R.p128c64k1s5")      \
   X(37, 2, 2, 2, 1, 1, 8, "R.p64c32k1s8")
+
+// Column-pair halo tiles (3x3, stride 1, at most 8 output channels): one
+// MFMA row block holds 8 output channels of two horizontally adjacent output
+// pixels, whose 3 x 4 input window is one K row, so the 16-row block carries
+// no channel padding: id, TH, TW (output tile of TH x TW pixel pairs), name.
+#define CBS_HALO_PAIR_CONFIG_LIST(X)         \
+  X(38, 4, 32, "P.t4x32")                    \
+  X(39, 8, 16, "P.t8x16")                    \
+  X(40, 2, 32, "P.t2x32")                    \
+  X(41, 4, 16, "P.t4x16")                    \
+  X(42, 8, 32, "P.t8x32")

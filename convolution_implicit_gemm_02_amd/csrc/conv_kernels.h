@@ -356,6 +356,17 @@ __device__ __forceinline__ Chunk decode_chunk(const ConvParams &p, int c) {
   return r;
 }
 
+// The same for the column-pair halo kernel: taps run over a 3 x 4 window.
+__device__ __forceinline__ Chunk decode_chunk_pair(const ConvParams &p, int c) {
+  Chunk r;
+  const int tap = (int)(((unsigned)c * p.cpt_magic) >> 20);
+  r.ci = (c - tap * p.chunks_per_tap) * p.chunk_ch;
+  r.dy = tap >> 2;
+  r.dx = tap & 3;
+  r.ok = c < p.total_chunks;
+  return r;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs; this remaps a
 // workgroup id to a logical tile so that each XCD receives a contiguous range
 // of logical tiles (the co tiles and K splits of one pixel tile then share
@@ -1066,7 +1077,17 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
 // weights straight into LDS with direct-to-LDS buffer loads (out-of-range
 // offsets supply the zero padding), then runs every tap of the convolution
 // from LDS on MFMA.  This is the direct-convolution path for the stem.
-template <int VAR, int TH, int TW, int NBMAX, bool EXACT>
+//
+// PAIR: column pairs.  With at most 8 output channels, a 16-row MFMA block
+// would be half padding.  Instead row 8*h + co of the block is output channel
+// co of the pixel 2*j + h of the pair j, and the pair's K row runs over its
+// 3 x 4 input window (tap = 4*dy + dx, dx = 0..3), with the weight of tap
+// (dy, dx) in row 8*h + co equal to W'[co, ., dy, dx - h] (zero where dx - h
+// falls outside 0..2).  The host lays out those weights (and a 16-row bias
+// with each channel's value twice); here a "pixel" of the tile is a pair: the
+// tile is TH x TW pairs, pair (ly, lx) starts at halo column 2*lx, and each
+// lane stores its 4 channels to pixel 2*j + (g >> 1), channels 4*(g & 1)..+3.
+template <int VAR, int TH, int TW, int NBMAX, bool EXACT, bool PAIR = false>
 __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   using V = Var<VAR>;
   using Frag = typename V::Frag;
@@ -1096,10 +1117,11 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   const int n = fdiv(rest, p.div_ty);
   const int ty = rest - n * p.tiles_y;
 
-  const int st_ = p.stride;
-  const int HWd = (TW - 1) * st_ + 3;  // halo width in pixels
-  const int HH = (TH - 1) * st_ + 3;   // halo height
-  const int oh0 = ty * TH, ow0 = tx * TW;
+  static_assert(!PAIR || (NBMAX == 1 && EXACT && !V::U8), "column pairs: one 16-row block, no uint8");
+  const int st_ = PAIR ? 1 : p.stride;
+  const int HWd = PAIR ? 2 * TW + 2 : (TW - 1) * st_ + 3;  // halo width in pixels
+  const int HH = (TH - 1) * st_ + 3;                        // halo height
+  const int oh0 = ty * TH, ow0 = tx * (PAIR ? 2 * TW : TW);
   const int iy0 = oh0 * st_ - p.pad, ix0 = ow0 * st_ - p.pad;
   const int cq = p.cin_pad >> 2;                 // 4-channel slots per pixel
   const int cql = p.halo_cq;                     // slots per pixel in LDS (cq, or cq + 1: see below)
@@ -1168,7 +1190,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   for (int mb = 0; mb < MB; mb++) {
     const int pi = (wave * MB + mb) * 16 + r;
     const int ly = pi / TW, lx = pi % TW;
-    lbase[mb] = (ly * st_) * HWd + lx * st_;
+    lbase[mb] = PAIR ? ly * HWd + 2 * lx : (ly * st_) * HWd + lx * st_;
   }
   const unsigned char *wl = smem + p.halo_bytes;
   // An fp32 pixel of an even number of 16-byte slots would put the 16
@@ -1182,7 +1204,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
       a[nb] = nb < nbl ? *(const Frag *)(wl + ((nb * p.steps + s) * 64 + lane) * 16) : Frag{};
     Frag b[MB];
     if constexpr (V::VEC == 1) {
-      Chunk c = decode_chunk(p, s * 4 + g);
+      Chunk c = PAIR ? decode_chunk_pair(p, s * 4 + g) : decode_chunk(p, s * 4 + g);
       if (!c.ok) c.dy = c.dx = c.ci = 0;  // past K: read a valid slot, then zero it
 #pragma unroll
       for (int mb = 0; mb < MB; mb++) {
@@ -1200,7 +1222,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
       for (int mb = 0; mb < MB; mb++) b[mb] = Frag{};
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        Chunk c = decode_chunk(p, (s * 4 + g) * 4 + j);
+        Chunk c = PAIR ? decode_chunk_pair(p, (s * 4 + g) * 4 + j) : decode_chunk(p, (s * 4 + g) * 4 + j);
         if (!c.ok) c.dy = c.dx = c.ci = 0;
 #pragma unroll
         for (int mb = 0; mb < MB; mb++) {
@@ -1232,12 +1254,12 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
 #pragma unroll
   for (int nb = 0; nb < NBMAX; nb++) {
     if (nb >= nbl) break;
-    const int co0 = nb * 16 + 4 * g;
+    const int co0 = PAIR ? 4 * (g & 1) : nb * 16 + 4 * g;
     if (co0 >= p.cout_pad) continue;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
       const int pi = (wave * MB + mb) * 16 + r;
-      const int oh = oh0 + pi / TW, ow = ow0 + pi % TW;
+      const int oh = oh0 + pi / TW, ow = PAIR ? ow0 + 2 * (pi % TW) + (g >> 1) : ow0 + pi % TW;
       if (oh >= p.OH || ow >= p.OW) continue;
       const int opix = (n * p.OH + oh) * p.pitch + ow;
       if constexpr (V::RAW) {
@@ -1288,6 +1310,19 @@ static hipError_t launch_halo(const ConvParams &p, hipStream_t stream) {
   else
     hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 4, false>), dim3(grid), dim3(256), smem, stream, p);
   return hipGetLastError();
+}
+
+// Column-pair halo tiles: one 16-row block (8 channels x 2 pixels).
+template <int VAR, int TH, int TW>
+static hipError_t launch_halo_pair(const ConvParams &p, hipStream_t stream) {
+  if constexpr (Var<VAR>::U8) {
+    return hipErrorInvalidValue;
+  } else {
+    if (p.splitk != 1 || p.co_blocks != 1 || p.k != 3 || p.stride != 1 || p.cout_pad > 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 1, true, true>), dim3((unsigned)p.px_tiles), dim3(256),
+                       (unsigned)p.smem_bytes, stream, p);
+    return hipGetLastError();
+  }
 }
 
 template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
@@ -1345,6 +1380,11 @@ static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t strea
   case id:                                  \
     return launch_lds<VAR, mb, nb, wm, wn, ks, ns>(p, stream);
     CBS_LDS_RING_CONFIG_LIST(X)
+#undef X
+#define X(id, th, tw, name) \
+  case id:                  \
+    return launch_halo_pair<VAR, th, tw>(p, stream);
+    CBS_HALO_PAIR_CONFIG_LIST(X)
 #undef X
     default:
       return hipErrorInvalidValue;

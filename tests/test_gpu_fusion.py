@@ -417,13 +417,20 @@ def test_slices_and_residual(idx, mode):
     check(case, prep, got)
 
 
+# (spec, in slice, out slice, residual slice): small enough for every halo tile; the
+# second has 8 output channels and an odd width, so the column-pair halo tiles run
+# too (a C3k2 bottleneck conv of the 16-channel stage) with a half-used last pair
+OPTION_CASES = [(spec(16, 16, 20, 20, 3, 1), (48, 16), (48, 32), (48, 16)),
+                (spec(8, 8, 20, 19, 3, 1), (24, 8), (24, 16), (24, 8))]
+
+
 @pytest.mark.parametrize("mode", [("f32", "f32"), ("i8", "i8"), ("u8", "u8")])
-def test_fused_options_on_every_config(mode):
+@pytest.mark.parametrize("oc", range(len(OPTION_CASES)))
+def test_fused_options_on_every_config(mode, oc):
     """Input slice + output slice + residual (+ int8 output) through every kernel configuration
     (register-direct, LDS-staged, halo) and, for the direct ones, cross-workgroup split-K."""
-    sp = spec(16, 16, 20, 20, 3, 1)  # small enough for every halo tile
-    case = Case(sp, n=1, dtype=mode[0], out=mode[1], in_sl=(48, 16), out_sl=(48, 32), res_sl=(48, 16),
-                extra=8, seed=30)
+    sp, ins, outs, res = OPTION_CASES[oc]
+    case = Case(sp, n=1, dtype=mode[0], out=mode[1], in_sl=ins, out_sl=outs, res_sl=res, extra=8, seed=30)
     prep = prepare(case)
     ran = 0
     for cfg in range(cbs.cbs_num_configs()):

@@ -187,7 +187,11 @@ def test_every_config_on_every_shape_f32():
     shapes, so that the tile table's choice cannot hide a broken variant."""
     rng = np.random.default_rng(6)
     specs = [W.LayerSpec("r3", 32, 32, 13, 11, 3, 1, 1), W.LayerSpec("r1", 40, 80, 9, 10, 1, 1, 0),
-             W.LayerSpec("s2", 12, 24, 15, 14, 3, 2, 1), W.LayerSpec("stem", 3, 16, 21, 22, 3, 2, 1)]
+             W.LayerSpec("s2", 12, 24, 15, 14, 3, 2, 1), W.LayerSpec("stem", 3, 16, 21, 22, 3, 2, 1),
+             # <= 8 output channels, 3x3 stride 1: the column-pair halo tiles run too (odd OW: a
+             # half-used last pair; 6 channels: padded rows; 3 channels: a 4-channel output pitch)
+             W.LayerSpec("c8", 8, 8, 13, 11, 3, 1, 1), W.LayerSpec("c6", 12, 6, 9, 14, 3, 1, 1),
+             W.LayerSpec("c3", 4, 3, 10, 9, 3, 1, 1)]
     for spec in specs:
         L = W.draw_layer(rng, spec, 2)
         y, s = _oracle_f32(L)
@@ -320,7 +324,9 @@ def test_i8_small_and_random_shapes():
 def test_every_config_on_every_shape_i8():
     rng = np.random.default_rng(10)
     specs = [W.LayerSpec("r3", 64, 32, 9, 11, 3, 1, 1), W.LayerSpec("r1", 48, 80, 9, 10, 1, 1, 0),
-             W.LayerSpec("c4", 12, 24, 15, 14, 3, 2, 1), W.LayerSpec("stem", 3, 16, 21, 22, 3, 2, 1)]
+             W.LayerSpec("c4", 12, 24, 15, 14, 3, 2, 1), W.LayerSpec("stem", 3, 16, 21, 22, 3, 2, 1),
+             # column-pair halo tiles on both int8 gathers (4- and 16-channel chunks)
+             W.LayerSpec("c8", 8, 8, 13, 11, 3, 1, 1), W.LayerSpec("c16to6", 16, 6, 7, 10, 3, 1, 1)]
     for spec in specs:
         L = W.draw_layer(rng, spec, 2)
         s_x = W.calibration_scale(L.x)
