@@ -443,7 +443,11 @@ def test_fused_options_on_every_config(mode, oc):
             got, _ = run(case, prep)
             check(case, prep, got)
             ran += 1
-    assert ran >= cbs.cbs_num_configs()
+    # every configuration runs at least once, except the column-pair tiles on layers
+    # with more than 8 output channels
+    names = [cbs.cbs_config_name(c) for c in range(cbs.cbs_num_configs())]
+    n_pair = sum(1 for nm in names if nm.startswith(("P.", "QP.")))
+    assert ran >= len(names) - (n_pair if sp.c_out > 8 or mode[0] == "u8" else 0)
 
 
 def test_residual_layer_needs_residual():
