@@ -281,15 +281,31 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
   return grid < 2147483647.0;
 }
 
+// Tile-table class of a layer (TileEntry::dtype): 0 fp32 and 1 int8 input
+// with the plain epilogue (SiLU, fp32 output, no residual), 2 uint8 input,
+// 3 int8 and 4 fp32 input with the general epilogue (byte output, identity
+// activation or a residual).  Classes 2-4 fall back to the plain entry of
+// their input type (uint8 layers run the int8 kernels with another gather and
+// start value), which the sweep writes for every shape.
+int table_class(const cbs_layer *L) {
+  if (L->d.dtype == CBS_U8) return 2;
+  const bool x = L->variant == VAR_F32_X || L->variant == VAR_I8_C16_X || L->variant == VAR_I8_C4_X;
+  if (L->d.dtype == CBS_F32) return x ? 4 : 0;
+  return x ? 3 : 1;
+}
+
 Choice choose(const cbs_layer *L) {
-  // 1) the offline-tuned table (uint8 layers run the int8 kernels with a
-  // different gather and start value, and take the int8 entries)
-  const int tdtype = L->d.dtype == CBS_U8 ? CBS_I8 : L->d.dtype;
-  for (const TileEntry &e : kTileTable) {
-    if (e.n == L->d.n && e.c_in == L->d.c_in && e.c_out == L->d.c_out && e.h == L->d.h &&
-        e.w == L->d.w && e.k == L->d.k && e.s == L->d.stride && e.dtype == tdtype &&
-        e.config < num_configs() && config_fits(L, e.config, e.splitk))
-      return {e.config, e.splitk};
+  // 1) the offline-tuned table: the entry of the layer's own class, else the
+  // plain entry of its input type
+  const int cls = table_class(L);
+  const int fallback = (cls == 0 || cls == 4) ? 0 : 1;
+  for (int key : {cls, fallback}) {
+    for (const TileEntry &e : kTileTable) {
+      if (e.n == L->d.n && e.c_in == L->d.c_in && e.c_out == L->d.c_out && e.h == L->d.h &&
+          e.w == L->d.w && e.k == L->d.k && e.s == L->d.stride && e.dtype == key &&
+          e.config < num_configs() && config_fits(L, e.config, e.splitk))
+        return {e.config, e.splitk};
+    }
   }
   // 2) the cost model.  Cross-workgroup split-K is never picked here: its
   // partial-tile round trip through memory costs about a microsecond per

@@ -14,6 +14,12 @@ usage: python -m convolution_implicit_gemm_02_amd.tile_sweep [--out PATH] [--jso
 cost model) picks and the configurations whose names start with NAME_PREFIX,
 and keeps the faster: a way to fold a new kernel family into the table without
 re-timing every configuration.
+
+--classes keeps the fp32 and int8 entries of the current table and sweeps
+every configuration for two more table classes per shape: int8 input with
+int8 output codes (the general epilogue) and uint8 input with fp32 output.  An
+entry is written for such a class only where its best configuration differs
+from, and beats by 2%, the int8 entry the class would fall back to.
 """
 from __future__ import annotations
 
@@ -25,6 +31,9 @@ import time
 
 import numpy as np
 
+# Table classes (TileEntry::dtype; see table_class in csrc/cbs_host.cpp).
+CLS_F32, CLS_I8, CLS_U8, CLS_I8_X = 0, 1, 2, 3
+
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_OUT = os.path.join(PKG_DIR, "csrc", "tile_table.inc")
 
@@ -32,7 +41,8 @@ HEADER = """// tile_table.inc -- per-shape kernel configuration chosen by measur
 // Written by convolution_implicit_gemm_02_amd/tile_sweep.py from a sweep of
 // every configuration (split-K 1, and 2-4 for grids below 256 workgroups) on %s;
 // shapes not listed fall back to the cost model in cbs_host.cpp.
-// Key: (n, c_in, c_out, h, w, k, stride, dtype) -> (config, splitk).
+// Key: (n, c_in, c_out, h, w, k, stride, class) -> (config, splitk); class 0
+// fp32, 1 int8 (plain epilogue), 2 uint8 input, 3 int8 input with int8 output.
 struct TileEntry {
   int n, c_in, c_out, h, w, k, s, dtype, config, splitk;
 };
@@ -82,6 +92,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="batch-1 shapes only")
     ap.add_argument("--merge", default=None, metavar="NAME_PREFIX",
                     help="time only the current choice and the configurations named NAME_PREFIX*")
+    ap.add_argument("--classes", action="store_true",
+                    help="keep the fp32/int8 entries; sweep the int8-output and uint8 classes")
     args = ap.parse_args()
 
     import torch
@@ -101,19 +113,31 @@ def main():
         w = (rng.standard_normal((spec.c_out, spec.c_in, spec.k, spec.k)) / np.sqrt(spec.c_in * spec.k * spec.k)
              ).astype(np.float32)
         ones, zeros = np.ones(spec.c_out, np.float32), np.zeros(spec.c_out, np.float32)
-        for dtype in (cbs.CBS_F32, cbs.CBS_I8):
+        classes = (CLS_F32, CLS_I8, CLS_I8_X, CLS_U8) if args.classes else (CLS_F32, CLS_I8)
+        for cls in classes:
+            dtype = {CLS_F32: cbs.CBS_F32, CLS_I8: cbs.CBS_I8, CLS_I8_X: cbs.CBS_I8, CLS_U8: cbs.CBS_U8}[cls]
+            extra = {}
+            if cls == CLS_I8_X:
+                extra = dict(out_dtype=cbs.CBS_I8, out_scale=0.05)
+            elif cls == CLS_U8:
+                extra = dict(in_zero_point=128)
             desc = cbs.make_desc(n, spec.c_in, spec.h, spec.w, spec.c_out, spec.k, spec.stride, spec.pad, dtype, 0,
-                                 0.05, W.BN_EPS)
+                                 0.05, W.BN_EPS, **extra)
             layer = cbs.cbs_create_layer(desc, w, ones, zeros, zeros, ones)
             info = cbs.cbs_layer_info(layer)
             xin = torch.zeros(info["in_bytes"], dtype=torch.int8, device=dev)
-            out = torch.empty(info["out_bytes"] // 4, dtype=torch.float32, device=dev)
+            out = torch.empty(max(1, info["out_bytes"] // 4), dtype=torch.float32, device=dev)
             results = []
             candidates = range(cbs.cbs_num_configs())
-            if args.merge is not None:
+            current = None
+            if args.merge is not None or (args.classes and cls in (CLS_F32, CLS_I8)):
                 cur = (info["config"], info["splitk"])
-                results.append((time_layer(cbs, torch, layer, xin, out), cur[0], cur[1]))
-                candidates = [c for c in candidates if cbs.cbs_config_name(c).startswith(args.merge)]
+                current = (time_layer(cbs, torch, layer, xin, out), cur[0], cur[1])
+                results.append(current)
+                candidates = [] if args.classes else [c for c in candidates if cbs.cbs_config_name(c).startswith(args.merge)]
+            elif args.classes:
+                # the fallback (this shape's int8 entry) is the choice to beat
+                current = (time_layer(cbs, torch, layer, xin, out), info["config"], info["splitk"])
             for cfg in candidates:
                 for sk in (1, 2, 3, 4):
                     if sk > 1 and info["grid"] >= 256:
@@ -123,26 +147,29 @@ def main():
                     except cbs.CbsError:
                         continue
                     results.append((time_layer(cbs, torch, layer, xin, out), cfg, sk))
-            current = results[0]
             results.sort()
             best_us, best_cfg, best_sk = results[0]
-            if args.merge is not None and best_us > 0.98 * current[0]:
+            if current is not None and best_us > 0.98 * current[0]:
                 best_us, best_cfg, best_sk = current  # within noise of the current choice: keep it
-            entries.append((n, spec.c_in, spec.c_out, spec.h, spec.w, spec.k, spec.stride, dtype, best_cfg, best_sk,
-                            best_us, spec.name))
-            report.append({"layer": spec.name, "n": n, "dtype": "int8" if dtype else "f32", "best_us": best_us,
-                           "config": cbs.cbs_config_name(best_cfg), "splitk": best_sk,
+            if cls in (CLS_F32, CLS_I8) or (best_cfg, best_sk) != current[1:]:
+                entries.append((n, spec.c_in, spec.c_out, spec.h, spec.w, spec.k, spec.stride, cls, best_cfg, best_sk,
+                                best_us, spec.name))
+            report.append({"layer": spec.name, "n": n, "dtype": ["f32", "int8", "uint8", "int8->int8"][cls],
+                           "best_us": best_us, "config": cbs.cbs_config_name(best_cfg), "splitk": best_sk,
                            "all": [(round(t, 3), cbs.cbs_config_name(c), s) for t, c, s in results[:6]]})
             del layer, xin, out
-        print("[%3d/%d] %-14s n=%-2d f32 %s/%d %.2f us | int8 %s/%d %.2f us  (%.0f s)" % (
-            si + 1, len(shapes), spec.name, n, report[-2]["config"], report[-2]["splitk"], report[-2]["best_us"],
-            report[-1]["config"], report[-1]["splitk"], report[-1]["best_us"], time.time() - t_start), flush=True)
+        print("[%3d/%d] %-14s n=%-2d %s  (%.0f s)" % (
+            si + 1, len(shapes), spec.name, n, " | ".join("%s %s/%d %.2f us" % (r["dtype"], r["config"], r["splitk"],
+                                                                                r["best_us"])
+                                                           for r in report[-len(classes):]),
+            time.time() - t_start), flush=True)
 
     with open(args.out, "w") as f:
         f.write(HEADER % name)
         for e in entries:
             f.write("    {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d},  // %s %s %.2f us\n" % (
-                e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7], e[8], e[9], e[11], "int8" if e[7] else "f32", e[10]))
+                e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7], e[8], e[9], e[11],
+                ["f32", "int8", "uint8", "int8->int8"][e[7]], e[10]))
         f.write("    {0, 0, 0, 0, 0, 0, 0, 0, 0, 1},  // sentinel: n == 0 never matches\n};\n")
     if args.json:
         with open(args.json, "w") as f:
