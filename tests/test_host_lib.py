@@ -237,3 +237,28 @@ def test_descriptor_layout_matches_header(cbs):
             names += [t.strip() for t in decl.split(None, 1)[1].split(",")]
     assert names == [f for f, _ in cbs.cbs_conv_desc._fields_]
     assert ctypes.sizeof(cbs.cbs_conv_desc) == 4 * len(names)
+
+
+def test_tile_table_entries(cbs):
+    """Every tile-table entry names an existing configuration with a split-K the
+    configuration allows, keys are unique, classes are 0-3, and every class 2/3
+    entry has the plain int8 entry of its shape to fall back to."""
+    import re
+    path = os.path.join(os.path.dirname(HEADER), "..", "convolution_implicit_gemm_02_amd", "csrc", "tile_table.inc")
+    rows = [tuple(int(v) for v in m.groups()) for m in re.finditer(
+        r"^\s*\{(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\},", open(path).read(), re.M)]
+    rows = [r for r in rows if r[0] != 0]  # the sentinel
+    assert len(rows) > 100
+    keys = [r[:8] for r in rows]
+    assert len(set(keys)) == len(keys), "duplicate tile-table keys"
+    n_cfg = cbs.cbs_num_configs()
+    for r in rows:
+        n, c_in, c_out, h, w, k, s, cls, cfg, sk = r
+        assert cls in (0, 1, 2, 3), r
+        assert 0 <= cfg < n_cfg, r
+        name = cbs.cbs_config_name(cfg)
+        assert sk >= 1 and (sk == 1 or name.startswith("c")), r  # split-K only on register-direct tiles
+        if name.startswith("P."):  # column pairs: 3x3 stride 1, <= 8 output channels, no uint8
+            assert k == 3 and s == 1 and c_out <= 8 and cls != 2, r
+        if cls in (2, 3):
+            assert (n, c_in, c_out, h, w, k, s, 1) in set(keys), r
