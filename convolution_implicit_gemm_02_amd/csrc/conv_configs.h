@@ -82,3 +82,18 @@
   X(40, 2, 32, "P.t2x32")                    \
   X(41, 4, 16, "P.t4x16")                    \
   X(42, 8, 32, "P.t8x32")
+
+// LDS-staged tiles whose activation loads go pixel by pixel (four lanes per
+// pixel, swizzled LDS slots; see conv_lds), filled by the direct-to-LDS ring
+// (RS, NS >= 2) or through registers (LS, NS = 0): id, MB, NB, WM, WN, KS, NS, name.
+#define CBS_LDS_RING_SWZ_CONFIG_LIST(X)         \
+  X(43, 2, 2, 2, 2, 1, 4, "RS.p64c64k1s4")      \
+  X(44, 2, 2, 2, 2, 2, 4, "RS.p64c64k2s4")      \
+  X(45, 2, 4, 2, 2, 1, 4, "RS.p64c128k1s4")     \
+  X(46, 4, 2, 2, 2, 1, 4, "RS.p128c64k1s4")     \
+  X(47, 2, 2, 2, 1, 1, 8, "RS.p64c32k1s8")      \
+  X(48, 4, 4, 2, 2, 1, 4, "RS.p128c128k1s4")    \
+  X(49, 2, 2, 2, 1, 2, 0, "LS.p64c32")          \
+  X(50, 2, 2, 2, 2, 2, 0, "LS.p64c64")          \
+  X(51, 2, 4, 2, 2, 2, 0, "LS.p64c128")         \
+  X(52, 4, 2, 2, 2, 2, 0, "LS.p128c64")

@@ -819,7 +819,13 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void *dst, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, off, 0, 0, 0);
 }
 
-template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS>
+// SWZ (one 16-byte chunk per lane): the activation loads of a fragment go pixel by pixel --
+// lane 4q + j loads chunk j ^ sw(q) of pixel q, sw(q) = (q >> 1) & 3 -- so
+// four consecutive lanes read one pixel's 64 contiguous bytes (when the four
+// chunks of a step lie in one tap) instead of 16 bytes of four pixels; the
+// MFMA side then reads lane (r, g)'s operand from slot 4r + (g ^ sw(r)), and
+// the XOR keeps each group of 8 lanes of a 16-byte LDS read on distinct banks.
+template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS, bool SWZ = false>
 __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   using V = Var<VAR>;
   using Frag = typename V::Frag;
@@ -833,6 +839,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   constexpr int NX = KS * BMB * 64 / NT;          // activation slots per thread per stage
   static_assert((KS * BNB * 64) % NT == 0 && (KS * BMB * 64) % NT == 0, "stage must split evenly over threads");
   constexpr bool DMA = NS >= 2 && V::VEC == 1;    // direct-to-LDS ring (see above)
+  constexpr bool SW = SWZ && V::VEC == 1;
   constexpr int NBUF = DMA ? NS : 2;
   __shared__ Frag lds[NBUF][KS * SB * 64];
 
@@ -848,13 +855,16 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   tile_of(p, logical, px_tile, co_tile);
 
   // pixels of this thread's activation slots (the same for every stage)
+  const int lq = lane >> 2, lj = (lane & 3) ^ ((lq >> 1) & 3);  // SW: pixel and chunk this lane loads
   Pix xpix[NX];
 #pragma unroll
   for (int i = 0; i < NX; i++) {
     const int j = tid + i * NT;
     const int pxb = (j >> 6) % BMB;
-    xpix[i] = pixel_of(p, (px_tile * BMB + pxb) * 16 + r);
+    xpix[i] = pixel_of(p, (px_tile * BMB + pxb) * 16 + (SW ? lq : r));
   }
+  // SW: the LDS slot that holds this lane's MFMA operand (pixel r, chunk g)
+  const int bslot = SW ? 4 * r + (g ^ ((r >> 1) & 3)) : lane;
   // epilogue operands of this wave's blocks
   f32x4 ep_bias[NB], ep_dq[NB];
   {
@@ -898,7 +908,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
       const int jw = wave + i * (NT / 64);
       const int ks = jw / BMB, pxb = jw % BMB;
       const int s = st * KS + ks;
-      load_lds16(xr, &lds[buf][(ks * SB + BNB + pxb) * 64], gather_off<V>(p, xpix[i], s * 4 + g));
+      load_lds16(xr, &lds[buf][(ks * SB + BNB + pxb) * 64], gather_off<V>(p, xpix[i], s * 4 + (SW ? lj : g)));
     }
   };
 
@@ -919,7 +929,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
       const int j = tid + i * NT;
       const int ks = j / (BMB * 64);
       const int s = st * KS + ks;
-      rx[i] = gather<V>(p, xr, xpix[i], s * 4 + g);
+      rx[i] = gather<V>(p, xr, xpix[i], s * 4 + (SW ? lj : g));
     }
   };
   auto sstore = [&](int buf) {
@@ -968,7 +978,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
       for (int nb = 0; nb < NB; nb++) a[nb] = lds[buf][(ks * SB + wn * NB + nb) * 64 + lane];
 #pragma unroll
       for (int mb = 0; mb < MB; mb++) {
-        b[mb] = lds[buf][(ks * SB + BNB + wm * MB + mb) * 64 + lane];
+        b[mb] = lds[buf][(ks * SB + BNB + wm * MB + mb) * 64 + bslot];
         // uint8 codes reach the direct-to-LDS ring unflipped (zeros where the
         // loads were out of range, which become -128 like every padding code)
         if constexpr (DMA && V::U8) b[mb] ^= kU8Flip;
@@ -1288,11 +1298,11 @@ static hipError_t launch_one(const ConvParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS = 0>
+template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS = 0, bool SWZ = false>
 static hipError_t launch_lds(const ConvParams &p, hipStream_t stream) {
   if (p.splitk != 1) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)p.px_tiles * (unsigned)p.co_tiles;
-  hipLaunchKernelGGL((conv_lds<VAR, MB, NB, WM, WN, KS, NS>), dim3(grid), dim3(64 * WM * WN), 0, stream, p);
+  hipLaunchKernelGGL((conv_lds<VAR, MB, NB, WM, WN, KS, NS, SWZ>), dim3(grid), dim3(64 * WM * WN), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1385,6 +1395,11 @@ static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t strea
   case id:                  \
     return launch_halo_pair<VAR, th, tw>(p, stream);
     CBS_HALO_PAIR_CONFIG_LIST(X)
+#undef X
+#define X(id, mb, nb, wm, wn, ks, ns, name) \
+  case id:                                  \
+    return launch_lds<VAR, mb, nb, wm, wn, ks, ns, true>(p, stream);
+    CBS_LDS_RING_SWZ_CONFIG_LIST(X)
 #undef X
     default:
       return hipErrorInvalidValue;
