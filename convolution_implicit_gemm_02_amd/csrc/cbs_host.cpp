@@ -750,7 +750,7 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   // dx - h is outside 0..2.  Same chunk order as above, 12 taps instead of 9.
   std::vector<unsigned char> frag_pair;
   std::vector<float> bias_pair, dq_pair;
-  L->pair = d.k == 3 && d.stride == 1 && d.pad == 1 && L->cout_pad <= 8 && d.dtype != CBS_U8;
+  L->pair = d.k == 3 && d.stride == 1 && d.pad == 1 && L->cout_pad <= 8;
   if (L->pair) {
     L->pair_total_chunks = 12 * L->chunks_per_tap;
     L->pair_steps = ceil_div(L->pair_total_chunks, chunks_per_step);

@@ -1127,7 +1127,7 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   const int n = fdiv(rest, p.div_ty);
   const int ty = rest - n * p.tiles_y;
 
-  static_assert(!PAIR || (NBMAX == 1 && EXACT && !V::U8), "column pairs: one 16-row block, no uint8");
+  static_assert(!PAIR || (NBMAX == 1 && EXACT), "column pairs: one 16-row block");
   const int st_ = PAIR ? 1 : p.stride;
   const int HWd = PAIR ? 2 * TW + 2 : (TW - 1) * st_ + 3;  // halo width in pixels
   const int HH = (TH - 1) * st_ + 3;                        // halo height
@@ -1184,11 +1184,16 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   for (int mb = 0; mb < MB; mb++) {
     int cls = 0;
     if constexpr (V::U8) {
+      // the correction of a row is that of its own pixel's 3x3 window (with
+      // column pairs, pixel 2j + (g >> 1); the fourth window column has zero
+      // weight in that row)
       const int pi = (wave * MB + mb) * 16 + r;
-      cls = border_class(p, (oh0 + pi / TW) * st_ - p.pad, (ow0 + pi % TW) * st_ - p.pad);
+      const int ox = PAIR ? ow0 + 2 * (pi % TW) + (g >> 1) : ow0 + pi % TW;
+      cls = border_class(p, (oh0 + pi / TW) * st_ - p.pad, ox * st_ - p.pad);
     }
 #pragma unroll
-    for (int nb = 0; nb < NBMAX; nb++) acc[nb][mb] = nb < nbl ? zp_correction<V>(p, cls, nb * 16 + 4 * g) : Acc{};
+    for (int nb = 0; nb < NBMAX; nb++)
+      acc[nb][mb] = nb < nbl ? zp_correction<V>(p, cls, PAIR ? 4 * (g & 1) : nb * 16 + 4 * g) : Acc{};
   }
 
   __builtin_amdgcn_s_waitcnt(0);
@@ -1325,14 +1330,10 @@ static hipError_t launch_halo(const ConvParams &p, hipStream_t stream) {
 // Column-pair halo tiles: one 16-row block (8 channels x 2 pixels).
 template <int VAR, int TH, int TW>
 static hipError_t launch_halo_pair(const ConvParams &p, hipStream_t stream) {
-  if constexpr (Var<VAR>::U8) {
-    return hipErrorInvalidValue;
-  } else {
-    if (p.splitk != 1 || p.co_blocks != 1 || p.k != 3 || p.stride != 1 || p.cout_pad > 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 1, true, true>), dim3((unsigned)p.px_tiles), dim3(256),
-                       (unsigned)p.smem_bytes, stream, p);
-    return hipGetLastError();
-  }
+  if (p.splitk != 1 || p.co_blocks != 1 || p.k != 3 || p.stride != 1 || p.cout_pad > 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 1, true, true>), dim3((unsigned)p.px_tiles), dim3(256),
+                     (unsigned)p.smem_bytes, stream, p);
+  return hipGetLastError();
 }
 
 template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>

@@ -13,7 +13,9 @@ usage: python -m convolution_implicit_gemm_02_amd.tile_sweep [--out PATH] [--jso
 --merge times, per shape, only the configuration the current table (or the
 cost model) picks and the configurations whose names start with NAME_PREFIX,
 and keeps the faster: a way to fold a new kernel family into the table without
-re-timing every configuration.
+re-timing every configuration.  In both modes below a change of configuration
+is kept only when the new one beats the current one by 2% in at least two of
+three interleaved, longer timings of both.
 
 --classes keeps the fp32 and int8 entries of the current table and sweeps
 every configuration for two more table classes per shape: int8 input with
@@ -136,7 +138,7 @@ def main():
                 results.append(current)
                 candidates = [] if args.classes else [c for c in candidates if cbs.cbs_config_name(c).startswith(args.merge)]
             elif args.classes:
-                # the fallback (this shape's int8 entry) is the choice to beat
+                # the layer's current choice (its own class entry, else the int8 one) is the one to beat
                 current = (time_layer(cbs, torch, layer, xin, out), info["config"], info["splitk"])
             for cfg in candidates:
                 for sk in (1, 2, 3, 4):
@@ -151,7 +153,25 @@ def main():
             best_us, best_cfg, best_sk = results[0]
             if current is not None and best_us > 0.98 * current[0]:
                 best_us, best_cfg, best_sk = current  # within noise of the current choice: keep it
-            if cls in (CLS_F32, CLS_I8) or (best_cfg, best_sk) != current[1:]:
+            elif current is not None and (best_cfg, best_sk) != current[1:]:
+                # a change: confirm it with longer, interleaved timings of both
+                # choices (one short run can be off by several percent)
+                wins, t_new = 0, []
+                for _ in range(3):
+                    cbs.cbs_layer_set_config(layer, best_cfg, best_sk)
+                    tn = time_layer(cbs, torch, layer, xin, out, min_ms=3.0, reps=5)
+                    cbs.cbs_layer_set_config(layer, current[1], current[2])
+                    tc = time_layer(cbs, torch, layer, xin, out, min_ms=3.0, reps=5)
+                    wins += tn < 0.98 * tc
+                    t_new.append(tn)
+                if wins < 2:
+                    best_us, best_cfg, best_sk = current
+                else:
+                    best_us = float(np.median(t_new))
+            if cls == CLS_I8:
+                i8_choice = (best_cfg, best_sk)
+            # classes 2 and 3 fall back to the int8 entry: write them only where they differ from it
+            if cls in (CLS_F32, CLS_I8) or (best_cfg, best_sk) != i8_choice:
                 entries.append((n, spec.c_in, spec.c_out, spec.h, spec.w, spec.k, spec.stride, cls, best_cfg, best_sk,
                                 best_us, spec.name))
             report.append({"layer": spec.name, "n": n, "dtype": ["f32", "int8", "uint8", "int8->int8"][cls],

@@ -312,7 +312,8 @@ def test_int8_output_equals_quantised_fp32_output():
 # ------------------------------------------ f2: asymmetric uint8 ----
 
 U8_SHAPES = SHAPES + [W.LayerSpec("f", 3, 16, 34, 30, 3, 2, 1, "uniform"), spec(40, 24, 9, 13, 3, 1),
-                      spec(12, 20, 6, 5, 3, 1), spec(20, 36, 10, 9, 3, 1)]  # 36: three 16-channel blocks
+                      spec(12, 20, 6, 5, 3, 1), spec(20, 36, 10, 9, 3, 1),  # 36: three 16-channel blocks
+                      spec(8, 8, 13, 11, 3, 1), spec(16, 6, 9, 12, 3, 1)]  # column-pair tiles, both gathers
 SENT_ACC = np.int32(np.uint32(0xA5A5A5A5).view(np.int32))
 
 
@@ -446,8 +447,8 @@ def test_fused_options_on_every_config(mode, oc):
     # every configuration runs at least once, except the column-pair tiles on layers
     # with more than 8 output channels
     names = [cbs.cbs_config_name(c) for c in range(cbs.cbs_num_configs())]
-    n_pair = sum(1 for nm in names if nm.startswith(("P.", "QP.")))
-    assert ran >= len(names) - (n_pair if sp.c_out > 8 or mode[0] == "u8" else 0)
+    n_pair = sum(1 for nm in names if nm.startswith("P."))
+    assert ran >= len(names) - (n_pair if sp.c_out > 8 else 0)
 
 
 def test_residual_layer_needs_residual():
