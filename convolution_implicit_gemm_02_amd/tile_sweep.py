@@ -93,7 +93,8 @@ def main():
     ap.add_argument("--json", default=None)
     ap.add_argument("--quick", action="store_true", help="batch-1 shapes only")
     ap.add_argument("--merge", default=None, metavar="NAME_PREFIX",
-                    help="time only the current choice and the configurations named NAME_PREFIX*")
+                    help="time only the current choice and the configurations named NAME_PREFIX* "
+                         "(several prefixes separated by commas)")
     ap.add_argument("--classes", action="store_true",
                     help="keep the fp32/int8 entries; sweep the int8-output and uint8 classes")
     args = ap.parse_args()
@@ -136,7 +137,8 @@ def main():
                 cur = (info["config"], info["splitk"])
                 current = (time_layer(cbs, torch, layer, xin, out), cur[0], cur[1])
                 results.append(current)
-                candidates = [] if args.classes else [c for c in candidates if cbs.cbs_config_name(c).startswith(args.merge)]
+                candidates = [] if args.classes else [c for c in candidates
+                                                      if cbs.cbs_config_name(c).startswith(tuple(args.merge.split(",")))]
             elif args.classes:
                 # the layer's current choice (its own class entry, else the int8 one) is the one to beat
                 current = (time_layer(cbs, torch, layer, xin, out), info["config"], info["splitk"])
