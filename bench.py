@@ -113,7 +113,7 @@ class ListBench:
     def group_head(self, us_layers, reps=20, rounds=5):
         """Run the head's six layers as two grouped launches (cbs_group_*) where
         that is faster.  Each group takes the fastest of the cost model's pick
-        and every register-direct configuration, timed here as graph replays of
+        and every register-direct and LDS-staged configuration, timed here as graph replays of
         `reps` back-to-back group launches on the group's own buffers (best of
         `rounds`); a group is kept only if it beats the sum of its members'
         back-to-back single-launch times (us_layers), else its members run
@@ -128,7 +128,8 @@ class ListBench:
             layers = [self.layers[i] for i in idx]
             ins, outs = [self.ins[i] for i in idx], [self.outs[i] for i in idx]
             best = None
-            for cfg in [-1] + [c for c in range(cbs.cbs_num_configs()) if cbs.cbs_config_name(c).startswith("c")]:
+            for cfg in [-1] + [c for c in range(cbs.cbs_num_configs())
+                               if not cbs.cbs_config_name(c).startswith(("H.", "P."))]:
                 try:
                     g = cbs.cbs_group_create(layers, cfg)
                 except cbs.CbsError:
@@ -328,7 +329,7 @@ class ChainBench:
     def group_head(self, us_layers, reps=20, rounds=5):
         """Run the head's six layers as two grouped launches (cbs_group_*) where
         that is faster.  Each group takes the fastest of the cost model's pick
-        and every register-direct configuration, timed here as graph replays of
+        and every register-direct and LDS-staged configuration, timed here as graph replays of
         `reps` back-to-back group launches on the group's own buffers (best of
         `rounds`); a group is kept only if it beats the sum of its members'
         back-to-back single-launch times (us_layers), else its members run
@@ -343,7 +344,8 @@ class ChainBench:
             layers = [self.layers[i] for i in idx]
             ins, outs = [self.ins[i] for i in idx], [self.outs[i] for i in idx]
             best = None
-            for cfg in [-1] + [c for c in range(cbs.cbs_num_configs()) if cbs.cbs_config_name(c).startswith("c")]:
+            for cfg in [-1] + [c for c in range(cbs.cbs_num_configs())
+                               if not cbs.cbs_config_name(c).startswith(("H.", "P."))]:
                 try:
                     g = cbs.cbs_group_create(layers, cfg)
                 except cbs.CbsError:

@@ -121,7 +121,7 @@ VARIANTS = 12  # kernel variants, one translation unit each (cbs_variant.hip wit
 CONV_KERNELS = r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+):"
 # grouped launches read their member's arguments in a second round, at an
 # offset that depends on the first (the group's workgroup ranges)
-GROUP_KERNELS = r"^(_ZN3cbs16conv_igemm_group\w+):"
+GROUP_KERNELS = r"^(_ZN3cbs(?:16conv_igemm_group|14conv_lds_group)\w+):"
 GROUP_VARIANTS = (0, 1, 2, 5, 6, 7, 8, 9)  # variants with grouped kernels (not the raw-accumulator hooks)
 
 

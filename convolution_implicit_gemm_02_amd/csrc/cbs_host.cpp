@@ -506,6 +506,10 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
 // several times longer than the others'.
 void group_splits(const cbs_layer *const *m, int n, int cfg, int *sk) {
   const KernelConfig &c = config(cfg);
+  if (c.lds) {  // LDS-staged tiles have no split-K
+    for (int i = 0; i < n; i++) sk[i] = 1;
+    return;
+  }
   double shallowest = 1e300;
   for (int i = 0; i < n; i++) shallowest = std::min(shallowest, std::ceil((double)m[i]->steps / c.wk));
   for (int i = 0; i < n; i++) {
@@ -539,7 +543,7 @@ double group_cost(const cbs_layer *const *m, int n, int cfg, const int *sk) {
 
 // Whether configuration cfg (with split-K factors sk) can run every member of a group.
 bool group_config_fits(const cbs_layer *const *m, int n, int cfg, const int *sk) {
-  if (cfg < 0 || cfg >= num_configs() || config(cfg).lds != 0) return false;
+  if (cfg < 0 || cfg >= num_configs() || config(cfg).lds > 1) return false;  // register-direct or LDS-staged
   double grid = 0.0;
   for (int i = 0; i < n; i++) {
     if (!config_fits(m[i], cfg, sk[i])) return false;
@@ -939,12 +943,12 @@ cbs_status cbs_group_create(cbs_layer *const *layers, int32_t n, int32_t config_
   for (int32_t i = 0; i < n; i++) g->member[i] = layers[g->slot[i]];
   int sk[kGroupMax];
   if (config_id >= 0) {
-    const bool direct = config_id < num_configs() && config(config_id).lds == 0;
-    if (direct) group_splits(g->member, n, config_id, sk);
-    if (!direct || !group_config_fits(g->member, n, config_id, sk)) {
+    const bool tiled = config_id < num_configs() && config(config_id).lds <= 1;
+    if (tiled) group_splits(g->member, n, config_id, sk);
+    if (!tiled || !group_config_fits(g->member, n, config_id, sk)) {
       delete g;
-      return fail(CBS_EUNSUPPORTED, "group_create: configuration %d is not a register-direct configuration "
-                                    "that fits every layer", (int)config_id);
+      return fail(CBS_EUNSUPPORTED, "group_create: configuration %d is not a register-direct or LDS-staged "
+                                    "configuration that fits every layer", (int)config_id);
     }
     g->config = config_id;
   } else {

@@ -825,15 +825,17 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void *dst, 
 // chunks of a step lie in one tap) instead of 16 bytes of four pixels; the
 // MFMA side then reads lane (r, g)'s operand from slot 4r + (g ^ sw(r)), and
 // the XOR keeps each group of 8 lanes of a 16-byte LDS read on distinct banks.
-template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS, bool SWZ = false>
-__global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
+// Workgroup `bid` of a grid of nblocks runs logical tile
+// xcd_major(nblocks, bid) - first of the layer described by p (first: the
+// layer's first logical tile in a grouped launch, 0 otherwise).
+template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS, bool SWZ>
+__device__ __forceinline__ void lds_workgroup(const ConvParams &p, const int nblocks, const int bid,
+                                              const int first) {
   using V = Var<VAR>;
   using Frag = typename V::Frag;
   using Acc = typename V::Acc;
   constexpr int NT = 64 * WM * WN;
   constexpr int BMB = MB * WM, BNB = NB * WN;     // 16-pixel and 16-channel blocks per workgroup
-  int nblocks = gridDim.x;
-  pin_tiled_args<V::U8>(p, nblocks, false);
   constexpr int SB = BMB + BNB;                   // fragment blocks per K step
   constexpr int NA = KS * BNB * 64 / NT;          // weight slots per thread per stage
   constexpr int NX = KS * BMB * 64 / NT;          // activation slots per thread per stage
@@ -848,9 +850,7 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   const int wm = wave % WM, wn = wave / WM;
   const int r = lane & 15, g = lane >> 4;
 
-  const int nb_ = nblocks, bid = blockIdx.x;
-  const int per = nb_ >> 3, rem = nb_ & 7, xcd = bid & 7, loc = bid >> 3;
-  const int logical = xcd * per + min(xcd, rem) + loc;  // branch-free form of the XCD-major order
+  const int logical = xcd_major(nblocks, bid) - first;
   int px_tile, co_tile;
   tile_of(p, logical, px_tile, co_tile);
 
@@ -1077,6 +1077,33 @@ __global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
   }
 }
 
+
+template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS, bool SWZ = false>
+__global__ __launch_bounds__(64 * WM * WN) void conv_lds(ConvParams p) {
+  int nblocks = gridDim.x;
+  pin_tiled_args<Var<VAR>::U8>(p, nblocks, false);
+  lds_workgroup<VAR, MB, NB, WM, WN, KS, NS, SWZ>(p, nblocks, blockIdx.x, 0);
+}
+
+// Several independent layers in one launch on LDS-staged tiles (see
+// conv_igemm_group; these tiles have no split-K).
+template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS, bool SWZ = false>
+__global__ __launch_bounds__(64 * WM * WN) void conv_lds_group(GroupArgs ga) {
+  int nblocks = gridDim.x;
+  const int logical = xcd_major(nblocks, blockIdx.x);
+  int member = 0, first = 0;
+#pragma unroll
+  for (int j = 1; j < kGroupMax; j++) {
+    const bool in_later = logical >= ga.first[j];  // unused slots hold INT_MAX
+    member += in_later ? 1 : 0;
+    first = in_later ? ga.first[j] : first;
+  }
+  member = __builtin_amdgcn_readfirstlane(member);
+  first = __builtin_amdgcn_readfirstlane(first);
+  ConvParams p = group_member(member);
+  pin_tiled_args<Var<VAR>::U8>(p, nblocks, false);
+  lds_workgroup<VAR, MB, NB, WM, WN, KS, NS, SWZ>(p, nblocks, blockIdx.x, first);
+}
 
 // ------------------------------------------------------ halo-tile kernel --
 // For 3x3 layers with few channels (the 3-channel stem and the 8..32-channel
@@ -1336,6 +1363,12 @@ static hipError_t launch_halo_pair(const ConvParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS = 0, bool SWZ = false>
+static hipError_t launch_group_lds(const GroupArgs &g, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((conv_lds_group<VAR, MB, NB, WM, WN, KS, NS, SWZ>), dim3(grid), dim3(64 * WM * WN), 0, stream, g);
+  return hipGetLastError();
+}
+
 template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
 static hipError_t launch_group_one(const GroupArgs &g, unsigned grid, hipStream_t stream) {
   hipLaunchKernelGGL((conv_igemm_group<VAR, CB, PB, WCO, WPX, WK, PF>), dim3(grid), dim3(64 * WCO * WPX * WK), 0,
@@ -1343,7 +1376,7 @@ static hipError_t launch_group_one(const GroupArgs &g, unsigned grid, hipStream_
   return hipGetLastError();
 }
 
-// Grouped launch of variant VAR with register-direct configuration `cfg`.
+// Grouped launch of variant VAR with register-direct or LDS-staged configuration `cfg`.
 template <int VAR>
 static hipError_t launch_group_variant(int cfg, const GroupArgs &g, unsigned grid, hipStream_t stream) {
   switch (cfg) {
@@ -1352,6 +1385,22 @@ static hipError_t launch_group_variant(int cfg, const GroupArgs &g, unsigned gri
     return launch_group_one<VAR, cb, pb, wco, wpx, wk, pf>(g, grid, stream);
     CBS_CONFIG_LIST(X)
     CBS_CONFIG_LIST_EXT(X)
+#undef X
+#define X(id, mb, nb, wm, wn, ks, name) \
+  case id:                              \
+    return launch_group_lds<VAR, mb, nb, wm, wn, ks>(g, grid, stream);
+    CBS_LDS_CONFIG_LIST(X)
+    CBS_LDS_CONFIG_LIST_EXT(X)
+#undef X
+#define X(id, mb, nb, wm, wn, ks, ns, name) \
+  case id:                                  \
+    return launch_group_lds<VAR, mb, nb, wm, wn, ks, ns>(g, grid, stream);
+    CBS_LDS_RING_CONFIG_LIST(X)
+#undef X
+#define X(id, mb, nb, wm, wn, ks, ns, name) \
+  case id:                                  \
+    return launch_group_lds<VAR, mb, nb, wm, wn, ks, ns, true>(g, grid, stream);
+    CBS_LDS_RING_SWZ_CONFIG_LIST(X)
 #undef X
     default:
       return hipErrorInvalidValue;

@@ -259,15 +259,17 @@ void cbs_graph_destroy(cbs_graph *graph);
  * multiples of 16, or not); and all with, or all without, an option of the
  * general epilogue (identity activation, byte output).  No member may have a
  * residual.  config is a register-direct configuration id (one whose
- * cbs_config_name starts with "c"), or -1 to let a cost model choose.  Each
- * member gets its own cross-workgroup split-K factor (1 to 4), which evens out
- * the K depth of the members' workgroups; the group allocates its own split-K
- * workspace here, so one group runs from one stream at a time.  The group
+ * cbs_config_name starts with "c") or an LDS-staged one ("L.", "LS.", "R.",
+ * "RS."), or -1 to let a cost model choose among the register-direct ones.
+ * With a register-direct configuration each member gets its own
+ * cross-workgroup split-K factor (1 to 4), which evens out the K depth of the
+ * members' workgroups; the group allocates its own split-K workspace here, so
+ * one group runs from one stream at a time.  LDS-staged tiles have no split-K.  The group
  * keeps pointers to the layers, which must outlive it; their own
  * configurations are not changed.  Errors: CBS_EINVAL (NULL out or layers, n
  * out of range, a NULL layer), CBS_EUNSUPPORTED (mixed variants or devices, a
- * residual, a configuration that is not register-direct or does not fit
- * every member), CBS_ENOMEM, CBS_EDEVICE.
+ * residual, a halo-tile configuration, or one that does not fit every
+ * member), CBS_ENOMEM, CBS_EDEVICE.
  *
  * cbs_group_run: enqueue the group on `stream`; member i reads ins[i] and
  * writes outs[i], with the layouts of cbs_run_layer.  No output may overlap
