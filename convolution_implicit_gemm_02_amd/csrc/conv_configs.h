@@ -85,7 +85,8 @@
 
 // LDS-staged tiles whose activation loads go pixel by pixel (four lanes per
 // pixel, swizzled LDS slots; see conv_lds), filled by the direct-to-LDS ring
-// (RS, NS >= 2) or through registers (LS, NS = 0): id, MB, NB, WM, WN, KS, NS, name.
+// (RS, NS >= 2) or through registers (LS, NS = 0); "w8": eight waves, two per
+// SIMD, share each stage: id, MB, NB, WM, WN, KS, NS, name.
 #define CBS_LDS_RING_SWZ_CONFIG_LIST(X)         \
   X(43, 2, 2, 2, 2, 1, 4, "RS.p64c64k1s4")      \
   X(44, 2, 2, 2, 2, 2, 4, "RS.p64c64k2s4")      \
@@ -96,4 +97,8 @@
   X(49, 2, 2, 2, 1, 2, 0, "LS.p64c32")          \
   X(50, 2, 2, 2, 2, 2, 0, "LS.p64c64")          \
   X(51, 2, 4, 2, 2, 2, 0, "LS.p64c128")         \
-  X(52, 4, 2, 2, 2, 2, 0, "LS.p128c64")
+  X(52, 4, 2, 2, 2, 2, 0, "LS.p128c64")         \
+  X(53, 2, 1, 2, 4, 2, 4, "RS.p64c64w8")        \
+  X(54, 2, 2, 4, 2, 2, 2, "RS.p128c64w8")       \
+  X(55, 2, 2, 2, 4, 2, 2, "RS.p64c128w8")       \
+  X(56, 2, 1, 2, 4, 2, 0, "LS.p64c64w8")
