@@ -129,7 +129,7 @@ class ListBench:
             ins, outs = [self.ins[i] for i in idx], [self.outs[i] for i in idx]
             best = None
             for cfg in [-1] + [c for c in range(cbs.cbs_num_configs())
-                               if not cbs.cbs_config_name(c).startswith(("H.", "P."))]:
+                               if not cbs.cbs_config_name(c).startswith(("H", "P"))]:
                 try:
                     g = cbs.cbs_group_create(layers, cfg)
                 except cbs.CbsError:
@@ -345,7 +345,7 @@ class ChainBench:
             ins, outs = [self.ins[i] for i in idx], [self.outs[i] for i in idx]
             best = None
             for cfg in [-1] + [c for c in range(cbs.cbs_num_configs())
-                               if not cbs.cbs_config_name(c).startswith(("H.", "P."))]:
+                               if not cbs.cbs_config_name(c).startswith(("H", "P"))]:
                 try:
                     g = cbs.cbs_group_create(layers, cfg)
                 except cbs.CbsError:

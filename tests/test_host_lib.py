@@ -258,7 +258,7 @@ def test_tile_table_entries(cbs):
         assert 0 <= cfg < n_cfg, r
         name = cbs.cbs_config_name(cfg)
         assert sk >= 1 and (sk == 1 or name.startswith("c")), r  # split-K only on register-direct tiles
-        if name.startswith("P."):  # column pairs: 3x3 stride 1, <= 8 output channels
+        if name.startswith("P"):  # column pairs: 3x3 stride 1, <= 8 output channels
             assert k == 3 and s == 1 and c_out <= 8, r
         if cls in (2, 3):
             assert (n, c_in, c_out, h, w, k, s, 1) in set(keys), r
