@@ -5,8 +5,9 @@ SiLU, inputs already resident in HBM in the library's NHWC layout), replayed
 as one captured HIP graph.  The detection head's three scales are independent
 of each other, so its three 3x3 layers, and its three 1x1 layers, run as one
 grouped launch each (cbs_group_run) wherever that measured faster than their
-separate launches; the list with one launch per layer (37 launches) is
-reported beside it.  The headline is FP32 at batch 1
+separate launches (the library's cbs_graph_create_grouped measures and
+decides that); the list with one launch per layer (37 launches) is reported
+beside it.  The headline is FP32 at batch 1
 (the configuration of the vision-rs "YOLO26N Inference Optimisation" page:
 YOLO26N, FP32, batch 1, 640x640); the same line also carries INT8 and batch 16.
 
@@ -107,76 +108,39 @@ class ListBench:
         return changed
 
     # the detection head's three scales are independent of each other: its 3x3
-    # layers form one grouped launch and its 1x1 layers another
+    # layers form one candidate group and its 1x1 layers another
     HEAD_GROUPS = (("head64.3x3", "head128.3x3", "head256.3x3"), ("head64.1x1", "head128.1x1", "head256.1x1"))
 
-    def group_head(self, us_layers, reps=20, rounds=5):
-        """Run the head's six layers as two grouped launches (cbs_group_*) where
-        that is faster.  Each group takes the fastest of the cost model's pick
-        and every register-direct and LDS-staged configuration, timed here as graph replays of
-        `reps` back-to-back group launches on the group's own buffers (best of
-        `rounds`); a group is kept only if it beats the sum of its members'
-        back-to-back single-launch times (us_layers), else its members run
-        separately.  Then captures the step (the other layers' single launches,
-        then the kept groups) as one graph.  Returns [(members, config name,
-        us, us separately, kept)]."""
-        torch, cbs = self.torch, self.cbs
+    def group_head(self):
+        """Capture the step with the head's scales as candidate groups
+        (cbs_graph_create_grouped): the library times each group's separate and
+        grouped launches on these buffers and keeps a grouped launch only where
+        it is faster.  Returns [(members, config name, us, us separately, kept)]."""
+        cbs = self.cbs
         names = [sp.name for sp in self.specs]
-        self.groups, chosen = [], []
-        for members in self.HEAD_GROUPS:
-            idx = [names.index(n) for n in members]
-            layers = [self.layers[i] for i in idx]
-            ins, outs = [self.ins[i] for i in idx], [self.outs[i] for i in idx]
-            best = None
-            for cfg in [-1] + [c for c in range(cbs.cbs_num_configs())
-                               if not cbs.cbs_config_name(c).startswith(("H", "P"))]:
-                try:
-                    g = cbs.cbs_group_create(layers, cfg)
-                except cbs.CbsError:
-                    continue
-                graph = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(graph):
-                    for _ in range(reps):
-                        cbs.cbs_group_run(g, ins, outs)
-                graph.replay()
-                torch.cuda.synchronize()
-                us = []
-                for _ in range(rounds):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                    graph.replay()
-                    e1.record()
-                    torch.cuda.synchronize()
-                    us.append(e0.elapsed_time(e1) * 1e3 / reps)
-                del graph
-                if best is None or min(us) < best[2]:
-                    best = (g, cbs.cbs_config_name(cbs.cbs_group_config(g)), min(us))
-            separate = sum(us_layers[i] for i in idx)
-            kept = best[2] < separate
-            if kept:
-                self.groups.append((best[0], idx))
-            chosen.append((members, best[1], round(best[2], 2), round(separate, 2), kept))
-        grouped = {i for _, idx in self.groups for i in idx}
-        self.grouped_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.grouped_graph):
-            for i in range(len(self.layers)):
-                if i not in grouped:
-                    cbs.cbs_run_layer(self.layers[i], self.ins[i], self.outs[i])
-            for g, idx in self.groups:
-                cbs.cbs_group_run(g, [self.ins[i] for i in idx], [self.outs[i] for i in idx])
-        torch.cuda.synchronize()
+        group_of = [-1] * len(names)
+        for gid, members in enumerate(self.HEAD_GROUPS):
+            for m in members:
+                group_of[names.index(m)] = gid
+        self.grouped_graph = cbs.cbs_graph_create_grouped(self.layers, self.ins, self.outs, group_of)
+        self.grouped_launches, ngroups = cbs.cbs_graph_info(self.grouped_graph)
+        chosen = []
+        for i in range(ngroups):
+            g = cbs.cbs_graph_group_info(self.grouped_graph, i)
+            chosen.append((self.HEAD_GROUPS[g["group_id"]], cbs.cbs_config_name(g["config"]),
+                           round(g["us_grouped"], 2), round(g["us_separate"], 2), bool(g["kept"])))
         return chosen
 
     def time_grouped(self, steps, warmup):
         """Time replays of the grouped step (see group_head)."""
-        torch = self.torch
+        torch, cbs = self.torch, self.cbs
         for _ in range(warmup):
-            self.grouped_graph.replay()
+            cbs.cbs_graph_launch(self.grouped_graph)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
-            self.grouped_graph.replay()
+            cbs.cbs_graph_launch(self.grouped_graph)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
@@ -214,17 +178,20 @@ class ListBench:
             torch.cuda.synchronize()
             # calibrate R so that one repeat takes >= min_ms
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ten = cbs.LayerList([layer] * 10, [xin] * 10, [out] * 10)
             e0.record()
-            cbs.cbs_run_layer_list([layer] * 10, [xin] * 10, [out] * 10)
+            ten.run()
             e1.record()
             torch.cuda.synchronize()
             per = max(e0.elapsed_time(e1) / 10, 1e-4)
             r = int(min(2000, max(10, min_ms / per)))
-            ls, ins, outs = [layer] * r, [xin] * r, [out] * r
+            # marshalled before the events, so that the host time of building the
+            # argument arrays is not counted as GPU time
+            lst = cbs.LayerList([layer] * r, [xin] * r, [out] * r)
             ts = []
             for _ in range(reps):
                 e0.record()
-                cbs.cbs_run_layer_list(ls, ins, outs)
+                lst.run()
                 e1.record()
                 torch.cuda.synchronize()
                 ts.append(e0.elapsed_time(e1) / r)
@@ -321,81 +288,6 @@ class ChainBench:
             cur, s_in = Y, s_act
         torch.cuda.synchronize()
         self.graph = cbs.cbs_graph_create_steps(self.steps)
-
-    # the detection head's three scales are independent of each other: its 3x3
-    # layers form one grouped launch and its 1x1 layers another
-    HEAD_GROUPS = (("head64.3x3", "head128.3x3", "head256.3x3"), ("head64.1x1", "head128.1x1", "head256.1x1"))
-
-    def group_head(self, us_layers, reps=20, rounds=5):
-        """Run the head's six layers as two grouped launches (cbs_group_*) where
-        that is faster.  Each group takes the fastest of the cost model's pick
-        and every register-direct and LDS-staged configuration, timed here as graph replays of
-        `reps` back-to-back group launches on the group's own buffers (best of
-        `rounds`); a group is kept only if it beats the sum of its members'
-        back-to-back single-launch times (us_layers), else its members run
-        separately.  Then captures the step (the other layers' single launches,
-        then the kept groups) as one graph.  Returns [(members, config name,
-        us, us separately, kept)]."""
-        torch, cbs = self.torch, self.cbs
-        names = [sp.name for sp in self.specs]
-        self.groups, chosen = [], []
-        for members in self.HEAD_GROUPS:
-            idx = [names.index(n) for n in members]
-            layers = [self.layers[i] for i in idx]
-            ins, outs = [self.ins[i] for i in idx], [self.outs[i] for i in idx]
-            best = None
-            for cfg in [-1] + [c for c in range(cbs.cbs_num_configs())
-                               if not cbs.cbs_config_name(c).startswith(("H", "P"))]:
-                try:
-                    g = cbs.cbs_group_create(layers, cfg)
-                except cbs.CbsError:
-                    continue
-                graph = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(graph):
-                    for _ in range(reps):
-                        cbs.cbs_group_run(g, ins, outs)
-                graph.replay()
-                torch.cuda.synchronize()
-                us = []
-                for _ in range(rounds):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                    graph.replay()
-                    e1.record()
-                    torch.cuda.synchronize()
-                    us.append(e0.elapsed_time(e1) * 1e3 / reps)
-                del graph
-                if best is None or min(us) < best[2]:
-                    best = (g, cbs.cbs_config_name(cbs.cbs_group_config(g)), min(us))
-            separate = sum(us_layers[i] for i in idx)
-            kept = best[2] < separate
-            if kept:
-                self.groups.append((best[0], idx))
-            chosen.append((members, best[1], round(best[2], 2), round(separate, 2), kept))
-        grouped = {i for _, idx in self.groups for i in idx}
-        self.grouped_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.grouped_graph):
-            for i in range(len(self.layers)):
-                if i not in grouped:
-                    cbs.cbs_run_layer(self.layers[i], self.ins[i], self.outs[i])
-            for g, idx in self.groups:
-                cbs.cbs_group_run(g, [self.ins[i] for i in idx], [self.outs[i] for i in idx])
-        torch.cuda.synchronize()
-        return chosen
-
-    def time_grouped(self, steps, warmup):
-        """Time replays of the grouped step (see group_head)."""
-        torch = self.torch
-        for _ in range(warmup):
-            self.grouped_graph.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            self.grouped_graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
 
     def time_steps(self, steps, warmup, use_graph=True):
         torch, cbs = self.torch, self.cbs
@@ -563,9 +455,10 @@ def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, spli
             b.infos[i] = cbs.cbs_layer_info(layer)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         cbs.cbs_run_layer_list([layer] * 10, [xin] * 10, [out] * 10)
+        lst = cbs.LayerList([layer] * launches, [xin] * launches, [out] * launches)
         torch.cuda.synchronize()
         e0.record()
-        cbs.cbs_run_layer_list([layer] * launches, [xin] * launches, [out] * launches)
+        lst.run()
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / launches * 1e3
@@ -581,6 +474,31 @@ def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, spli
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_each": copy_bytes, "copies": 5}), flush=True)
+
+
+FLOOR_FILE = os.path.join(ROOT, "bench_best.json")
+FLOOR_FRACTION = 0.97
+
+
+def floor_check(line, best):
+    """Regression floor: each figure named in `best` (the best committed value of
+    a key of the JSON line, higher is better) must reach FLOOR_FRACTION of it;
+    keys this run did not measure are reported with ok None and not counted.
+    Returns {key: {"best", "now", "ratio", "ok"}} and whether all measured are ok."""
+    res, ok = {}, True
+    for key, ref in sorted(best.items()):
+        if key.startswith("_"):
+            continue
+        now = line.get(key)
+        if isinstance(now, dict):
+            now = now.get("value")
+        if now is None:  # not measured in this run (e.g. --quick)
+            res[key] = {"best": ref, "now": None, "ratio": None, "ok": None}
+            continue
+        ratio = now / ref
+        res[key] = {"best": ref, "now": now, "ratio": round(ratio, 4), "ok": ratio >= FLOOR_FRACTION}
+        ok &= ratio >= FLOOR_FRACTION
+    return res, ok
 
 
 def grouped_line(r):
@@ -603,6 +521,8 @@ def main():
     ap.add_argument("--batch", type=int, default=1, help="profile mode batch")
     ap.add_argument("--launches", type=int, default=200, help="profile mode launches")
     ap.add_argument("--config", type=int, default=None, help="profile mode: force this kernel configuration")
+    ap.add_argument("--check-floor", action="store_true",
+                    help="exit with status 3 when a figure of bench_best.json falls below 97%% of its best")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the batch-16 list shards over images with no "
@@ -644,9 +564,9 @@ def main():
         results[key] = {"ms_per_step": ms_graph, "wall_ms_per_step": wall_graph, "ms_per_step_plain_launches": ms_list,
                         "flops": b.flops, "rows": rows, "sum_us_single_launch": round(sum(us_single), 2),
                         "sum_us_flushed": round(sum(us_flushed), 2)}
-        chosen = b.group_head(us_layers)
+        chosen = b.group_head()
         ms_grouped = b.time_grouped(steps, args.warmup)
-        launches = len(b.layers) - 2 * sum(1 for c in chosen if c[4])
+        launches = b.grouped_launches
         results[key]["grouped_head"] = {
             "ms_per_step": ms_grouped, "launches": launches,
             "groups": [{"layers": list(m), "config": c, "us": u, "us_separately": sep, "kept": kept}
@@ -748,6 +668,11 @@ def main():
                      "grouped_head": grouped_line(r)}
     line.update(tuned)
     line.update(chains)
+    floor_ok = True
+    if os.path.exists(FLOOR_FILE):
+        line["floor"], floor_ok = floor_check(line, json.load(open(FLOOR_FILE)))
+        if not floor_ok:
+            log("bench floor: below %.0f%% of the committed best: %s" % (100 * FLOOR_FRACTION, line["floor"]))
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(W)
     outdir = os.path.join(ROOT, "gpurun_out")
@@ -755,6 +680,8 @@ def main():
         with open(os.path.join(outdir, "bench_layers.json"), "w") as f:
             json.dump({"device": props.name, "results": results}, f, indent=1)
     print(json.dumps(line), flush=True)
+    if args.check_floor and not floor_ok:
+        sys.exit(3)
 
 
 if __name__ == "__main__":

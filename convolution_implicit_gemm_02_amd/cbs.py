@@ -6,6 +6,13 @@ kernels of libcbs.so.  Device buffers may be given as torch tensors (their
 ``torch.cuda.Stream`` objects, raw handles or None (the current torch stream).
 Host arrays (weights, BN parameters) are numpy arrays.
 
+A tensor handed to a run call is checked before the call: it must live on a
+GPU and its storage must hold, from the tensor's first byte, at least the
+bytes the layer reads or writes there (cbs_layer_info's in_bytes, out_bytes,
+res_bytes); the kernels take their buffer ranges from the layer, not from
+the allocation, so a host pointer or a short buffer would otherwise become an
+out-of-range device access.  Raw integer addresses are passed unchecked.
+
 torch is imported before libcbs.so is loaded so that both share the one HIP
 runtime (libamdhip64.so.7) that torch loads.  If libcbs.so is missing this
 module raises at import: there is no fallback path.
@@ -67,6 +74,11 @@ class cbs_layer_info_t(ctypes.Structure):
                 ("res_bytes", ctypes.c_int64)]
 
 
+class cbs_graph_group_info_t(ctypes.Structure):
+    _fields_ = [("group_id", ctypes.c_int32), ("members", ctypes.c_int32), ("kept", ctypes.c_int32),
+                ("config", ctypes.c_int32), ("us_grouped", ctypes.c_float), ("us_separate", ctypes.c_float)]
+
+
 class cbs_step(ctypes.Structure):
     _fields_ = [("layer", ctypes.c_void_p), ("in_", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("residual", ctypes.c_void_p)]
@@ -86,6 +98,10 @@ _SIGNATURES = {
     "cbs_run_layer_list": (_I, [ctypes.POINTER(_P), _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
     "cbs_graph_create": (_I, [ctypes.POINTER(_P), _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _P,
                               ctypes.POINTER(_P)]),
+    "cbs_graph_create_grouped": (_I, [ctypes.POINTER(_P), _I, ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                      ctypes.POINTER(_I), _P, ctypes.POINTER(_P)]),
+    "cbs_graph_info": (_I, [_P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "cbs_graph_group_info": (_I, [_P, _I, ctypes.POINTER(cbs_graph_group_info_t)]),
     "cbs_graph_launch": (_I, [_P, _P]),
     "cbs_graph_destroy": (None, [_P]),
     "cbs_group_create": (_I, [ctypes.POINTER(_P), _I, _I, ctypes.POINTER(_P)]),
@@ -128,12 +144,34 @@ def _check(status: int, where: str) -> None:
         raise CbsError(status, where, msg.decode() if msg else "")
 
 
-def _dev_ptr(buf) -> int:
+def _dev_ptr(buf, need: int = 0, what: str = "buffer") -> int:
+    """Device address of a tensor (or a raw address, unchecked).  A tensor must be
+    on a GPU and its storage must hold at least `need` bytes from its first byte."""
     if buf is None:
         return 0
     if isinstance(buf, int):
         return buf
-    return int(buf.data_ptr())
+    if not buf.is_cuda:
+        raise ValueError("%s is not on a GPU (device %s)" % (what, buf.device))
+    ptr = int(buf.data_ptr())
+    if need > 0:
+        st = buf.untyped_storage()
+        avail = int(st.data_ptr()) + int(st.nbytes()) - ptr
+        if avail < need:
+            raise ValueError("%s holds %d bytes from its start; the layer needs %d" % (what, avail, need))
+    return ptr
+
+
+def _in_ptr(layer, buf, what="input"):
+    return _dev_ptr(buf, layer.in_bytes, what)
+
+
+def _out_ptr(layer, buf, what="output"):
+    return _dev_ptr(buf, layer.out_bytes, what)
+
+
+def _res_ptr(layer, buf, what="residual"):
+    return _dev_ptr(buf, layer.res_bytes, what)
 
 
 def _stream(stream) -> int:
@@ -151,9 +189,20 @@ def _host(a, dtype):
 
 @dataclass
 class Layer:
-    """Handle of a created layer (a cbs_layer*), destroyed on garbage collection."""
+    """Handle of a created layer (a cbs_layer*), destroyed on garbage collection.
+    The byte counts are the buffer sizes a run reads or writes (cbs_layer_info)."""
     handle: int
     desc: cbs_conv_desc
+    in_bytes: int = 0
+    out_bytes: int = 0
+    res_bytes: int = 0
+    acc_bytes: int = 0  # int32 accumulators of cbs_run_layer_raw_acc
+
+    def __post_init__(self):
+        info = cbs_layer_info_t()
+        _check(lib.cbs_layer_info(self.handle, ctypes.byref(info)), "cbs_layer_info")
+        self.in_bytes, self.out_bytes, self.res_bytes = int(info.in_bytes), int(info.out_bytes), int(info.res_bytes)
+        self.acc_bytes = self.desc.n * info.oh * info.out_row_pitch * info.c_out_pad * 4
 
     def __del__(self):
         if getattr(self, "handle", 0) and lib is not None:
@@ -193,12 +242,13 @@ def cbs_destroy_layer(layer: Layer) -> None:
 
 
 def cbs_run_layer(layer: Layer, inp, out, stream=None) -> None:
-    _check(lib.cbs_run_layer(layer.handle, _dev_ptr(inp), _dev_ptr(out), _stream(stream)), "cbs_run_layer")
+    _check(lib.cbs_run_layer(layer.handle, _in_ptr(layer, inp), _out_ptr(layer, out), _stream(stream)),
+           "cbs_run_layer")
 
 
 def cbs_run_layer_res(layer: Layer, inp, out, residual, stream=None) -> None:
-    _check(lib.cbs_run_layer_res(layer.handle, _dev_ptr(inp), _dev_ptr(out), _dev_ptr(residual), _stream(stream)),
-           "cbs_run_layer_res")
+    _check(lib.cbs_run_layer_res(layer.handle, _in_ptr(layer, inp), _out_ptr(layer, out), _res_ptr(layer, residual),
+                                 _stream(stream)), "cbs_run_layer_res")
 
 
 def _step_array(steps):
@@ -207,7 +257,9 @@ def _step_array(steps):
     for i, st in enumerate(steps):
         layer, inp, out = st[:3]
         res = st[3] if len(st) > 3 else None
-        arr[i] = cbs_step(layer.handle, _dev_ptr(inp), _dev_ptr(out), _dev_ptr(res))
+        w = "step %d " % i
+        arr[i] = cbs_step(layer.handle, _in_ptr(layer, inp, w + "input"), _out_ptr(layer, out, w + "output"),
+                          _res_ptr(layer, res, w + "residual"))
     return arr
 
 
@@ -229,12 +281,32 @@ def _ptr_array(items):
     return arr
 
 
+def _list_arrays(layers, ins, outs):
+    if not (len(layers) == len(ins) == len(outs)):
+        raise ValueError("layers, ins and outs differ in length")
+    return (_ptr_array([l.handle for l in layers]),
+            _ptr_array([_in_ptr(l, b, "input %d" % i) for i, (l, b) in enumerate(zip(layers, ins))]),
+            _ptr_array([_out_ptr(l, b, "output %d" % i) for i, (l, b) in enumerate(zip(layers, outs))]))
+
+
 def cbs_run_layer_list(layers, ins, outs, stream=None) -> None:
-    n = len(layers)
-    _check(lib.cbs_run_layer_list(_ptr_array([l.handle for l in layers]), n,
-                                  _ptr_array([_dev_ptr(b) for b in ins]),
-                                  _ptr_array([_dev_ptr(b) for b in outs]), _stream(stream)),
-           "cbs_run_layer_list")
+    la, ia, oa = _list_arrays(layers, ins, outs)
+    _check(lib.cbs_run_layer_list(la, len(layers), ia, oa, _stream(stream)), "cbs_run_layer_list")
+
+
+class LayerList:
+    """A layer list marshalled once (pointer arrays built and checked here), so
+    that run() costs one C call: used where the host time of building the
+    arguments must stay out of a timed region."""
+
+    def __init__(self, layers, ins, outs):
+        self.n = len(layers)
+        self._arrays = _list_arrays(layers, ins, outs)
+        self._keep = (list(layers), list(ins), list(outs))
+
+    def run(self, stream=None) -> None:
+        la, ia, oa = self._arrays
+        _check(lib.cbs_run_layer_list(la, self.n, ia, oa, _stream(stream)), "cbs_run_layer_list")
 
 
 class Graph:
@@ -252,11 +324,34 @@ class Graph:
 
 def cbs_graph_create(layers, ins, outs, stream=None) -> Graph:
     h = _P()
-    _check(lib.cbs_graph_create(_ptr_array([l.handle for l in layers]), len(layers),
-                                _ptr_array([_dev_ptr(b) for b in ins]),
-                                _ptr_array([_dev_ptr(b) for b in outs]), _stream(stream), ctypes.byref(h)),
-           "cbs_graph_create")
+    la, ia, oa = _list_arrays(layers, ins, outs)
+    _check(lib.cbs_graph_create(la, len(layers), ia, oa, _stream(stream), ctypes.byref(h)), "cbs_graph_create")
     return Graph(h.value, (list(layers), list(ins), list(outs)))
+
+
+def cbs_graph_create_grouped(layers, ins, outs, group_of, stream=None) -> Graph:
+    """group_of: one int per layer, its candidate group (>= 0) or -1 (alone)."""
+    h = _P()
+    la, ia, oa = _list_arrays(layers, ins, outs)
+    if len(group_of) != len(layers):
+        raise ValueError("group_of has %d entries for %d layers" % (len(group_of), len(layers)))
+    ga = (_I * max(1, len(group_of)))(*[int(g) for g in group_of])
+    _check(lib.cbs_graph_create_grouped(la, len(layers), ia, oa, ga, _stream(stream), ctypes.byref(h)),
+           "cbs_graph_create_grouped")
+    return Graph(h.value, (list(layers), list(ins), list(outs)))
+
+
+def cbs_graph_info(graph: Graph):
+    """-> (kernel launches per replay, candidate groups)."""
+    a, b = _I(), _I()
+    _check(lib.cbs_graph_info(graph.handle, ctypes.byref(a), ctypes.byref(b)), "cbs_graph_info")
+    return a.value, b.value
+
+
+def cbs_graph_group_info(graph: Graph, i: int) -> dict:
+    info = cbs_graph_group_info_t()
+    _check(lib.cbs_graph_group_info(graph.handle, int(i), ctypes.byref(info)), "cbs_graph_group_info")
+    return {name: getattr(info, name) for name, _ in cbs_graph_group_info_t._fields_}
 
 
 def cbs_graph_launch(graph: Graph, stream=None) -> None:
@@ -293,8 +388,8 @@ def cbs_group_create(layers, config: int = -1) -> Group:
 
 
 def cbs_group_run(group: Group, ins, outs, stream=None) -> None:
-    _check(lib.cbs_group_run(group.handle, _ptr_array([_dev_ptr(b) for b in ins]),
-                             _ptr_array([_dev_ptr(b) for b in outs]), _stream(stream)), "cbs_group_run")
+    _, ia, oa = _list_arrays(group._layers, ins, outs)
+    _check(lib.cbs_group_run(group.handle, ia, oa, _stream(stream)), "cbs_group_run")
 
 
 def cbs_group_config(group: Group) -> int:
@@ -316,8 +411,9 @@ def cbs_layer_set_config(layer: Layer, config: int, splitk: int = 0) -> None:
 def cbs_layer_autotune(layer: Layer, inp, out, residual=None, iters=0, flags=0, stream=None):
     """Time every configuration on these buffers and keep the fastest; returns (config, splitk)."""
     c, k = _I(), _I()
-    _check(lib.cbs_layer_autotune(layer.handle, _dev_ptr(inp), _dev_ptr(out), _dev_ptr(residual), int(iters),
-                                  int(flags), _stream(stream), ctypes.byref(c), ctypes.byref(k)),
+    _check(lib.cbs_layer_autotune(layer.handle, _in_ptr(layer, inp), _out_ptr(layer, out),
+                                  _res_ptr(layer, residual), int(iters), int(flags), _stream(stream),
+                                  ctypes.byref(c), ctypes.byref(k)),
            "cbs_layer_autotune")
     return c.value, k.value
 
@@ -341,23 +437,28 @@ def cbs_last_error() -> str:
 
 
 def cbs_pack_nhwc_f32(nchw, nhwc, n, c, h, w, c_pad, stream=None) -> None:
-    _check(lib.cbs_pack_nhwc_f32(_dev_ptr(nchw), _dev_ptr(nhwc), n, c, h, w, c_pad, _stream(stream)),
+    _check(lib.cbs_pack_nhwc_f32(_dev_ptr(nchw, 4 * n * c * h * w, "NCHW input"),
+                                 _dev_ptr(nhwc, 4 * n * h * w * c_pad, "NHWC output"), n, c, h, w, c_pad,
+                                 _stream(stream)),
            "cbs_pack_nhwc_f32")
 
 
 def cbs_quantize_nhwc_i8(nchw, nhwc, s_x, n, c, h, w, c_pad, stream=None) -> None:
-    _check(lib.cbs_quantize_nhwc_i8(_dev_ptr(nchw), _dev_ptr(nhwc), float(s_x), n, c, h, w, c_pad,
+    _check(lib.cbs_quantize_nhwc_i8(_dev_ptr(nchw, 4 * n * c * h * w, "NCHW input"),
+                                    _dev_ptr(nhwc, n * h * w * c_pad, "NHWC output"), float(s_x), n, c, h, w, c_pad,
                                     _stream(stream)), "cbs_quantize_nhwc_i8")
 
 
 def cbs_quantize_nhwc_u8(nchw, nhwc, s_x, z, n, c, h, w, c_pad, stream=None) -> None:
-    _check(lib.cbs_quantize_nhwc_u8(_dev_ptr(nchw), _dev_ptr(nhwc), float(s_x), int(z), n, c, h, w, c_pad,
+    _check(lib.cbs_quantize_nhwc_u8(_dev_ptr(nchw, 4 * n * c * h * w, "NCHW input"),
+                                    _dev_ptr(nhwc, n * h * w * c_pad, "NHWC output"), float(s_x), int(z), n, c, h, w,
+                                    c_pad,
                                     _stream(stream)), "cbs_quantize_nhwc_u8")
 
 
 def cbs_run_layer_raw_acc(layer: Layer, inp, acc, stream=None) -> None:
-    _check(lib.cbs_run_layer_raw_acc(layer.handle, _dev_ptr(inp), _dev_ptr(acc), _stream(stream)),
-           "cbs_run_layer_raw_acc")
+    _check(lib.cbs_run_layer_raw_acc(layer.handle, _in_ptr(layer, inp), _dev_ptr(acc, layer.acc_bytes, "accumulators"),
+                                     _stream(stream)), "cbs_run_layer_raw_acc")
 
 
 def cbs_get_qweights(layer: Layer):

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -79,9 +80,17 @@ struct cbs_layer {
   void *d_wfrag_pair = nullptr;
   float *d_bias_pair = nullptr;
   float *d_dq_pair = nullptr;
+  // Cross-workgroup split-K partial tiles and arrival counters.  A captured
+  // graph holds these addresses in its kernel arguments, so they never move
+  // while a graph references the layer (graph_refs > 0): a configuration that
+  // needs more than the current capacity is then refused instead of
+  // reallocating.  Counters are zero between launches (each tile's last
+  // workgroup re-arms its own).
   float *d_ws = nullptr;
   unsigned *d_counters = nullptr;
-  size_t ws_bytes = 0, counters_len = 0;
+  size_t ws_bytes = 0, counters_len = 0;  // in use by the current configuration
+  size_t ws_cap = 0, counters_cap = 0;    // allocated
+  mutable std::atomic<int> graph_refs{0};
   // host copies for the test hooks
   std::vector<float> h_wfold;   // fp32 W' OIHW
   std::vector<float> h_bias;    // fp32 b'
@@ -89,9 +98,19 @@ struct cbs_layer {
   std::vector<double> h_sw;     // s_w
 };
 
+// Per candidate group of cbs_graph_create_grouped: what was measured and kept.
+struct GraphGroup {
+  int id = -1, members = 0, kept = 0, config = -1;
+  float us_grouped = 0.f, us_separate = 0.f;
+};
+
 struct cbs_graph {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  std::vector<const cbs_layer *> layers;  // each holds one graph reference (see cbs_layer::graph_refs)
+  std::vector<cbs_group *> groups;        // grouped launches owned by the graph
+  std::vector<GraphGroup> group_info;
+  int launches = 0;
 };
 
 // Independent layers run by one grouped launch.  The members are kept in
@@ -357,32 +376,62 @@ void release(cbs_layer *L) {
   L->d_bias = L->d_dq = L->d_ws = nullptr;
   L->d_corr = nullptr;
   L->d_counters = nullptr;
+  L->ws_cap = L->counters_cap = 0;
 }
 
-// (Re)allocate the split-K workspace and the zeroed arrival counters for the
-// layer's current configuration.  Runs at create / set_config only.
+// Partial-tile bytes and arrival counters that configuration cfg with a
+// cross-workgroup split of splitk needs for layer L (both 0 without a split).
+void splitk_need(const cbs_layer *L, int cfg, int splitk, size_t *ws_bytes, size_t *counters) {
+  *ws_bytes = 0;
+  *counters = 0;
+  if (splitk <= 1) return;
+  const KernelConfig &c = config(cfg);
+  int pxt, cot;
+  tiles_of(L, cfg, &pxt, &cot);
+  const size_t tiles = (size_t)pxt * cot;
+  const size_t tile_vecs = (size_t)c.wco * c.wpx * c.cb * c.pb * 64;
+  *ws_bytes = tiles * splitk * tile_vecs * 16;
+  *counters = tiles;
+}
+
+// Whether the layer's current workspace already holds what (cfg, splitk) needs.
+bool splitk_fits_workspace(const cbs_layer *L, int cfg, int splitk) {
+  size_t ws, cnt;
+  splitk_need(L, cfg, splitk, &ws, &cnt);
+  return ws <= L->ws_cap && cnt <= L->counters_cap;
+}
+
+// Make the split-K workspace and the zeroed arrival counters hold what the
+// layer's current configuration needs.  Runs at create, set_config and
+// autotune only.  The workspace only grows, and only while no graph holds
+// its address.
 cbs_status setup_splitk(cbs_layer *L) {
+  size_t ws, cnt;
+  splitk_need(L, L->config, L->splitk, &ws, &cnt);
+  if (ws <= L->ws_cap && cnt <= L->counters_cap) {
+    L->ws_bytes = ws;
+    L->counters_len = cnt;
+    return CBS_OK;
+  }
+  if (L->graph_refs.load() > 0)
+    return fail(CBS_EINVAL, "configuration %s with split-K %d needs a larger split-K workspace than the "
+                            "layer holds, and a live graph holds the current one's address; destroy the "
+                            "graph first", config(L->config).name, L->splitk);
   if (L->d_ws) (void)hipFree(L->d_ws);
   if (L->d_counters) (void)hipFree(L->d_counters);
   L->d_ws = nullptr;
   L->d_counters = nullptr;
-  L->ws_bytes = 0;
-  L->counters_len = 0;
-  if (L->splitk <= 1) return CBS_OK;
-  const KernelConfig &c = config(L->config);
-  int pxt, cot;
-  tiles_of(L, L->config, &pxt, &cot);
-  const size_t tiles = (size_t)pxt * cot;
-  const size_t tile_vecs = (size_t)c.wco * c.wpx * c.cb * c.pb * 64;
-  L->ws_bytes = tiles * L->splitk * tile_vecs * 16;
-  L->counters_len = tiles;
-  cbs_status st = dev_alloc((void **)&L->d_ws, L->ws_bytes);
+  L->ws_cap = L->counters_cap = 0;
+  L->ws_bytes = L->counters_len = 0;
+  cbs_status st = dev_alloc((void **)&L->d_ws, ws);
   if (st != CBS_OK) return st;
-  st = dev_alloc((void **)&L->d_counters, tiles * sizeof(unsigned));
+  st = dev_alloc((void **)&L->d_counters, cnt * sizeof(unsigned));
   if (st != CBS_OK) return st;
-  hipError_t e = hipMemset(L->d_counters, 0, tiles * sizeof(unsigned));
+  hipError_t e = hipMemset(L->d_counters, 0, cnt * sizeof(unsigned));
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return fail(CBS_EDEVICE, "counter init: %s", hipGetErrorString(e));
+  L->ws_cap = L->ws_bytes = ws;
+  L->counters_cap = L->counters_len = cnt;
   return CBS_OK;
 }
 
@@ -1025,24 +1074,58 @@ cbs_status cbs_run_steps(const cbs_step *steps, int32_t n, void *stream) {
 
 namespace {
 
-// Capture a validated step list into an instantiated graph.  The capture runs
-// on a private stream (the caller's may be the null stream, which cannot be
-// captured), at default priority.
-cbs_status capture(const std::vector<cbs_step> &steps, cbs_graph **out) {
+// One launch of a captured step list: a layer's own launch, or a grouped
+// launch (group != nullptr) of the layers `slots` of the list.
+struct Launch {
+  int step = -1;
+  cbs_group *group = nullptr;
+  std::vector<int> slots;
+};
+
+// Capture a validated step list into an instantiated graph, as the given
+// launches (in order).  The capture runs on a private stream (the caller's
+// may be the null stream, which cannot be captured), at default priority.
+// Every captured layer gets one graph reference, which keeps its split-K
+// workspace in place until the graph is destroyed.  On success the graph owns
+// the launches' groups; on failure they are destroyed.
+cbs_status capture(const std::vector<cbs_step> &steps, const std::vector<Launch> &launches, cbs_graph **out) {
   cbs_graph *G = new (std::nothrow) cbs_graph();
-  if (!G) return fail(CBS_ENOMEM, "host allocation");
+  if (!G) {
+    for (const Launch &l : launches) cbs_group_destroy(l.group);
+    return fail(CBS_ENOMEM, "host allocation");
+  }
+  for (const cbs_step &t : steps) {
+    t.layer->graph_refs.fetch_add(1);
+    G->layers.push_back(t.layer);
+  }
+  for (const Launch &l : launches)
+    if (l.group) G->groups.push_back(l.group);
+  G->launches = (int)launches.size();
   hipStream_t cs = nullptr;
   hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
   if (e != hipSuccess) {
-    delete G;
+    cbs_graph_destroy(G);
     return fail(CBS_EDEVICE, "capture stream: %s", hipGetErrorString(e));
   }
   e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   cbs_status st = CBS_OK;
   if (e != hipSuccess) st = fail(CBS_EDEVICE, "begin capture: %s", hipGetErrorString(e));
   if (st == CBS_OK) {
-    for (size_t i = 0; i < steps.size() && st == CBS_OK; i++)
-      st = launch(steps[i].layer, steps[i].in, steps[i].out, steps[i].residual, cs);
+    for (size_t i = 0; i < launches.size() && st == CBS_OK; i++) {
+      const Launch &l = launches[i];
+      if (!l.group) {
+        const cbs_step &t = steps[l.step];
+        st = launch(t.layer, t.in, t.out, t.residual, cs);
+      } else {
+        std::vector<const void *> ins;
+        std::vector<void *> outs;
+        for (int k : l.slots) {
+          ins.push_back(steps[k].in);
+          outs.push_back(steps[k].out);
+        }
+        st = cbs_group_run(l.group, ins.data(), outs.data(), cs);
+      }
+    }
     hipGraph_t g = nullptr;
     e = hipStreamEndCapture(cs, &g);
     if (st == CBS_OK && e != hipSuccess) st = fail(CBS_EDEVICE, "end capture: %s", hipGetErrorString(e));
@@ -1061,6 +1144,13 @@ cbs_status capture(const std::vector<cbs_step> &steps, cbs_graph **out) {
   return CBS_OK;
 }
 
+// One launch per step, in order.
+std::vector<Launch> plain_launches(size_t n) {
+  std::vector<Launch> v(n);
+  for (size_t i = 0; i < n; i++) v[i].step = (int)i;
+  return v;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1077,7 +1167,7 @@ cbs_status cbs_graph_create(cbs_layer *const *layers, int32_t n, const void *con
     if (st != CBS_OK) return st;
     steps[i] = cbs_step{layers[i], ins[i], outs[i], nullptr};
   }
-  return capture(steps, out);
+  return capture(steps, plain_launches(steps.size()), out);
 }
 
 cbs_status cbs_graph_create_steps(const cbs_step *steps, int32_t n, void *stream, cbs_graph **out) {
@@ -1089,7 +1179,233 @@ cbs_status cbs_graph_create_steps(const cbs_step *steps, int32_t n, void *stream
     cbs_status st = check_step(steps[i].layer, steps[i].in, steps[i].out, steps[i].residual, "graph_create_steps", i);
     if (st != CBS_OK) return st;
   }
-  return capture(std::vector<cbs_step>(steps, steps + n), out);
+  return capture(std::vector<cbs_step>(steps, steps + n), plain_launches(n), out);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Bytes a layer's run reads from its input pointer and writes from its output
+// pointer (the whole pixel rows, slices included, guard pixels included).
+int64_t in_span(const cbs_layer *L) {
+  return (int64_t)L->d.n * L->d.h * L->d.w * L->in_cs * (L->d.dtype == CBS_F32 ? 4 : 1);
+}
+int64_t out_span(const cbs_layer *L) {
+  return (int64_t)L->d.n * L->oh * L->pitch * L->out_cs * (L->d.out_dtype == CBS_F32 ? 4 : 1);
+}
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
+  const char *pa = (const char *)a, *pb = (const char *)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+// Microseconds per copy of the work that enqueue(stream) enqueues, timed as
+// replays of a graph holding `reps` back-to-back copies of it on a private
+// stream: the best of `rounds` replays after one warm-up replay.
+template <class F>
+cbs_status time_replays(F enqueue, int reps, int rounds, float *us) {
+  hipStream_t cs = nullptr;
+  hipGraph_t g = nullptr;
+  hipGraphExec_t ex = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess)
+    return fail(CBS_EDEVICE, "timing: stream creation failed");
+  cbs_status st = CBS_OK;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess)
+    st = fail(CBS_EDEVICE, "timing: begin capture failed");
+  if (st == CBS_OK) {
+    for (int i = 0; i < reps && st == CBS_OK; i++) st = enqueue(cs);
+    const hipError_t e = hipStreamEndCapture(cs, &g);
+    if (st == CBS_OK && e != hipSuccess) st = fail(CBS_EDEVICE, "timing: end capture: %s", hipGetErrorString(e));
+  }
+  if (st == CBS_OK && hipGraphInstantiate(&ex, g, nullptr, nullptr, 0) != hipSuccess)
+    st = fail(CBS_EDEVICE, "timing: graph instantiate failed");
+  if (st == CBS_OK && (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess))
+    st = fail(CBS_EDEVICE, "timing: event creation failed");
+  float best = 1e30f;
+  if (st == CBS_OK && (hipGraphLaunch(ex, cs) != hipSuccess || hipStreamSynchronize(cs) != hipSuccess))
+    st = fail(CBS_EDEVICE, "timing: warm-up replay failed");
+  for (int r = 0; r < rounds && st == CBS_OK; r++) {
+    float ms = 0.f;
+    if (hipEventRecord(e0, cs) != hipSuccess || hipGraphLaunch(ex, cs) != hipSuccess ||
+        hipEventRecord(e1, cs) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+      st = fail(CBS_EDEVICE, "timing: replay failed");
+    else
+      best = std::min(best, ms);
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (ex) (void)hipGraphExecDestroy(ex);
+  if (g) (void)hipGraphDestroy(g);
+  (void)hipStreamDestroy(cs);
+  *us = best * 1000.f / (float)reps;
+  return st;
+}
+
+constexpr int kGroupTimingReps = 20, kGroupTimingRounds = 5;
+
+}  // namespace
+
+extern "C" {
+
+cbs_status cbs_graph_create_grouped(cbs_layer *const *layers, int32_t n, const void *const *ins,
+                                    void *const *outs, const int32_t *group_of, void *stream, cbs_graph **out) {
+  (void)stream;
+  if (!out) return fail(CBS_EINVAL, "graph_create_grouped: out is NULL");
+  *out = nullptr;
+  if (n < 1 || !layers || !ins || !outs) return fail(CBS_EINVAL, "graph_create_grouped: bad arguments");
+  std::vector<cbs_step> steps(n);
+  for (int32_t i = 0; i < n; i++) {
+    cbs_status st = check_step(layers[i], ins[i], outs[i], nullptr, "graph_create_grouped", i);
+    if (st != CBS_OK) return st;
+    steps[i] = cbs_step{layers[i], ins[i], outs[i], nullptr};
+  }
+  if (!group_of) return capture(steps, plain_launches(steps.size()), out);
+
+  // candidate groups, in order of their first member
+  std::vector<int> ids;
+  std::map<int, std::vector<int>> members;
+  for (int32_t i = 0; i < n; i++) {
+    const int g = group_of[i];
+    if (g < -1) return fail(CBS_EINVAL, "graph_create_grouped: group_of[%d] = %d (must be >= -1)", (int)i, g);
+    if (g < 0) continue;
+    if (!members.count(g)) ids.push_back(g);
+    members[g].push_back((int)i);
+  }
+  // Each group's launch takes the place of its last member, so that every
+  // producer of a member's input runs before it.  That is only the same
+  // computation if no member reads another member's output and no layer
+  // between the group's first and last member depends on a member that it
+  // would now run before.
+  for (int g : ids) {
+    const std::vector<int> &m = members[g];
+    if ((int)m.size() > kGroupMax)
+      return fail(CBS_EINVAL, "graph_create_grouped: group %d has %d layers (at most %d)", g, (int)m.size(),
+                  kGroupMax);
+    for (int a : m)
+      for (int b : m) {
+        if (a == b) continue;
+        if (overlap(outs[a], out_span(layers[a]), ins[b], in_span(layers[b])) ||
+            overlap(outs[a], out_span(layers[a]), outs[b], out_span(layers[b])))
+          return fail(CBS_EINVAL, "graph_create_grouped: group %d: layer %d's output overlaps layer %d's input or "
+                                  "output", g, a, b);
+      }
+    for (int j = m.front() + 1; j < m.back(); j++) {
+      if (group_of[j] == g) continue;
+      for (int a : m) {
+        if (a > j) continue;
+        if (overlap(outs[a], out_span(layers[a]), ins[j], in_span(layers[j])) ||
+            overlap(outs[j], out_span(layers[j]), ins[a], in_span(layers[a])) ||
+            overlap(outs[j], out_span(layers[j]), outs[a], out_span(layers[a])))
+          return fail(CBS_EINVAL, "graph_create_grouped: group %d: layer %d between its members shares a buffer "
+                                  "with member %d", g, j, a);
+      }
+    }
+  }
+
+  // measure each candidate: the members' separate launches against the group
+  // under every register-direct and LDS-staged configuration that fits
+  std::vector<GraphGroup> info;
+  std::map<int, cbs_group *> kept;
+  cbs_status st = CBS_OK;
+  for (int g : ids) {
+    const std::vector<int> &m = members[g];
+    GraphGroup gi;
+    gi.id = g;
+    gi.members = (int)m.size();
+    std::vector<cbs_layer *> ml;
+    std::vector<const void *> mi;
+    std::vector<void *> mo;
+    for (int k : m) {
+      ml.push_back(layers[k]);
+      mi.push_back(ins[k]);
+      mo.push_back(outs[k]);
+    }
+    float sep = 0.f;
+    for (size_t k = 0; k < m.size() && st == CBS_OK; k++) {
+      float us = 0.f;
+      const cbs_layer *L = ml[k];
+      const void *in = mi[k];
+      void *o = mo[k];
+      st = time_replays([&](hipStream_t cs) { return launch(L, in, o, nullptr, cs); }, kGroupTimingReps,
+                        kGroupTimingRounds, &us);
+      sep += us;
+    }
+    gi.us_separate = sep;
+    cbs_group *best = nullptr;
+    float best_us = 1e30f;
+    for (int cfg = 0; cfg < num_configs() && st == CBS_OK && m.size() > 1; cfg++) {
+      if (config(cfg).lds > 1) continue;
+      cbs_group *grp = nullptr;
+      if (cbs_group_create(ml.data(), (int32_t)ml.size(), cfg, &grp) != CBS_OK) continue;  // does not fit
+      float us = 0.f;
+      st = time_replays([&](hipStream_t cs) { return cbs_group_run(grp, mi.data(), mo.data(), cs); },
+                        kGroupTimingReps, kGroupTimingRounds, &us);
+      if (st == CBS_OK && us < best_us) {
+        cbs_group_destroy(best);
+        best = grp;
+        best_us = us;
+      } else {
+        cbs_group_destroy(grp);
+      }
+    }
+    if (best) {
+      gi.config = best->config;
+      gi.us_grouped = best_us;
+    }
+    if (best && st == CBS_OK && best_us < sep) {
+      gi.kept = 1;
+      kept[g] = best;
+    } else {
+      cbs_group_destroy(best);
+    }
+    info.push_back(gi);
+  }
+  if (st == CBS_OK && !ids.empty() && info.empty()) st = fail(CBS_EINVAL, "graph_create_grouped: no group");
+  if (st != CBS_OK) {
+    for (auto &kv : kept) cbs_group_destroy(kv.second);
+    return st;
+  }
+  std::vector<Launch> launches;
+  for (int32_t i = 0; i < n; i++) {
+    const int g = group_of[i];
+    if (g < 0 || !kept.count(g)) {
+      Launch l;
+      l.step = (int)i;
+      launches.push_back(l);
+    } else if (members[g].back() == (int)i) {
+      Launch l;
+      l.group = kept[g];
+      l.slots = members[g];
+      launches.push_back(l);
+    }
+  }
+  st = capture(steps, launches, out);
+  if (st == CBS_OK) (*out)->group_info = info;
+  return st;
+}
+
+cbs_status cbs_graph_info(const cbs_graph *graph, int32_t *launches, int32_t *groups) {
+  if (!graph) return fail(CBS_EINVAL, "graph_info: null graph");
+  if (launches) *launches = graph->launches;
+  if (groups) *groups = (int32_t)graph->group_info.size();
+  return CBS_OK;
+}
+
+cbs_status cbs_graph_group_info(const cbs_graph *graph, int32_t i, cbs_graph_group_info_t *info) {
+  if (!graph || !info) return fail(CBS_EINVAL, "graph_group_info: null argument");
+  if (i < 0 || i >= (int32_t)graph->group_info.size())
+    return fail(CBS_EINVAL, "graph_group_info: group %d out of range", (int)i);
+  const GraphGroup &g = graph->group_info[i];
+  std::memset(info, 0, sizeof(*info));
+  info->group_id = g.id;
+  info->members = g.members;
+  info->kept = g.kept;
+  info->config = g.config;
+  info->us_grouped = g.us_grouped;
+  info->us_separate = g.us_separate;
+  return CBS_OK;
 }
 
 cbs_status cbs_graph_launch(const cbs_graph *graph, void *stream) {
@@ -1103,6 +1419,8 @@ void cbs_graph_destroy(cbs_graph *graph) {
   if (!graph) return;
   if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
   if (graph->graph) (void)hipGraphDestroy(graph->graph);
+  for (cbs_group *g : graph->groups) cbs_group_destroy(g);
+  for (const cbs_layer *L : graph->layers) L->graph_refs.fetch_sub(1);
   delete graph;
 }
 
@@ -1232,6 +1550,8 @@ cbs_status cbs_layer_autotune(cbs_layer *L, const void *in, void *out, const voi
           int pxt, cot;
           tiles_of(L, cfg, &pxt, &cot);
           if ((long)pxt * cot >= 256) continue;
+          // a live graph holds the workspace's address: only what fits it
+          if (L->graph_refs.load() > 0 && !splitk_fits_workspace(L, cfg, sk)) continue;
         }
         L->config = cfg;
         L->splitk = sk;

@@ -207,18 +207,75 @@ cbs_status cbs_run_layer_res(const cbs_layer *layer, const void *in, void *out, 
 /*
  * Enqueue layers[0..n-1] in order on one stream, layer i reading ins[i] and
  * writing outs[i] (any of them may alias another layer's output to chain
- * layers).  Stops at the first failing launch and returns its status.
+ * layers).  Stops at the first failing launch and returns its status.  The
+ * whole shape table of a network runs back to back with nothing between the
+ * convolutions: no per-call memset or scratch allocation ("YOLO26N Inference
+ * Optimisation", "Improvements" #5, persistent scratch) and no layout change
+ * inside the graph ("NHWC migration", the all-or-nothing constraint).
  */
 cbs_status cbs_run_layer_list(cbs_layer *const *layers, int32_t n, const void *const *ins,
                               void *const *outs, void *stream);
 
 /*
- * Capture the same layer list, with these buffers, into a HIP graph (stream
- * capture on `stream`, which must not be capturing already), instantiate it
- * and return it in *out.  The layers and buffers must outlive the graph.
+ * Capture the same layer list, with these buffers, into a HIP graph and
+ * instantiate it (the capture runs on a private stream; `stream` is unused).
+ * The layers and buffers must outlive the graph.  The graph keeps the
+ * addresses of each layer's split-K workspace in its kernel arguments, so
+ * while it exists cbs_layer_set_config refuses a configuration that would
+ * need a larger workspace (CBS_EINVAL), and cbs_layer_autotune skips such
+ * configurations; a replay always runs the configurations captured.  This is
+ * the vision-rs page's CUDA-graph replay of the whole forward pass ("YOLO26N
+ * Inference Optimisation": the runtime line of its header, and "Baseline
+ * benchmark", which credits graph capture for beating eager PyTorch).
  */
 cbs_status cbs_graph_create(cbs_layer *const *layers, int32_t n, const void *const *ins,
                             void *const *outs, void *stream, cbs_graph **out);
+
+/*
+ * The same capture with independent layers merged into grouped launches
+ * (see cbs_group_create) where that measures faster: the page's observation
+ * that a small kernel leaves the GPU nearly idle while every launch costs a
+ * few microseconds ("YOLO26N Inference Optimisation", "Key observations" 1
+ * and 4), applied to layers that do not depend on each other, such as the
+ * three scales of a detection head.
+ *
+ * group_of[i] >= 0 names layer i's candidate group, -1 leaves it alone;
+ * group_of == NULL is cbs_graph_create.  A group has at most CBS_GROUP_MAX
+ * layers of one kernel variant without residual (cbs_group_create's rules).
+ * Its launch takes the place of its last member in the list, so no member may
+ * read or overlap another member's output, and no layer between its first
+ * and last member may read a member's output or write a member's input or
+ * output: all of this is checked on the buffer ranges the layers read and
+ * write (CBS_EINVAL otherwise).  For each candidate the library times, on
+ * these buffers, its members' separate launches and the grouped launch under
+ * every register-direct and LDS-staged configuration that fits (each as
+ * replays of 20 back-to-back launches, best of 5), and keeps the fastest
+ * grouped launch only if it beats the separate ones.  This blocks for the
+ * timing, writes the outputs as runs do, and allocates the groups' split-K
+ * workspaces, which the graph owns.  Errors as cbs_graph_create, plus
+ * CBS_EINVAL for a bad grouping.
+ */
+cbs_status cbs_graph_create_grouped(cbs_layer *const *layers, int32_t n, const void *const *ins,
+                                    void *const *outs, const int32_t *group_of, void *stream,
+                                    cbs_graph **out);
+
+/* Kernel launches per replay of a graph, and the number of candidate groups
+ * it was created with (0 unless by cbs_graph_create_grouped).  Either pointer
+ * may be NULL. */
+cbs_status cbs_graph_info(const cbs_graph *graph, int32_t *launches, int32_t *groups);
+
+typedef struct cbs_graph_group_info_t {
+    int32_t group_id;  /* the caller's group id */
+    int32_t members;   /* layers in the group */
+    int32_t kept;      /* 1: runs as one grouped launch; 0: its members run separately */
+    int32_t config;    /* configuration of the fastest grouped launch (-1: none fit) */
+    float us_grouped;  /* measured microseconds of that grouped launch */
+    float us_separate; /* measured microseconds of the members' separate launches, summed */
+} cbs_graph_group_info_t;
+
+/* What cbs_graph_create_grouped measured and chose for candidate group i
+ * (0 <= i < the count from cbs_graph_info, in order of first member). */
+cbs_status cbs_graph_group_info(const cbs_graph *graph, int32_t i, cbs_graph_group_info_t *info);
 /*
  * One step of a chained block: a layer with its input, output and residual
  * (NULL unless the layer was created with one).  Consecutive steps share
@@ -295,6 +352,10 @@ cbs_status cbs_layer_info(const cbs_layer *layer, cbs_layer_info_t *info);
  * default for that config).  Returns CBS_EUNSUPPORTED when the configuration
  * cannot run this layer (the layer is then unchanged).  Used by tests, which
  * force every configuration on every shape, and by the offline tile sweep.
+ * A cross-workgroup split-K needs a workspace of partial tiles; the layer
+ * keeps the largest it has allocated (it never shrinks).  While a graph holds
+ * the layer (cbs_graph_create*), a configuration that needs more returns
+ * CBS_EINVAL and the layer is unchanged.
  */
 cbs_status cbs_layer_set_config(cbs_layer *layer, int32_t config, int32_t splitk);
 int32_t cbs_num_configs(void);
@@ -306,7 +367,8 @@ int32_t cbs_num_configs(void);
  * kernel configuration that can run this layer (split-K 1, plus 2, 3 and 4 for
  * register-direct configurations whose grid is below 256 workgroups) with
  * `iters` launches each (0 = 20) after two warm-ups, with HIP events on
- * `stream`, on the caller's buffers, and keeps the fastest.  The choice is
+ * `stream`, on the caller's buffers, and keeps the fastest (while a graph
+ * holds the layer, only split-K factors that fit its current workspace).  The choice is
  * cached in the process per device, shape, dtype, epilogue and channel
  * strides: a later call for the same key takes it without timing, unless
  * flags has CBS_TUNE_FORCE.  Blocks until the timing is done, may allocate

@@ -39,6 +39,13 @@ SENT_I8 = np.int8(-91)                              # 0xA5
 SENT_U8 = np.uint8(0xA5)
 RES_TERM = 2.0 ** -22
 I8_BAND = 2.0 ** -18
+# Largest share of byte codes allowed inside the ambiguity band, so that the
+# check stays close to exact.  The oracle alone fixes the band: over every
+# byte-output case of this file it holds at most 9.8% of the codes (mean 4.1%)
+# when the convolution is FP32 (the band is the FP32 tolerance 1e-4 * S) and
+# at most 0.22% for integer convolutions (the fp32 epilogue's bound).
+AMBIGUOUS_F32_CONV = 0.12
+AMBIGUOUS_INT_CONV = 0.005
 
 
 def dev():
@@ -254,7 +261,7 @@ def check(case, prep, got):
     assert not bad.any(), "%r: %d/%d codes outside the accepted interval (e.g. got %s want %s..%s)" % (
         case, int(bad.sum()), bad.size, g[bad][:5], lo[bad][:5], hi[bad][:5])
     ambiguous = int(np.count_nonzero(lo != hi))
-    limit = 0.5 if case.dtype == "f32" else 0.02
+    limit = AMBIGUOUS_F32_CONV if case.dtype == "f32" else AMBIGUOUS_INT_CONV
     assert ambiguous <= limit * g.size, "%r: %d/%d codes within the band: the check is too weak" % (
         case, ambiguous, g.size)
     return ambiguous

@@ -9,7 +9,8 @@ are +0.0.
 
 Workloads (seeded, synthetic): one 3x3 32->32 layer on 40x40; the ragged
 sweep at output widths 80/40/20; the large-spatial stem layers; the 37-layer
-YOLO26n-shaped list at batch 1 (every output) and batch 16 (sampled outputs).
+YOLO26n-shaped list at batch 1 and batch 16, every output compared with the
+whole-tensor oracle.
 """
 import numpy as np
 import pytest
@@ -137,29 +138,16 @@ def test_f32_yolo26n_list_bs1():
         _check_f32_full(L)
 
 
-def test_f32_yolo26n_list_bs16_sampled():
-    rng = np.random.default_rng(16)
+def test_f32_yolo26n_list_bs16_full():
+    """Every output of the batch-16 list against the whole-tensor oracle (FP32 bound),
+    guards and padded lanes included."""
     for L in W.generate("yolo26n", n=16, seed=0):
-        r = run_f32(L)
-        sp = L.spec
-        pts = sample_points(rng, L.n, sp.c_out, sp.oh, sp.ow, 600)
-        y, s = oracle.conv_bn_silu_f32_points(L.x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, sp.stride, sp.pad, pts)
-        got = r["y"][pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
-        assert_f32_parity(got, y, s, "%s bs16" % sp.name)
-        assert check_guards(r["host"], L, r["info"]) == 0
-        assert np.all(r["valid"][..., sp.c_out:] == 0)
-        assert np.isfinite(r["y"]).all()
+        _check_f32_full(L)
 
 
-def test_f32_ragged_bs16_sampled():
-    rng = np.random.default_rng(17)
+def test_f32_ragged_and_stem_batched_full():
     for L in W.generate("ragged", n=16, seed=0) + W.generate("stem", n=2, seed=0):
-        r = run_f32(L)
-        sp = L.spec
-        pts = sample_points(rng, L.n, sp.c_out, sp.oh, sp.ow, 600)
-        y, s = oracle.conv_bn_silu_f32_points(L.x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, sp.stride, sp.pad, pts)
-        assert_f32_parity(r["y"][pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]], y, s, sp.name)
-        assert check_guards(r["host"], L, r["info"]) == 0
+        _check_f32_full(L)
 
 
 def _small_cases():
@@ -251,25 +239,67 @@ def test_determinism_and_streams():
         assert np.array_equal(a, b), cbs.cbs_layer_info(layer)["config_name"]
 
 
-def test_layer_list_and_graph_replay():
-    """cbs_run_layer_list and a captured graph give the eager per-layer results;
-    the graph is replayed several times with other work in between."""
-    layers_in = W.generate("ragged", n=1, seed=3)[:4]
-    layers, ins, outs, eager = [], [], [], []
-    for L in layers_in:
-        layer = create(L, cbs.CBS_F32)
-        xin = pack_input(L, cbs.CBS_F32)
+def _list_case():
+    """Six layers for the list and graph tests: FP32 ragged layers (one forced to a
+    cross-workgroup split-K), and INT8 layers (one forced to split-K as well).
+    Returns [(LayerInputs, dtype, s_x, layer, input, output buffer)] and the oracle
+    answers [(y, bound)]."""
+    rows, refs = [], []
+    fp = W.generate("ragged", n=1, seed=3)[:4]
+    i8 = W.generate("ragged", n=1, seed=4)[2:4]
+    for k, (L, dt) in enumerate([(L, cbs.CBS_F32) for L in fp] + [(L, cbs.CBS_I8) for L in i8]):
+        s_x = W.calibration_scale(L.x) if dt == cbs.CBS_I8 else None
+        layer = create(L, dt, s_x=s_x)
+        if k in (2, 4):  # the 256-channel 20x20 3x3 layers: force a split-K register-direct configuration
+            for cfg in range(cbs.cbs_num_configs()):
+                try:
+                    cbs.cbs_layer_set_config(layer, cfg, 3)
+                    break
+                except cbs.CbsError:
+                    continue
+            assert cbs.cbs_layer_info(layer)["splitk"] == 3
+        xin = pack_input(L, dt, s_x=s_x)
         buf, info = alloc_out(L, layer)
+        rows.append((L, dt, s_x, layer, xin, buf))
+        if dt == cbs.CBS_F32:
+            y, b = _oracle_f32(L)
+            refs.append((y, 1e-4 * b + 1e-6))
+        else:
+            r = oracle.conv_bn_silu_i8(L.x, s_x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, L.spec.stride,
+                                       L.spec.pad)
+            refs.append((r["y"], 1e-4 * r["f"].astype(np.float64)[None, :, None, None] * r["absacc"] + 1e-6))
+    return rows, refs
+
+
+def _check_list_outputs(rows, refs, what):
+    for (L, dt, s_x, layer, xin, buf), (y, tol) in zip(rows, refs):
+        info = cbs.cbs_layer_info(layer)
+        host = buf.cpu().numpy()
+        valid, _, _ = split_out(host, L, info)
+        got = valid.view(np.float32)[..., : L.spec.c_out].transpose(0, 3, 1, 2)
+        name = "%s %s %s" % (what, L.spec.name, info["config_name"])
+        err = np.abs(got.astype(np.float64) - y)
+        assert not np.isnan(got).any() and not (err > tol).any(), name + ": outside tolerance"
+        assert check_guards(host, L, info) == 0, name + ": guard pixels written"
+
+
+def test_layer_list_and_graph_replay():
+    """cbs_run_layer_list and a captured graph, FP32 and INT8 layers with forced split-K
+    among them, against the oracle; the graph is replayed several times with other
+    eager work in between (every replay re-arms the split-K tickets)."""
+    rows, refs = _list_case()
+    layers, ins, outs = [r[3] for r in rows], [r[4] for r in rows], [r[5] for r in rows]
+    eager = []
+    for layer, xin, buf in zip(layers, ins, outs):
         cbs.cbs_run_layer(layer, xin, buf)
-        torch.cuda.synchronize()
-        eager.append(buf.cpu().numpy())
-        layers.append(layer)
-        ins.append(xin)
-        outs.append(buf)
+    torch.cuda.synchronize()
+    _check_list_outputs(rows, refs, "eager")
+    eager = [b.cpu().numpy() for b in outs]
     for b in outs:
         b.fill_(int(SENTINEL))
     cbs.cbs_run_layer_list(layers, ins, outs)
     torch.cuda.synchronize()
+    _check_list_outputs(rows, refs, "list")
     for e, b in zip(eager, outs):
         assert np.array_equal(e, b.cpu().numpy())
     g = cbs.cbs_graph_create(layers, ins, outs)
@@ -279,9 +309,93 @@ def test_layer_list_and_graph_replay():
         torch.cuda.synchronize()
         cbs.cbs_graph_launch(g)
         torch.cuda.synchronize()
+        _check_list_outputs(rows, refs, "replay %d" % rep)
         for e, b in zip(eager, outs):
             assert np.array_equal(e, b.cpu().numpy()), "replay %d" % rep
         _ = torch.randn(1000, device=dev()).sum().item()  # unrelated eager work between replays
+
+
+def test_graph_keeps_splitk_workspace():
+    """A graph holds its layers' split-K workspace addresses: while it lives, a
+    configuration needing a larger workspace is refused (the layer is unchanged), a
+    smaller one is accepted without moving the workspace, and replays still run the
+    captured configuration correctly; after the graph is destroyed the larger one is
+    accepted."""
+    rng = np.random.default_rng(12)
+    L = W.draw_layer(rng, W.LayerSpec("ws", 128, 128, 20, 20, 3, 1, 1), 1)
+    y, b = _oracle_f32(L)
+    tol = 1e-4 * b + 1e-6
+    layer = create(L, cbs.CBS_F32)
+    cfg = None
+    for c in range(cbs.cbs_num_configs()):
+        try:
+            cbs.cbs_layer_set_config(layer, c, 2)
+            cfg = c
+            break
+        except cbs.CbsError:
+            continue
+    assert cfg is not None
+    xin = pack_input(L, cbs.CBS_F32)
+    buf, info = alloc_out(L, layer)
+    g = cbs.cbs_graph_create([layer], [xin], [buf])
+    with pytest.raises(cbs.CbsError) as e:
+        cbs.cbs_layer_set_config(layer, cfg, 4)  # twice the partial tiles
+    assert e.value.status == cbs.CBS_EINVAL
+    assert cbs.cbs_layer_info(layer)["splitk"] == 2
+    cbs.cbs_layer_set_config(layer, cfg, 1)      # fits: accepted, the workspace stays
+    for rep in range(3):
+        buf.fill_(int(SENTINEL))
+        torch.cuda.synchronize()
+        cbs.cbs_graph_launch(g)                  # still the captured split-K 2
+        torch.cuda.synchronize()
+        host = buf.cpu().numpy()
+        got = split_out(host, L, info)[0].view(np.float32)[..., : L.spec.c_out].transpose(0, 3, 1, 2)
+        assert not (np.abs(got.astype(np.float64) - y) > tol).any(), "replay %d" % rep
+        assert check_guards(host, L, info) == 0
+        r = run_f32(L, layer=layer)              # eager split-K 1 in between
+        assert_f32_parity(r["y"], y, b, "eager sk1")
+    del g
+    import gc
+    gc.collect()
+    cbs.cbs_layer_set_config(layer, cfg, 4)
+    r = run_f32(L, layer=layer)
+    assert_f32_parity(r["y"], y, b, "sk4 after the graph")
+
+
+def test_graph_create_grouped():
+    """cbs_graph_create_grouped: the grouped step gives the oracle's outputs whether a
+    group is kept or not, reports its measurements, and refuses groupings that would
+    reorder dependent layers."""
+    rows, refs = _list_case()
+    rows, refs = rows[:4], refs[:4]  # FP32 layers: one variant
+    layers, ins, outs = [r[3] for r in rows], [r[4] for r in rows], [r[5] for r in rows]
+    g = cbs.cbs_graph_create_grouped(layers, ins, outs, [0, 1, 0, 1])
+    launches, ngroups = cbs.cbs_graph_info(g)
+    assert ngroups == 2
+    infos = [cbs.cbs_graph_group_info(g, i) for i in range(2)]
+    assert [i["group_id"] for i in infos] == [0, 1] and all(i["members"] == 2 for i in infos)
+    assert launches == 4 - sum(i["kept"] for i in infos)
+    assert all(i["us_separate"] > 0 for i in infos)
+    for rep in range(2):
+        for b in outs:
+            b.fill_(int(SENTINEL))
+        torch.cuda.synchronize()
+        cbs.cbs_graph_launch(g)
+        torch.cuda.synchronize()
+        _check_list_outputs(rows, refs, "grouped replay %d" % rep)
+    # a member reading another member's output: layer 0 writes a buffer that layer 1 reads
+    shared = torch.empty(max(layers[0].out_bytes, layers[1].in_bytes), dtype=torch.uint8, device=dev())
+    with pytest.raises(cbs.CbsError) as e:
+        cbs.cbs_graph_create_grouped(layers[:2], [ins[0], shared], [shared, outs[1]], [0, 0])
+    assert e.value.status == cbs.CBS_EINVAL
+    # a layer between two members reading the first member's output
+    with pytest.raises(cbs.CbsError):
+        cbs.cbs_graph_create_grouped(layers[:3], [ins[0], shared, ins[2]], [shared, outs[1], outs[2]], [0, -1, 0])
+    # more than CBS_GROUP_MAX members, a bad id
+    with pytest.raises(cbs.CbsError):
+        cbs.cbs_graph_create_grouped(layers + layers[:1], ins + ins[:1], outs + outs[:1], [0] * 5)
+    with pytest.raises(cbs.CbsError):
+        cbs.cbs_graph_create_grouped(layers, ins, outs, [0, -2, 0, 1])
 
 
 # ----------------------------------------------------------------- INT8 --
@@ -297,21 +411,11 @@ def test_i8_yolo26n_list_bs1():
         _check_i8_full(L)
 
 
-def test_i8_yolo26n_list_bs16_sampled():
-    rng = np.random.default_rng(26)
+def test_i8_yolo26n_list_bs16_full():
+    """Every int32 accumulator of the batch-16 list bit-exact, every output within the
+    INT8 bound, against the whole-tensor oracle."""
     for L in W.generate("yolo26n", n=16, seed=0):
-        s_x = W.calibration_scale(L.x)
-        r = run_i8(L, s_x)
-        sp = L.spec
-        pts = sample_points(rng, L.n, sp.c_out, sp.oh, sp.ow, 600)
-        y, acc, absacc = oracle.conv_bn_silu_i8_points(L.x, s_x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps,
-                                                       sp.stride, sp.pad, pts)
-        got_acc = r["acc"][pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]]
-        assert np.array_equal(got_acc, acc), sp.name
-        f = (np.float64(s_x) * cbs.cbs_get_qweights(r["layer"])[1]).astype(np.float32)
-        tol_abs = f.astype(np.float64)[pts[:, 1]] * absacc
-        assert_i8_parity(r["y"][pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]], y, None, tol_abs, sp.name)
-        assert check_guards(r["host"], L, r["info"]) == 0
+        _check_i8_full(L)
 
 
 def test_i8_small_and_random_shapes():

@@ -262,3 +262,52 @@ def test_tile_table_entries(cbs):
             assert k == 3 and s == 1 and c_out <= 8, r
         if cls in (2, 3):
             assert (n, c_in, c_out, h, w, k, s, 1) in set(keys), r
+
+
+def test_binding_rejects_host_and_short_buffers(cbs):
+    """The binding checks tensors before a run call reaches the library: a CPU tensor,
+    or a device tensor whose storage holds fewer bytes (from its first byte) than the
+    layer reads or writes there, raises ValueError; raw addresses pass unchecked."""
+    import torch
+    from types import SimpleNamespace
+
+    layer = SimpleNamespace(handle=0, in_bytes=1024, out_bytes=4096, res_bytes=0, acc_bytes=4096)
+    host = torch.zeros(1024, dtype=torch.float32)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        cbs.cbs_run_layer(layer, host, host)
+
+    class FakeStorage:
+        def __init__(self, base, nbytes):
+            self.base, self.n = base, nbytes
+
+        def data_ptr(self):
+            return self.base
+
+        def nbytes(self):
+            return self.n
+
+    class FakeDeviceTensor:  # stands in for a GPU tensor: a view starting `off` bytes into its storage
+        is_cuda = True
+        device = "cuda:0"
+
+        def __init__(self, nbytes, off=0):
+            self.st, self.off = FakeStorage(1 << 20, nbytes), off
+
+        def data_ptr(self):
+            return self.st.base + self.off
+
+        def untyped_storage(self):
+            return self.st
+
+    assert cbs._dev_ptr(FakeDeviceTensor(1024), 1024) == 1 << 20
+    with pytest.raises(ValueError, match="holds 1023 bytes"):
+        cbs._dev_ptr(FakeDeviceTensor(1023), 1024)
+    with pytest.raises(ValueError, match="holds 960 bytes"):
+        cbs._dev_ptr(FakeDeviceTensor(1024, off=64), 1024)  # a view 64 bytes into its storage
+    with pytest.raises(ValueError, match="output"):
+        cbs.cbs_run_layer(layer, FakeDeviceTensor(1024), FakeDeviceTensor(4095))
+    with pytest.raises(ValueError, match="accumulators"):
+        cbs.cbs_run_layer_raw_acc(layer, FakeDeviceTensor(1024), FakeDeviceTensor(100))
+    with pytest.raises(ValueError, match="NHWC output"):
+        cbs.cbs_pack_nhwc_f32(FakeDeviceTensor(4 * 3 * 8 * 8), FakeDeviceTensor(10), 1, 3, 8, 8, 4)
+    assert cbs._dev_ptr(12345, 1 << 30) == 12345
