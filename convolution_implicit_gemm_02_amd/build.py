@@ -197,6 +197,9 @@ def build(verbose: bool = True) -> str:
     k_obj = os.path.join(BUILD_DIR, "cbs_kernels.o")
     cmds.append([hipcc, "-c", os.path.join(CSRC, "cbs_kernels.hip"), "-o", k_obj, "-O3"] + COMMON + DEVICE_FLAGS)
     objs.append(k_obj)
+    n_obj = os.path.join(BUILD_DIR, "cbs_noalloc.o")
+    cmds.append([hipcc, "-c", os.path.join(CSRC, "cbs_noalloc.hip"), "-o", n_obj, "-O3"] + COMMON + DEVICE_FLAGS)
+    objs.append(n_obj)
     for v in range(VARIANTS):
         o = os.path.join(BUILD_DIR, "cbs_variant_%d.o" % v)
         cmds.append([hipcc, "-c", os.path.join(CSRC, "cbs_variant.hip"), "-o", o, "-O3", "-DCBS_VAR=%d" % v]

@@ -93,6 +93,7 @@ _SIGNATURES = {
     "cbs_destroy_layer": (None, [_P]),
     "cbs_run_layer": (_I, [_P, _P, _P, _P]),
     "cbs_run_layer_res": (_I, [_P, _P, _P, _P, _P]),
+    "cbs_run_layer_noalloc": (_I, [_P, _P, _P, _I, _P]),
     "cbs_run_steps": (_I, [ctypes.POINTER(cbs_step), _I, _P]),
     "cbs_graph_create_steps": (_I, [ctypes.POINTER(cbs_step), _I, _P, ctypes.POINTER(_P)]),
     "cbs_run_layer_list": (_I, [ctypes.POINTER(_P), _I, ctypes.POINTER(_P), ctypes.POINTER(_P), _P]),
@@ -244,6 +245,15 @@ def cbs_destroy_layer(layer: Layer) -> None:
 def cbs_run_layer(layer: Layer, inp, out, stream=None) -> None:
     _check(lib.cbs_run_layer(layer.handle, _in_ptr(layer, inp), _out_ptr(layer, out), _stream(stream)),
            "cbs_run_layer")
+
+
+CBS_NOALLOC_PARTIAL_BYTES = 8 << 20
+CBS_NOALLOC_TICKETS = 16384
+
+
+def cbs_run_layer_noalloc(layer: Layer, inp, out, splitk: int = 0, stream=None) -> None:
+    _check(lib.cbs_run_layer_noalloc(layer.handle, _in_ptr(layer, inp), _out_ptr(layer, out), int(splitk),
+                                     _stream(stream)), "cbs_run_layer_noalloc")
 
 
 def cbs_run_layer_res(layer: Layer, inp, out, residual, stream=None) -> None:

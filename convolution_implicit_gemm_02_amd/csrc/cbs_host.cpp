@@ -29,6 +29,7 @@
 
 #include "../../include/cbs.h"
 #include "cbs_internal.h"
+#include "cbs_scratch.h"
 
 using namespace cbs;
 
@@ -647,6 +648,47 @@ cbs_status check_step(const cbs_layer *L, const void *in, const void *out, const
   if (!L->res_cs && res) return fail(CBS_EINVAL, "%s: layer %d has no residual but one was given", where, idx);
   return CBS_OK;
 }
+
+}  // namespace
+
+namespace cbs {
+
+cbs_status report_error(cbs_status st, const char *what, const char *detail) {
+  return fail(st, "%s: %s", what, detail ? detail : "");
+}
+
+cbs_status scratch_launch(const cbs_layer *L, const void *in, void *out, int32_t splitk, void *ws, size_t ws_cap,
+                          unsigned *counters, size_t counters_cap, ConvParams *p, int *variant, int *cfg,
+                          unsigned *tiles) {
+  cbs_status st = check_step(L, in, out, nullptr, "run_layer_noalloc", 0);
+  if (st != CBS_OK) return st;
+  if (splitk < 0 || splitk > 64) return fail(CBS_EINVAL, "run_layer_noalloc: splitk %d not in [0, 64]", (int)splitk);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != L->device)
+    return fail(CBS_EINVAL, "run_layer_noalloc: the current device (%d) is not the layer's (%d)", dev, L->device);
+  const int sk = splitk == 0 ? L->splitk : (int)splitk;
+  if (!config_fits(L, L->config, sk))
+    return fail(CBS_EUNSUPPORTED, "run_layer_noalloc: configuration %s cannot run this layer with split-K %d "
+                                  "(a split needs a register-direct configuration and enough K steps)",
+                config(L->config).name, sk);
+  size_t need_ws, need_cnt;
+  splitk_need(L, L->config, sk, &need_ws, &need_cnt);
+  if (need_ws > ws_cap || need_cnt > counters_cap)
+    return fail(CBS_EUNSUPPORTED, "run_layer_noalloc: split-K %d of configuration %s needs %zu bytes of partial "
+                                  "tiles and %zu tickets; the static scratch holds %zu and %zu",
+                sk, config(L->config).name, need_ws, need_cnt, ws_cap, counters_cap);
+  *p = make_params(L, in, out, nullptr, false, L->config, sk);
+  p->ws = sk > 1 ? (float *)ws : nullptr;
+  p->counters = sk > 1 ? counters : nullptr;
+  *variant = L->variant;
+  *cfg = L->config;
+  *tiles = (unsigned)need_cnt;
+  return CBS_OK;
+}
+
+}  // namespace cbs
+
+namespace {
 
 // ------------------------------------------------------------ create ----
 

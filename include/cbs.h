@@ -197,6 +197,32 @@ void cbs_destroy_layer(cbs_layer *layer);
 cbs_status cbs_run_layer(const cbs_layer *layer, const void *in, void *out, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops where hipMalloc is not allowed): cbs_run_layer with
+ * the cross-workgroup split-K factor chosen per call (splitk >= 1, or 0 for
+ * the layer's own), whose partial tiles and arrival tickets live in a fixed
+ * array of the library on each device ("scratch": CBS_NOALLOC_PARTIAL_BYTES
+ * of partial tiles and CBS_NOALLOC_TICKETS tickets, held by every device the
+ * library runs on until the process ends) instead of a workspace of the layer.
+ * No call allocates or frees anything (the first call on a device looks up
+ * the array's address).  Same layouts, arguments and results as
+ * cbs_run_layer; a split needs the layer's configuration to be register-direct.
+ * It enqueues a small kernel that clears the tickets it uses, then the
+ * layer's kernel.  Every call on one device shares that device's array:
+ * calls whose runs overlap on one device (other streams, other threads) race
+ * and give wrong results; calls in one stream are ordered and safe.
+ * Errors: CBS_EINVAL (null layer or buffer, a layer with a residual, splitk
+ * outside [0, 64], a current device other than the layer's),
+ * CBS_EUNSUPPORTED (the configuration cannot run that split, or the run needs
+ * more partial-tile bytes or tickets than the array holds), CBS_EDEVICE,
+ * CBS_ELAUNCH.
+ */
+#define CBS_NOALLOC_PARTIAL_BYTES (8u << 20)
+#define CBS_NOALLOC_TICKETS 16384u
+cbs_status cbs_run_layer_noalloc(const cbs_layer *layer, const void *in, void *out, int32_t splitk,
+                                 void *stream);
+
+/*
  * Same for a layer created with a residual (res_c_stride > 0): residual is
  * the device tensor added after the activation (layout above).  CBS_EINVAL if
  * the layer has no residual or residual is NULL.
