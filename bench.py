@@ -167,37 +167,47 @@ class ListBench:
             self.cbs.cbs_run_layer_list(self.layers, self.ins, self.outs)
 
     def time_layers(self, min_ms=2.0, reps=5):
-        """Per layer: median over `reps` of (event pair around R back-to-back launches)/R,
-        on the stream the library launches on (torch's current stream).  The R
-        launches are enqueued by one cbs_run_layer_list call, so the host loop is C,
-        not Python."""
+        """Per layer: (graph us, eager us).  graph: median over `reps` of (event pair
+        around one replay of a captured graph of R back-to-back launches)/R, the way
+        the list step launches its kernels; eager: the same R launches enqueued by one
+        cbs_run_layer_list call (marshalled before the events).  R is chosen so that
+        one repeat takes >= min_ms.  All on the stream the library launches on
+        (torch's current stream)."""
         torch, cbs = self.torch, self.cbs
-        res = []
+        graph_us, eager_us = [], []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for layer, xin, out in zip(self.layers, self.ins, self.outs):
             cbs.cbs_run_layer_list([layer] * 3, [xin] * 3, [out] * 3)
-            torch.cuda.synchronize()
-            # calibrate R so that one repeat takes >= min_ms
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ten = cbs.LayerList([layer] * 10, [xin] * 10, [out] * 10)
+            torch.cuda.synchronize()
             e0.record()
             ten.run()
             e1.record()
             torch.cuda.synchronize()
             per = max(e0.elapsed_time(e1) / 10, 1e-4)
             r = int(min(2000, max(10, min_ms / per)))
-            # marshalled before the events, so that the host time of building the
-            # argument arrays is not counted as GPU time
             lst = cbs.LayerList([layer] * r, [xin] * r, [out] * r)
-            ts = []
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                lst.run()
+            g.replay()
+            torch.cuda.synchronize()
+            tg, te = [], []
             for _ in range(reps):
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                tg.append(e0.elapsed_time(e1) / r)
                 e0.record()
                 lst.run()
                 e1.record()
                 torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1) / r)
-            res.append(float(np.median(ts)) * 1e3)  # microseconds
-        return res
-
+                te.append(e0.elapsed_time(e1) / r)
+            del g
+            graph_us.append(float(np.median(tg)) * 1e3)  # microseconds
+            eager_us.append(float(np.median(te)) * 1e3)
+        return graph_us, eager_us
 
     def time_layers_single(self, scratch, reps=9):
         """Per layer, one launch between two events: the median over `reps` with warm
@@ -318,13 +328,14 @@ def warm_device(torch, seconds=0.5):
     torch.cuda.empty_cache()
 
 
-def layer_rows(bench, us, single=None, flushed=None):
+def layer_rows(bench, us, single=None, flushed=None, eager=None):
     int8 = bench.dtype != bench.cbs.CBS_F32
     peak = PEAK_INT8 if int8 else PEAK_FP32
     rows = []
     single = single or [None] * len(us)
     flushed = flushed or [None] * len(us)
-    for sp, info, t, t1, tf in zip(bench.specs, bench.infos, us, single, flushed):
+    eager = eager or [None] * len(us)
+    for sp, info, t, t1, tf, te in zip(bench.specs, bench.infos, us, single, flushed, eager):
         fl, by = info["flops"], info["alg_bytes"]
         t_mfma, t_hbm = fl / peak, by / PEAK_HBM
         bound = "mfma" if t_mfma >= t_hbm else "hbm"
@@ -334,7 +345,8 @@ def layer_rows(bench, us, single=None, flushed=None):
                      "gbs": round(by / (t * 1e-6) / 1e9, 1), "flops": fl, "alg_bytes": by, "bound": bound,
                      "roof_us": round(roof_us, 3), "frac": round(roof_us / t, 4), "config": info["config_name"],
                      "grid": info["grid"], "us_single": None if t1 is None else round(t1, 3),
-                     "us_flushed": None if tf is None else round(tf, 3)})
+                     "us_flushed": None if tf is None else round(tf, 3),
+                     "us_eager": None if te is None else round(te, 3)})
     return rows
 
 
@@ -442,8 +454,9 @@ def cpu_baseline(W, min_seconds=10.0, max_seconds=20.0):
 
 def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, splitk=0):
     """Run only one layer of the list (or, for name "all", every layer in list
-    order) `launches` times back to back after 10 warm-up launches, for a
-    profiler run on exactly those kernels; then a plain device copy of known
+    order) `launches` times back to back after 10 warm-up launches, the
+    `launches` replayed as one captured graph, for a profiler run on exactly
+    those kernels; then a plain device copy of known
     size (the reference for scaling the profiler's byte counters).  Prints one
     JSON line per layer."""
     b = ListBench(cbs, W, torch, dtype, batch)
@@ -456,11 +469,15 @@ def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, spli
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         cbs.cbs_run_layer_list([layer] * 10, [xin] * 10, [out] * 10)
         lst = cbs.LayerList([layer] * launches, [xin] * launches, [out] * launches)
+        g = torch.cuda.CUDAGraph()  # the launches replayed as one graph, as bench.py times them
+        with torch.cuda.graph(g):
+            lst.run()
         torch.cuda.synchronize()
         e0.record()
-        lst.run()
+        g.replay()
         e1.record()
         torch.cuda.synchronize()
+        del g
         us = e0.elapsed_time(e1) / launches * 1e3
         info = b.infos[i]
         print(json.dumps({"layer": names[i], "batch": batch, "dtype": "int8" if dtype else "f32",
@@ -556,9 +573,9 @@ def main():
         steps = args.steps if bs == 1 else max(10, args.steps // 8)
         ms_graph, wall_graph = b.time_steps(steps, args.warmup, use_graph=True)
         ms_list, _ = b.time_steps(steps, args.warmup, use_graph=False)
-        us_layers = b.time_layers()
+        us_layers, us_eager = b.time_layers()
         us_single, us_flushed = b.time_layers_single(scratch)
-        rows = layer_rows(b, us_layers, us_single, us_flushed)
+        rows = layer_rows(b, us_layers, us_single, us_flushed, us_eager)
         key = "%s_bs%d" % (name, bs)
         layer_tables[key] = rows
         results[key] = {"ms_per_step": ms_graph, "wall_ms_per_step": wall_graph, "ms_per_step_plain_launches": ms_list,
@@ -580,10 +597,11 @@ def main():
             % (key, ms_graph * 1e3, ms_list * 1e3, b.flops / (ms_graph * 1e-3) / 1e12, sum(us_layers), sum(us_single),
                sum(us_flushed), sum(r["roof_us"] for r in rows)))
         for r in rows:
-            log("  %-13s %4d->%-4d %4d k%d s%d  %8.2f us (single %6.2f, flushed %6.2f)  %7.2f TF/s  %7.1f GB/s  "
-                "roof %6.2f us (%s)  frac %.3f  %s"
-                % (r["layer"], r["c_in"], r["c_out"], r["h_in"], r["k"], r["s"], r["us"], r["us_single"],
-                   r["us_flushed"], r["tflops"], r["gbs"], r["roof_us"], r["bound"], r["frac"], r["config"]))
+            log("  %-13s %4d->%-4d %4d k%d s%d  %8.2f us (eager %6.2f, single %6.2f, flushed %6.2f)  %7.2f TF/s  "
+                "%7.1f GB/s  roof %6.2f us (%s)  frac %.3f  %s"
+                % (r["layer"], r["c_in"], r["c_out"], r["h_in"], r["k"], r["s"], r["us"], r["us_eager"],
+                   r["us_single"], r["us_flushed"], r["tflops"], r["gbs"], r["roof_us"], r["bound"], r["frac"],
+                   r["config"]))
         del b
         torch.cuda.empty_cache()
 

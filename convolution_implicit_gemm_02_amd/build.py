@@ -76,12 +76,28 @@ def masked_mfma_kernels(text: str, pattern: str):
     return bad
 
 
+SCALAR_LINE = 64  # bytes per scalar data cache line
+
+
+def _sload_lines(line: str):
+    """Scalar-cache lines an s_load_dword[xN] sX, s[0:1], OFF of the argument block touches."""
+    import re
+    m = re.match(r"s_load_dword(?:x(\d+))?\s+\S+,\s*s\[0:1\],\s*(0x[0-9a-f]+|\d+)", line)
+    if not m:
+        return None
+    n = int(m.group(1) or 1)
+    off = int(m.group(2), 0)
+    return set(range(off // SCALAR_LINE, (off + 4 * n - 1) // SCALAR_LINE + 1))
+
+
 def late_argument_loads(text: str, pattern: str, max_rounds: int = 1):
     """Kernels of a device assembly whose kernel-argument reads (scalar loads:
     the conv kernels make no other) cost more than one memory round trip:
-    loads issued after a wait for earlier ones, or after the first MFMA (a
-    dependent round trip after the main loop).  Returns (flagged names, number
-    of kernels with at least one argument load before their first MFMA)."""
+    loads issued after a wait for earlier ones that touch a cache line of the
+    argument block no earlier round requested (a load of a line already on its
+    way hits the scalar cache), or any load after the first MFMA (a dependent
+    round trip after the main loop).  Returns (flagged names, number of
+    kernels with at least one argument load before their first MFMA)."""
     import re
     bad, early = [], 0
     for name in re.findall(pattern, text, re.M):
@@ -89,11 +105,17 @@ def late_argument_loads(text: str, pattern: str, max_rounds: int = 1):
         body = [line.strip() for line in text[i:text.index(".Lfunc_end", i)].split("\n")]
         first = next((k for k, line in enumerate(body) if line.startswith("v_mfma")), len(body))
         rounds, pending, late = 0, False, False
+        requested = set()
         for k, line in enumerate(body):
             if line.startswith("s_load_"):
-                if not pending:
+                lines = _sload_lines(line)
+                new_lines = lines is None or not lines <= requested
+                if not pending and new_lines:
                     rounds += 1
-                pending = True
+                if new_lines:
+                    pending = True
+                if lines:
+                    requested |= lines
                 late |= k > first
             elif "lgkmcnt" in line:
                 pending = False
@@ -118,7 +140,7 @@ def flat_memory_ops(text: str, pattern: str):
 
 
 VARIANTS = 12  # kernel variants, one translation unit each (cbs_variant.hip with -DCBS_VAR=n)
-CONV_KERNELS = r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+):"
+CONV_KERNELS = r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo|7conv_sk)\w+):"
 # grouped launches read their member's arguments in a second round, at an
 # offset that depends on the first (the group's workgroup ranges)
 GROUP_KERNELS = r"^(_ZN3cbs(?:16conv_igemm_group|14conv_lds_group)\w+):"

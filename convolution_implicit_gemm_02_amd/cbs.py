@@ -277,6 +277,18 @@ def cbs_run_steps(steps, stream=None) -> None:
     _check(lib.cbs_run_steps(_step_array(steps), len(steps), _stream(stream)), "cbs_run_steps")
 
 
+class StepList:
+    """A step list marshalled once (see LayerList), so that run() costs one C call."""
+
+    def __init__(self, steps):
+        self.n = len(steps)
+        self._arr = _step_array(steps)
+        self._keep = list(steps)
+
+    def run(self, stream=None) -> None:
+        _check(lib.cbs_run_steps(self._arr, self.n, _stream(stream)), "cbs_run_steps")
+
+
 def cbs_graph_create_steps(steps, stream=None) -> "Graph":
     h = _P()
     _check(lib.cbs_graph_create_steps(_step_array(steps), len(steps), _stream(stream), ctypes.byref(h)),

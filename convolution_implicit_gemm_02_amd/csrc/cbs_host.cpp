@@ -69,6 +69,7 @@ struct cbs_layer {
   unsigned cpt_magic;
   int config, splitk;
   int device;
+  int cus;           // compute units of the device (stream-K launches one workgroup per CU)
   // device memory
   void *d_wfrag = nullptr;
   float *d_bias = nullptr;
@@ -232,6 +233,52 @@ void tiles_of(const cbs_layer *L, int cfg, int *px_tiles, int *co_tiles) {
   *px_tiles = ceil_div(L->M, tpx);
 }
 
+// Stream-K geometry of configuration cfg (lds == 4) for layer L: the grid
+// (one workgroup per CU, fewer for short layers), the tile-steps per
+// workgroup, the most workgroups that share one tile, and the most tiles one
+// workgroup touches.
+struct SkGeom {
+  int grid = 0, len = 0, maxc = 0, max_tiles = 0;
+  long long total = 0;
+};
+
+SkGeom sk_geometry(const cbs_layer *L, int cfg) {
+  SkGeom gm;
+  int pxt, cot;
+  tiles_of(L, cfg, &pxt, &cot);
+  const long long tiles = (long long)pxt * cot, S = L->steps;
+  gm.total = tiles * S;
+  if (gm.total <= 0 || gm.total >= INT_MAX) return gm;
+  const int cus = std::max(1, L->cus);
+  gm.len = (int)((gm.total + cus - 1) / cus);
+  gm.grid = (int)((gm.total + gm.len - 1) / gm.len);
+  for (long long t = 0; t < tiles; t++) {
+    const long long first = t * S / gm.len, last = ((t + 1) * S - 1) / gm.len;
+    gm.maxc = std::max(gm.maxc, (int)(last - first + 1));
+  }
+  for (int g = 0; g < gm.grid; g++) {
+    const long long a = (long long)g * gm.len, b = std::min(gm.total, a + gm.len);
+    gm.max_tiles = std::max(gm.max_tiles, (int)((b - 1) / S - a / S + 1));
+  }
+  return gm;
+}
+
+// Whether stream-K configuration cfg can run layer L: every wave's share of
+// its workgroup's range is at most one tile's K (so it spans at most two
+// tiles), each wave finishes at most two (tile, block) pairs, and the
+// partial-tile workspace stays below 2^31 bytes.
+bool sk_fits(const cbs_layer *L, int cfg) {
+  const KernelConfig &c = config(cfg);
+  const SkGeom gm = sk_geometry(L, cfg);
+  if (gm.grid < 1) return false;
+  const int nw = c.wk, nblk = c.cb * c.pb;
+  if ((gm.len + nw - 1) / nw > L->steps) return false;
+  if ((long long)gm.max_tiles * nblk > 2LL * nw) return false;
+  int pxt, cot;
+  tiles_of(L, cfg, &pxt, &cot);
+  return (double)pxt * cot * gm.maxc * nblk * 64 * 16 < 2147483647.0 - 64.0;
+}
+
 // LDS bytes of a halo-tile workgroup: the input window (4-channel slots,
 // rounded up to whole waves of slots) followed by all fragment-ordered weights.
 // 4-channel slots per halo pixel in LDS: fp32 pixels of an even number of
@@ -287,6 +334,7 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
   const KernelConfig &c = config(cfg);
   if (splitk < 1 || splitk > 64) return false;
   if (c.lds && splitk != 1) return false;
+  if (c.lds == 4) return sk_fits(L, cfg);
   if (c.lds == 2 || c.lds == 3) {
     if (L->d.k != 3 || L->co_blocks > 4) return false;
     if (c.lds == 3 && !L->pair) return false;
@@ -385,8 +433,16 @@ void release(cbs_layer *L) {
 void splitk_need(const cbs_layer *L, int cfg, int splitk, size_t *ws_bytes, size_t *counters) {
   *ws_bytes = 0;
   *counters = 0;
-  if (splitk <= 1) return;
   const KernelConfig &c = config(cfg);
+  if (c.lds == 4) {  // stream-K: a slot per sharing workgroup of every tile
+    const SkGeom gm = sk_geometry(L, cfg);
+    int pxt, cot;
+    tiles_of(L, cfg, &pxt, &cot);
+    *ws_bytes = (size_t)pxt * cot * gm.maxc * c.cb * c.pb * 64 * 16;
+    *counters = (size_t)pxt * cot;
+    return;
+  }
+  if (splitk <= 1) return;
   int pxt, cot;
   tiles_of(L, cfg, &pxt, &cot);
   const size_t tiles = (size_t)pxt * cot;
@@ -547,6 +603,19 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
   p.div_sk = make_fastdiv(p.splitk);
   p.div_tx = make_fastdiv(p.tiles_x);
   p.div_ty = make_fastdiv(p.tiles_y);
+  if (kc.lds == 4) {  // stream-K: the grid is one workgroup per CU; the tiles are counted in sk_tiles
+    const SkGeom gm = sk_geometry(L, cfg);
+    p.sk_tiles = p.px_tiles * p.co_tiles;
+    p.sk_len = gm.len;
+    p.sk_maxc = gm.maxc;
+    p.div_steps = make_fastdiv(L->steps);
+    p.div_len = make_fastdiv(gm.len);
+    p.px_tiles = gm.grid;
+    p.co_tiles = 1;
+    p.ws = L->d_ws;
+    p.counters = L->d_counters;
+    p.smem_bytes = 64 * 1024;  // unused: keeps a second workgroup off the CU (see launch_sk)
+  }
   return p;
 }
 
@@ -678,8 +747,8 @@ cbs_status scratch_launch(const cbs_layer *L, const void *in, void *out, int32_t
                                   "tiles and %zu tickets; the static scratch holds %zu and %zu",
                 sk, config(L->config).name, need_ws, need_cnt, ws_cap, counters_cap);
   *p = make_params(L, in, out, nullptr, false, L->config, sk);
-  p->ws = sk > 1 ? (float *)ws : nullptr;
-  p->counters = sk > 1 ? counters : nullptr;
+  p->ws = need_ws ? (float *)ws : nullptr;
+  p->counters = need_cnt ? counters : nullptr;
   *variant = L->variant;
   *cfg = L->config;
   *tiles = (unsigned)need_cnt;
@@ -713,9 +782,10 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   if (!L) return fail(CBS_ENOMEM, "host allocation");
   L->d = *desc;
   const cbs_conv_desc &d = L->d;
-  if (hipGetDevice(&L->device) != hipSuccess) {
+  if (hipGetDevice(&L->device) != hipSuccess ||
+      hipDeviceGetAttribute(&L->cus, hipDeviceAttributeMultiprocessorCount, L->device) != hipSuccess) {
     delete L;
-    return fail(CBS_EDEVICE, "hipGetDevice failed");
+    return fail(CBS_EDEVICE, "hipGetDevice / CU count failed");
   }
   L->oh = out_dim(d.h, d.k, d.stride, d.pad);
   L->ow = out_dim(d.w, d.k, d.stride, d.pad);
@@ -1492,6 +1562,7 @@ cbs_status cbs_layer_info(const cbs_layer *L, cbs_layer_info_t *info) {
   tiles_of(L, L->config, &pxt, &cot);
   info->grid = pxt * cot * L->splitk;
   const KernelConfig &c = config(L->config);
+  if (c.lds == 4) info->grid = sk_geometry(L, L->config).grid;
   info->threads = 64 * c.wco * c.wpx * c.wk;
   std::snprintf(info->config_name, sizeof(info->config_name), "%s/sk%d", c.name, L->splitk);
   return CBS_OK;
@@ -1534,23 +1605,15 @@ TuneKey tune_key(const cbs_layer *L) {
                  L->out_cs, L->res_cs};
 }
 
-// Mean time of `iters` back-to-back launches (after two warm-ups), in ms.
-cbs_status time_config(cbs_layer *L, const void *in, void *out, const void *res, int iters, hipStream_t st,
-                       hipEvent_t e0, hipEvent_t e1, float *ms) {
-  for (int i = 0; i < 2; i++) {
-    cbs_status s = launch(L, in, out, res, st);
-    if (s != CBS_OK) return s;
-  }
-  if (hipEventRecord(e0, st) != hipSuccess) return fail(CBS_EDEVICE, "autotune: event record failed");
-  for (int i = 0; i < iters; i++) {
-    cbs_status s = launch(L, in, out, res, st);
-    if (s != CBS_OK) return s;
-  }
-  if (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess)
-    return fail(CBS_EDEVICE, "autotune: event wait failed");
-  if (hipEventElapsedTime(ms, e0, e1) != hipSuccess) return fail(CBS_EDEVICE, "autotune: elapsed time failed");
-  *ms /= (float)iters;
-  return CBS_OK;
+// Time per launch of `iters` back-to-back launches, captured as one graph and
+// replayed (the best of three replays after a warm-up one), in ms: the way a
+// captured list runs them.  An eager launch costs the GPU about 3 us of its
+// own, which would hide the differences between configurations of small layers.
+cbs_status time_config(cbs_layer *L, const void *in, void *out, const void *res, int iters, float *ms) {
+  float us = 0.f;
+  const cbs_status s = time_replays([&](hipStream_t cs) { return launch(L, in, out, res, cs); }, iters, 3, &us);
+  *ms = us * 1e-3f;
+  return s;
 }
 
 }  // namespace
@@ -1576,12 +1639,9 @@ cbs_status cbs_layer_autotune(cbs_layer *L, const void *in, void *out, const voi
     }
   }
   if (!cached) {
-    hipStream_t hs = (hipStream_t)stream;
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
-      if (e0) (void)hipEventDestroy(e0);
-      return fail(CBS_EDEVICE, "layer_autotune: event creation failed");
-    }
+    // wait for the caller's stream: the timing runs on a private one
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+      return fail(CBS_EDEVICE, "layer_autotune: stream synchronisation failed");
     const int old_cfg = L->config, old_sk = L->splitk;
     float best_ms = 1e30f;
     st = CBS_OK;
@@ -1592,14 +1652,14 @@ cbs_status cbs_layer_autotune(cbs_layer *L, const void *in, void *out, const voi
           int pxt, cot;
           tiles_of(L, cfg, &pxt, &cot);
           if ((long)pxt * cot >= 256) continue;
-          // a live graph holds the workspace's address: only what fits it
-          if (L->graph_refs.load() > 0 && !splitk_fits_workspace(L, cfg, sk)) continue;
         }
+        // a live graph holds the workspace's address: only what fits it
+        if (L->graph_refs.load() > 0 && !splitk_fits_workspace(L, cfg, sk)) continue;
         L->config = cfg;
         L->splitk = sk;
         st = setup_splitk(L);
         float ms = 0.f;
-        if (st == CBS_OK) st = time_config(L, in, out, residual, iters, hs, e0, e1, &ms);
+        if (st == CBS_OK) st = time_config(L, in, out, residual, iters, &ms);
         if (st != CBS_OK) break;
         if (ms < best_ms) {
           best_ms = ms;
@@ -1607,8 +1667,6 @@ cbs_status cbs_layer_autotune(cbs_layer *L, const void *in, void *out, const voi
         }
       }
     }
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
     if (st != CBS_OK) {
       L->config = old_cfg;
       L->splitk = old_sk;

@@ -391,10 +391,14 @@ int32_t cbs_num_configs(void);
  * form ("Improvements" #1: benchmark candidate tiles per unique layer shape,
  * since one fixed tile spans 5 to 556 us across call sites).  Times every
  * kernel configuration that can run this layer (split-K 1, plus 2, 3 and 4 for
- * register-direct configurations whose grid is below 256 workgroups) with
- * `iters` launches each (0 = 20) after two warm-ups, with HIP events on
- * `stream`, on the caller's buffers, and keeps the fastest (while a graph
- * holds the layer, only split-K factors that fit its current workspace).  The choice is
+ * register-direct configurations whose grid is below 256 workgroups), each as
+ * a captured graph of `iters` back-to-back launches (0 = 20) replayed with HIP
+ * events (the best of three replays after a warm-up one), on a private stream
+ * after waiting for `stream`, on the caller's buffers, and keeps the fastest
+ * (while a graph holds the layer, only configurations whose split-K workspace
+ * fits the current one).  Graph replay is how a captured list runs its
+ * kernels; an eager launch costs the GPU a few microseconds of its own, which
+ * would hide the differences between configurations of small layers.  The choice is
  * cached in the process per device, shape, dtype, epilogue and channel
  * strides: a later call for the same key takes it without timing, unless
  * flags has CBS_TUNE_FORCE.  Blocks until the timing is done, may allocate

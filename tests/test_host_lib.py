@@ -241,8 +241,9 @@ def test_descriptor_layout_matches_header(cbs):
 
 def test_tile_table_entries(cbs):
     """Every tile-table entry names an existing configuration with a split-K the
-    configuration allows, keys are unique, classes are 0-3, and every class 2/3
-    entry has the plain int8 entry of its shape to fall back to."""
+    configuration allows, keys are unique, classes are 0-4, every class 2/3
+    entry has the plain int8 entry of its shape to fall back to, and every
+    class 4 entry the plain fp32 one."""
     import re
     path = os.path.join(os.path.dirname(HEADER), "..", "convolution_implicit_gemm_02_amd", "csrc", "tile_table.inc")
     rows = [tuple(int(v) for v in m.groups()) for m in re.finditer(
@@ -254,7 +255,7 @@ def test_tile_table_entries(cbs):
     n_cfg = cbs.cbs_num_configs()
     for r in rows:
         n, c_in, c_out, h, w, k, s, cls, cfg, sk = r
-        assert cls in (0, 1, 2, 3), r
+        assert cls in (0, 1, 2, 3, 4), r
         assert 0 <= cfg < n_cfg, r
         name = cbs.cbs_config_name(cfg)
         assert sk >= 1 and (sk == 1 or name.startswith("c")), r  # split-K only on register-direct tiles
@@ -262,6 +263,8 @@ def test_tile_table_entries(cbs):
             assert k == 3 and s == 1 and c_out <= 8, r
         if cls in (2, 3):
             assert (n, c_in, c_out, h, w, k, s, 1) in set(keys), r
+        if cls == 4:
+            assert (n, c_in, c_out, h, w, k, s, 0) in set(keys), r
 
 
 def test_binding_rejects_host_and_short_buffers(cbs):
