@@ -69,7 +69,6 @@ struct cbs_layer {
   unsigned cpt_magic;
   int config, splitk;
   int device;
-  int cus;           // compute units of the device (stream-K launches one workgroup per CU)
   // device memory
   void *d_wfrag = nullptr;
   float *d_bias = nullptr;
@@ -233,52 +232,6 @@ void tiles_of(const cbs_layer *L, int cfg, int *px_tiles, int *co_tiles) {
   *px_tiles = ceil_div(L->M, tpx);
 }
 
-// Stream-K geometry of configuration cfg (lds == 4) for layer L: the grid
-// (one workgroup per CU, fewer for short layers), the tile-steps per
-// workgroup, the most workgroups that share one tile, and the most tiles one
-// workgroup touches.
-struct SkGeom {
-  int grid = 0, len = 0, maxc = 0, max_tiles = 0;
-  long long total = 0;
-};
-
-SkGeom sk_geometry(const cbs_layer *L, int cfg) {
-  SkGeom gm;
-  int pxt, cot;
-  tiles_of(L, cfg, &pxt, &cot);
-  const long long tiles = (long long)pxt * cot, S = L->steps;
-  gm.total = tiles * S;
-  if (gm.total <= 0 || gm.total >= INT_MAX) return gm;
-  const int cus = std::max(1, L->cus);
-  gm.len = (int)((gm.total + cus - 1) / cus);
-  gm.grid = (int)((gm.total + gm.len - 1) / gm.len);
-  for (long long t = 0; t < tiles; t++) {
-    const long long first = t * S / gm.len, last = ((t + 1) * S - 1) / gm.len;
-    gm.maxc = std::max(gm.maxc, (int)(last - first + 1));
-  }
-  for (int g = 0; g < gm.grid; g++) {
-    const long long a = (long long)g * gm.len, b = std::min(gm.total, a + gm.len);
-    gm.max_tiles = std::max(gm.max_tiles, (int)((b - 1) / S - a / S + 1));
-  }
-  return gm;
-}
-
-// Whether stream-K configuration cfg can run layer L: every wave's share of
-// its workgroup's range is at most one tile's K (so it spans at most two
-// tiles), each wave finishes at most two (tile, block) pairs, and the
-// partial-tile workspace stays below 2^31 bytes.
-bool sk_fits(const cbs_layer *L, int cfg) {
-  const KernelConfig &c = config(cfg);
-  const SkGeom gm = sk_geometry(L, cfg);
-  if (gm.grid < 1) return false;
-  const int nw = c.wk, nblk = c.cb * c.pb;
-  if ((gm.len + nw - 1) / nw > L->steps) return false;
-  if ((long long)gm.max_tiles * nblk > 2LL * nw) return false;
-  int pxt, cot;
-  tiles_of(L, cfg, &pxt, &cot);
-  return (double)pxt * cot * gm.maxc * nblk * 64 * 16 < 2147483647.0 - 64.0;
-}
-
 // LDS bytes of a halo-tile workgroup: the input window (4-channel slots,
 // rounded up to whole waves of slots) followed by all fragment-ordered weights.
 // 4-channel slots per halo pixel in LDS: fp32 pixels of an even number of
@@ -334,7 +287,6 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
   const KernelConfig &c = config(cfg);
   if (splitk < 1 || splitk > 64) return false;
   if (c.lds && splitk != 1) return false;
-  if (c.lds == 4) return sk_fits(L, cfg);
   if (c.lds == 2 || c.lds == 3) {
     if (L->d.k != 3 || L->co_blocks > 4) return false;
     if (c.lds == 3 && !L->pair) return false;
@@ -433,16 +385,8 @@ void release(cbs_layer *L) {
 void splitk_need(const cbs_layer *L, int cfg, int splitk, size_t *ws_bytes, size_t *counters) {
   *ws_bytes = 0;
   *counters = 0;
-  const KernelConfig &c = config(cfg);
-  if (c.lds == 4) {  // stream-K: a slot per sharing workgroup of every tile
-    const SkGeom gm = sk_geometry(L, cfg);
-    int pxt, cot;
-    tiles_of(L, cfg, &pxt, &cot);
-    *ws_bytes = (size_t)pxt * cot * gm.maxc * c.cb * c.pb * 64 * 16;
-    *counters = (size_t)pxt * cot;
-    return;
-  }
   if (splitk <= 1) return;
+  const KernelConfig &c = config(cfg);
   int pxt, cot;
   tiles_of(L, cfg, &pxt, &cot);
   const size_t tiles = (size_t)pxt * cot;
@@ -603,19 +547,6 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
   p.div_sk = make_fastdiv(p.splitk);
   p.div_tx = make_fastdiv(p.tiles_x);
   p.div_ty = make_fastdiv(p.tiles_y);
-  if (kc.lds == 4) {  // stream-K: the grid is one workgroup per CU; the tiles are counted in sk_tiles
-    const SkGeom gm = sk_geometry(L, cfg);
-    p.sk_tiles = p.px_tiles * p.co_tiles;
-    p.sk_len = gm.len;
-    p.sk_maxc = gm.maxc;
-    p.div_steps = make_fastdiv(L->steps);
-    p.div_len = make_fastdiv(gm.len);
-    p.px_tiles = gm.grid;
-    p.co_tiles = 1;
-    p.ws = L->d_ws;
-    p.counters = L->d_counters;
-    p.smem_bytes = 64 * 1024;  // unused: keeps a second workgroup off the CU (see launch_sk)
-  }
   return p;
 }
 
@@ -782,10 +713,9 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   if (!L) return fail(CBS_ENOMEM, "host allocation");
   L->d = *desc;
   const cbs_conv_desc &d = L->d;
-  if (hipGetDevice(&L->device) != hipSuccess ||
-      hipDeviceGetAttribute(&L->cus, hipDeviceAttributeMultiprocessorCount, L->device) != hipSuccess) {
+  if (hipGetDevice(&L->device) != hipSuccess) {
     delete L;
-    return fail(CBS_EDEVICE, "hipGetDevice / CU count failed");
+    return fail(CBS_EDEVICE, "hipGetDevice failed");
   }
   L->oh = out_dim(d.h, d.k, d.stride, d.pad);
   L->ow = out_dim(d.w, d.k, d.stride, d.pad);
@@ -1562,7 +1492,6 @@ cbs_status cbs_layer_info(const cbs_layer *L, cbs_layer_info_t *info) {
   tiles_of(L, L->config, &pxt, &cot);
   info->grid = pxt * cot * L->splitk;
   const KernelConfig &c = config(L->config);
-  if (c.lds == 4) info->grid = sk_geometry(L, L->config).grid;
   info->threads = 64 * c.wco * c.wpx * c.wk;
   std::snprintf(info->config_name, sizeof(info->config_name), "%s/sk%d", c.name, L->splitk);
   return CBS_OK;

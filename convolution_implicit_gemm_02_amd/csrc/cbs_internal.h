@@ -14,8 +14,7 @@ struct KernelConfig {
   int cb, pb, wco, wpx, wk;
   int lds;  // 0: operands straight to registers (conv_igemm); 1: LDS-staged tiles (conv_lds);
             // 2: input halo tile + all weights in LDS (conv_halo, 3x3 with <= 64 output channels);
-            // 3: conv_halo on column pairs (3x3 stride 1 with <= 8 output channels; th x tw pairs);
-            // 4: stream-K (conv_sk): one workgroup of wk waves per CU, equal ranges of tile-steps
+            // 3: conv_halo on column pairs (3x3 stride 1 with <= 8 output channels; th x tw pairs)
   int th, tw;  // conv_halo: output tile of th x tw pixels
   const char *name;
 };
@@ -108,12 +107,6 @@ struct ConvParams {
   int splitk;            // workgroups per output tile along K
   int steps_per_split;   // K steps per split-K workgroup
   FastDiv div_sk;            // by splitk
-  // ---- stream-K (conv_sk): tile t, K step s is tile-step t*steps + s
-  int sk_tiles;          // output tiles (px_tiles * co_tiles)
-  int sk_len;            // tile-steps per workgroup (the last may have fewer, or none)
-  int sk_maxc;           // most workgroups sharing one tile (partial-tile slots per tile)
-  FastDiv div_steps;         // by steps: tile-step -> tile
-  FastDiv div_len;           // by sk_len: tile-step -> workgroup
   // ---- conv_halo
   int cin_pad;
   int tiles_x, tiles_y;  // output tiles along a row and along the rows of one image

@@ -33,9 +33,6 @@ static const KernelConfig kConfigs[] = {
 #define X(id, mb, nb, wm, wn, ks, ns, name) {nb, mb, wn, wm, 1, 1, 0, 0, name},
     CBS_LDS_RING_SWZ_CONFIG_LIST(X)
 #undef X
-#define X(id, cb, pb, nw, pf, name) {cb, pb, 1, 1, nw, 4, 0, 0, name},
-    CBS_SK_CONFIG_LIST(X)
-#undef X
 };
 
 // A configuration's id is its index in kConfigs (the launch switch and the
@@ -44,7 +41,6 @@ constexpr int kConfigIds[] = {
 #define X(id, ...) id,
     CBS_CONFIG_LIST(X) CBS_LDS_CONFIG_LIST(X) CBS_HALO_CONFIG_LIST(X) CBS_CONFIG_LIST_EXT(X) CBS_LDS_CONFIG_LIST_EXT(X)
     CBS_LDS_RING_CONFIG_LIST(X) CBS_HALO_PAIR_CONFIG_LIST(X) CBS_LDS_RING_SWZ_CONFIG_LIST(X)
-    CBS_SK_CONFIG_LIST(X)
 #undef X
 };
 constexpr bool config_ids_in_order() {

@@ -103,12 +103,3 @@
   X(55, 2, 2, 2, 4, 2, 2, "RS.p64c128w8")       \
   X(56, 2, 1, 2, 4, 2, 0, "LS.p64c64w8")
 
-// Stream-K conv_sk: id, CB, PB (16-channel / 16-pixel blocks per wave), NW
-// (waves per workgroup, one workgroup per CU), PF (prefetch depth), name.
-// The output tiles are CB*16 channels x PB*16 pixels; their K steps, laid end
-// to end, are cut into one equal range per CU, so every CU gets the same MFMA
-// work whatever the tile count (the batch-1 3x3 layers have 100-800 tiles).
-#define CBS_SK_CONFIG_LIST(X)                   \
-  X(57, 2, 1, 8, 4, "S.c32p16w8")               \
-  X(58, 4, 1, 8, 4, "S.c64p16w8")               \
-  X(59, 2, 2, 8, 4, "S.c32p32w8")

@@ -1348,300 +1348,6 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   }
 }
 
-// ------------------------------------------------------ stream-K kernel --
-// At batch 1 the 3x3 layers at 20x20 to 80x80 have a few hundred output tiles
-// (200 of 32 channels x 16 pixels for 256 channels at 20x20), which do not
-// divide over the 256 CUs: some CUs run two tiles while others idle.  Here
-// the K steps of all tiles are laid end to end (tile-step u = t*steps + s,
-// t = the tile, s = its K step) and cut into equal contiguous ranges, one per
-// workgroup, with one workgroup of NW waves per CU, so every CU gets the same
-// MFMA work.  Each wave takes an equal sub-range of its workgroup's range,
-// which covers at most two tiles (the host checks that a sub-range is never
-// longer than one tile's K).  Its partial sums are reduced through LDS in
-// wave order; a tile whose steps lie in several workgroups is finished as in
-// the cross-workgroup split-K above (partials written through to memory, a
-// ticket per tile, the last workgroup sums them in workgroup order), so the
-// result does not depend on which workgroup arrives last.
-template <int VAR, int CB, int PB, int NW, int PF>
-__global__ __launch_bounds__(64 * NW) void conv_sk(ConvParams p) {
-  using V = Var<VAR>;
-  using Frag = typename V::Frag;
-  using Acc = typename V::Acc;
-  constexpr int NBLK = CB * PB;   // 16 x 16 blocks per tile
-  constexpr int MAXP = 2;         // (tile, block) pairs each wave finishes (the host checks the bound)
-  int nblocks = gridDim.x;
-  pin_tiled_args<V::U8>(p, nblocks, true);
-  pin_sgpr(p.sk_tiles);
-  pin_sgpr(p.sk_len);
-  pin_sgpr(p.sk_maxc);
-  pin_sgpr(p.div_steps.magic);
-  pin_sgpr(p.div_steps.shift);
-  pin_sgpr(p.div_len.magic);
-  pin_sgpr(p.div_len.shift);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (see conv_igemm)
-  const int r = lane & 15, g = lane >> 4;
-
-  const int gid = xcd_major(nblocks, blockIdx.x);
-  const int total = p.sk_tiles * p.steps;
-  // the host sizes the grid so that every workgroup has a non-empty range;
-  // an empty one would find no segment and no (tile, block) pair below
-  const int A = gid * p.sk_len;
-  const int B = max(A, min(total, A + p.sk_len));
-  const int len = B - A;
-  const int q0 = A + (len * wave) / NW, q1 = A + (len * (wave + 1)) / NW;
-  const int tA = fdiv(A, p.div_steps), tB = fdiv(B - 1, p.div_steps);
-
-  __shared__ Acc red[NW][2][NBLK][64];  // each wave's partial sums of its (at most two) segments
-  __shared__ int seg_tile[NW][2];       // the tile of each segment, -1 for none
-  __shared__ int s_last[2];             // this workgroup finishes its first / last tile
-
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
-
-  // The K steps [sa, sb) of tile t into acc, with a ring of PF steps of loads in
-  // flight (loads past sb - 1 are clamped onto it, as in conv_igemm).
-  auto segment = [&](int t, int sa, int sb, Acc(&acc)[CB][PB]) {
-    int px_tile, co_tile;
-    tile_of(p, t, px_tile, co_tile);
-    int pixbase[PB], iy0[PB], ix0[PB];
-    bool mval[PB];
-#pragma unroll
-    for (int b = 0; b < PB; b++) {
-      const int m = (px_tile * PB + b) * 16 + r;
-      mval[b] = m < p.M;
-      const int mm = mval[b] ? m : 0;
-      const int tt = fdiv(mm, p.div_ow);
-      const int ow = mm - tt * p.OW;
-      const int n = fdiv(tt, p.div_oh);
-      const int oh = tt - n * p.OH;
-      iy0[b] = oh * p.stride - p.pad;
-      ix0[b] = ow * p.stride - p.pad;
-      pixbase[b] = (n * p.H + iy0[b]) * p.W + ix0[b];
-    }
-    unsigned wvoff[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++) {
-      const int blk = co_tile * CB + cb;
-      wvoff[cb] = blk < p.co_blocks ? ((unsigned)(blk * p.steps) * 64u + (unsigned)lane) * 16u : kOutOfRange;
-    }
-    auto load = [&](int s, Frag(&aa)[CB], Frag(&bb)[PB]) {
-#pragma unroll
-      for (int cb = 0; cb < CB; cb++)
-        aa[cb] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], s * 1024, 0));
-      if constexpr (V::VEC == 1) {
-        const Chunk c = decode_chunk(p, s * 4 + g);
-        const int doff = (c.dy * p.W + c.dx) * p.x_cs + c.ci;
-#pragma unroll
-        for (int b = 0; b < PB; b++) {
-          const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
-          const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
-          const unsigned off = v ? (unsigned)(pixbase[b] * p.x_cs + doff) * (unsigned)V::ESIZE : kOutOfRange;
-          bb[b] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const Chunk c = decode_chunk(p, (s * 4 + g) * 4 + j);
-          const int doff = (c.dy * p.W + c.dx) * p.x_cs + c.ci;
-#pragma unroll
-          for (int b = 0; b < PB; b++) {
-            const int iy = iy0[b] + c.dy, ix = ix0[b] + c.dx;
-            const bool v = c.ok && mval[b] && (unsigned)iy < (unsigned)p.H && (unsigned)ix < (unsigned)p.W;
-            const unsigned off = v ? (unsigned)(pixbase[b] * p.x_cs + doff) : kOutOfRange;
-            bb[b][j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
-          }
-        }
-      }
-    };
-    auto mma = [&](const Frag(&aa)[CB], const Frag(&bb_in)[PB]) {
-      Frag bb[PB];
-#pragma unroll
-      for (int b = 0; b < PB; b++) {
-        if constexpr (V::U8)
-          bb[b] = bb_in[b] ^ kU8Flip;
-        else
-          bb[b] = bb_in[b];
-      }
-      if constexpr (!V::I8) {
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-          for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-            for (int b = 0; b < PB; b++)
-              acc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[cb][j], bb[b][j], acc[cb][b], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-          for (int b = 0; b < PB; b++)
-            acc[cb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa[cb], bb[b], acc[cb][b], 0, 0, 0);
-      }
-    };
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-      for (int b = 0; b < PB; b++) acc[cb][b] = Acc{};
-    const int s_last_step = sb - 1;
-    Frag a[PF][CB], b[PF][PB];
-#pragma unroll
-    for (int i = 0; i < PF; i++) load(min(sa + i, s_last_step), a[i], b[i]);
-    int s = sa;
-    for (; s + PF - 1 < sb; s += PF) {
-#pragma unroll
-      for (int i = 0; i < PF; i++) {
-        mma(a[i], b[i]);
-        load(min(s + i + PF, s_last_step), a[i], b[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PF; i++)
-      if (s + i < sb) mma(a[i], b[i]);
-  };
-
-  // 1) this wave's segments: tile of q0 from its step to the sub-range's end
-  //    or the tile's end, then (if the sub-range goes on) the next tile
-  {
-    int t0 = -1, t1 = -1;
-    if (q0 < q1) {
-      t0 = fdiv(q0, p.div_steps);
-      const int tile_end = (t0 + 1) * p.steps;
-      Acc acc[CB][PB];
-      segment(t0, q0 - t0 * p.steps, min(q1, tile_end) - t0 * p.steps, acc);
-#pragma unroll
-      for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-        for (int b = 0; b < PB; b++) red[wave][0][cb * PB + b][lane] = acc[cb][b];
-      if (q1 > tile_end) {
-        t1 = t0 + 1;
-        segment(t1, 0, q1 - tile_end, acc);
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-          for (int b = 0; b < PB; b++) red[wave][1][cb * PB + b][lane] = acc[cb][b];
-      }
-    }
-    if (lane == 0) {
-      seg_tile[wave][0] = t0;
-      seg_tile[wave][1] = t1;
-    }
-  }
-  __syncthreads();
-
-  // 2) the workgroup's sum of each (tile, block) pair it touches, in wave
-  //    order; pair k = (tile tA + k / NBLK, block k % NBLK) is finished by
-  //    wave k % NW (at most MAXP per wave)
-  const int npairs = len > 0 ? (tB - tA + 1) * NBLK : 0;
-  Acc sum[MAXP];
-#pragma unroll
-  for (int i = 0; i < MAXP; i++) {
-    sum[i] = Acc{};
-    const int k = wave + i * NW;
-    if (k >= npairs) continue;
-    const int t = tA + k / NBLK, blk = k % NBLK;
-#pragma unroll
-    for (int w = 0; w < NW; w++)
-#pragma unroll
-      for (int j = 0; j < 2; j++)
-        if (seg_tile[w][j] == t) sum[i] += red[w][j][blk][lane];
-  }
-
-  // 3) a tile whose steps all lie in this workgroup is complete; the first and
-  //    the last tile may be shared with neighbours: publish this workgroup's
-  //    part, take the tile's ticket, and the last workgroup to arrive sums the
-  //    parts in workgroup order.  (See the split-K publication in conv_igemm
-  //    for why no fence is needed.)
-  auto shared_tile = [&](int t) { return A > t * p.steps || B < (t + 1) * p.steps; };
-  auto slot_of = [&](int t) { return gid - fdiv(t * p.steps, p.div_len); };
-  auto ws_off = [&](int t, int slot, int blk) {
-    return (unsigned)((((t * p.sk_maxc + slot) * NBLK + blk) * 64 + lane) * 16);
-  };
-  const __amdgpu_buffer_rsrc_t wsr = rsrc(p.ws, (unsigned)(p.sk_tiles * p.sk_maxc * NBLK * 64 * 16));
-  const bool any_shared = len > 0 && (shared_tile(tA) || shared_tile(tB));
-  if (any_shared) {
-#pragma unroll
-    for (int i = 0; i < MAXP; i++) {
-      const int k = wave + i * NW;
-      if (k >= npairs) continue;
-      const int t = tA + k / NBLK, blk = k % NBLK;
-      if (shared_tile(t))
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sum[i]), wsr, ws_off(t, slot_of(t), blk), 0,
-                                               kPartialStore);
-    }
-    partials_published();
-    __syncthreads();
-    if (threadIdx.x < 2) {
-      const int t = threadIdx.x == 0 ? tA : tB;
-      int last = 1;
-      if (shared_tile(t) && (threadIdx.x == 0 || tB != tA)) {
-        const int first = fdiv(t * p.steps, p.div_len), lastg = fdiv((t + 1) * p.steps - 1, p.div_len);
-        const unsigned prev =
-            __hip_atomic_fetch_add(gmem<unsigned>(p.counters) + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = prev == (unsigned)(lastg - first);
-        if (last) __hip_atomic_store(gmem<unsigned>(p.counters) + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      s_last[threadIdx.x] = last;
-    }
-    __syncthreads();
-    partials_acquired();
-  }
-
-  // 4) epilogue of every pair this wave finishes
-  const __amdgpu_buffer_rsrc_t rr = rsrc(p.res, p.res_bytes);
-  const __amdgpu_buffer_rsrc_t br =
-      __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t dr =
-      __builtin_amdgcn_make_buffer_rsrc((void *)p.dq, 0, V::I8 ? (int)(p.co_blocks * 64) : 0, kRsrcWord3);
-#pragma unroll
-  for (int i = 0; i < MAXP; i++) {
-    const int k = wave + i * NW;
-    if (k >= npairs) continue;
-    const int t = tA + k / NBLK, blk = k % NBLK;
-    Acc acc = sum[i];
-    if (any_shared && shared_tile(t)) {
-      if (!s_last[t == tA ? 0 : 1]) continue;
-      const int first = fdiv(t * p.steps, p.div_len), lastg = fdiv((t + 1) * p.steps - 1, p.div_len);
-      Acc tot = Acc{};
-      for (int gg = first; gg <= lastg; gg++) {
-        const Acc v = gg == gid ? acc
-                                : __builtin_bit_cast(Acc, __builtin_amdgcn_raw_buffer_load_b128(
-                                                              wsr, ws_off(t, gg - first, blk), 0, kPartialLoad));
-        tot += v;
-      }
-      acc = tot;
-    }
-    int px_tile, co_tile;
-    tile_of(p, t, px_tile, co_tile);
-    const int cb = blk / PB, b = blk % PB;
-    const int m = (px_tile * PB + b) * 16 + r;
-    const int co0 = (co_tile * CB + cb) * 16 + 4 * g;
-    if (m >= p.M || co0 >= p.cout_pad) continue;
-    const int tt = fdiv(m, p.div_ow);
-    const int ow = m - tt * p.OW;
-    const int n = fdiv(tt, p.div_oh);
-    const int oh = tt - n * p.OH;
-    const int opix = (n * p.OH + oh) * p.pitch + ow;
-    if constexpr (V::U8) acc += zp_correction<V>(p, border_class(p, oh * p.stride - p.pad, ow * p.stride - p.pad), co0);
-    if constexpr (V::RAW) {
-      store16(p, (unsigned)(opix * p.out_cs + co0) * 4u, acc);
-    } else {
-      const f32x4 bias = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, (unsigned)(co0 * 4), 0, 0));
-      f32x4 dq = f32x4{1.f, 1.f, 1.f, 1.f};
-      if constexpr (V::I8) dq = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, (unsigned)(co0 * 4), 0, 0));
-      f32x4 z;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        if constexpr (V::I8)
-          z[e] = (float)acc[e] * dq[e] + bias[e];
-        else
-          z[e] = acc[e] + bias[e];
-      }
-      epilogue_store<V::X>(p, rr, z, opix, m, co0);
-    }
-  }
-}
-
 // ---------------------------------------------------------------- launch --
 template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
 static hipError_t launch_one(const ConvParams &p, hipStream_t stream) {
@@ -1680,17 +1386,6 @@ template <int VAR, int TH, int TW>
 static hipError_t launch_halo_pair(const ConvParams &p, hipStream_t stream) {
   if (p.splitk != 1 || p.co_blocks != 1 || p.k != 3 || p.stride != 1 || p.cout_pad > 8) return hipErrorInvalidValue;
   hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 1, true, true>), dim3((unsigned)p.px_tiles), dim3(256),
-                     (unsigned)p.smem_bytes, stream, p);
-  return hipGetLastError();
-}
-
-// Stream-K: one workgroup per CU (p.px_tiles holds the grid).  The dynamic LDS
-// it asks for is never used: with it a workgroup takes more than half of a
-// CU's 160 KB of LDS, so no CU runs two of them while another has none.
-template <int VAR, int CB, int PB, int NW, int PF>
-static hipError_t launch_sk(const ConvParams &p, hipStream_t stream) {
-  if (p.splitk != 1 || p.sk_tiles < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((conv_sk<VAR, CB, PB, NW, PF>), dim3((unsigned)p.px_tiles), dim3(64 * NW),
                      (unsigned)p.smem_bytes, stream, p);
   return hipGetLastError();
 }
@@ -1782,11 +1477,6 @@ static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t strea
   case id:                                  \
     return launch_lds<VAR, mb, nb, wm, wn, ks, ns, true>(p, stream);
     CBS_LDS_RING_SWZ_CONFIG_LIST(X)
-#undef X
-#define X(id, cb, pb, nw, pf, name) \
-  case id:                          \
-    return launch_sk<VAR, cb, pb, nw, pf>(p, stream);
-    CBS_SK_CONFIG_LIST(X)
 #undef X
     default:
       return hipErrorInvalidValue;

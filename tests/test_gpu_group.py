@@ -42,8 +42,8 @@ def register_direct_configs():
 
 
 def groupable_configs():
-    """Register-direct and LDS-staged tiles (halo and stream-K tiles have no grouped kernel)."""
-    return [i for i in range(cbs.cbs_num_configs()) if not cbs.cbs_config_name(i).startswith(("H", "P", "S."))]
+    """Register-direct and LDS-staged tiles (halo tiles have no grouped kernel)."""
+    return [i for i in range(cbs.cbs_num_configs()) if not cbs.cbs_config_name(i).startswith(("H", "P"))]
 
 
 class Member:
