@@ -361,9 +361,10 @@ KERNEL_SOURCES = ("convolution_implicit_gemm_02_amd/csrc/conv_kernels.h",
 
 def measured_traffic(layer):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary (profiles/traffic_dominant.json), scaled by
-    the counters of a plain copy of known size.  None when that summary is for
-    another layer or the kernel sources changed since it was taken."""
+    FETCH_SIZE / WRITE_SIZE summaries (profiles/traffic_dominant.json, one entry
+    per layer that can come out dominant), scaled by the counters of a plain
+    copy of known size.  None when no entry covers the layer or the kernel
+    sources changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic_dominant.json")
     if not os.path.exists(path):
@@ -372,9 +373,10 @@ def measured_traffic(layer):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, f), "rb").read())
-    if rec.get("layer") != layer or rec.get("source_sha256") != h.hexdigest():
+    entry = rec.get("layers", {}).get(layer)
+    if entry is None or rec.get("source_sha256") != h.hexdigest():
         return None
-    return rec["traffic_bytes"]
+    return entry["traffic_bytes"]
 
 
 def cpu_model():

@@ -3,12 +3,15 @@
 Two kinds, each from runs whose commands the summary itself records:
 
   python -m convolution_implicit_gemm_02_amd.profile_summary dominant OUT_DIR
-      OUT_DIR/prof_dom (--kernel-trace --stats), OUT_DIR/pmc_fetch and
-      OUT_DIR/pmc_write (--pmc FETCH_SIZE, --pmc WRITE_SIZE) of
-      `bench.py --only-layer neck256.3x3`, plus OUT_DIR/bench.log (a default
-      bench run of the same tree): profiles/conv_igemm_<layer>_f32_bs1.md and
-      profiles/traffic_dominant.json (the traffic figure bench.py reports while
-      the kernel sources hash to the profiled ones).
+      for each layer L of DOMINANT_LAYERS (the batch-1 FP32 layers whose
+      per-launch times tie at the top of the list): OUT_DIR/prof_dom_L
+      (--kernel-trace --stats, with the program's output in prof_dom_L.log),
+      OUT_DIR/pmc_fetch_L and OUT_DIR/pmc_write_L (--pmc FETCH_SIZE,
+      --pmc WRITE_SIZE) of `bench.py --only-layer L`, plus OUT_DIR/bench.log
+      and bench_layers.json (a default bench run of the same tree):
+      profiles/conv_igemm_L_f32_bs1.md and profiles/traffic_dominant.json
+      (per-layer traffic that bench.py reports while the kernel sources hash
+      to the profiled ones).
 
   python -m convolution_implicit_gemm_02_amd.profile_summary layers OUT_DIR DTYPE BATCH
       OUT_DIR/lp_<dtype>_bs<batch>/{trace,mfma,fetch,write} of
@@ -43,14 +46,26 @@ def _copy_factor(rows, counter):
     return COPY_KIB / (sum(v) / len(v)), sum(v) / len(v)
 
 
-def dominant(out_dir, layer="neck256.3x3"):
+DOMINANT_LAYERS = ("neck256.3x3", "neck64.3x3", "head64.3x3")
+
+
+def _source_hash():
     sys.path.insert(0, ROOT)
     import bench
-    stats = _rows(os.path.join(out_dir, "prof_dom", "*kernel_stats.csv"))
+    h = hashlib.sha256()
+    for f in bench.KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def _dominant_one(out_dir, layer, bench_line):
+    sub = lambda kind: os.path.join(out_dir, "%s_%s" % (kind, layer))
+    stats = _rows(os.path.join(sub("prof_dom"), "*kernel_stats.csv"))
     kern = [s for s in stats if s["Name"].startswith("void cbs::conv")][0]
     kname = kern["Name"]
-    fr = _rows(os.path.join(out_dir, "pmc_fetch", "*counter_collection.csv"))
-    wr = _rows(os.path.join(out_dir, "pmc_write", "*counter_collection.csv"))
+    fr = _rows(os.path.join(sub("pmc_fetch"), "*counter_collection.csv"))
+    wr = _rows(os.path.join(sub("pmc_write"), "*counter_collection.csv"))
+    info = [json.loads(line) for line in open(sub("prof_dom") + ".log") if line.startswith('{"layer"')][0]
 
     def avg(rows):
         v = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == kname]
@@ -60,56 +75,88 @@ def dominant(out_dir, layer="neck256.3x3"):
     ff, fcopy = _copy_factor(fr, "FETCH_SIZE")
     wf, wcopy = _copy_factor(wr, "WRITE_SIZE")
     traffic = int(round((fk * ff + wk * wf) * 1024))
-    h = hashlib.sha256()
-    for f in bench.KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    line = json.loads(open(os.path.join(out_dir, "bench.log")).read().strip().split("\n")[-1])
-    ev = line["roofline"]["us_per_launch"]
-    rec = {"layer": layer, "dtype": "f32", "batch": 1, "kernel": kname, "source_sha256": h.hexdigest(),
-           "fetch_kib": fk, "write_kib": wk, "fetch_factor": ff, "write_factor": wf, "traffic_bytes": traffic,
-           "rocprof_avg_ns": float(kern["AverageNs"]), "summary": "profiles/conv_igemm_%s_f32_bs1.md" % layer}
-    with open(os.path.join(ROOT, "profiles", "traffic_dominant.json"), "w") as f:
-        json.dump(rec, f, indent=1)
-        f.write("\n")
+    alg = int(info["alg_bytes"])
+    rec = {"kernel": kname, "config": info["config"], "grid": info["grid"], "fetch_kib": fk, "write_kib": wk,
+           "fetch_factor": ff, "write_factor": wf, "traffic_bytes": traffic, "alg_bytes": alg,
+           "rocprof_avg_ns": float(kern["AverageNs"]), "graph_us_per_launch": info["us_per_launch"],
+           "summary": "profiles/conv_igemm_%s_f32_bs1.md" % layer}
     tbl = "\n".join("| `%s` | %s | %.1f | %s | %s |" % (s["Name"][:90], s["Calls"], float(s["AverageNs"]), s["MinNs"],
                                                          s["MaxNs"]) for s in stats)
+    bench_row = None
+    if bench_line is not None:
+        bench_row = [r for r in bench_line.get("_rows", []) if r["layer"] == layer]
+    ev = ("`bench.py` (default run of the same tree) reports %.3f us per launch for this layer in the "
+          "list's per-layer table" % bench_row[0]["us"]) if bench_row else ""
+    dom_note = ""
+    if bench_line is not None:
+        roof = bench_line["roofline"]
+        dom_note = ("In that run the dominant layer was %s (%.3f us per launch)." %
+                    (roof["layer"], roof["us_per_launch"]))
     md = f"""# rocprofv3 summary: {kname}, layer {layer} (batch 1, FP32)
 
-Dominant kernel of the batch-1 FP32 YOLO26n list step (largest per-launch time in `bench.py`).
+One of the three layers of the batch-1 FP32 YOLO26n list step whose per-launch times lie within a few
+tenths of a microsecond of each other at the top of the list (neck256.3x3, neck64.3x3, head64.3x3);
+`bench.py` reports the one that measures largest in its run as the dominant kernel. {dom_note}
 
 ## Kernel trace (`--kernel-trace --stats`)
 
 Command (from the repository root on the GPU box):
 
 ```
-rocprofv3 --kernel-trace --stats --output-format csv -d $PWD/gpurun_out/prof_dom -o dom -- python bench.py --only-layer {layer} --launches 200
+rocprofv3 --kernel-trace --stats --output-format csv -d $PWD/gpurun_out/prof_dom_{layer} -o dom -- python bench.py --only-layer {layer} --launches 200
 ```
+
+The program launches the layer 10 times eagerly, then replays one captured graph of 200 launches
+(the way the list step runs its kernels), then five 256 MiB device copies.
 
 | Kernel | Calls | Average ns | Min ns | Max ns |
 |---|---|---|---|---|
 {tbl}
 
-`bench.py` event timing in the default run of the same tree: {ev:.3f} us per launch (rocprofv3 average {float(kern['AverageNs']) / 1000:.3f} us).
+Event timing of the 200-launch graph replay inside the profiled program: {info['us_per_launch']:.3f} us per launch
+(rocprofv3 average {float(kern['AverageNs']) / 1000:.3f} us over all 210 dispatches). {ev}.
 
 ## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, separate runs)
 
 ```
-rocprofv3 --pmc FETCH_SIZE --output-format csv -d $PWD/gpurun_out/pmc_fetch -o fetch -- python bench.py --only-layer {layer} --launches 20
-rocprofv3 --pmc WRITE_SIZE --output-format csv -d $PWD/gpurun_out/pmc_write -o write -- python bench.py --only-layer {layer} --launches 20
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d $PWD/gpurun_out/pmc_fetch_{layer} -o fetch -- python bench.py --only-layer {layer} --launches 20
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d $PWD/gpurun_out/pmc_write_{layer} -o write -- python bench.py --only-layer {layer} --launches 20
 ```
 
-Reference: the same runs end with device copies of 256 MiB (`__amd_rocclr_copyBuffer`); their counters read FETCH_SIZE = {fcopy:.0f} KiB and WRITE_SIZE = {wcopy:.0f} KiB per copy against 262144 KiB moved, so the scale factors are {ff:.3f} (fetch) and {wf:.3f} (write).
+Reference: the same runs end with device copies of 256 MiB (`__amd_rocclr_copyBuffer`); their counters read
+FETCH_SIZE = {fcopy:.0f} KiB and WRITE_SIZE = {wcopy:.0f} KiB per copy against 262144 KiB moved, so the scale
+factors are {ff:.3f} (fetch) and {wf:.3f} (write).
 
 | Kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | scaled bytes/dispatch |
 |---|---|---|---|
 | `{kname}` | {fk:.2f} | {wk:.2f} | {traffic} |
 
-Algorithmic bytes per launch: 3,180,544 (input 409,600 + weights 2,359,296 + output 409,600 + folded bias and scale 2,048). The L2-miss traffic is {traffic / 3180544:.2f}x that: each of the eight XCDs fetches the whole input and its share of the weights.
+Algorithmic bytes per launch: {alg:,} (input + weights + output + folded bias and scale, each once).
+The counted L2-miss traffic is {traffic / alg:.2f}x that; misses may be served by the 256 MB MALL
+rather than HBM, and every XCD's L2 fetches its own copy of what its workgroups read.
 
 Summarised by `python -m convolution_implicit_gemm_02_amd.profile_summary dominant gpurun_out`.
 """
     with open(os.path.join(ROOT, "profiles", "conv_igemm_%s_f32_bs1.md" % layer), "w") as f:
         f.write(md)
+    return rec
+
+
+def dominant(out_dir, layers=DOMINANT_LAYERS):
+    """Per-layer traffic of the candidates for the dominant kernel, from
+    OUT_DIR/{prof_dom,pmc_fetch,pmc_write}_<layer>, and OUT_DIR/bench.log."""
+    bench_line = None
+    blog = os.path.join(out_dir, "bench.log")
+    if os.path.exists(blog):
+        bench_line = json.loads(open(blog).read().strip().split("\n")[-1])
+        bl = os.path.join(out_dir, "bench_layers.json")
+        if os.path.exists(bl):
+            bench_line["_rows"] = json.load(open(bl))["results"]["f32_bs1"]["rows"]
+    rec = {"dtype": "f32", "batch": 1, "source_sha256": _source_hash(),
+           "layers": {layer: _dominant_one(out_dir, layer, bench_line) for layer in layers}}
+    with open(os.path.join(ROOT, "profiles", "traffic_dominant.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
     return rec
 
 
