@@ -160,6 +160,23 @@ class ListBench:
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall / steps * 1e3
 
+    def time_prefix(self, n, steps, warmup):
+        """The first n layers of the list as one captured graph (one launch per
+        layer, in list order): ms per replay."""
+        torch, cbs = self.torch, self.cbs
+        g = cbs.cbs_graph_create(self.layers[:n], self.ins[:n], self.outs[:n])
+        for _ in range(warmup):
+            cbs.cbs_graph_launch(g)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            cbs.cbs_graph_launch(g)
+        e1.record()
+        torch.cuda.synchronize()
+        cbs.cbs_graph_destroy(g)
+        return e0.elapsed_time(e1) / steps
+
     def _step(self, use_graph):
         if use_graph:
             self.cbs.cbs_graph_launch(self.graph)
@@ -298,6 +315,40 @@ class ChainBench:
             cur, s_in = Y, s_act
         torch.cuda.synchronize()
         self.graph = cbs.cbs_graph_create_steps(self.steps)
+
+    def time_layers(self, min_ms=2.0, reps=5):
+        """Per chained step: the median over `reps` of (event pair around one replay
+        of a captured graph of R back-to-back launches of that step)/R, in us, as
+        ListBench.time_layers times the list's layers."""
+        torch, cbs = self.torch, self.cbs
+        out = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for st in self.steps:
+            cbs.cbs_run_steps([st] * 3)
+            ten = cbs.StepList([st] * 10)
+            torch.cuda.synchronize()
+            e0.record()
+            ten.run()
+            e1.record()
+            torch.cuda.synchronize()
+            per = max(e0.elapsed_time(e1) / 10, 1e-4)
+            r = int(min(2000, max(10, min_ms / per)))
+            lst = cbs.StepList([st] * r)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                lst.run()
+            g.replay()
+            torch.cuda.synchronize()
+            t = []
+            for _ in range(reps):
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                t.append(e0.elapsed_time(e1) / r)
+            del g
+            out.append(float(np.median(t)) * 1e3)
+        return out
 
     def time_steps(self, steps, warmup, use_graph=True):
         torch, cbs = self.torch, self.cbs
@@ -583,6 +634,8 @@ def main():
         results[key] = {"ms_per_step": ms_graph, "wall_ms_per_step": wall_graph, "ms_per_step_plain_launches": ms_list,
                         "flops": b.flops, "rows": rows, "sum_us_single_launch": round(sum(us_single), 2),
                         "sum_us_flushed": round(sum(us_flushed), 2)}
+        if name in ("f32", "int8out") and not args.quick:  # the unchained twins of the chained backbone
+            results[key]["us_first25_graph"] = round(b.time_prefix(25, steps, args.warmup) * 1e3, 2)
         chosen = b.group_head()
         ms_grouped = b.time_grouped(steps, args.warmup)
         launches = b.grouped_launches
@@ -633,14 +686,23 @@ def main():
         steps = args.steps if bs == 1 else max(10, args.steps // 8)
         ms_graph = c.time_steps(steps, args.warmup, use_graph=True)
         ms_plain = c.time_steps(steps, args.warmup, use_graph=False)
+        us_steps = c.time_layers()
         lst = results.get("%s_bs%d" % ("int8out" if int8 else "f32", bs))
         indep = round(sum(r["us"] for r in lst["rows"][:25]), 2) if lst else None
+        indep_graph = lst.get("us_first25_graph") if lst else None
         key = "chain_%s_bs%d" % (name, bs)
         chains[key] = {"value": round(c.flops / (ms_graph * 1e-3) / 1e12, 4), "unit": "TOP/s" if int8 else "TFLOP/s",
                        "total_us": round(ms_graph * 1e3, 2), "total_us_plain_launches": round(ms_plain * 1e3, 2),
-                       "layers": len(c.layers), "sum_us_same_layers_unchained": indep}
-        log("%s: 25 chained backbone layers %.1f us (graph), %.1f us (plain); the same layers unchained, "
-            "sum of per-layer %s us" % (key, ms_graph * 1e3, ms_plain * 1e3, indep))
+                       "layers": len(c.layers), "sum_us_chained_steps": round(sum(us_steps), 2),
+                       "total_us_same_layers_unchained_graph": indep_graph,
+                       "sum_us_same_layers_unchained": indep}
+        log("%s: 25 chained backbone layers %.1f us (graph), %.1f us (plain), sum of per-step %.1f us; the same "
+            "layers unchained: %s us as one graph, sum of per-layer %s us"
+            % (key, ms_graph * 1e3, ms_plain * 1e3, sum(us_steps), indep_graph, indep))
+        if lst:
+            for r, u, st in zip(lst["rows"][:25], us_steps, c.steps):
+                log("  %-13s chained %8.2f us (%s)  unchained %8.2f us (%s)"
+                    % (r["layer"], u, cbs.cbs_layer_info(st[0])["config_name"], r["us"], r["config"]))
         del c
         torch.cuda.empty_cache()
 
