@@ -140,7 +140,7 @@ def flat_memory_ops(text: str, pattern: str):
 
 
 VARIANTS = 12  # kernel variants, one translation unit each (cbs_variant.hip with -DCBS_VAR=n)
-CONV_KERNELS = r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo)\w+):"
+CONV_KERNELS = r"^(_ZN3cbs(?:10conv_igemm|8conv_lds|9conv_halo|7conv_ws)\w+):"
 # grouped launches read their member's arguments in a second round, at an
 # offset that depends on the first (the group's workgroup ranges)
 GROUP_KERNELS = r"^(_ZN3cbs(?:16conv_igemm_group|14conv_lds_group)\w+):"

@@ -69,6 +69,7 @@ struct cbs_layer {
   unsigned cpt_magic;
   int config, splitk;
   int device;
+  int cus = 256;     // compute units of the device (sizes the conv_ws grid)
   // device memory
   void *d_wfrag = nullptr;
   float *d_bias = nullptr;
@@ -227,6 +228,12 @@ void tiles_of(const cbs_layer *L, int cfg, int *px_tiles, int *co_tiles) {
     *px_tiles = L->d.n * ceil_div(L->oh, c.th) * ceil_div(L->ow, c.lds == 3 ? 2 * c.tw : c.tw);
     return;
   }
+  if (c.lds == 4) {  // conv_ws: channel groups x runs of 16-pixel blocks, about th workgroups per CU
+    *co_tiles = ceil_div(L->co_blocks, c.cb * c.wco);
+    const int blocks = ceil_div(L->M, 16);
+    *px_tiles = std::max(1, std::min(blocks, (L->cus * c.th + *co_tiles / 2) / *co_tiles));
+    return;
+  }
   const int tco = c.cb * 16 * c.wco, tpx = c.pb * 16 * c.wpx;
   *co_tiles = ceil_div(L->co_blocks * 16, tco);
   *px_tiles = ceil_div(L->M, tpx);
@@ -287,6 +294,13 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
   const KernelConfig &c = config(cfg);
   if (splitk < 1 || splitk > 64) return false;
   if (c.lds && splitk != 1) return false;
+  if (c.lds == 4) {  // conv_ws: fp32 1x1 stride 1, whole 16-channel K steps of the compiled depths
+    if (L->d.dtype != CBS_F32 || L->d.k != 1 || L->d.stride != 1 || L->d.pad != 0) return false;
+    if (L->cin_pad % 16 != 0) return false;
+    const int ks = L->steps;
+    if (!(ks == 4 || ks == 6 || ks == 8 || ks == 12 || ks == 16 || ks == 24)) return false;
+    if (ks > ws_max_steps(c.cb)) return false;  // deepest K the launcher instantiates
+  }
   if (c.lds == 2 || c.lds == 3) {
     if (L->d.k != 3 || L->co_blocks > 4) return false;
     if (c.lds == 3 && !L->pair) return false;
@@ -535,6 +549,11 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
     p.w_bytes = (unsigned)((size_t)L->pair_steps * 64 * 16);
   }
   tiles_of(L, cfg, &p.px_tiles, &p.co_tiles);
+  if (kc.lds == 4) {  // conv_ws runs: as equal as whole 16-pixel blocks allow
+    const int blocks = ceil_div(L->M, 16);
+    p.run_base = blocks / p.px_tiles;
+    p.run_rem = blocks % p.px_tiles;
+  }
   // Workgroup order (see tile_of in conv_kernels.h): pixel tiles inner when
   // the weights are larger than the input, so that each XCD's L2 fetches only
   // the weights of its own channel tiles.
@@ -716,6 +735,13 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   if (hipGetDevice(&L->device) != hipSuccess) {
     delete L;
     return fail(CBS_EDEVICE, "hipGetDevice failed");
+  }
+  {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device) == hipSuccess && cus > 0)
+      L->cus = cus;
+    else
+      (void)hipGetLastError();
   }
   L->oh = out_dim(d.h, d.k, d.stride, d.pad);
   L->ow = out_dim(d.w, d.k, d.stride, d.pad);

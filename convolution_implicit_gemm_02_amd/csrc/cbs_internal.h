@@ -15,9 +15,15 @@ struct KernelConfig {
   int lds;  // 0: operands straight to registers (conv_igemm); 1: LDS-staged tiles (conv_lds);
             // 2: input halo tile + all weights in LDS (conv_halo, 3x3 with <= 64 output channels);
             // 3: conv_halo on column pairs (3x3 stride 1 with <= 8 output channels; th x tw pairs)
-  int th, tw;  // conv_halo: output tile of th x tw pixels
+            // 4: conv_ws (fp32 1x1 stride 1: weights held in registers, runs of pixel blocks)
+  int th, tw;  // conv_halo: output tile of th x tw pixels; conv_ws: th = workgroups per CU
   const char *name;
 };
+
+// conv_ws: deepest K (in 16-channel steps) compiled for waves holding cb
+// channel blocks each, so that weights and two blocks of activations fit the
+// registers of a wave without spilling.
+constexpr int ws_max_steps(int cb) { return cb == 2 ? 16 : 24; }
 
 // Kernel-variant families (dtype x operand gathering x epilogue).
 enum Variant {
@@ -101,6 +107,7 @@ struct ConvParams {
   int px_inner;          // 1: pixel tiles inner (channel-major order), 0: channel tiles inner
   FastDiv div_ow, div_oh;    // by OW and OH: pixel index -> (n, oh, ow)
   FastDiv div_inner;         // by inner_tiles: workgroup -> (outer tile, inner tile)
+  int run_base, run_rem;     // conv_ws: run t holds 16-pixel blocks [t*run_base + min(t, run_rem), +run_base + (t < run_rem))
   // ---- cross-workgroup split-K (conv_igemm)
   float *ws;             // split-K partial tiles (null when splitk == 1)
   unsigned *counters;    // split-K arrival counters, one per output tile (zero between launches)

@@ -103,3 +103,9 @@
   X(55, 2, 2, 2, 4, 2, 2, "RS.p64c128w8")       \
   X(56, 2, 1, 2, 4, 2, 0, "LS.p64c64w8")
 
+// conv_ws (fp32 1x1 stride 1): id, 16-channel blocks per wave, waves per
+// workgroup, workgroups per CU.
+#define CBS_WS_CONFIG_LIST(X)                \
+  X(57, 2, 4, 1, "W.c32x4")                  \
+  X(58, 2, 4, 2, "W.c32x4o2")                \
+  X(59, 1, 4, 1, "W.c16x4")

@@ -1348,6 +1348,129 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   }
 }
 
+// ------------------------------------------------ weight-stationary 1x1 --
+// fp32 1x1 stride-1 layers at large M (the batch-16 1x1 convolutions with
+// 64-384 input channels).  There the output is thousands of 16-pixel blocks
+// deep but only a few channel blocks wide, K is short (4-24 K steps), and a
+// tile of the other kernels pays its prologue (weights, first activations)
+// and its epilogue once per 64-128 pixels.  Here a workgroup of WCO waves
+// owns WCO*CBW channel blocks and a contiguous run of pixel blocks; each wave
+// loads the weights of its CBW channel blocks for all KS steps into registers
+// once, then streams the run's pixel blocks through them.  The activations of
+// the next block are loaded (into a second register set) while the current
+// block's MFMAs and epilogue run.  Runs differ by at
+// most one block, so the work is spread evenly over the grid, which the host
+// sizes to a few workgroups per CU.  The input pixel of an output pixel is its
+// logical index (1x1, stride 1, no padding).
+template <int VAR, int CBW, int WCO, int KS>
+__global__ __launch_bounds__(64 * WCO) void conv_ws(ConvParams p) {
+  using V = Var<VAR>;
+  static_assert(!V::I8, "fp32 activations only");
+  using Frag = typename V::Frag;
+  using Acc = typename V::Acc;
+  int nblocks = gridDim.x;
+  pin_tiled_args<false>(p, nblocks, false);
+  pin_sgpr(p.run_base);
+  pin_sgpr(p.run_rem);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: MFMA guards are scalar
+  const int r = lane & 15, g = lane >> 4;
+  int run, co_tile;
+  tile_of(p, xcd_major(nblocks, blockIdx.x), run, co_tile);
+  const int b0 = run * p.run_base + min(run, p.run_rem);
+  const int b1 = b0 + p.run_base + (run < p.run_rem ? 1 : 0);
+  const int cob0 = (co_tile * WCO + wave) * CBW;
+
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
+  // Activations of pixel block b, K step s: lane (g, r) reads channels
+  // 16s + 4g .. +3 of pixel 16b + r (zero past the run or past M).
+  auto act_off = [&](int b) -> unsigned {
+    const int m = b * 16 + r;
+    return (b < b1 && m < p.M) ? (unsigned)(m * p.x_cs + 4 * g) * 4u : kOutOfRange;
+  };
+  Frag ba[KS], bb[KS];  // activations of the current and of the next pixel block
+  {
+    const unsigned off0 = act_off(b0);
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+      ba[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off0, s * 64, 0));
+  }
+  // this wave's weights (zero for channel blocks past the end) and bias
+  Frag a[CBW][KS];
+  f32x4 bias[CBW];
+  {
+    const __amdgpu_buffer_rsrc_t br =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++) {
+      const unsigned wv = (cob0 + cb) < p.co_blocks
+                              ? ((unsigned)((cob0 + cb) * p.steps) * 64u + (unsigned)lane) * 16u
+                              : kOutOfRange;
+#pragma unroll
+      for (int s = 0; s < KS; s++)
+        a[cb][s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(wr, wv, s * 1024, 0));
+      bias[cb] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, (unsigned)(((cob0 + cb) * 16 + 4 * g) * 4), 0, 0));
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rr = rsrc(p.res, p.res_bytes);
+  // One pixel block, in three phases kept apart by scheduling barriers:
+  //  1. every load of block b + 1 into `nxt`, at an offset computed before
+  //     the previous block's stores (below);
+  //  2. the MFMAs on `cur` (the compiler would otherwise sink the loads below
+  //     them and leave the next block's latency exposed);
+  //  3. the offset of block b + 2, then the epilogue and its stores.
+  // A VALU write to a register that a store still reads waits until the store
+  // has completed, so nothing but loads and MFMAs follows the stores until the
+  // next block's epilogue, a whole block of MFMAs later.
+  unsigned off = act_off(b0 + 1);
+  auto block = [&](int b, const Frag(&cur)[KS], Frag(&nxt)[KS]) {
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+      nxt[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, s * 64, 0));
+    __builtin_amdgcn_sched_barrier(0);
+    Acc acc[CBW];
+#pragma unroll
+    for (int cb = 0; cb < CBW; cb++) acc[cb] = Acc{};
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int cb = 0; cb < CBW; cb++)
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cb][s][j], cur[s][j], acc[cb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    off = act_off(b + 2);
+    // epilogue: 4 channels of pixel 16b + r per lane and channel block
+    const int m = b * 16 + r;
+    if (m < p.M) {
+      const int t = fdiv(m, p.div_ow);
+      const int ow = m - t * p.OW;
+      const int n = fdiv(t, p.div_oh);
+      const int oh = t - n * p.OH;
+      const int opix = (n * p.OH + oh) * p.pitch + ow;
+#pragma unroll
+      for (int cb = 0; cb < CBW; cb++) {
+        const int co0 = (cob0 + cb) * 16 + 4 * g;
+        if (co0 >= p.cout_pad) continue;
+        f32x4 z;
+#pragma unroll
+        for (int i = 0; i < 4; i++) z[i] = acc[cb][i] + bias[cb][i];
+        epilogue_store<V::X>(p, rr, z, opix, m, co0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The prologue's loads are waited for here, so that the loop is entered with
+  // nothing in flight.
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int b = b0; b < b1; b += 2) {
+    block(b, ba, bb);
+    if (b + 1 < b1) block(b + 1, bb, ba);
+  }
+}
+
 // ---------------------------------------------------------------- launch --
 template <int VAR, int CB, int PB, int WCO, int WPX, int WK, int PF>
 static hipError_t launch_one(const ConvParams &p, hipStream_t stream) {
@@ -1388,6 +1511,37 @@ static hipError_t launch_halo_pair(const ConvParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((conv_halo<VAR, TH, TW, 1, true, true>), dim3((unsigned)p.px_tiles), dim3(256),
                      (unsigned)p.smem_bytes, stream, p);
   return hipGetLastError();
+}
+
+// Weight-stationary 1x1 tiles: the K depth is a template argument (the
+// weights of all K steps sit in registers), instantiated for the depths of the
+// batch-16 1x1 layers; fp32 variants only.
+template <int VAR, int CBW, int WCO, int KS>
+static hipError_t launch_ws_k(const ConvParams &p, hipStream_t stream) {
+  hipLaunchKernelGGL((conv_ws<VAR, CBW, WCO, KS>), dim3((unsigned)p.px_tiles * (unsigned)p.co_tiles),
+                     dim3(64 * WCO), 0, stream, p);
+  return hipGetLastError();
+}
+template <int VAR, int CBW, int WCO>
+static hipError_t launch_ws(const ConvParams &p, hipStream_t stream) {
+  if constexpr (VAR != VAR_F32 && VAR != VAR_F32_X) {
+    (void)p, (void)stream;
+    return hipErrorInvalidValue;
+  } else {
+    if (p.splitk != 1 || p.k != 1 || p.stride != 1 || p.pad != 0 || p.chunk_ch != 4) return hipErrorInvalidValue;
+    constexpr int kMax = ws_max_steps(CBW);  // deepest K that fits the registers without spilling
+    switch (p.steps) {
+      case 4: return launch_ws_k<VAR, CBW, WCO, 4>(p, stream);
+      case 6: return launch_ws_k<VAR, CBW, WCO, 6>(p, stream);
+      case 8: return launch_ws_k<VAR, CBW, WCO, 8>(p, stream);
+      case 12: return launch_ws_k<VAR, CBW, WCO, 12>(p, stream);
+      case 16: return launch_ws_k<VAR, CBW, WCO, 16>(p, stream);
+      case 24:
+        if constexpr (kMax >= 24) return launch_ws_k<VAR, CBW, WCO, 24>(p, stream);
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
+  }
 }
 
 template <int VAR, int MB, int NB, int WM, int WN, int KS, int NS = 0, bool SWZ = false>
@@ -1477,6 +1631,11 @@ static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t strea
   case id:                                  \
     return launch_lds<VAR, mb, nb, wm, wn, ks, ns, true>(p, stream);
     CBS_LDS_RING_SWZ_CONFIG_LIST(X)
+#undef X
+#define X(id, cbw, wco, occ, name) \
+  case id:                         \
+    return launch_ws<VAR, cbw, wco>(p, stream);
+    CBS_WS_CONFIG_LIST(X)
 #undef X
     default:
       return hipErrorInvalidValue;

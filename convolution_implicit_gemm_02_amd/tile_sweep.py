@@ -106,6 +106,20 @@ def time_layer(cbs, torch, layer, xin, out, min_ms=1.0, reps=3, res=None):
     return float(np.median(ts))
 
 
+def other_class_entries(path):
+    """Entry lines of classes 2-4 in the table at `path` (a full sweep or a merge
+    times classes 0 and 1 only and keeps these as they are)."""
+    import re
+    keep = []
+    if not os.path.exists(path):
+        return keep
+    for line in open(path):
+        m = re.match(r"\s*\{\s*(-?\d+(?:,\s*-?\d+){9})\}", line)
+        if m and int(m.group(1).split(",")[0]) != 0 and int(m.group(1).split(",")[7]) in (CLS_U8, CLS_I8_X, CLS_F32_X):
+            keep.append(line if line.endswith("\n") else line + "\n")
+    return keep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=DEFAULT_OUT)
@@ -213,11 +227,14 @@ def main():
                                                            for r in report[-len(classes):]),
             time.time() - t_start), flush=True)
 
+    kept = [] if args.classes else other_class_entries(DEFAULT_OUT)
     with open(args.out, "w") as f:
         f.write(HEADER % name)
         for e in entries:
             f.write("    {%d, %d, %d, %d, %d, %d, %d, %d, %d, %d},  // %s %s %.2f us\n" % (
                 e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7], e[8], e[9], e[11], CLASS_NAMES[e[7]], e[10]))
+        for line in kept:  # classes this mode does not sweep: the current table's entries, unchanged
+            f.write(line)
         f.write("    {0, 0, 0, 0, 0, 0, 0, 0, 0, 1},  // sentinel: n == 0 never matches\n};\n")
     if args.json:
         with open(args.json, "w") as f:

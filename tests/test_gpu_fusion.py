@@ -429,7 +429,23 @@ def test_slices_and_residual(idx, mode):
 # second has 8 output channels and an odd width, so the column-pair halo tiles run
 # too (a C3k2 bottleneck conv of the 16-channel stage) with a half-used last pair
 OPTION_CASES = [(spec(16, 16, 20, 20, 3, 1), (48, 16), (48, 32), (48, 16)),
-                (spec(8, 8, 20, 19, 3, 1), (24, 8), (24, 16), (24, 8))]
+                (spec(8, 8, 20, 19, 3, 1), (24, 8), (24, 16), (24, 8)),
+                # a 1x1 that the fp32 weight-stationary tiles take (the C3k2 cv1 / cv2 shapes)
+                (spec(64, 32, 20, 19, 1, 1), (96, 16), (96, 64), (96, 0))]
+
+
+def runs_on(name, sp, dtype):
+    """Whether configuration `name` can run layer `sp` of input type `dtype` (families
+    that apply to some shapes only: halo tiles need 3x3, column pairs also stride 1
+    and at most 8 output channels, weight-stationary tiles fp32 1x1 stride 1 with
+    C_in in 64, 96, 128, 192, 256, 384)."""
+    if name.startswith("P"):
+        return sp.k == 3 and sp.stride == 1 and sp.c_out <= 8
+    if name.startswith("H"):
+        return sp.k == 3
+    if name.startswith("W."):
+        return dtype == "f32" and sp.k == 1 and sp.stride == 1 and sp.c_in in (64, 96, 128, 192, 256, 384)
+    return True
 
 
 @pytest.mark.parametrize("mode", [("f32", "f32"), ("i8", "i8"), ("u8", "u8")])
@@ -440,7 +456,7 @@ def test_fused_options_on_every_config(mode, oc):
     sp, ins, outs, res = OPTION_CASES[oc]
     case = Case(sp, n=1, dtype=mode[0], out=mode[1], in_sl=ins, out_sl=outs, res_sl=res, extra=8, seed=30)
     prep = prepare(case)
-    ran = 0
+    ran = set()
     for cfg in range(cbs.cbs_num_configs()):
         for sk in (1, 2):
             try:
@@ -450,12 +466,11 @@ def test_fused_options_on_every_config(mode, oc):
                 continue
             got, _ = run(case, prep)
             check(case, prep, got)
-            ran += 1
-    # every configuration runs at least once, except the column-pair tiles on layers
-    # with more than 8 output channels
+            ran.add(cfg)
+    # every configuration whose family applies to the layer runs
     names = [cbs.cbs_config_name(c) for c in range(cbs.cbs_num_configs())]
-    n_pair = sum(1 for nm in names if nm.startswith("P"))
-    assert ran >= len(names) - (n_pair if sp.c_out > 8 else 0)
+    missing = [nm for c, nm in enumerate(names) if runs_on(nm, sp, mode[0]) and c not in ran]
+    assert not missing, missing
 
 
 def test_residual_layer_needs_residual():

@@ -42,8 +42,8 @@ def register_direct_configs():
 
 
 def groupable_configs():
-    """Register-direct and LDS-staged tiles (halo tiles have no grouped kernel)."""
-    return [i for i in range(cbs.cbs_num_configs()) if not cbs.cbs_config_name(i).startswith(("H", "P"))]
+    """Register-direct and LDS-staged tiles (halo and weight-stationary tiles have no grouped kernel)."""
+    return [i for i in range(cbs.cbs_num_configs()) if not cbs.cbs_config_name(i).startswith(("H", "P", "W."))]
 
 
 class Member:

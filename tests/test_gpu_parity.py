@@ -197,6 +197,44 @@ def test_every_config_on_every_shape_f32():
                 assert check_guards(r["host"], L, r["info"]) == 0, name
 
 
+# fp32 1x1 shapes for the weight-stationary tiles (W.*): every compiled K depth,
+# channel counts that leave a workgroup's last channel blocks empty, ragged
+# pixel counts, and (larger batches) runs of several 16-pixel blocks per
+# workgroup, odd run lengths included.
+WS_SPECS = [(W.LayerSpec("ws64", 64, 80, 9, 13, 1, 1, 0), 2), (W.LayerSpec("ws96", 96, 40, 7, 9, 1, 1, 0), 2),
+            (W.LayerSpec("ws128", 128, 136, 11, 5, 1, 1, 0), 2), (W.LayerSpec("ws192", 192, 24, 5, 7, 1, 1, 0), 2),
+            (W.LayerSpec("ws256", 256, 48, 6, 6, 1, 1, 0), 2), (W.LayerSpec("ws384", 384, 20, 3, 5, 1, 1, 0), 2),
+            (W.LayerSpec("ws128runs", 128, 72, 49, 50, 1, 1, 0), 3),
+            (W.LayerSpec("ws128long", 128, 128, 40, 40, 1, 1, 0), 8)]
+
+
+def test_weight_stationary_tiles_f32():
+    rng = np.random.default_rng(13)
+    ws = [c for c in range(cbs.cbs_num_configs()) if cbs.cbs_config_name(c).startswith("W.")]
+    assert ws
+    for spec, n in WS_SPECS:
+        L = W.draw_layer(rng, spec, n)
+        y, s = _oracle_f32(L)
+        layer = create(L, cbs.CBS_F32)
+        ran = []
+        for cfg in ws:
+            try:
+                cbs.cbs_layer_set_config(layer, cfg, 1)
+            except cbs.CbsError as e:
+                assert e.status == cbs.CBS_EUNSUPPORTED
+                continue
+            r = run_f32(L, layer=layer)
+            name = "%s n=%d %s" % (spec.name, n, r["info"]["config_name"])
+            assert_f32_parity(r["y"], y, s, name)
+            assert check_guards(r["host"], L, r["info"]) == 0, name
+            ran.append(r["info"]["config_name"])
+        # every depth runs on the 16-channel tiles; K = 384 only there
+        assert "W.c16x4/sk1" in ran and len(ran) == (1 if spec.c_in == 384 else 3), (spec.name, ran)
+        with pytest.raises(cbs.CbsError) as e:  # no cross-workgroup split-K on these tiles
+            cbs.cbs_layer_set_config(layer, ws[0], 2)
+        assert e.value.status == cbs.CBS_EUNSUPPORTED
+
+
 def test_folded_delta_kernel_gives_silu_of_input():
     """cbs_create_layer_folded with W = delta (3x3 centre), scale 1, bias 0: y = SiLU(x)."""
     rng = np.random.default_rng(7)
