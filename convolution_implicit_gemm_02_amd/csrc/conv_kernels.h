@@ -82,6 +82,9 @@ constexpr int kU8Flip = (int)0x80808080u;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr unsigned kOutOfRange = 0x80000000u;
 
+// A compile-time flag passed to a generic lambda.
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
 // SiLU(z) = z / (1 + e^-z), with the hardware exponential and reciprocal
 // (each within about one ulp): a correctly rounded division costs ten
 // instructions per value, which made the epilogue of the small layers the
@@ -1254,37 +1257,41 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
   __syncthreads();
 
   // 2) every tap from LDS: lane (r, g) of block mb holds pixel r of that block
-  int lbase[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; mb++) {
-    const int pi = (wave * MB + mb) * 16 + r;
-    const int ly = pi / TW, lx = pi % TW;
-    lbase[mb] = PAIR ? ly * HWd + 2 * lx : (ly * st_) * HWd + lx * st_;
-  }
-  const unsigned char *wl = smem + p.halo_bytes;
   // An fp32 pixel of an even number of 16-byte slots would put the 16
   // pixels of a fragment read on repeating LDS banks; the host pads it to an
   // odd number of slots (a zero slot), which makes those reads conflict-free.
   const int pix_bytes = cql * SLOT;
-  for (int s = 0; s < p.steps; s++) {
+  unsigned lb[MB];  // byte offset in the halo of pixel r of each of this wave's blocks
+#pragma unroll
+  for (int mb = 0; mb < MB; mb++) {
+    const int pi = (wave * MB + mb) * 16 + r;
+    const int ly = pi / TW, lx = pi % TW;
+    lb[mb] = (unsigned)((PAIR ? ly * HWd + 2 * lx : (ly * st_) * HWd + lx * st_) * pix_bytes);
+  }
+  const unsigned char *wl = smem + p.halo_bytes + lane * 16;  // this lane's slot of each weight fragment
+  // One K step.  Only the last step can hold chunks past K (every chunk of the
+  // steps before it is below total_chunks), so only it masks: elsewhere the
+  // operands go to the MFMAs as read.
+  auto step = [&](int s, auto last) {
+    constexpr bool MASK = decltype(last)::value;
     Frag a[NBMAX];
 #pragma unroll
     for (int nb = 0; nb < NBMAX; nb++)
-      a[nb] = nb < nbl ? *(const Frag *)(wl + ((nb * p.steps + s) * 64 + lane) * 16) : Frag{};
+      a[nb] = nb < nbl ? *(const Frag *)(wl + (nb * p.steps + s) * 1024) : Frag{};
     Frag b[MB];
     if constexpr (V::VEC == 1) {
       Chunk c = PAIR ? decode_chunk_pair(p, s * 4 + g) : decode_chunk(p, s * 4 + g);
-      if (!c.ok) c.dy = c.dx = c.ci = 0;  // past K: read a valid slot, then zero it
+      if (MASK && !c.ok) c.dy = c.dx = c.ci = 0;  // past K: read a valid slot, then zero it
+      const unsigned woff = (unsigned)((c.dy * HWd + c.dx) * pix_bytes + c.ci * V::ESIZE);
 #pragma unroll
       for (int mb = 0; mb < MB; mb++) {
         // 16-byte aligned (pixels are whole 16-byte slots and a chunk starts a
         // slot): said explicitly, so the read is one ds_read_b128, whose lanes
         // the slot padding spreads over distinct banks, and not two 8-byte
         // reads, which it does not
-        Frag v = *(const Frag *)__builtin_assume_aligned(
-            smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci * V::ESIZE, 16);
+        Frag v = *(const Frag *)__builtin_assume_aligned(smem + (lb[mb] + woff), 16);
         if constexpr (V::U8) v ^= kU8Flip;  // zero-filled padding becomes -128, as in conv_igemm
-        b[mb] = c.ok ? v : Frag{};
+        b[mb] = (!MASK || c.ok) ? v : Frag{};
       }
     } else {
 #pragma unroll
@@ -1292,12 +1299,13 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         Chunk c = PAIR ? decode_chunk_pair(p, (s * 4 + g) * 4 + j) : decode_chunk(p, (s * 4 + g) * 4 + j);
-        if (!c.ok) c.dy = c.dx = c.ci = 0;
+        if (MASK && !c.ok) c.dy = c.dx = c.ci = 0;
+        const unsigned woff = (unsigned)((c.dy * HWd + c.dx) * pix_bytes + c.ci);
 #pragma unroll
         for (int mb = 0; mb < MB; mb++) {
-          int v = *(const int *)(smem + (lbase[mb] + c.dy * HWd + c.dx) * pix_bytes + c.ci);
+          int v = *(const int *)(smem + (lb[mb] + woff));
           if constexpr (V::U8) v ^= kU8Flip;
-          b[mb][j] = c.ok ? v : 0;
+          b[mb][j] = (!MASK || c.ok) ? v : 0;
         }
       }
     }
@@ -1316,7 +1324,16 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
           acc[nb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[nb], b[mb], acc[nb][mb], 0, 0, 0);
       }
     }
+  };
+  // two steps per iteration, so that the next step's LDS reads can be issued
+  // under the current step's MFMAs
+  int s = 0;
+  for (; s + 1 < p.steps - 1; s += 2) {
+    step(s, BoolC<false>{});
+    step(s + 1, BoolC<false>{});
   }
+  if (s < p.steps - 1) step(s, BoolC<false>{});
+  step(p.steps - 1, BoolC<true>{});
 
   // 3) epilogue, masked to the image and to the real channels
   const __amdgpu_buffer_rsrc_t rr = rsrc(p.res, p.res_bytes);
