@@ -70,6 +70,7 @@ struct cbs_layer {
   int config, splitk;
   int device;
   int cus = 256;     // compute units of the device (sizes the conv_ws grid)
+  int lds_max = 65536;  // LDS bytes a workgroup may use on the device (bounds the halo tiles)
   // device memory
   void *d_wfrag = nullptr;
   float *d_bias = nullptr;
@@ -306,7 +307,7 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
     if (c.lds == 3 && !L->pair) return false;
     int hb, sb;
     halo_lds(L, cfg, &hb, &sb);
-    if (sb > 64 * 1024) return false;
+    if (sb > L->lds_max) return false;  // 160 KiB on gfx950
   }
   if (splitk > 1 && L->steps < splitk * c.wk) return false;
   int pxt, cot;
@@ -737,9 +738,14 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
     return fail(CBS_EDEVICE, "hipGetDevice failed");
   }
   {
-    int cus = 0;
+    int cus = 0, lds = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L->device) == hipSuccess && cus > 0)
       L->cus = cus;
+    else
+      (void)hipGetLastError();
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, L->device) == hipSuccess &&
+        lds >= 65536)
+      L->lds_max = lds;
     else
       (void)hipGetLastError();
   }

@@ -179,7 +179,9 @@ def test_every_config_on_every_shape_f32():
              # <= 8 output channels, 3x3 stride 1: the column-pair halo tiles run too (odd OW: a
              # half-used last pair; 6 channels: padded rows; 3 channels: a 4-channel output pitch)
              W.LayerSpec("c8", 8, 8, 13, 11, 3, 1, 1), W.LayerSpec("c6", 12, 6, 9, 14, 3, 1, 1),
-             W.LayerSpec("c3", 4, 3, 10, 9, 3, 1, 1)]
+             W.LayerSpec("c3", 4, 3, 10, 9, 3, 1, 1),
+             # halo tiles above 64 KiB of LDS (input window + 36 or 72 KiB of fp32 weights)
+             W.LayerSpec("lds32", 32, 32, 21, 23, 3, 1, 1), W.LayerSpec("lds64s2", 32, 64, 17, 19, 3, 2, 1)]
     for spec in specs:
         L = W.draw_layer(rng, spec, 2)
         y, s = _oracle_f32(L)
