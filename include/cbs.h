@@ -415,7 +415,24 @@ cbs_status cbs_layer_autotune(cbs_layer *layer, const void *in, void *out, const
                               int32_t *splitk_out);
 /* Forget every cached tuning result (all devices). */
 void cbs_autotune_clear_cache(void);
-/* Name of configuration i, or NULL when i is out of range.  Static storage. */
+/*
+ * Name of configuration i, or NULL when i is out of range.  Static storage.
+ * The prefix names the kernel family and the shapes it can run:
+ *   "c..."         operands straight to registers (any layer; cross-workgroup
+ *                  split-K allowed);
+ *   "L.", "LS."    LDS-staged tiles filled through registers, "R.", "RS."
+ *                  filled by direct-to-LDS loads into a ring of stages (any
+ *                  layer; "S" = pixel-major activation loads);
+ *   "H."           input window and all weights in LDS (3x3 layers with at
+ *                  most 64 output channels whose window and weights fit the
+ *                  device's workgroup LDS);
+ *   "P."           the same on column pairs (3x3 stride 1, at most 8 output
+ *                  channels);
+ *   "W."           weights held in registers, runs of 16-pixel blocks per
+ *                  workgroup (fp32 1x1 stride 1 without padding, C_in in 64,
+ *                  96, 128, 192, 256 or 384).
+ * Only "c..." tiles take a split-K above 1.
+ */
 const char *cbs_config_name(int32_t config);
 
 /* Message for the calling thread's last failure ("" if none).  Thread-local storage. */
