@@ -429,8 +429,9 @@ void cbs_autotune_clear_cache(void);
  *   "P."           the same on column pairs (3x3 stride 1, at most 8 output
  *                  channels);
  *   "W."           weights held in registers, runs of 16-pixel blocks per
- *                  workgroup (fp32 1x1 stride 1 without padding, C_in in 64,
- *                  96, 128, 192, 256 or 384).
+ *                  workgroup (fp32 1x1 stride 1 without padding, C_in
+ *                  rounded up to a multiple of 4 in 64, 96, 128, 192, 256 or
+ *                  384; 384 on the 16-channel "W.c16" tiles only).
  * Only "c..." tiles take a split-K above 1.
  */
 const char *cbs_config_name(int32_t config);
