@@ -507,11 +507,12 @@ def cpu_baseline(W, min_seconds=10.0, max_seconds=20.0):
 
 def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, splitk=0):
     """Run only one layer of the list (or, for name "all", every layer in list
-    order) `launches` times back to back after 10 warm-up launches, the
-    `launches` replayed as one captured graph, for a profiler run on exactly
-    those kernels; then a plain device copy of known
-    size (the reference for scaling the profiler's byte counters).  Prints one
-    JSON line per layer."""
+    order): 10 eager warm-up launches, then `launches` back-to-back launches
+    captured as one graph, replayed twice (an untimed warm-up replay, then the
+    timed one, as bench.py's per-layer figures are timed), for a profiler run
+    on exactly those kernels: 10 + 2 * launches dispatches per layer.  Then a
+    plain device copy of known size (the reference for scaling the
+    profiler's byte counters).  Prints one JSON line per layer."""
     b = ListBench(cbs, W, torch, dtype, batch)
     names = [s.name for s in b.specs]
     for i in range(len(names)) if name == "all" else [names.index(name)]:
@@ -525,6 +526,7 @@ def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, spli
         g = torch.cuda.CUDAGraph()  # the launches replayed as one graph, as bench.py times them
         with torch.cuda.graph(g):
             lst.run()
+        g.replay()  # warm-up replay
         torch.cuda.synchronize()
         e0.record()
         g.replay()
@@ -534,7 +536,8 @@ def profile_layer(cbs, W, torch, name, dtype, batch, launches, config=None, spli
         us = e0.elapsed_time(e1) / launches * 1e3
         info = b.infos[i]
         print(json.dumps({"layer": names[i], "batch": batch, "dtype": "int8" if dtype else "f32",
-                          "launches": launches, "warmup_launches": 10, "us_per_launch": round(us, 3),
+                          "launches": launches, "warmup_launches": 10, "warmup_replays": 1,
+                          "us_per_launch": round(us, 3),
                           "config": info["config_name"], "grid": info["grid"], "flops": info["flops"],
                           "alg_bytes": info["alg_bytes"]}), flush=True)
     copy_bytes = 256 << 20
@@ -607,6 +610,7 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log("device: %s, %d CUs" % (props.name, props.multi_processor_count))
     if args.only_layer:
+        warm_device(torch)  # as before the timed regions below: clocks up before the first timing
         profile_layer(cbs, W, torch, args.only_layer, cbs.CBS_I8 if args.dtype == "int8" else cbs.CBS_F32,
                       args.batch, args.launches, args.config)
         return

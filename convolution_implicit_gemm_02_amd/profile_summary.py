@@ -63,9 +63,17 @@ def _dominant_one(out_dir, layer, bench_line):
     stats = _rows(os.path.join(sub("prof_dom"), "*kernel_stats.csv"))
     kern = [s for s in stats if s["Name"].startswith("void cbs::conv")][0]
     kname = kern["Name"]
+    trace = sorted((r for r in _rows(os.path.join(sub("prof_dom"), "*kernel_trace.csv")) if r["Kernel_Name"] == kname),
+                   key=lambda r: int(r["Dispatch_Id"]))
+    timed = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace[-200:]]
+    timed_avg = sum(timed) / len(timed)
     fr = _rows(os.path.join(sub("pmc_fetch"), "*counter_collection.csv"))
     wr = _rows(os.path.join(sub("pmc_write"), "*counter_collection.csv"))
     info = [json.loads(line) for line in open(sub("prof_dom") + ".log") if line.startswith('{"layer"')][0]
+    noprof = None  # the same program without the profiler (OUT_DIR/noprof_L.log), if it was run
+    npath = os.path.join(out_dir, "noprof_%s.log" % layer)
+    if os.path.exists(npath):
+        noprof = [json.loads(line) for line in open(npath) if line.startswith('{"layer"')][0]["us_per_launch"]
 
     def avg(rows):
         v = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == kname]
@@ -78,7 +86,9 @@ def _dominant_one(out_dir, layer, bench_line):
     alg = int(info["alg_bytes"])
     rec = {"kernel": kname, "config": info["config"], "grid": info["grid"], "fetch_kib": fk, "write_kib": wk,
            "fetch_factor": ff, "write_factor": wf, "traffic_bytes": traffic, "alg_bytes": alg,
-           "rocprof_avg_ns": float(kern["AverageNs"]), "graph_us_per_launch": info["us_per_launch"],
+           "rocprof_avg_ns": float(kern["AverageNs"]), "rocprof_timed_replay_avg_us": round(timed_avg, 3),
+           "graph_us_per_launch": info["us_per_launch"],
+           "graph_us_per_launch_without_profiler": noprof,
            "summary": "profiles/conv_igemm_%s_f32_bs1.md" % layer}
     tbl = "\n".join("| `%s` | %s | %.1f | %s | %s |" % (s["Name"][:90], s["Calls"], float(s["AverageNs"]), s["MinNs"],
                                                          s["MaxNs"]) for s in stats)
@@ -92,6 +102,10 @@ def _dominant_one(out_dir, layer, bench_line):
         roof = bench_line["roofline"]
         dom_note = ("In that run the dominant layer was %s (%.3f us per launch)." %
                     (roof["layer"], roof["us_per_launch"]))
+    nop = ("The same program without the profiler (`python bench.py --only-layer %s --launches 200`, same call): "
+           "%.3f us per launch, so the profiler slows these launches by %.0f%%. " % (layer, noprof,
+                                                                                     100 * (info["us_per_launch"] / noprof - 1))
+           if noprof else "")
     md = f"""# rocprofv3 summary: {kname}, layer {layer} (batch 1, FP32)
 
 One of the three layers of the batch-1 FP32 YOLO26n list step whose per-launch times lie within a few
@@ -106,15 +120,17 @@ Command (from the repository root on the GPU box):
 rocprofv3 --kernel-trace --stats --output-format csv -d $PWD/gpurun_out/prof_dom_{layer} -o dom -- python bench.py --only-layer {layer} --launches 200
 ```
 
-The program launches the layer 10 times eagerly, then replays one captured graph of 200 launches
-(the way the list step runs its kernels), then five 256 MiB device copies.
+The program launches the layer 10 times eagerly, then captures 200 launches as one graph and
+replays it twice (an untimed warm-up replay, then the timed one, the way the list step runs its kernels
+and bench.py times them), then five 256 MiB device copies.
 
 | Kernel | Calls | Average ns | Min ns | Max ns |
 |---|---|---|---|---|
 {tbl}
 
-Event timing of the 200-launch graph replay inside the profiled program: {info['us_per_launch']:.3f} us per launch
-(rocprofv3 average {float(kern['AverageNs']) / 1000:.3f} us over all 210 dispatches). {ev}.
+Kernel duration in the trace, averaged over the 200 dispatches of the timed replay: {timed_avg:.3f} us
+(the table above averages all 410 dispatches). Event timing of the timed replay inside the profiled
+program: {info['us_per_launch']:.3f} us per launch. {nop}{ev}.
 
 ## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, separate runs)
 
@@ -173,9 +189,10 @@ def layers(out_dir, dtype, batch):
         return rs
 
     def per_layer(rs, launches, key):
-        per = 10 + launches
+        # per layer: 10 eager warm-up launches, a warm-up replay and the timed replay
+        per = 10 + 2 * launches
         assert len(rs) == per * len(info), (len(rs), per, len(info))
-        return [[key(r) for r in rs[i * per + 10:(i + 1) * per]] for i in range(len(info))]
+        return [[key(r) for r in rs[(i + 1) * per - launches:(i + 1) * per]] for i in range(len(info))]
 
     tr = per_layer(conv_rows("trace"), 20, lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
 
@@ -208,7 +225,7 @@ def layers(out_dir, dtype, batch):
     D, B = dtype, batch
     md = f"""# rocprofv3 per-layer summary: YOLO26n-shaped list, {title}, batch {B}
 
-Every layer of the 37-layer list, in list order, each launched 10 times to warm up and then repeatedly back to back (`bench.py --only-layer all`). Four runs of the same program, from the repository root on the GPU box:
+Every layer of the 37-layer list, in list order, each launched 10 times to warm up and then repeatedly back to back as a captured graph, replayed once untimed and once timed (`bench.py --only-layer all`). Four runs of the same program, from the repository root on the GPU box:
 
 ```
 rocprofv3 --kernel-trace --output-format csv -d $PWD/gpurun_out/lp_{D}_bs{B}/trace -o t -- python bench.py --only-layer all --dtype {D} --batch {B} --launches 20
@@ -220,7 +237,7 @@ rocprofv3 --pmc WRITE_SIZE --output-format csv -d $PWD/gpurun_out/lp_{D}_bs{B}/w
 The second run also collected `SQ_BUSY_CU_CYCLES` and `GRBM_GUI_ACTIVE`; the table does not use them.
 
 Columns:
-- `us`: mean kernel duration over the last 20 launches of the kernel-trace run;
+- `us`: mean kernel duration over the timed replay of 20 launches in the kernel-trace run (after 10 eager launches and a warm-up replay);
 - `MFMA busy / alg.`: `SQ_VALU_MFMA_BUSY_CYCLES` over the cycles the layer's algorithmic FLOPs need ({mfma_note}); above 1 means padded work;
 - `MFMA util`: the busy cycles over `us` x 2.4 GHz x 1024 SIMDs;
 - `fetch MB`, `write MB`: `FETCH_SIZE` and `WRITE_SIZE` per dispatch, scaled by what they read for a 256 MiB device copy in the same runs (factors {ff:.3f} and {wf:.3f}); these count L2 misses, which the 256 MB MALL may serve;
