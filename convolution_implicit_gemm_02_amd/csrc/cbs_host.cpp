@@ -229,7 +229,7 @@ void tiles_of(const cbs_layer *L, int cfg, int *px_tiles, int *co_tiles) {
     *px_tiles = L->d.n * ceil_div(L->oh, c.th) * ceil_div(L->ow, c.lds == 3 ? 2 * c.tw : c.tw);
     return;
   }
-  if (c.lds == 4) {  // conv_ws: channel groups x runs of 16-pixel blocks, about th workgroups per CU
+  if (c.lds == 4 || c.lds == 5) {  // conv_ws: channel groups x runs of 16-pixel blocks, about th workgroups per CU
     *co_tiles = ceil_div(L->co_blocks, c.cb * c.wco);
     const int blocks = ceil_div(L->M, 16);
     *px_tiles = std::max(1, std::min(blocks, (L->cus * c.th + *co_tiles / 2) / *co_tiles));
@@ -302,6 +302,15 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
     if (!(ks == 4 || ks == 6 || ks == 8 || ks == 12 || ks == 16 || ks == 24)) return false;
     if (ks > ws_max_steps(c.cb)) return false;  // deepest K the launcher instantiates
   }
+  if (c.lds == 5) {  // conv_ws with the window gather: fp32 3x3, K steps each within one tap, depths 9 and 18
+    if (L->d.dtype != CBS_F32 || L->d.k != 3 || L->chunks_per_tap % 4 != 0) return false;
+    if (!(L->steps == 9 || L->steps == 18)) return false;
+    // its pixel arithmetic multiplies in 24 bits: pixel indices and strides below 2^23
+    const int64_t lim = int64_t(1) << 23;
+    if ((int64_t)L->d.n * L->d.h * L->d.w >= lim || (int64_t)L->d.n * L->oh >= lim || L->pitch >= lim ||
+        L->in_cs >= lim)
+      return false;
+  }
   if (c.lds == 2 || c.lds == 3) {
     if (L->d.k != 3 || L->co_blocks > 4) return false;
     if (c.lds == 3 && !L->pair) return false;
@@ -349,7 +358,7 @@ Choice choose(const cbs_layer *L) {
   Choice best{2, 1};
   double best_cost = 1e300;
   for (int cfg = 0; cfg < num_configs(); cfg++) {
-    if (config(cfg).lds >= 2) continue;  // halo tiles are chosen by measurement only
+    if (config(cfg).lds >= 2) continue;  // halo and weight-stationary tiles are chosen by measurement only
     for (int sk : {1}) {
       if (!config_fits(L, cfg, sk)) continue;
       const double cost = model_cost(L, cfg, sk);
@@ -550,7 +559,7 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
     p.w_bytes = (unsigned)((size_t)L->pair_steps * 64 * 16);
   }
   tiles_of(L, cfg, &p.px_tiles, &p.co_tiles);
-  if (kc.lds == 4) {  // conv_ws runs: as equal as whole 16-pixel blocks allow
+  if (kc.lds == 4 || kc.lds == 5) {  // conv_ws runs: as equal as whole 16-pixel blocks allow
     const int blocks = ceil_div(L->M, 16);
     p.run_base = blocks / p.px_tiles;
     p.run_rem = blocks % p.px_tiles;

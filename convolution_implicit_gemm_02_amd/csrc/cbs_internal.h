@@ -16,6 +16,8 @@ struct KernelConfig {
             // 2: input halo tile + all weights in LDS (conv_halo, 3x3 with <= 64 output channels);
             // 3: conv_halo on column pairs (3x3 stride 1 with <= 8 output channels; th x tw pairs)
             // 4: conv_ws (fp32 1x1 stride 1: weights held in registers, runs of pixel blocks)
+            // 5: conv_ws with the window gather (fp32 3x3, 9 or 18 K steps each within one tap;
+            //    wpx waves interleave the run's blocks)
   int th, tw;  // conv_halo: output tile of th x tw pixels; conv_ws: th = workgroups per CU
   const char *name;
 };

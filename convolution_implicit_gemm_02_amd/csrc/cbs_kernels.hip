@@ -36,6 +36,9 @@ static const KernelConfig kConfigs[] = {
 #define X(id, cbw, wco, occ, name) {cbw, 1, wco, 1, 1, 4, occ, 0, name},
     CBS_WS_CONFIG_LIST(X)
 #undef X
+#define X(id, cbw, wpx, occ, name) {cbw, 1, 1, wpx, 1, 5, occ, 0, name},
+    CBS_WSG_CONFIG_LIST(X)
+#undef X
 };
 
 // A configuration's id is its index in kConfigs (the launch switch and the
@@ -44,6 +47,7 @@ constexpr int kConfigIds[] = {
 #define X(id, ...) id,
     CBS_CONFIG_LIST(X) CBS_LDS_CONFIG_LIST(X) CBS_HALO_CONFIG_LIST(X) CBS_CONFIG_LIST_EXT(X) CBS_LDS_CONFIG_LIST_EXT(X)
     CBS_LDS_RING_CONFIG_LIST(X) CBS_HALO_PAIR_CONFIG_LIST(X) CBS_LDS_RING_SWZ_CONFIG_LIST(X) CBS_WS_CONFIG_LIST(X)
+    CBS_WSG_CONFIG_LIST(X)
 #undef X
 };
 constexpr bool config_ids_in_order() {

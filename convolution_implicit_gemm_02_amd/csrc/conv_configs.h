@@ -109,3 +109,13 @@
   X(57, 2, 4, 1, "W.c32x4")                  \
   X(58, 2, 4, 2, "W.c32x4o2")                \
   X(59, 1, 4, 1, "W.c16x4")
+
+// Weight-stationary tiles with the window gather (fp32 3x3 layers with 16
+// or 32 padded input channels, 9 or 18 K steps): id, 16-channel blocks per
+// wave, waves per workgroup (all on the same channel blocks, interleaving the
+// run's pixel blocks), workgroups per CU.
+#define CBS_WSG_CONFIG_LIST(X)               \
+  X(60, 2, 4, 1, "G.c32x4")                  \
+  X(61, 2, 4, 2, "G.c32x4o2")                \
+  X(62, 1, 4, 2, "G.c16x4o2")                \
+  X(63, 1, 4, 3, "G.c16x4o3")

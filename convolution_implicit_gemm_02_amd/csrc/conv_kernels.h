@@ -282,13 +282,13 @@ __device__ __forceinline__ void store4(const ConvParams &p, unsigned byte_off, u
 // wave-uniform.
 template <bool X>
 __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buffer_rsrc_t rr, f32x4 z, int opix,
-                                               int m, int co0) {
+                                               int m, int co0, bool ok = true) {
   f32x4 y;
   // plain: SiLU, fp32 store (also the general variant's path when no option is set)
   if (!X || (p.act == ACT_SILU && !p.res_cs && !p.out_q)) {
 #pragma unroll
     for (int i = 0; i < 4; i++) y[i] = silu_f(z[i]);
-    store16(p, (unsigned)(opix * p.out_cs + co0) * 4u, y);
+    store16(p, ok ? (unsigned)(opix * p.out_cs + co0) * 4u : kOutOfRange, y);
     return;
   }
   if (p.act == ACT_NONE) {
@@ -298,14 +298,14 @@ __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buf
     for (int i = 0; i < 4; i++) y[i] = silu_f(z[i]);
   }
   if (p.res_cs) {
-    const unsigned e = (unsigned)(m * p.res_cs + co0);
+    const unsigned e = (unsigned)(m * p.res_cs + co0);  // element index (masked lanes read nothing)
     if (p.out_q) {
       // byte codes: int8 as (b ^ 0x80) - 128, uint8 as b - z_r (both exact in fp32)
-      const unsigned w = __builtin_amdgcn_raw_buffer_load_b32(rr, e, 0, 0) ^ p.res_xor;
+      const unsigned w = __builtin_amdgcn_raw_buffer_load_b32(rr, ok ? e : kOutOfRange, 0, 0) ^ p.res_xor;
 #pragma unroll
       for (int i = 0; i < 4; i++) y[i] += p.res_scale * ((float)((w >> (8 * i)) & 0xffu) - p.res_zp);
     } else {
-      y += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, e * 4u, 0, 0));
+      y += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, ok ? e * 4u : kOutOfRange, 0, 0));
     }
   }
   const unsigned o = (unsigned)(opix * p.out_cs + co0);  // element index; byte offsets stay below 2^31
@@ -327,9 +327,9 @@ __device__ __forceinline__ void epilogue_store(const ConvParams &p, __amdgpu_buf
       t = fminf(fmaxf(t, p.out_lo), p.out_hi);
       word |= ((unsigned)((int)t & 0xff)) << (8 * i);
     }
-    store4(p, o, word);
+    store4(p, ok ? o : kOutOfRange, word);
   } else {
-    store16(p, o * 4u, y);
+    store16(p, ok ? o * 4u : kOutOfRange, y);
   }
 }
 
@@ -773,6 +773,7 @@ __global__ __launch_bounds__(64 * WCO * WPX * WK) void conv_igemm_group(GroupArg
 
 struct Pix {
   int base, iy0, ix0, out;
+  int xb;  // base * x_cs: element offset of the window's top-left tap (may be negative in the padding)
   bool ok;
 };
 
@@ -787,6 +788,7 @@ __device__ __forceinline__ Pix pixel_of(const ConvParams &p, int m) {
   q.iy0 = oh * p.stride - p.pad;
   q.ix0 = ow * p.stride - p.pad;
   q.base = (n * p.H + q.iy0) * p.W + q.ix0;
+  q.xb = q.base * p.x_cs;
   q.out = (n * p.OH + oh) * p.pitch + ow;
   return q;
 }
@@ -1379,8 +1381,20 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
 // most one block, so the work is spread evenly over the grid, which the host
 // sizes to a few workgroups per CU.  The input pixel of an output pixel is its
 // logical index (1x1, stride 1, no padding).
-template <int VAR, int CBW, int WCO, int KS>
-__global__ __launch_bounds__(64 * WCO) void conv_ws(ConvParams p) {
+//
+// GATHER: the same for small-weight 3x3 layers with 16 or 32 (padded) input
+// channels, 9 or 18 K steps: K step s then lies in tap 9s/KS, so the tap of
+// every step is known at compile time and a block needs one offset per tap
+// (the pixel's window corner plus the tap's fixed displacement, or out of
+// range where the tap falls in the padding), computed where the 1x1 form
+// computes its single offset; the 16-channel steps of one tap read at
+// immediate offsets from it.  The block's output pixel index comes with its
+// offsets, and the pixel arithmetic uses 24-bit multiplies (full rate, where
+// 32-bit ones take four issue cycles), which the host allows only for
+// tensors whose pixel and element indices fit (below 2^23).  WPX waves of a
+// workgroup share the channel blocks and take every WPX-th block of the run.
+template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false>
+__global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
   using V = Var<VAR>;
   static_assert(!V::I8, "fp32 activations only");
   using Frag = typename V::Frag;
@@ -1391,27 +1405,65 @@ __global__ __launch_bounds__(64 * WCO) void conv_ws(ConvParams p) {
   pin_sgpr(p.run_rem);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: MFMA guards are scalar
+  const int wpx = wave % WPX, wco = wave / WPX;
   const int r = lane & 15, g = lane >> 4;
   int run, co_tile;
   tile_of(p, xcd_major(nblocks, blockIdx.x), run, co_tile);
-  const int b0 = run * p.run_base + min(run, p.run_rem);
-  const int b1 = b0 + p.run_base + (run < p.run_rem ? 1 : 0);
-  const int cob0 = (co_tile * WCO + wave) * CBW;
+  const int b0 = run * p.run_base + min(run, p.run_rem) + wpx;  // this wave's first block
+  const int b1 = run * p.run_base + min(run, p.run_rem) + p.run_base + (run < p.run_rem ? 1 : 0);
+  const int cob0 = (co_tile * WCO + wco) * CBW;
 
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
-  // Activations of pixel block b, K step s: lane (g, r) reads channels
-  // 16s + 4g .. +3 of pixel 16b + r (zero past the run or past M).
-  auto act_off = [&](int b) -> unsigned {
+  // Offsets of pixel block b (zero-filled past the run or past M).  1x1: lane
+  // (g, r) reads channels 16s + 4g .. +3 of pixel 16b + r for K step s.
+  // GATHER: channels 16j + 4g .. +3 of tap t of pixel 16b + r's window for
+  // K step s = t * KS/9 + j.
+  static_assert(!GATHER || KS == 9 || KS == 18, "gathered K depths: 9 or 18 steps");
+  constexpr int NOFF = GATHER ? 9 : 1;
+  constexpr int SPT = GATHER ? KS / 9 : KS;  // K steps per offset
+  unsigned tap_off[NOFF];
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int t = 0; t < 9; t++) tap_off[t] = (unsigned)(((t / 3) * p.W + t % 3) * p.x_cs) * 4u;
+  }
+  auto block_offs = [&](int b, unsigned(&o)[NOFF], int &opix) {
     const int m = b * 16 + r;
-    return (b < b1 && m < p.M) ? (unsigned)(m * p.x_cs + 4 * g) * 4u : kOutOfRange;
+    if constexpr (GATHER) {
+      const bool ok = b < b1 && m < p.M;
+      const int mm = ok ? m : 0;
+      const int t = fdiv(mm, p.div_ow);  // n * OH + oh
+      const int ow = mm - __mul24(t, p.OW);
+      const int n = fdiv(t, p.div_oh);
+      const int oh = t - __mul24(n, p.OH);
+      const int iy0 = __mul24(oh, p.stride) - p.pad, ix0 = __mul24(ow, p.stride) - p.pad;
+      const int xb = __mul24(__mul24(__mul24(n, p.H) + iy0, p.W) + ix0, p.x_cs);  // window corner, elements
+      opix = __mul24(t, p.pitch) + ow;
+      const unsigned lb = (unsigned)(xb + 4 * g) * 4u;  // wraps for corners in the padding
+      bool rv[3], cv[3];
+#pragma unroll
+      for (int d = 0; d < 3; d++) {
+        rv[d] = ok && (unsigned)(iy0 + d) < (unsigned)p.H;
+        cv[d] = (unsigned)(ix0 + d) < (unsigned)p.W;
+      }
+#pragma unroll
+      for (int tp = 0; tp < 9; tp++) o[tp] = (rv[tp / 3] && cv[tp % 3]) ? lb + tap_off[tp] : kOutOfRange;
+    } else {
+      (void)opix;
+      o[0] = (b < b1 && m < p.M) ? (unsigned)(m * p.x_cs + 4 * g) * 4u : kOutOfRange;
+    }
   };
-  Frag ba[KS], bb[KS];  // activations of the current and of the next pixel block
-  {
-    const unsigned off0 = act_off(b0);
+  auto load_block = [&](const unsigned(&o)[NOFF], Frag(&dst)[KS]) {
 #pragma unroll
     for (int s = 0; s < KS; s++)
-      ba[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off0, s * 64, 0));
+      dst[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, o[s / SPT], (s % SPT) * 64, 0));
+  };
+  Frag ba[KS], bb[KS];  // activations of the current and of the next pixel block
+  int op_cur = 0, op_nxt = 0;  // GATHER: output pixels of the current and the next block
+  {
+    unsigned o0[NOFF];
+    block_offs(b0, o0, op_cur);
+    load_block(o0, ba);
   }
   // this wave's weights (zero for channel blocks past the end) and bias
   Frag a[CBW][KS];
@@ -1433,19 +1485,18 @@ __global__ __launch_bounds__(64 * WCO) void conv_ws(ConvParams p) {
   }
   const __amdgpu_buffer_rsrc_t rr = rsrc(p.res, p.res_bytes);
   // One pixel block, in three phases kept apart by scheduling barriers:
-  //  1. every load of block b + 1 into `nxt`, at an offset computed before
+  //  1. every load of block b + WPX into `nxt`, at offsets computed before
   //     the previous block's stores (below);
   //  2. the MFMAs on `cur` (the compiler would otherwise sink the loads below
   //     them and leave the next block's latency exposed);
-  //  3. the offset of block b + 2, then the epilogue and its stores.
+  //  3. the offsets of block b + 2 WPX, then the epilogue and its stores.
   // A VALU write to a register that a store still reads waits until the store
   // has completed, so nothing but loads and MFMAs follows the stores until the
   // next block's epilogue, a whole block of MFMAs later.
-  unsigned off = act_off(b0 + 1);
+  unsigned off[NOFF];
+  block_offs(b0 + WPX, off, op_nxt);
   auto block = [&](int b, const Frag(&cur)[KS], Frag(&nxt)[KS]) {
-#pragma unroll
-    for (int s = 0; s < KS; s++)
-      nxt[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, off, s * 64, 0));
+    load_block(off, nxt);
     __builtin_amdgcn_sched_barrier(0);
     Acc acc[CBW];
 #pragma unroll
@@ -1458,15 +1509,19 @@ __global__ __launch_bounds__(64 * WCO) void conv_ws(ConvParams p) {
         for (int cb = 0; cb < CBW; cb++)
           acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cb][s][j], cur[s][j], acc[cb], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    off = act_off(b + 2);
+    int op_next2 = 0;
+    block_offs(b + 2 * WPX, off, op_next2);
     // epilogue: 4 channels of pixel 16b + r per lane and channel block
     const int m = b * 16 + r;
     if (m < p.M) {
-      const int t = fdiv(m, p.div_ow);
-      const int ow = m - t * p.OW;
-      const int n = fdiv(t, p.div_oh);
-      const int oh = t - n * p.OH;
-      const int opix = (n * p.OH + oh) * p.pitch + ow;
+      int opix = op_cur;
+      if constexpr (!GATHER) {
+        const int t = fdiv(m, p.div_ow);
+        const int ow = m - t * p.OW;
+        const int n = fdiv(t, p.div_oh);
+        const int oh = t - n * p.OH;
+        opix = (n * p.OH + oh) * p.pitch + ow;
+      }
 #pragma unroll
       for (int cb = 0; cb < CBW; cb++) {
         const int co0 = (cob0 + cb) * 16 + 4 * g;
@@ -1477,14 +1532,16 @@ __global__ __launch_bounds__(64 * WCO) void conv_ws(ConvParams p) {
         epilogue_store<V::X>(p, rr, z, opix, m, co0);
       }
     }
+    op_cur = op_nxt;
+    op_nxt = op_next2;
     __builtin_amdgcn_sched_barrier(0);
   };
   // The prologue's loads are waited for here, so that the loop is entered with
   // nothing in flight.
   __builtin_amdgcn_s_waitcnt(0);
-  for (int b = b0; b < b1; b += 2) {
+  for (int b = b0; b < b1; b += 2 * WPX) {
     block(b, ba, bb);
-    if (b + 1 < b1) block(b + 1, bb, ba);
+    if (b + WPX < b1) block(b + WPX, bb, ba);
   }
 }
 
@@ -1533,11 +1590,27 @@ static hipError_t launch_halo_pair(const ConvParams &p, hipStream_t stream) {
 // Weight-stationary 1x1 tiles: the K depth is a template argument (the
 // weights of all K steps sit in registers), instantiated for the depths of the
 // batch-16 1x1 layers; fp32 variants only.
-template <int VAR, int CBW, int WCO, int KS>
+template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false>
 static hipError_t launch_ws_k(const ConvParams &p, hipStream_t stream) {
-  hipLaunchKernelGGL((conv_ws<VAR, CBW, WCO, KS>), dim3((unsigned)p.px_tiles * (unsigned)p.co_tiles),
-                     dim3(64 * WCO), 0, stream, p);
+  hipLaunchKernelGGL((conv_ws<VAR, CBW, WCO, KS, WPX, GATHER>), dim3((unsigned)p.px_tiles * (unsigned)p.co_tiles),
+                     dim3(64 * WCO * WPX), 0, stream, p);
   return hipGetLastError();
+}
+// Weight-stationary tiles with the window gather (configurations G.*): the K
+// depths of 3x3 layers with 16 or 32 input channels.
+template <int VAR, int CBW, int WPX>
+static hipError_t launch_wsg(const ConvParams &p, hipStream_t stream) {
+  if constexpr (VAR != VAR_F32 && VAR != VAR_F32_X) {
+    (void)p, (void)stream;
+    return hipErrorInvalidValue;
+  } else {
+    if (p.splitk != 1 || p.k != 3 || p.chunk_ch != 4 || (p.chunks_per_tap & 3) != 0) return hipErrorInvalidValue;
+    switch (p.steps) {
+      case 9: return launch_ws_k<VAR, CBW, 1, 9, WPX, true>(p, stream);
+      case 18: return launch_ws_k<VAR, CBW, 1, 18, WPX, true>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
 }
 template <int VAR, int CBW, int WCO>
 static hipError_t launch_ws(const ConvParams &p, hipStream_t stream) {
@@ -1653,6 +1726,11 @@ static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t strea
   case id:                         \
     return launch_ws<VAR, cbw, wco>(p, stream);
     CBS_WS_CONFIG_LIST(X)
+#undef X
+#define X(id, cbw, wpx, occ, name) \
+  case id:                         \
+    return launch_wsg<VAR, cbw, wpx>(p, stream);
+    CBS_WSG_CONFIG_LIST(X)
 #undef X
     default:
       return hipErrorInvalidValue;

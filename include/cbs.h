@@ -431,7 +431,10 @@ void cbs_autotune_clear_cache(void);
  *   "W."           weights held in registers, runs of 16-pixel blocks per
  *                  workgroup (fp32 1x1 stride 1 without padding, C_in
  *                  rounded up to a multiple of 4 in 64, 96, 128, 192, 256 or
- *                  384; 384 on the 16-channel "W.c16" tiles only).
+ *                  384; 384 on the 16-channel "W.c16" tiles only);
+ *   "G."           the same with the 3x3 window gathered per pixel (fp32 3x3,
+ *                  any stride and padding, C_in rounded up to a multiple of 4
+ *                  equal to 16 or 32).
  * Only "c..." tiles take a split-K above 1.
  */
 const char *cbs_config_name(int32_t config);

@@ -431,20 +431,24 @@ def test_slices_and_residual(idx, mode):
 OPTION_CASES = [(spec(16, 16, 20, 20, 3, 1), (48, 16), (48, 32), (48, 16)),
                 (spec(8, 8, 20, 19, 3, 1), (24, 8), (24, 16), (24, 8)),
                 # a 1x1 that the fp32 weight-stationary tiles take (the C3k2 cv1 / cv2 shapes)
-                (spec(64, 32, 20, 19, 1, 1), (96, 16), (96, 64), (96, 0))]
+                (spec(64, 32, 20, 19, 1, 1), (96, 16), (96, 64), (96, 0)),
+                # a 3x3 with 32 input channels (the fp32 gather tiles' second depth)
+                (spec(32, 24, 21, 18, 3, 1), (72, 40), (48, 16), (48, 16))]
 
 
 def runs_on(name, sp, dtype):
     """Whether configuration `name` can run layer `sp` of input type `dtype` (families
     that apply to some shapes only: halo tiles need 3x3, column pairs also stride 1
     and at most 8 output channels, weight-stationary tiles fp32 1x1 stride 1 with
-    C_in in 64, 96, 128, 192, 256, 384)."""
+    C_in in 64, 96, 128, 192, 256, 384, their gather form fp32 3x3 with C_in 16 or 32)."""
     if name.startswith("P"):
         return sp.k == 3 and sp.stride == 1 and sp.c_out <= 8
     if name.startswith("H"):
         return sp.k == 3
     if name.startswith("W."):
         return dtype == "f32" and sp.k == 1 and sp.stride == 1 and sp.c_in in (64, 96, 128, 192, 256, 384)
+    if name.startswith("G."):
+        return dtype == "f32" and sp.k == 3 and sp.c_in in (16, 32)
     return True
 
 

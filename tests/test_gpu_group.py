@@ -43,7 +43,7 @@ def register_direct_configs():
 
 def groupable_configs():
     """Register-direct and LDS-staged tiles (halo and weight-stationary tiles have no grouped kernel)."""
-    return [i for i in range(cbs.cbs_num_configs()) if not cbs.cbs_config_name(i).startswith(("H", "P", "W."))]
+    return [i for i in range(cbs.cbs_num_configs()) if not cbs.cbs_config_name(i).startswith(("H", "P", "W.", "G."))]
 
 
 class Member:

@@ -237,6 +237,43 @@ def test_weight_stationary_tiles_f32():
         assert e.value.status == cbs.CBS_EUNSUPPORTED
 
 
+# 3x3 layers for the weight-stationary tiles with the window gather: 16 and 32
+# input channels (9 and 18 K steps), stride 1 and 2, with and without padding,
+# ragged rows and channel counts, several pixel blocks per run; 24 and 48 input
+# channels (K steps across taps) must be refused.
+WSG_SPECS = [(W.LayerSpec("g16", 16, 16, 21, 23, 3, 1, 1), 2), (W.LayerSpec("g16s2", 16, 40, 33, 29, 3, 2, 1), 2),
+             (W.LayerSpec("g32", 32, 32, 17, 19, 3, 1, 1), 3), (W.LayerSpec("g32s2", 32, 64, 26, 31, 3, 2, 1), 2),
+             (W.LayerSpec("g32p0", 32, 24, 11, 14, 3, 1, 0), 2), (W.LayerSpec("g16runs", 16, 32, 80, 80, 3, 1, 1), 4),
+             (W.LayerSpec("g24", 24, 16, 9, 9, 3, 1, 1), 1), (W.LayerSpec("g48", 48, 16, 9, 9, 3, 1, 1), 1)]
+
+
+def test_weight_stationary_gather_tiles_f32():
+    rng = np.random.default_rng(14)
+    gs = [c for c in range(cbs.cbs_num_configs()) if cbs.cbs_config_name(c).startswith("G.")]
+    assert gs
+    for spec, n in WSG_SPECS:
+        L = W.draw_layer(rng, spec, n)
+        y, s = _oracle_f32(L)
+        layer = create(L, cbs.CBS_F32)
+        ran = []
+        for cfg in gs:
+            try:
+                cbs.cbs_layer_set_config(layer, cfg, 1)
+            except cbs.CbsError as e:
+                assert e.status == cbs.CBS_EUNSUPPORTED
+                continue
+            r = run_f32(L, layer=layer)
+            name = "%s n=%d %s" % (spec.name, n, r["info"]["config_name"])
+            assert_f32_parity(r["y"], y, s, name)
+            assert check_guards(r["host"], L, r["info"]) == 0, name
+            ran.append(r["info"]["config_name"])
+        assert len(ran) == (len(gs) if spec.c_in in (16, 32) else 0), (spec.name, ran)
+        if ran:
+            with pytest.raises(cbs.CbsError) as e:  # no cross-workgroup split-K on these tiles
+                cbs.cbs_layer_set_config(layer, gs[0], 2)
+            assert e.value.status == cbs.CBS_EUNSUPPORTED
+
+
 def test_folded_delta_kernel_gives_silu_of_input():
     """cbs_create_layer_folded with W = delta (3x3 centre), scale 1, bias 0: y = SiLU(x)."""
     rng = np.random.default_rng(7)
