@@ -25,7 +25,7 @@ struct KernelConfig {
 // conv_ws: deepest K (in 16-channel steps) compiled for waves holding cb
 // channel blocks each, so that weights and two blocks of activations fit the
 // registers of a wave without spilling.
-constexpr int ws_max_steps(int cb) { return cb == 2 ? 16 : 24; }
+constexpr int ws_max_steps(int cb) { return cb == 1 ? 24 : cb == 2 ? 16 : 8; }
 
 // Kernel-variant families (dtype x operand gathering x epilogue).
 enum Variant {

@@ -33,11 +33,14 @@ static const KernelConfig kConfigs[] = {
 #define X(id, mb, nb, wm, wn, ks, ns, name) {nb, mb, wn, wm, 1, 1, 0, 0, name},
     CBS_LDS_RING_SWZ_CONFIG_LIST(X)
 #undef X
-#define X(id, cbw, wco, occ, name) {cbw, 1, wco, 1, 1, 4, occ, 0, name},
+#define X(id, cbw, wco, wpx, occ, name) {cbw, 1, wco, wpx, 1, 4, occ, 0, name},
     CBS_WS_CONFIG_LIST(X)
 #undef X
 #define X(id, cbw, wpx, occ, name) {cbw, 1, 1, wpx, 1, 5, occ, 0, name},
     CBS_WSG_CONFIG_LIST(X)
+#undef X
+#define X(id, cbw, wco, wpx, occ, name) {cbw, 1, wco, wpx, 1, 4, occ, 0, name},
+    CBS_WS_CONFIG_LIST_EXT(X)
 #undef X
 };
 
@@ -47,7 +50,7 @@ constexpr int kConfigIds[] = {
 #define X(id, ...) id,
     CBS_CONFIG_LIST(X) CBS_LDS_CONFIG_LIST(X) CBS_HALO_CONFIG_LIST(X) CBS_CONFIG_LIST_EXT(X) CBS_LDS_CONFIG_LIST_EXT(X)
     CBS_LDS_RING_CONFIG_LIST(X) CBS_HALO_PAIR_CONFIG_LIST(X) CBS_LDS_RING_SWZ_CONFIG_LIST(X) CBS_WS_CONFIG_LIST(X)
-    CBS_WSG_CONFIG_LIST(X)
+    CBS_WSG_CONFIG_LIST(X) CBS_WS_CONFIG_LIST_EXT(X)
 #undef X
 };
 constexpr bool config_ids_in_order() {

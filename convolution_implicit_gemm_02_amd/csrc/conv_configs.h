@@ -104,11 +104,12 @@
   X(56, 2, 1, 2, 4, 2, 0, "LS.p64c64w8")
 
 // conv_ws (fp32 1x1 stride 1): id, 16-channel blocks per wave, waves per
-// workgroup, workgroups per CU.
+// workgroup along channels, waves per workgroup along pixels (on the same
+// channel blocks, interleaving the run's pixel blocks), workgroups per CU.
 #define CBS_WS_CONFIG_LIST(X)                \
-  X(57, 2, 4, 1, "W.c32x4")                  \
-  X(58, 2, 4, 2, "W.c32x4o2")                \
-  X(59, 1, 4, 1, "W.c16x4")
+  X(57, 2, 4, 1, 1, "W.c32x4")               \
+  X(58, 2, 4, 1, 2, "W.c32x4o2")             \
+  X(59, 1, 4, 1, 1, "W.c16x4")
 
 // Weight-stationary tiles with the window gather (fp32 3x3 layers with 16
 // or 32 padded input channels, 9 or 18 K steps): id, 16-channel blocks per
@@ -119,3 +120,13 @@
   X(61, 2, 4, 2, "G.c32x4o2")                \
   X(62, 1, 4, 2, "G.c16x4o2")                \
   X(63, 1, 4, 3, "G.c16x4o3")
+
+// More conv_ws tiles, with the waves of a workgroup along pixels: layers with
+// 16-32 output channels or 80 (the detection head's class branch), whose
+// channel blocks one wave holds.  Same fields as CBS_WS_CONFIG_LIST.
+#define CBS_WS_CONFIG_LIST_EXT(X)            \
+  X(64, 1, 1, 4, 2, "W.c16p4o2")             \
+  X(65, 1, 1, 4, 4, "W.c16p4o4")             \
+  X(66, 2, 1, 4, 2, "W.c32p4o2")             \
+  X(67, 5, 1, 4, 1, "W.c80p4")               \
+  X(68, 5, 1, 4, 2, "W.c80p4o2")

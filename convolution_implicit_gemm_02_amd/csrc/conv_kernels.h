@@ -1612,7 +1612,7 @@ static hipError_t launch_wsg(const ConvParams &p, hipStream_t stream) {
     }
   }
 }
-template <int VAR, int CBW, int WCO>
+template <int VAR, int CBW, int WCO, int WPX>
 static hipError_t launch_ws(const ConvParams &p, hipStream_t stream) {
   if constexpr (VAR != VAR_F32 && VAR != VAR_F32_X) {
     (void)p, (void)stream;
@@ -1621,13 +1621,19 @@ static hipError_t launch_ws(const ConvParams &p, hipStream_t stream) {
     if (p.splitk != 1 || p.k != 1 || p.stride != 1 || p.pad != 0 || p.chunk_ch != 4) return hipErrorInvalidValue;
     constexpr int kMax = ws_max_steps(CBW);  // deepest K that fits the registers without spilling
     switch (p.steps) {
-      case 4: return launch_ws_k<VAR, CBW, WCO, 4>(p, stream);
-      case 6: return launch_ws_k<VAR, CBW, WCO, 6>(p, stream);
-      case 8: return launch_ws_k<VAR, CBW, WCO, 8>(p, stream);
-      case 12: return launch_ws_k<VAR, CBW, WCO, 12>(p, stream);
-      case 16: return launch_ws_k<VAR, CBW, WCO, 16>(p, stream);
+      case 1: return launch_ws_k<VAR, CBW, WCO, 1, WPX>(p, stream);
+      case 2: return launch_ws_k<VAR, CBW, WCO, 2, WPX>(p, stream);
+      case 4: return launch_ws_k<VAR, CBW, WCO, 4, WPX>(p, stream);
+      case 6: return launch_ws_k<VAR, CBW, WCO, 6, WPX>(p, stream);
+      case 8: return launch_ws_k<VAR, CBW, WCO, 8, WPX>(p, stream);
+      case 12:
+        if constexpr (kMax >= 12) return launch_ws_k<VAR, CBW, WCO, 12, WPX>(p, stream);
+        return hipErrorInvalidValue;
+      case 16:
+        if constexpr (kMax >= 16) return launch_ws_k<VAR, CBW, WCO, 16, WPX>(p, stream);
+        return hipErrorInvalidValue;
       case 24:
-        if constexpr (kMax >= 24) return launch_ws_k<VAR, CBW, WCO, 24>(p, stream);
+        if constexpr (kMax >= 24) return launch_ws_k<VAR, CBW, WCO, 24, WPX>(p, stream);
         return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
@@ -1722,10 +1728,10 @@ static hipError_t launch_variant(int cfg, const ConvParams &p, hipStream_t strea
     return launch_lds<VAR, mb, nb, wm, wn, ks, ns, true>(p, stream);
     CBS_LDS_RING_SWZ_CONFIG_LIST(X)
 #undef X
-#define X(id, cbw, wco, occ, name) \
-  case id:                         \
-    return launch_ws<VAR, cbw, wco>(p, stream);
-    CBS_WS_CONFIG_LIST(X)
+#define X(id, cbw, wco, wpx, occ, name) \
+  case id:                              \
+    return launch_ws<VAR, cbw, wco, wpx>(p, stream);
+    CBS_WS_CONFIG_LIST(X) CBS_WS_CONFIG_LIST_EXT(X)
 #undef X
 #define X(id, cbw, wpx, occ, name) \
   case id:                         \

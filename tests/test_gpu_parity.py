@@ -207,7 +207,19 @@ WS_SPECS = [(W.LayerSpec("ws64", 64, 80, 9, 13, 1, 1, 0), 2), (W.LayerSpec("ws96
             (W.LayerSpec("ws128", 128, 136, 11, 5, 1, 1, 0), 2), (W.LayerSpec("ws192", 192, 24, 5, 7, 1, 1, 0), 2),
             (W.LayerSpec("ws256", 256, 48, 6, 6, 1, 1, 0), 2), (W.LayerSpec("ws384", 384, 20, 3, 5, 1, 1, 0), 2),
             (W.LayerSpec("ws128runs", 128, 72, 49, 50, 1, 1, 0), 3),
-            (W.LayerSpec("ws128long", 128, 128, 40, 40, 1, 1, 0), 8)]
+            (W.LayerSpec("ws128long", 128, 128, 40, 40, 1, 1, 0), 8),
+            (W.LayerSpec("ws16", 16, 16, 31, 29, 1, 1, 0), 3), (W.LayerSpec("ws32", 32, 24, 17, 21, 1, 1, 0), 2),
+            (W.LayerSpec("ws16runs", 16, 32, 80, 80, 1, 1, 0), 4), (W.LayerSpec("ws64c80", 64, 80, 40, 40, 1, 1, 0), 4),
+            (W.LayerSpec("ws128c80", 128, 80, 20, 20, 1, 1, 0), 3), (W.LayerSpec("ws48", 48, 16, 5, 5, 1, 1, 0), 1)]
+
+
+def ws_runs(name, c_in):
+    """Whether weight-stationary 1x1 configuration `name` takes a layer with c_in input
+    channels: K steps (c_in / 16) of a compiled depth, within the wave's register budget
+    (24 steps with one channel block per wave, 16 with two, 8 with five)."""
+    cb = {"c16": 1, "c32": 2, "c80": 5}[name[2:5]]
+    ks = c_in // 16
+    return c_in % 16 == 0 and ks in (1, 2, 4, 6, 8, 12, 16, 24) and ks <= {1: 24, 2: 16, 5: 8}[cb]
 
 
 def test_weight_stationary_tiles_f32():
@@ -230,8 +242,10 @@ def test_weight_stationary_tiles_f32():
             assert_f32_parity(r["y"], y, s, name)
             assert check_guards(r["host"], L, r["info"]) == 0, name
             ran.append(r["info"]["config_name"])
-        # every depth runs on the 16-channel tiles; K = 384 only there
-        assert "W.c16x4/sk1" in ran and len(ran) == (1 if spec.c_in == 384 else 3), (spec.name, ran)
+        want = sorted(cbs.cbs_config_name(c) + "/sk1" for c in ws if ws_runs(cbs.cbs_config_name(c), spec.c_in))
+        assert sorted(ran) == want, (spec.name, ran, want)
+        if spec.c_in != 48:
+            assert "W.c16x4/sk1" in ran  # every depth runs on the 16-channel tiles
         with pytest.raises(cbs.CbsError) as e:  # no cross-workgroup split-K on these tiles
             cbs.cbs_layer_set_config(layer, ws[0], 2)
         assert e.value.status == cbs.CBS_EUNSUPPORTED
