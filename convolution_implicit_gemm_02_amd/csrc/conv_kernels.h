@@ -1369,11 +1369,12 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
 
 // ------------------------------------------------ weight-stationary 1x1 --
 // fp32 1x1 stride-1 layers at large M (the batch-16 1x1 convolutions with
-// 64-384 input channels).  There the output is thousands of 16-pixel blocks
-// deep but only a few channel blocks wide, K is short (4-24 K steps), and a
+// 16-384 input channels).  There the output is thousands of 16-pixel blocks
+// deep but only a few channel blocks wide, K is short (1-24 K steps), and a
 // tile of the other kernels pays its prologue (weights, first activations)
-// and its epilogue once per 64-128 pixels.  Here a workgroup of WCO waves
-// owns WCO*CBW channel blocks and a contiguous run of pixel blocks; each wave
+// and its epilogue once per 64-128 pixels.  Here a workgroup of WCO x WPX
+// waves owns WCO*CBW channel blocks and a contiguous run of pixel blocks (the
+// WPX waves on the same channel blocks take every WPX-th block of it); each wave
 // loads the weights of its CBW channel blocks for all KS steps into registers
 // once, then streams the run's pixel blocks through them.  The activations of
 // the next block are loaded (into a second register set) while the current
