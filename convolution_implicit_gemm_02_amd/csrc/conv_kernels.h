@@ -1394,7 +1394,11 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
 // 32-bit ones take four issue cycles), which the host allows only for
 // tensors whose pixel and element indices fit (below 2^23).  WPX waves of a
 // workgroup share the channel blocks and take every WPX-th block of the run.
-template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false>
+//
+// PARTIAL (1x1): C_in is not a multiple of 16, so the last K step holds fewer
+// than four chunks; that step has its own offset, out of range for the lanes
+// whose chunk lies past C_in.
+template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false, bool PARTIAL = false>
 __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
   using V = Var<VAR>;
   static_assert(!V::I8, "fp32 activations only");
@@ -1421,7 +1425,8 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
   // GATHER: channels 16j + 4g .. +3 of tap t of pixel 16b + r's window for
   // K step s = t * KS/9 + j.
   static_assert(!GATHER || KS == 9 || KS == 18, "gathered K depths: 9 or 18 steps");
-  constexpr int NOFF = GATHER ? 9 : 1;
+  static_assert(!(GATHER && PARTIAL), "partial K steps: 1x1 only");
+  constexpr int NOFF = GATHER ? 9 : PARTIAL ? 2 : 1;
   constexpr int SPT = GATHER ? KS / 9 : KS;  // K steps per offset
   unsigned tap_off[NOFF];
   if constexpr (GATHER) {
@@ -1452,12 +1457,15 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
     } else {
       (void)opix;
       o[0] = (b < b1 && m < p.M) ? (unsigned)(m * p.x_cs + 4 * g) * 4u : kOutOfRange;
+      if constexpr (PARTIAL) o[NOFF - 1] = 4 * (KS - 1) + g < p.total_chunks ? o[0] : kOutOfRange;
     }
   };
   auto load_block = [&](const unsigned(&o)[NOFF], Frag(&dst)[KS]) {
 #pragma unroll
-    for (int s = 0; s < KS; s++)
-      dst[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, o[s / SPT], (s % SPT) * 64, 0));
+    for (int s = 0; s < KS; s++) {
+      const unsigned os = GATHER ? o[s / SPT] : o[s == KS - 1 ? NOFF - 1 : 0];
+      dst[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, os, (s % SPT) * 64, 0));
+    }
   };
   Frag ba[KS], bb[KS];  // activations of the current and of the next pixel block
   int op_cur = 0, op_nxt = 0;  // GATHER: output pixels of the current and the next block
@@ -1591,9 +1599,9 @@ static hipError_t launch_halo_pair(const ConvParams &p, hipStream_t stream) {
 // Weight-stationary 1x1 tiles: the K depth is a template argument (the
 // weights of all K steps sit in registers), instantiated for the depths of the
 // batch-16 1x1 layers; fp32 variants only.
-template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false>
+template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false, bool PARTIAL = false>
 static hipError_t launch_ws_k(const ConvParams &p, hipStream_t stream) {
-  hipLaunchKernelGGL((conv_ws<VAR, CBW, WCO, KS, WPX, GATHER>), dim3((unsigned)p.px_tiles * (unsigned)p.co_tiles),
+  hipLaunchKernelGGL((conv_ws<VAR, CBW, WCO, KS, WPX, GATHER, PARTIAL>), dim3((unsigned)p.px_tiles * (unsigned)p.co_tiles),
                      dim3(64 * WCO * WPX), 0, stream, p);
   return hipGetLastError();
 }
@@ -1621,9 +1629,18 @@ static hipError_t launch_ws(const ConvParams &p, hipStream_t stream) {
   } else {
     if (p.splitk != 1 || p.k != 1 || p.stride != 1 || p.pad != 0 || p.chunk_ch != 4) return hipErrorInvalidValue;
     constexpr int kMax = ws_max_steps(CBW);  // deepest K that fits the registers without spilling
+    if (p.total_chunks < 4 * p.steps) {  // a partial last K step: depths 1-3 only
+      switch (p.steps) {
+        case 1: return launch_ws_k<VAR, CBW, WCO, 1, WPX, false, true>(p, stream);
+        case 2: return launch_ws_k<VAR, CBW, WCO, 2, WPX, false, true>(p, stream);
+        case 3: return launch_ws_k<VAR, CBW, WCO, 3, WPX, false, true>(p, stream);
+        default: return hipErrorInvalidValue;
+      }
+    }
     switch (p.steps) {
       case 1: return launch_ws_k<VAR, CBW, WCO, 1, WPX>(p, stream);
       case 2: return launch_ws_k<VAR, CBW, WCO, 2, WPX>(p, stream);
+      case 3: return launch_ws_k<VAR, CBW, WCO, 3, WPX>(p, stream);
       case 4: return launch_ws_k<VAR, CBW, WCO, 4, WPX>(p, stream);
       case 6: return launch_ws_k<VAR, CBW, WCO, 6, WPX>(p, stream);
       case 8: return launch_ws_k<VAR, CBW, WCO, 8, WPX>(p, stream);

@@ -440,17 +440,18 @@ def runs_on(name, sp, dtype):
     """Whether configuration `name` can run layer `sp` of input type `dtype` (families
     that apply to some shapes only: halo tiles need 3x3, column pairs also stride 1
     and at most 8 output channels, weight-stationary tiles fp32 1x1 stride 1 with
-    C_in in 16, 32, 64, 96, 128, 192, 256, 384 up to the tile's register budget, their
-    gather form fp32 3x3 with C_in 16 or 32)."""
+    1-4, 6, 8, 12, 16 or 24 K steps of 16 channels (a partial last one at 1-3 steps) up to
+    the tile's register budget, their gather form fp32 3x3 with C_in 16 or 32)."""
     if name.startswith("P"):
         return sp.k == 3 and sp.stride == 1 and sp.c_out <= 8
     if name.startswith("H"):
         return sp.k == 3
     if name.startswith("W."):
         cb = {"c16": 1, "c32": 2, "c80": 5}[name[2:5]]
-        ks = sp.c_in // 16
-        return (dtype == "f32" and sp.k == 1 and sp.stride == 1 and sp.c_in % 16 == 0
-                and ks in (1, 2, 4, 6, 8, 12, 16, 24) and ks <= {1: 24, 2: 16, 5: 8}[cb])
+        cin_pad = -(-sp.c_in // 4) * 4
+        ks = -(-cin_pad // 16)
+        return (dtype == "f32" and sp.k == 1 and sp.stride == 1 and ks in (1, 2, 3, 4, 6, 8, 12, 16, 24)
+                and ks <= {1: 24, 2: 16, 5: 8}[cb] and (cin_pad % 16 == 0 or ks <= 3))
     if name.startswith("G."):
         return dtype == "f32" and sp.k == 3 and sp.c_in in (16, 32)
     return True
