@@ -1398,14 +1398,20 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
 // PARTIAL (1x1): C_in is not a multiple of 16, so the last K step holds fewer
 // than four chunks; that step has its own offset, out of range for the lanes
 // whose chunk lies past C_in.
+//
+// int8 and uint8 activations (1x1, 16-channel chunks): a K step is 64
+// channels and one 16x16x64 MFMA; the dequantising epilogue, the raw int32
+// accumulators and the uint8 zero-point start value (the interior border class:
+// a 1x1 window without padding never leaves the image) follow the other kernels.
 template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false, bool PARTIAL = false>
 __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
   using V = Var<VAR>;
-  static_assert(!V::I8, "fp32 activations only");
+  static_assert(!V::I8 || (V::VEC == 1 && !GATHER), "int8: 16-channel chunks, 1x1 only");
+  constexpr int CH = V::I8 ? 16 : 4;  // channels of one lane's chunk
   using Frag = typename V::Frag;
   using Acc = typename V::Acc;
   int nblocks = gridDim.x;
-  pin_tiled_args<false>(p, nblocks, false);
+  pin_tiled_args<V::U8>(p, nblocks, false);
   pin_sgpr(p.run_base);
   pin_sgpr(p.run_rem);
   const int lane = threadIdx.x & 63;
@@ -1456,7 +1462,7 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
       for (int tp = 0; tp < 9; tp++) o[tp] = (rv[tp / 3] && cv[tp % 3]) ? lb + tap_off[tp] : kOutOfRange;
     } else {
       (void)opix;
-      o[0] = (b < b1 && m < p.M) ? (unsigned)(m * p.x_cs + 4 * g) * 4u : kOutOfRange;
+      o[0] = (b < b1 && m < p.M) ? (unsigned)(m * p.x_cs + CH * g) * (unsigned)V::ESIZE : kOutOfRange;
       if constexpr (PARTIAL) o[NOFF - 1] = 4 * (KS - 1) + g < p.total_chunks ? o[0] : kOutOfRange;
     }
   };
@@ -1474,12 +1480,16 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
     block_offs(b0, o0, op_cur);
     load_block(o0, ba);
   }
-  // this wave's weights (zero for channel blocks past the end) and bias
+  // this wave's weights (zero for channel blocks past the end), bias, int8
+  // dequant factors and uint8 start values
   Frag a[CBW][KS];
-  f32x4 bias[CBW];
+  f32x4 bias[CBW], dq[CBW];
+  Acc acc0[CBW];
   {
     const __amdgpu_buffer_rsrc_t br =
         __builtin_amdgcn_make_buffer_rsrc((void *)p.bias, 0, (int)(p.co_blocks * 64), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t dr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.dq, 0, V::I8 ? (int)(p.co_blocks * 64) : 0, kRsrcWord3);
 #pragma unroll
     for (int cb = 0; cb < CBW; cb++) {
       const unsigned wv = (cob0 + cb) < p.co_blocks
@@ -1490,6 +1500,11 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
         a[cb][s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(wr, wv, s * 1024, 0));
       bias[cb] = __builtin_bit_cast(
           f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, (unsigned)(((cob0 + cb) * 16 + 4 * g) * 4), 0, 0));
+      dq[cb] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (V::I8 && !V::RAW)
+        dq[cb] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(dr, (unsigned)(((cob0 + cb) * 16 + 4 * g) * 4), 0, 0));
+      acc0[cb] = zp_correction<V>(p, V::U8 ? border_class(p, 0, 0) : 0, (cob0 + cb) * 16 + 4 * g);
     }
   }
   const __amdgpu_buffer_rsrc_t rr = rsrc(p.res, p.res_bytes);
@@ -1509,14 +1524,21 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
     __builtin_amdgcn_sched_barrier(0);
     Acc acc[CBW];
 #pragma unroll
-    for (int cb = 0; cb < CBW; cb++) acc[cb] = Acc{};
+    for (int cb = 0; cb < CBW; cb++) acc[cb] = acc0[cb];
 #pragma unroll
-    for (int s = 0; s < KS; s++)
+    for (int s = 0; s < KS; s++) {
+      if constexpr (V::I8) {
+        const Frag bs = V::U8 ? (cur[s] ^ kU8Flip) : cur[s];
 #pragma unroll
-      for (int j = 0; j < 4; j++)
+        for (int cb = 0; cb < CBW; cb++) acc[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[cb][s], bs, acc[cb], 0, 0, 0);
+      } else {
 #pragma unroll
-        for (int cb = 0; cb < CBW; cb++)
-          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cb][s][j], cur[s][j], acc[cb], 0, 0, 0);
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int cb = 0; cb < CBW; cb++)
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cb][s][j], cur[s][j], acc[cb], 0, 0, 0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     int op_next2 = 0;
     block_offs(b + 2 * WPX, off, op_next2);
@@ -1535,10 +1557,19 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
       for (int cb = 0; cb < CBW; cb++) {
         const int co0 = (cob0 + cb) * 16 + 4 * g;
         if (co0 >= p.cout_pad) continue;
-        f32x4 z;
+        if constexpr (V::RAW) {
+          store16(p, (unsigned)(opix * p.out_cs + co0) * 4u, acc[cb]);
+        } else {
+          f32x4 z;
 #pragma unroll
-        for (int i = 0; i < 4; i++) z[i] = acc[cb][i] + bias[cb][i];
-        epilogue_store<V::X>(p, rr, z, opix, m, co0);
+          for (int i = 0; i < 4; i++) {
+            if constexpr (V::I8)
+              z[i] = (float)acc[cb][i] * dq[cb][i] + bias[cb][i];
+            else
+              z[i] = acc[cb][i] + bias[cb][i];
+          }
+          epilogue_store<V::X>(p, rr, z, opix, m, co0);
+        }
       }
     }
     op_cur = op_nxt;
@@ -1623,9 +1654,29 @@ static hipError_t launch_wsg(const ConvParams &p, hipStream_t stream) {
 }
 template <int VAR, int CBW, int WCO, int WPX>
 static hipError_t launch_ws(const ConvParams &p, hipStream_t stream) {
-  if constexpr (VAR != VAR_F32 && VAR != VAR_F32_X) {
+  using V = Var<VAR>;
+  if constexpr (V::I8 && V::VEC != 1) {  // int8 and uint8: 16-channel chunks only
     (void)p, (void)stream;
     return hipErrorInvalidValue;
+  } else if constexpr (V::I8) {
+    // K steps of 64 channels: depths 1-4 and 6, a partial last step at 1-3
+    if (p.splitk != 1 || p.k != 1 || p.stride != 1 || p.pad != 0 || p.chunk_ch != 16) return hipErrorInvalidValue;
+    if (p.total_chunks < 4 * p.steps) {
+      switch (p.steps) {
+        case 1: return launch_ws_k<VAR, CBW, WCO, 1, WPX, false, true>(p, stream);
+        case 2: return launch_ws_k<VAR, CBW, WCO, 2, WPX, false, true>(p, stream);
+        case 3: return launch_ws_k<VAR, CBW, WCO, 3, WPX, false, true>(p, stream);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    switch (p.steps) {
+      case 1: return launch_ws_k<VAR, CBW, WCO, 1, WPX>(p, stream);
+      case 2: return launch_ws_k<VAR, CBW, WCO, 2, WPX>(p, stream);
+      case 3: return launch_ws_k<VAR, CBW, WCO, 3, WPX>(p, stream);
+      case 4: return launch_ws_k<VAR, CBW, WCO, 4, WPX>(p, stream);
+      case 6: return launch_ws_k<VAR, CBW, WCO, 6, WPX>(p, stream);
+      default: return hipErrorInvalidValue;
+    }
   } else {
     if (p.splitk != 1 || p.k != 1 || p.stride != 1 || p.pad != 0 || p.chunk_ch != 4) return hipErrorInvalidValue;
     constexpr int kMax = ws_max_steps(CBW);  // deepest K that fits the registers without spilling

@@ -429,11 +429,13 @@ void cbs_autotune_clear_cache(void);
  *   "P."           the same on column pairs (3x3 stride 1, at most 8 output
  *                  channels);
  *   "W."           weights held in registers, runs of 16-pixel blocks per
- *                  workgroup (fp32 1x1 stride 1 without padding, C_in
+ *                  workgroup (1x1 stride 1 without padding; fp32: C_in
  *                  rounded up to a multiple of 4 spanning 1, 2, 3, 4, 6, 8,
- *                  12, 16 or 24 steps of 16 channels, the last one partial
- *                  only at 1-3 steps; 24 steps on the 16-channel "W.c16" tiles only,
- *                  at most 16 on "W.c32", at most 8 on "W.c80");
+ *                  12, 16 or 24 steps of 16 channels, 24 steps on the
+ *                  16-channel "W.c16" tiles only, at most 16 on "W.c32", at
+ *                  most 8 on "W.c80"; int8 and uint8: 16-channel aligned
+ *                  input spanning 1, 2, 3, 4 or 6 steps of 64 channels; the
+ *                  last step partial only at 1-3 steps);
  *   "G."           the same with the 3x3 window gathered per pixel (fp32 3x3,
  *                  any stride and padding, C_in rounded up to a multiple of 4
  *                  equal to 16 or 32).

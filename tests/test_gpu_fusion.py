@@ -439,19 +439,26 @@ OPTION_CASES = [(spec(16, 16, 20, 20, 3, 1), (48, 16), (48, 32), (48, 16)),
 def runs_on(name, sp, dtype):
     """Whether configuration `name` can run layer `sp` of input type `dtype` (families
     that apply to some shapes only: halo tiles need 3x3, column pairs also stride 1
-    and at most 8 output channels, weight-stationary tiles fp32 1x1 stride 1 with
-    1-4, 6, 8, 12, 16 or 24 K steps of 16 channels (a partial last one at 1-3 steps) up to
-    the tile's register budget, their gather form fp32 3x3 with C_in 16 or 32)."""
+    and at most 8 output channels, weight-stationary tiles 1x1 stride 1 with fp32 1-4,
+    6, 8, 12, 16 or 24 K steps of 16 channels up to the tile's register budget, or int8
+    / uint8 16-channel chunks in 1-4 or 6 steps of 64 (a partial last step at 1-3 steps),
+    their gather form fp32 3x3 with C_in 16 or 32)."""
     if name.startswith("P"):
         return sp.k == 3 and sp.stride == 1 and sp.c_out <= 8
     if name.startswith("H"):
         return sp.k == 3
     if name.startswith("W."):
         cb = {"c16": 1, "c32": 2, "c80": 5}[name[2:5]]
-        cin_pad = -(-sp.c_in // 4) * 4
-        ks = -(-cin_pad // 16)
-        return (dtype == "f32" and sp.k == 1 and sp.stride == 1 and ks in (1, 2, 3, 4, 6, 8, 12, 16, 24)
-                and ks <= {1: 24, 2: 16, 5: 8}[cb] and (cin_pad % 16 == 0 or ks <= 3))
+        if sp.k != 1 or sp.stride != 1:
+            return False
+        if dtype == "f32":
+            cin_pad = -(-sp.c_in // 4) * 4
+            ks = -(-cin_pad // 16)
+            return (ks in (1, 2, 3, 4, 6, 8, 12, 16, 24) and ks <= {1: 24, 2: 16, 5: 8}[cb]
+                    and (cin_pad % 16 == 0 or ks <= 3))
+        # int8 and uint8: 16-channel chunks (these cases' slices are 16-channel aligned)
+        ks = -(-sp.c_in // 64)
+        return sp.c_in % 16 == 0 and ks in (1, 2, 3, 4, 6) and (sp.c_in % 64 == 0 or ks <= 3)
     if name.startswith("G."):
         return dtype == "f32" and sp.k == 3 and sp.c_in in (16, 32)
     return True

@@ -270,6 +270,47 @@ WSG_SPECS = [(W.LayerSpec("g16", 16, 16, 21, 23, 3, 1, 1), 2), (W.LayerSpec("g16
              (W.LayerSpec("g24", 24, 16, 9, 9, 3, 1, 1), 1), (W.LayerSpec("g48", 48, 16, 9, 9, 3, 1, 1), 1)]
 
 
+# int8 1x1 shapes for the weight-stationary tiles (16-channel chunks, 64-channel K
+# steps): depths 1, 2, 4 and 6, partial last steps (16, 32, 96 input channels),
+# runs of several blocks, channel counts that leave channel blocks empty.
+WS_I8_SPECS = [(W.LayerSpec("wq16", 16, 16, 31, 29, 1, 1, 0), 3), (W.LayerSpec("wq32", 32, 24, 17, 21, 1, 1, 0), 2),
+               (W.LayerSpec("wq64c80", 64, 80, 40, 40, 1, 1, 0), 4), (W.LayerSpec("wq96", 96, 64, 9, 11, 1, 1, 0), 2),
+               (W.LayerSpec("wq128", 128, 136, 11, 5, 1, 1, 0), 2), (W.LayerSpec("wq256", 256, 48, 6, 6, 1, 1, 0), 2),
+               (W.LayerSpec("wq384", 384, 20, 3, 5, 1, 1, 0), 2), (W.LayerSpec("wq64runs", 64, 32, 49, 50, 1, 1, 0), 3)]
+
+
+def test_weight_stationary_tiles_i8():
+    """int8 activations on the weight-stationary 1x1 tiles: int32 accumulators bit-exact
+    (raw output), dequantised output within the int8 band, guards untouched."""
+    rng = np.random.default_rng(16)
+    ws = [c for c in range(cbs.cbs_num_configs()) if cbs.cbs_config_name(c).startswith("W.")]
+    for spec, n in WS_I8_SPECS:
+        L = W.draw_layer(rng, spec, n)
+        s_x = W.calibration_scale(L.x)
+        ref = oracle.conv_bn_silu_i8(L.x, s_x, L.w, L.gamma, L.beta, L.mean, L.var, L.eps, spec.stride, spec.pad)
+        layer = create(L, cbs.CBS_I8, s_x=s_x)
+        ran = []
+        for cfg in ws:
+            try:
+                cbs.cbs_layer_set_config(layer, cfg, 1)
+            except cbs.CbsError as e:
+                assert e.status == cbs.CBS_EUNSUPPORTED
+                continue
+            r = run_i8(L, s_x, layer=layer)
+            name = "%s n=%d %s" % (spec.name, n, r["info"]["config_name"])
+            assert np.array_equal(r["acc"], ref["acc"]), name
+            assert_i8_parity(r["y"], ref["y"], ref["f"], ref["absacc"], name)
+            assert check_guards(r["host"], L, r["info"]) == 0, name
+            assert np.all(r["valid"][..., spec.c_out:] == 0), name
+            ran.append(r["info"]["config_name"])
+        ks = -(-spec.c_in // 64)
+        max_steps = {"c16": 24, "c32": 16, "c80": 8}
+        want = sorted(cbs.cbs_config_name(c) + "/sk1" for c in ws
+                      if ks in (1, 2, 3, 4, 6) and (spec.c_in % 64 == 0 or ks <= 3)
+                      and ks <= max_steps[cbs.cbs_config_name(c)[2:5]])
+        assert sorted(ran) == want, (spec.name, ran, want)
+
+
 def test_weight_stationary_gather_tiles_f32():
     rng = np.random.default_rng(14)
     gs = [c for c in range(cbs.cbs_num_configs()) if cbs.cbs_config_name(c).startswith("G.")]
