@@ -1368,8 +1368,8 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
 }
 
 // ------------------------------------------------ weight-stationary 1x1 --
-// fp32 1x1 stride-1 layers at large M (the batch-16 1x1 convolutions with
-// 16-384 input channels).  There the output is thousands of 16-pixel blocks
+// 1x1 stride-1 layers at large M (the batch-16 1x1 convolutions with 16-384
+// input channels).  There the output is thousands of 16-pixel blocks
 // deep but only a few channel blocks wide, K is short (1-24 K steps), and a
 // tile of the other kernels pays its prologue (weights, first activations)
 // and its epilogue once per 64-128 pixels.  Here a workgroup of WCO x WPX
@@ -1627,9 +1627,9 @@ static hipError_t launch_halo_pair(const ConvParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Weight-stationary 1x1 tiles: the K depth is a template argument (the
-// weights of all K steps sit in registers), instantiated for the depths of the
-// batch-16 1x1 layers; fp32 variants only.
+// Weight-stationary tiles: the K depth is a template argument (the weights of
+// all K steps sit in registers), instantiated for the depths the configuration
+// lists allow.
 template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false, bool PARTIAL = false>
 static hipError_t launch_ws_k(const ConvParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((conv_ws<VAR, CBW, WCO, KS, WPX, GATHER, PARTIAL>), dim3((unsigned)p.px_tiles * (unsigned)p.co_tiles),
