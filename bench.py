@@ -257,14 +257,17 @@ class ListBench:
 
 class ChainBench:
     """The 25 backbone layers of the list chained as they run in the network: five
-    stages, each a 3x3 s2 downsample and a C3k2 block (cv1 1x1 into the first c
-    channels of a 1.5c-channel buffer T; the bottleneck's two 3x3 convs read the
-    second half of cv1's output in place and the second adds it back and writes
-    the last c/2 channels of T; cv2 1x1 reads T whole).  Each stage's output is
-    the next stage's input.  One step = 25 kernels, no cat / chunk / add kernel,
-    replayed as one captured graph.  INT8: every tensor is int8 codes (scales:
-    the calibration of the list layers' generated inputs; timing does not
-    depend on them)."""
+    stages, each a 3x3 s2 downsample and a C3k2 block (cv1 1x1; the bottleneck's
+    two 3x3 convs read the second half of cv1's output in place and the second
+    adds it back; cv2 1x1 reads the concatenation of cv1's output and the
+    bottleneck's).  FP32 at batch 16 keeps that concatenation as two dense
+    tensors, which cv2 reads as its two inputs; INT8, and FP32 at batch 1, keep
+    one 1.5c-channel buffer T that cv1 (the first c channels) and the bottleneck
+    (the last c/2) write slices of.
+    Each stage's output is the next stage's input.  One step = 25 kernels, no
+    cat / chunk / add kernel, replayed as one captured graph.  INT8: every
+    tensor is int8 codes (scales: the calibration of the list layers'
+    generated inputs; timing does not depend on them)."""
 
     def __init__(self, cbs, W, torch, int8, batch, seed=0):
         self.cbs, self.torch, self.batch = cbs, torch, batch
@@ -289,8 +292,15 @@ class ChainBench:
             down, cv1, b1, b2, cv2 = gen[5 * st: 5 * st + 5]
             c, h = cv1.spec.c_out, cv1.spec.h
             half = c // 2
+            # FP32 at batch 16 keeps the concatenation as two dense tensors (cv1's
+            # output and b2's), which cv2 reads as its two inputs; INT8, and FP32 at
+            # batch 1, keep one buffer that cv1 and b2 write slices of (at batch 1
+            # the second input would hold cv2 to the weight-stationary tiles, which
+            # lose there)
+            split = not int8 and batch > 1
             D = torch.empty(batch * h * h * c, dtype=tdt, device=dev)
-            T = torch.empty(batch * h * h * 3 * half, dtype=tdt, device=dev)
+            T = torch.empty(batch * h * h * (c if split else 3 * half), dtype=tdt, device=dev)
+            T2 = torch.empty(batch * h * h * half, dtype=tdt, device=dev) if split else None
             U = torch.empty(batch * h * h * half, dtype=tdt, device=dev)
             Y = torch.empty(batch * h * h * c, dtype=tdt, device=dev)
 
@@ -305,13 +315,21 @@ class ChainBench:
                 return layer
 
             ld = mk(down, s_in)
-            l1 = mk(cv1, s_act, out_c_stride=3 * half, out_c_offset=0)
-            lb1 = mk(b1, s_act, in_c_stride=3 * half, in_c_offset=half)
-            lb2 = mk(b2, s_act, out_c_stride=3 * half, out_c_offset=2 * half, res_c_stride=3 * half,
-                     res_c_offset=half, res_scale=float(s_act) if int8 else 0.0)
-            l2 = mk(cv2, s_act)
-            self.steps += [(ld, cur, D), (l1, D, T), (lb1, T, U), (lb2, U, T, T), (l2, T, Y)]
-            self.bufs += [D, T, U, Y]
+            if split:
+                l1 = mk(cv1, s_act)
+                lb1 = mk(b1, s_act, in_c_stride=c, in_c_offset=half)
+                lb2 = mk(b2, s_act, res_c_stride=c, res_c_offset=half)
+                l2 = mk(cv2, s_act, in2_channels=half)
+                self.steps += [(ld, cur, D), (l1, D, T), (lb1, T, U), (lb2, U, T2, T), (l2, T, Y, None, T2)]
+                self.bufs += [D, T, T2, U, Y]
+            else:
+                l1 = mk(cv1, s_act, out_c_stride=3 * half, out_c_offset=0)
+                lb1 = mk(b1, s_act, in_c_stride=3 * half, in_c_offset=half)
+                lb2 = mk(b2, s_act, out_c_stride=3 * half, out_c_offset=2 * half, res_c_stride=3 * half,
+                         res_c_offset=half, res_scale=float(s_act) if int8 else 0.0)
+                l2 = mk(cv2, s_act)
+                self.steps += [(ld, cur, D), (l1, D, T), (lb1, T, U), (lb2, U, T, T), (l2, T, Y)]
+                self.bufs += [D, T, U, Y]
             cur, s_in = Y, s_act
         torch.cuda.synchronize()
         self.graph = cbs.cbs_graph_create_steps(self.steps)

@@ -62,7 +62,7 @@ class cbs_conv_desc(ctypes.Structure):
                 ("out_c_stride", ctypes.c_int32), ("out_c_offset", ctypes.c_int32),
                 ("res_c_stride", ctypes.c_int32), ("res_c_offset", ctypes.c_int32), ("res_scale", ctypes.c_float),
                 ("in_zero_point", ctypes.c_int32), ("out_zero_point", ctypes.c_int32),
-                ("res_zero_point", ctypes.c_int32)]
+                ("res_zero_point", ctypes.c_int32), ("in2_channels", ctypes.c_int32), ("in2_c_stride", ctypes.c_int32)]
 
 
 class cbs_layer_info_t(ctypes.Structure):
@@ -71,7 +71,7 @@ class cbs_layer_info_t(ctypes.Structure):
                 ("in_bytes", ctypes.c_int64), ("out_bytes", ctypes.c_int64), ("flops", ctypes.c_int64),
                 ("alg_bytes", ctypes.c_int64), ("config", ctypes.c_int32), ("splitk", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("threads", ctypes.c_int32), ("config_name", ctypes.c_char * 48),
-                ("res_bytes", ctypes.c_int64)]
+                ("res_bytes", ctypes.c_int64), ("in2_bytes", ctypes.c_int64)]
 
 
 class cbs_graph_group_info_t(ctypes.Structure):
@@ -81,7 +81,7 @@ class cbs_graph_group_info_t(ctypes.Structure):
 
 class cbs_step(ctypes.Structure):
     _fields_ = [("layer", ctypes.c_void_p), ("in_", ctypes.c_void_p), ("out", ctypes.c_void_p),
-                ("residual", ctypes.c_void_p)]
+                ("residual", ctypes.c_void_p), ("in2", ctypes.c_void_p)]
 
 
 # Every symbol the header declares, with (restype, argtypes).
@@ -93,6 +93,7 @@ _SIGNATURES = {
     "cbs_destroy_layer": (None, [_P]),
     "cbs_run_layer": (_I, [_P, _P, _P, _P]),
     "cbs_run_layer_res": (_I, [_P, _P, _P, _P, _P]),
+    "cbs_run_layer_in2": (_I, [_P, _P, _P, _P, _P, _P]),
     "cbs_run_layer_noalloc": (_I, [_P, _P, _P, _I, _P]),
     "cbs_run_steps": (_I, [ctypes.POINTER(cbs_step), _I, _P]),
     "cbs_graph_create_steps": (_I, [ctypes.POINTER(cbs_step), _I, _P, ctypes.POINTER(_P)]),
@@ -175,6 +176,10 @@ def _res_ptr(layer, buf, what="residual"):
     return _dev_ptr(buf, layer.res_bytes, what)
 
 
+def _in2_ptr(layer, buf, what="second input"):
+    return _dev_ptr(buf, layer.in2_bytes, what)
+
+
 def _stream(stream) -> int:
     if stream is None:
         return int(torch.cuda.current_stream().cuda_stream)
@@ -197,12 +202,14 @@ class Layer:
     in_bytes: int = 0
     out_bytes: int = 0
     res_bytes: int = 0
+    in2_bytes: int = 0
     acc_bytes: int = 0  # int32 accumulators of cbs_run_layer_raw_acc
 
     def __post_init__(self):
         info = cbs_layer_info_t()
         _check(lib.cbs_layer_info(self.handle, ctypes.byref(info)), "cbs_layer_info")
         self.in_bytes, self.out_bytes, self.res_bytes = int(info.in_bytes), int(info.out_bytes), int(info.res_bytes)
+        self.in2_bytes = int(info.in2_bytes)
         self.acc_bytes = self.desc.n * info.oh * info.out_row_pitch * info.c_out_pad * 4
 
     def __del__(self):
@@ -214,11 +221,12 @@ class Layer:
 def make_desc(n, c_in, h, w, c_out, k, stride, pad, dtype=CBS_F32, out_row_pitch=0, in_scale=0.0,
               bn_eps=1e-3, act=CBS_ACT_SILU, out_dtype=CBS_F32, out_scale=0.0, in_c_stride=0, in_c_offset=0,
               out_c_stride=0, out_c_offset=0, res_c_stride=0, res_c_offset=0, res_scale=0.0, in_zero_point=0,
-              out_zero_point=0, res_zero_point=0) -> cbs_conv_desc:
+              out_zero_point=0, res_zero_point=0, in2_channels=0, in2_c_stride=0) -> cbs_conv_desc:
     return cbs_conv_desc(n, c_in, h, w, c_out, k, stride, pad, dtype, out_row_pitch, float(in_scale),
                          float(bn_eps), act, out_dtype, float(out_scale), in_c_stride, in_c_offset,
                          out_c_stride, out_c_offset, res_c_stride, res_c_offset, float(res_scale),
-                         int(in_zero_point), int(out_zero_point), int(res_zero_point))
+                         int(in_zero_point), int(out_zero_point), int(res_zero_point), int(in2_channels),
+                         int(in2_c_stride))
 
 
 def cbs_create_layer(desc: cbs_conv_desc, w_oihw, gamma, beta, mean, var) -> Layer:
@@ -261,15 +269,22 @@ def cbs_run_layer_res(layer: Layer, inp, out, residual, stream=None) -> None:
                                  _stream(stream)), "cbs_run_layer_res")
 
 
+def cbs_run_layer_in2(layer: Layer, inp, in2, out, residual=None, stream=None) -> None:
+    _check(lib.cbs_run_layer_in2(layer.handle, _in_ptr(layer, inp), _in2_ptr(layer, in2), _out_ptr(layer, out),
+                                 _res_ptr(layer, residual), _stream(stream)), "cbs_run_layer_in2")
+
+
 def _step_array(steps):
-    """steps: (layer, in, out) or (layer, in, out, residual) tuples."""
+    """steps: (layer, in, out), (layer, in, out, residual) or (layer, in, out, residual,
+    second input) tuples (residual None when the layer has none)."""
     arr = (cbs_step * max(1, len(steps)))()
     for i, st in enumerate(steps):
         layer, inp, out = st[:3]
         res = st[3] if len(st) > 3 else None
+        in2 = st[4] if len(st) > 4 else None
         w = "step %d " % i
         arr[i] = cbs_step(layer.handle, _in_ptr(layer, inp, w + "input"), _out_ptr(layer, out, w + "output"),
-                          _res_ptr(layer, res, w + "residual"))
+                          _res_ptr(layer, res, w + "residual"), _in2_ptr(layer, in2, w + "second input"))
     return arr
 
 

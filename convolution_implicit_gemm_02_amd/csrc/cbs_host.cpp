@@ -63,6 +63,7 @@ struct cbs_layer {
   cbs_conv_desc d;
   int oh, ow, pitch, cin_pad, cout_pad, co_blocks, M;
   int in_cs, out_cs, res_cs;  // channel strides of input, output, residual (res_cs 0: none)
+  int in2_ch = 0, in2_cs = 0;  // second input: its channels (the last of C_in; 0: none) and pixel stride
   int variant;       // fused-epilogue variant
   int raw_variant;   // raw-accumulator variant (INT8), -1 for fp32
   int chunk_ch, chunks_per_tap, total_chunks, steps;
@@ -178,7 +179,7 @@ cbs_status validate(const cbs_conv_desc *d) {
   struct Slice {
     const char *what;
     int stride, offset, channels;
-  } slices[3] = {{"in", d->in_c_stride, d->in_c_offset, d->c_in},
+  } slices[3] = {{"in", d->in_c_stride, d->in_c_offset, d->c_in - d->in2_channels},
                  {"out", d->out_c_stride, d->out_c_offset, d->c_out},
                  {"res", d->res_c_stride, d->res_c_offset, d->c_out}};
   for (const Slice &sl : slices) {
@@ -197,8 +198,25 @@ cbs_status validate(const cbs_conv_desc *d) {
   }
   if (d->res_c_stride > 0 && d->out_dtype != CBS_F32 && !(d->res_scale > 0.0f && std::isfinite(d->res_scale)))
     return fail(CBS_EINVAL, "byte residual needs a finite res_scale > 0");
+  // second input: the last in2_channels of C_in, from a tensor of its own
+  if (d->in2_channels < 0 || d->in2_c_stride < 0) return fail(CBS_EINVAL, "in2_channels / in2_c_stride must be >= 0");
+  if (d->in2_channels == 0 && d->in2_c_stride != 0) return fail(CBS_EINVAL, "in2_c_stride set without in2_channels");
+  if (d->in2_channels > 0) {
+    if (d->dtype != CBS_F32 || d->k != 1 || d->stride != 1 || d->pad != 0)
+      return fail(CBS_EUNSUPPORTED, "a second input needs an fp32 1x1 stride-1 layer");
+    const int c1 = d->c_in - d->in2_channels;
+    if (c1 < 16 || c1 % 16)
+      return fail(CBS_EUNSUPPORTED, "with a second input the first supplies a positive multiple of 16 channels "
+                                    "(got %d of %d)", c1, d->c_in);
+    const int s2 = d->in2_c_stride ? d->in2_c_stride : round_up(d->in2_channels, 4);
+    if (d->in2_channels % 4 || s2 % 4 || s2 < d->in2_channels)
+      return fail(CBS_EINVAL, "second input: channels %d and stride %d must be multiples of 4, stride >= channels",
+                  d->in2_channels, s2);
+    if ((double)d->n * d->h * d->w * s2 * 4.0 >= 2147483648.0 - 64.0)
+      return fail(CBS_EUNSUPPORTED, "second input above 2^31 bytes");
+  }
   const int pitch = d->out_row_pitch ? d->out_row_pitch : ow;
-  const int in_cs = d->in_c_stride ? d->in_c_stride : round_up(d->c_in, 4);
+  const int in_cs = d->in_c_stride ? d->in_c_stride : round_up(d->c_in - d->in2_channels, 4);
   const int out_cs = d->out_c_stride ? d->out_c_stride : round_up(d->c_out, 4);
   const double in_elems = (double)d->n * d->h * d->w * in_cs;
   const double out_elems = (double)d->n * oh * pitch * out_cs;
@@ -295,6 +313,9 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
   const KernelConfig &c = config(cfg);
   if (splitk < 1 || splitk > 64) return false;
   if (c.lds && splitk != 1) return false;
+  if (L->in2_ch && (c.lds != 4 || !(L->steps == 2 || L->steps == 3 || L->steps == 6 || L->steps == 12 ||
+                                      L->steps == 24)))
+    return false;  // a second input: weight-stationary 1x1 tiles, at the depths compiled for it
   if (c.lds == 4) {  // conv_ws: 1x1 stride 1, K steps (the last one may be partial) of the compiled depths
     if (L->d.k != 1 || L->d.stride != 1 || L->d.pad != 0) return false;
     const int ks = L->steps;
@@ -356,6 +377,20 @@ Choice choose(const cbs_layer *L) {
           e.config < num_configs() && config_fits(L, e.config, e.splitk))
         return {e.config, e.splitk};
     }
+  }
+  // a second input runs on the weight-stationary 1x1 tiles only: the one whose
+  // workgroup covers the fewest channel blocks at or above the layer's, else the widest
+  if (L->in2_ch) {
+    int pick = -1, pick_cov = 0;
+    for (int cfg = 0; cfg < num_configs(); cfg++) {
+      const KernelConfig &c = config(cfg);
+      if (c.lds != 4 || !config_fits(L, cfg, 1)) continue;
+      const int cov = c.cb * c.wco, need = L->co_blocks;
+      const bool better = pick < 0 || (cov >= need && (pick_cov < need || cov < pick_cov)) ||
+                          (cov < need && pick_cov < need && cov > pick_cov);
+      if (better) pick = cfg, pick_cov = cov;
+    }
+    if (pick >= 0) return {pick, 1};
   }
   // 2) the cost model.  Cross-workgroup split-K is never picked here: its
   // partial-tile round trip through memory costs about a microsecond per
@@ -482,7 +517,7 @@ FastDiv make_fastdiv(int d) {
 // Kernel arguments of one launch of layer L with configuration cfg and split-K
 // factor splitk (the layer's own, or a group's).
 ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void *res, bool raw, int cfg,
-                       int splitk) {
+                       int splitk, const void *in2 = nullptr) {
   ConvParams p;
   std::memset(&p, 0, sizeof(p));
   const size_t esz_in = L->d.dtype == CBS_F32 ? 4 : 1;
@@ -490,6 +525,12 @@ ConvParams make_params(const cbs_layer *L, const void *in, void *out, const void
   p.x = (const char *)in + (size_t)L->d.in_c_offset * esz_in;
   p.x_cs = L->in_cs;
   p.x_bytes = (unsigned)((size_t)L->d.n * L->d.h * L->d.w * L->in_cs * esz_in - (size_t)L->d.in_c_offset * esz_in);
+  if (L->in2_ch) {  // second input (fp32): channels c1 .. C_in - 1
+    p.x2 = in2;
+    p.x2_cs = L->in2_cs;
+    p.x2_bytes = (unsigned)((size_t)L->d.n * L->d.h * L->d.w * L->in2_cs * 4);
+    p.c1 = L->d.c_in - L->in2_ch;
+  }
   p.wfrag = L->d_wfrag;
   p.bias = L->d_bias;
   p.dq = L->d_dq;
@@ -667,20 +708,26 @@ cbs_status group_setup_splitk(cbs_group *g) {
   return CBS_OK;
 }
 
-cbs_status launch(const cbs_layer *L, const void *in, void *out, const void *res, void *stream, bool raw = false) {
-  ConvParams p = make_params(L, in, out, res, raw, L->config, L->splitk);
+cbs_status launch(const cbs_layer *L, const void *in, void *out, const void *res, void *stream, bool raw = false,
+                  const void *in2 = nullptr) {
+  ConvParams p = make_params(L, in, out, res, raw, L->config, L->splitk, in2);
   hipError_t e = launch_conv(raw ? L->raw_variant : L->variant, L->config, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(CBS_ELAUNCH, "conv launch: %s", hipGetErrorString(e));
   return CBS_OK;
 }
 
-// Argument check of one step: buffers present, residual given iff the layer has one.
+// Argument check of one step: buffers present, residual and second input given
+// iff the layer has them.
 cbs_status check_step(const cbs_layer *L, const void *in, const void *out, const void *res, const char *where,
-                      int idx) {
+                      int idx, const void *in2 = nullptr) {
   if (!L || !in || !out) return fail(CBS_EINVAL, "%s: null layer or buffer (entry %d)", where, idx);
   if (L->res_cs && !res)
     return fail(CBS_EINVAL, "%s: layer %d was created with a residual and needs one", where, idx);
   if (!L->res_cs && res) return fail(CBS_EINVAL, "%s: layer %d has no residual but one was given", where, idx);
+  if (L->in2_ch && !in2)
+    return fail(CBS_EINVAL, "%s: layer %d was created with a second input and needs one", where, idx);
+  if (!L->in2_ch && in2)
+    return fail(CBS_EINVAL, "%s: layer %d has no second input but one was given", where, idx);
   return CBS_OK;
 }
 
@@ -769,7 +816,9 @@ cbs_status create_impl(const cbs_conv_desc *desc, const float *w, const float *g
   L->pitch = d.out_row_pitch ? d.out_row_pitch : L->ow;
   L->cin_pad = round_up(d.c_in, 4);
   L->cout_pad = round_up(d.c_out, 4);
-  L->in_cs = d.in_c_stride ? d.in_c_stride : L->cin_pad;
+  L->in2_ch = d.in2_channels;
+  L->in2_cs = d.in2_channels ? (d.in2_c_stride ? d.in2_c_stride : round_up(d.in2_channels, 4)) : 0;
+  L->in_cs = d.in_c_stride ? d.in_c_stride : (L->in2_ch ? d.c_in - L->in2_ch : L->cin_pad);
   L->out_cs = d.out_c_stride ? d.out_c_stride : L->cout_pad;
   L->res_cs = d.res_c_stride;
   L->co_blocks = ceil_div(L->cout_pad, 16);
@@ -1048,6 +1097,14 @@ cbs_status cbs_run_layer_res(const cbs_layer *layer, const void *in, void *out, 
   return launch(layer, in, out, residual, stream);
 }
 
+cbs_status cbs_run_layer_in2(const cbs_layer *layer, const void *in, const void *in2, void *out,
+                             const void *residual, void *stream) {
+  if (!in2) return fail(CBS_EINVAL, "run_layer_in2: in2 is NULL");
+  cbs_status st = check_step(layer, in, out, residual, "run_layer_in2", 0, in2);
+  if (st != CBS_OK) return st;
+  return launch(layer, in, out, residual, stream, false, in2);
+}
+
 cbs_status cbs_run_layer_list(cbs_layer *const *layers, int32_t n, const void *const *ins,
                               void *const *outs, void *stream) {
   if (n < 0 || (n > 0 && (!layers || !ins || !outs))) return fail(CBS_EINVAL, "run_layer_list: bad arguments");
@@ -1068,6 +1125,7 @@ cbs_status cbs_group_create(cbs_layer *const *layers, int32_t n, int32_t config_
     const cbs_layer *L = layers[i];
     if (!L) return fail(CBS_EINVAL, "group_create: layer %d is NULL", (int)i);
     if (L->res_cs) return fail(CBS_EUNSUPPORTED, "group_create: layer %d has a residual", (int)i);
+    if (L->in2_ch) return fail(CBS_EUNSUPPORTED, "group_create: layer %d has a second input", (int)i);
     if (L->variant != layers[0]->variant || L->device != layers[0]->device)
       return fail(CBS_EUNSUPPORTED, "group_create: layer %d differs from layer 0 in kernel variant (dtype, "
                                     "input chunking or epilogue) or device", (int)i);
@@ -1152,8 +1210,8 @@ cbs_status cbs_run_steps(const cbs_step *steps, int32_t n, void *stream) {
   if (n < 0 || (n > 0 && !steps)) return fail(CBS_EINVAL, "run_steps: bad arguments");
   for (int32_t i = 0; i < n; i++) {
     const cbs_step &t = steps[i];
-    cbs_status st = check_step(t.layer, t.in, t.out, t.residual, "run_steps", i);
-    if (st == CBS_OK) st = launch(t.layer, t.in, t.out, t.residual, stream);
+    cbs_status st = check_step(t.layer, t.in, t.out, t.residual, "run_steps", i, t.in2);
+    if (st == CBS_OK) st = launch(t.layer, t.in, t.out, t.residual, stream, false, t.in2);
     if (st != CBS_OK) return st;
   }
   return CBS_OK;
@@ -1204,7 +1262,7 @@ cbs_status capture(const std::vector<cbs_step> &steps, const std::vector<Launch>
       const Launch &l = launches[i];
       if (!l.group) {
         const cbs_step &t = steps[l.step];
-        st = launch(t.layer, t.in, t.out, t.residual, cs);
+        st = launch(t.layer, t.in, t.out, t.residual, cs, false, t.in2);
       } else {
         std::vector<const void *> ins;
         std::vector<void *> outs;
@@ -1265,7 +1323,8 @@ cbs_status cbs_graph_create_steps(const cbs_step *steps, int32_t n, void *stream
   *out = nullptr;
   if (n < 1 || !steps) return fail(CBS_EINVAL, "graph_create_steps: bad arguments");
   for (int32_t i = 0; i < n; i++) {
-    cbs_status st = check_step(steps[i].layer, steps[i].in, steps[i].out, steps[i].residual, "graph_create_steps", i);
+    cbs_status st = check_step(steps[i].layer, steps[i].in, steps[i].out, steps[i].residual, "graph_create_steps", i,
+                               steps[i].in2);
     if (st != CBS_OK) return st;
   }
   return capture(std::vector<cbs_step>(steps, steps + n), plain_launches(n), out);
@@ -1528,6 +1587,7 @@ cbs_status cbs_layer_info(const cbs_layer *L, cbs_layer_info_t *info) {
   info->in_bytes = (int64_t)d.n * d.h * d.w * L->in_cs * esz;
   info->out_bytes = (int64_t)d.n * L->oh * L->pitch * L->out_cs * osz;
   info->res_bytes = (int64_t)d.n * L->oh * L->ow * L->res_cs * osz;
+  info->in2_bytes = (int64_t)d.n * d.h * d.w * L->in2_cs * 4;
   const int64_t kk = (int64_t)d.k * d.k;
   const int64_t out_elems = (int64_t)d.n * L->oh * L->ow * d.c_out;
   info->flops = 2 * out_elems * d.c_in * kk;

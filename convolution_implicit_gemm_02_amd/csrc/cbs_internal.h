@@ -110,6 +110,10 @@ struct ConvParams {
   FastDiv div_ow, div_oh;    // by OW and OH: pixel index -> (n, oh, ow)
   FastDiv div_inner;         // by inner_tiles: workgroup -> (outer tile, inner tile)
   int run_base, run_rem;     // conv_ws: run t holds 16-pixel blocks [t*run_base + min(t, run_rem), +run_base + (t < run_rem))
+  const void *x2;            // conv_ws 1x1: second input, channels c1 .. C_in - 1 (null: none)
+  int x2_cs;                 // its elements between consecutive pixels
+  unsigned x2_bytes;         // bytes of its buffer (buffer-load range)
+  int c1;                    // channels from the first input (a multiple of 16)
   // ---- cross-workgroup split-K (conv_igemm)
   float *ws;             // split-K partial tiles (null when splitk == 1)
   unsigned *counters;    // split-K arrival counters, one per output tile (zero between launches)

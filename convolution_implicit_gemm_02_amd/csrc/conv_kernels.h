@@ -1403,10 +1403,18 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
 // channels and one 16x16x64 MFMA; the dequantising epilogue, the raw int32
 // accumulators and the uint8 zero-point start value (the interior border class:
 // a 1x1 window without padding never leaves the image) follow the other kernels.
-template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false, bool PARTIAL = false>
+//
+// IN2 (fp32 1x1): the input channels are a concatenation of two tensors, the
+// first c1 (a multiple of 16, so every K step lies in one of them) from x and
+// the rest from x2: K step s reads x below step c1/16 and x2 from there, at a
+// per-lane offset of its own (out of range, in the last step, for lanes past
+// the second tensor's channels).
+template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false, bool PARTIAL = false,
+          bool IN2 = false>
 __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
   using V = Var<VAR>;
   static_assert(!V::I8 || (V::VEC == 1 && !GATHER), "int8: 16-channel chunks, 1x1 only");
+  static_assert(!IN2 || (!V::I8 && !GATHER && !PARTIAL), "second input: fp32 1x1");
   constexpr int CH = V::I8 ? 16 : 4;  // channels of one lane's chunk
   using Frag = typename V::Frag;
   using Acc = typename V::Acc;
@@ -1414,6 +1422,12 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
   pin_tiled_args<V::U8>(p, nblocks, false);
   pin_sgpr(p.run_base);
   pin_sgpr(p.run_rem);
+  if constexpr (IN2) {
+    pin_sgpr(p.x2);
+    pin_sgpr(p.x2_cs);
+    pin_sgpr(p.x2_bytes);
+    pin_sgpr(p.c1);
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: MFMA guards are scalar
   const int wpx = wave % WPX, wco = wave / WPX;
@@ -1426,13 +1440,16 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
 
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void *)p.wfrag, 0, (int)p.w_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)p.x_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xr2 =
+      __builtin_amdgcn_make_buffer_rsrc((void *)p.x2, 0, IN2 ? (int)p.x2_bytes : 0, kRsrcWord3);
+  const int s1 = IN2 ? p.c1 >> 4 : KS;  // IN2: the first K step of the second input
   // Offsets of pixel block b (zero-filled past the run or past M).  1x1: lane
   // (g, r) reads channels 16s + 4g .. +3 of pixel 16b + r for K step s.
   // GATHER: channels 16j + 4g .. +3 of tap t of pixel 16b + r's window for
   // K step s = t * KS/9 + j.
   static_assert(!GATHER || KS == 9 || KS == 18, "gathered K depths: 9 or 18 steps");
   static_assert(!(GATHER && PARTIAL), "partial K steps: 1x1 only");
-  constexpr int NOFF = GATHER ? 9 : PARTIAL ? 2 : 1;
+  constexpr int NOFF = GATHER ? 9 : IN2 ? 3 : PARTIAL ? 2 : 1;
   constexpr int SPT = GATHER ? KS / 9 : KS;  // K steps per offset
   unsigned tap_off[NOFF];
   if constexpr (GATHER) {
@@ -1464,11 +1481,25 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
       (void)opix;
       o[0] = (b < b1 && m < p.M) ? (unsigned)(m * p.x_cs + CH * g) * (unsigned)V::ESIZE : kOutOfRange;
       if constexpr (PARTIAL) o[NOFF - 1] = 4 * (KS - 1) + g < p.total_chunks ? o[0] : kOutOfRange;
+      if constexpr (IN2) {
+        // second input: its own pixel stride; the last K step masks the lanes past its channels
+        o[1] = (b < b1 && m < p.M) ? (unsigned)(m * p.x2_cs + 4 * g) * 4u : kOutOfRange;
+        o[2] = 4 * (KS - 1) + g < p.total_chunks ? o[1] : kOutOfRange;
+      }
     }
   };
   auto load_block = [&](const unsigned(&o)[NOFF], Frag(&dst)[KS]) {
 #pragma unroll
     for (int s = 0; s < KS; s++) {
+      if constexpr (IN2) {
+        // steps below s1 read the first input, the rest the second (s1 is uniform)
+        if (s < s1)
+          dst[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, o[0], s * 64, 0));
+        else
+          dst[s] = __builtin_bit_cast(
+              Frag, __builtin_amdgcn_raw_buffer_load_b128(xr2, o[s == KS - 1 ? 2 : 1], (s - s1) * 64, 0));
+        continue;
+      }
       const unsigned os = GATHER ? o[s / SPT] : o[s == KS - 1 ? NOFF - 1 : 0];
       dst[s] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(xr, os, (s % SPT) * 64, 0));
     }
@@ -1630,9 +1661,10 @@ static hipError_t launch_halo_pair(const ConvParams &p, hipStream_t stream) {
 // Weight-stationary tiles: the K depth is a template argument (the weights of
 // all K steps sit in registers), instantiated for the depths the configuration
 // lists allow.
-template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false, bool PARTIAL = false>
+template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false, bool PARTIAL = false,
+          bool IN2 = false>
 static hipError_t launch_ws_k(const ConvParams &p, hipStream_t stream) {
-  hipLaunchKernelGGL((conv_ws<VAR, CBW, WCO, KS, WPX, GATHER, PARTIAL>), dim3((unsigned)p.px_tiles * (unsigned)p.co_tiles),
+  hipLaunchKernelGGL((conv_ws<VAR, CBW, WCO, KS, WPX, GATHER, PARTIAL, IN2>), dim3((unsigned)p.px_tiles * (unsigned)p.co_tiles),
                      dim3(64 * WCO * WPX), 0, stream, p);
   return hipGetLastError();
 }
@@ -1680,6 +1712,21 @@ static hipError_t launch_ws(const ConvParams &p, hipStream_t stream) {
   } else {
     if (p.splitk != 1 || p.k != 1 || p.stride != 1 || p.pad != 0 || p.chunk_ch != 4) return hipErrorInvalidValue;
     constexpr int kMax = ws_max_steps(CBW);  // deepest K that fits the registers without spilling
+    if (p.x2) {  // a second input: the concatenation depths of a C3k2 block's last 1x1 (1.5 to 24 steps)
+      if (p.c1 <= 0 || (p.c1 & 15) || 16 * p.steps <= p.c1) return hipErrorInvalidValue;
+      switch (p.steps) {
+        case 2: return launch_ws_k<VAR, CBW, WCO, 2, WPX, false, false, true>(p, stream);
+        case 3: return launch_ws_k<VAR, CBW, WCO, 3, WPX, false, false, true>(p, stream);
+        case 6: return launch_ws_k<VAR, CBW, WCO, 6, WPX, false, false, true>(p, stream);
+        case 12:
+          if constexpr (kMax >= 12) return launch_ws_k<VAR, CBW, WCO, 12, WPX, false, false, true>(p, stream);
+          return hipErrorInvalidValue;
+        case 24:
+          if constexpr (kMax >= 24) return launch_ws_k<VAR, CBW, WCO, 24, WPX, false, false, true>(p, stream);
+          return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+      }
+    }
     if (p.total_chunks < 4 * p.steps) {  // a partial last K step: depths 1-3 only
       switch (p.steps) {
         case 1: return launch_ws_k<VAR, CBW, WCO, 1, WPX, false, true>(p, stream);

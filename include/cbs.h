@@ -68,6 +68,16 @@
  *            channels get 0.  Slice: C_out, out_c_offset and out_c_stride are
  *            multiples of 4 and out_c_offset + C_out <= out_c_stride (writing
  *            into a channel_cat buffer in place).
+ *   second input (in2_channels > 0; fp32 1x1 stride-1 layers): the layer's
+ *            input channels are the concatenation of the first input's C_in -
+ *            in2_channels channels (a positive multiple of 16; in_c_stride and
+ *            in_c_offset describe that input as usual, dense stride C_in -
+ *            in2_channels) and the second input's in2_channels channels, NHWC
+ *            [N][H][W][in2_c_stride] from channel 0 (in2_channels and
+ *            in2_c_stride multiples of 4).  The producers of a concatenation can
+ *            then write dense rows instead of slices of a wider pixel, and the
+ *            consumer reads both tensors (run with cbs_run_layer_in2 or steps
+ *            that name the second input).
  *   residual (res_c_stride > 0): NHWC [N][OH][OW][res_c_stride] (dense rows,
  *            like an input), of the output's dtype; the layer reads channels
  *            res_c_offset .. res_c_offset + C_out - 1.  C_out, res_c_offset and
@@ -141,6 +151,9 @@ typedef struct cbs_conv_desc {
     int32_t in_zero_point;  /* dtype CBS_U8: z_x */
     int32_t out_zero_point; /* out_dtype CBS_U8: z_y */
     int32_t res_zero_point; /* out_dtype CBS_U8 with a residual: zero point of its codes */
+    /* ---- second input (a channel concatenation kept as two dense tensors); 0 = none ---- */
+    int32_t in2_channels;  /* the last in2_channels of the C_in channels come from the second input */
+    int32_t in2_c_stride;  /* channels between its pixels; 0 = round_up(in2_channels, 4) (dense) */
 } cbs_conv_desc;
 
 typedef struct cbs_layer_info_t {
@@ -160,6 +173,7 @@ typedef struct cbs_layer_info_t {
     int32_t threads;              /* threads per workgroup */
     char config_name[48];         /* human-readable configuration name */
     int64_t res_bytes;            /* size of the residual buffer read (0 without residual) */
+    int64_t in2_bytes;            /* size of the second input buffer read (0 without one) */
 } cbs_layer_info_t;
 
 /*
@@ -227,6 +241,18 @@ cbs_status cbs_run_layer_noalloc(const cbs_layer *layer, const void *in, void *o
  * the device tensor added after the activation (layout above).  CBS_EINVAL if
  * the layer has no residual or residual is NULL.
  */
+/*
+ * Run a layer created with a second input (in2_channels > 0): `in` holds the
+ * first C_in - in2_channels input channels and `in2` the rest, each with its
+ * own pixel stride (a concatenation read from two tensors, "YOLO26N Inference
+ * Optimisation", section "Improvements": the channel_cat and channel_chunk
+ * operations become pointer arithmetic).  `residual` as in cbs_run_layer_res,
+ * NULL when the layer has none.  Layers without a second input are rejected
+ * (CBS_EINVAL), and so are layers with one in every other run entry point.
+ */
+cbs_status cbs_run_layer_in2(const cbs_layer *layer, const void *in, const void *in2, void *out,
+                             const void *residual, void *stream);
+
 cbs_status cbs_run_layer_res(const cbs_layer *layer, const void *in, void *out, const void *residual,
                              void *stream);
 
@@ -314,6 +340,7 @@ typedef struct cbs_step {
     const void *in;
     void *out;
     const void *residual;
+    const void *in2; /* the second input (NULL unless the layer was created with one) */
 } cbs_step;
 
 /* Enqueue steps[0..n-1] in order on one stream; stops at the first failure. */

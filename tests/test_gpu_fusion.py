@@ -632,7 +632,10 @@ def _u8_chain(specs, params, x0, scales, half):
     return specs, params, ora, x0, scales
 
 
-def _create_chain(specs, params, n, dtype, scales, c):
+def _create_chain(specs, params, n, dtype, scales, c, split=False):
+    """split (fp32): the concatenation kept as two dense tensors, cv1's output T1
+    (c channels) and b2's T2 (half), which cv2 reads as its two inputs; otherwise
+    one 3*half-channel buffer that cv1 and b2 write slices of."""
     half = c // 2
     DT = DTYPES[dtype]
     sc = scales or {}
@@ -650,6 +653,14 @@ def _create_chain(specs, params, n, dtype, scales, c):
                           out_dtype=DT, out_scale=float(s_out), in_zero_point=z_in, out_zero_point=z_out, **kw)
         return cbs.cbs_create_layer(d, P.w, P.gamma, P.beta, P.mean, P.var)
 
+    if split:
+        return {
+            "down": mk("down", "x0", "d"),
+            "cv1": mk("cv1", "d", "t"),
+            "b1": mk("b1", "t", "u", in_c_stride=c, in_c_offset=half),
+            "b2": mk("b2", "u", "t", res_key="t", res_c_stride=c, res_c_offset=half),
+            "cv2": mk("cv2", "t", "y", in2_channels=half),
+        }
     return {
         "down": mk("down", "x0", "d"),
         "cv1": mk("cv1", "d", "t", out_c_stride=3 * half, out_c_offset=0),
@@ -660,30 +671,44 @@ def _create_chain(specs, params, n, dtype, scales, c):
     }
 
 
-def _run_chain(layers, x0_dev, n, c, h, dtype, graph_replays=0):
+def _run_chain(layers, x0_dev, n, c, h, dtype, graph_replays=0, split=False):
     half = c // 2
     tdt = {"f32": torch.float32, "i8": torch.int8, "u8": torch.uint8}[dtype]
     D = torch.empty(n * h * h * c, dtype=tdt, device=dev())
-    T = torch.empty(n * h * h * 3 * half, dtype=tdt, device=dev())
+    T = torch.empty(n * h * h * (c if split else 3 * half), dtype=tdt, device=dev())
     U = torch.empty(n * h * h * half, dtype=tdt, device=dev())
     Y = torch.empty(n * h * h * c, dtype=tdt, device=dev())
-    steps = [(layers["down"], x0_dev, D), (layers["cv1"], D, T), (layers["b1"], T, U), (layers["b2"], U, T, T),
-             (layers["cv2"], T, Y)]
+    if split:
+        T2 = torch.empty(n * h * h * half, dtype=tdt, device=dev())
+        steps = [(layers["down"], x0_dev, D), (layers["cv1"], D, T), (layers["b1"], T, U),
+                 (layers["b2"], U, T2, T), (layers["cv2"], T, Y, None, T2)]
+    else:
+        steps = [(layers["down"], x0_dev, D), (layers["cv1"], D, T), (layers["b1"], T, U), (layers["b2"], U, T, T),
+                 (layers["cv2"], T, Y)]
     outs = []
     if graph_replays:
         g = cbs.cbs_graph_create_steps(steps)
         for _ in range(graph_replays):
-            for b in (D, T, U, Y):
+            for b in (D, T, U, Y) + ((T2,) if split else ()):
                 b.zero_()
             cbs.cbs_graph_launch(g)
             torch.cuda.synchronize()
-            outs.append({k: v.cpu().numpy() for k, v in zip("DTUY", (D, T, U, Y))})
+            outs.append(_chain_host(D, T, U, Y, T2 if split else None, n, h, c))
         del g
     else:
         cbs.cbs_run_steps(steps)
         torch.cuda.synchronize()
-        outs.append({k: v.cpu().numpy() for k, v in zip("DTUY", (D, T, U, Y))})
+        outs.append(_chain_host(D, T, U, Y, T2 if split else None, n, h, c))
     return outs
+
+
+def _chain_host(D, T, U, Y, T2, n, h, c):
+    """Host copies; with a split concatenation T is rebuilt as the one-buffer layout."""
+    out = {k: v.cpu().numpy() for k, v in zip("DTUY", (D, T, U, Y))}
+    if T2 is not None:
+        t1 = out["T"].reshape(n, h, h, c)
+        out["T"] = np.concatenate([t1, T2.cpu().numpy().reshape(n, h, h, c // 2)], axis=-1).reshape(-1)
+    return out
 
 
 def _chain_nchw(out, n, c, h):
@@ -694,12 +719,16 @@ def _chain_nchw(out, n, c, h):
             "cv2": out["Y"].reshape(n, h, h, c).transpose(0, 3, 1, 2)}
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("c,h,n", [(32, 20, 2), (64, 40, 1)])
-def test_c3k2_block_fp32(c, h, n):
+def test_c3k2_block_fp32(c, h, n, split):
+    """The block with its concatenation in one buffer of slices, or (split) as two dense
+    tensors that cv2 reads as its two inputs."""
     specs, params, ora, x0, _ = _build_chain(c, h, n, "f32", seed=40 + c)
-    layers = _create_chain(specs, params, n, "f32", None, c)
+    layers = _create_chain(specs, params, n, "f32", None, c, split=split)
     x0_dev = torch.from_numpy(_nhwc(x0)).to(dev())
-    runs = _run_chain(layers, x0_dev, n, c, h, "f32") + _run_chain(layers, x0_dev, n, c, h, "f32", graph_replays=3)
+    runs = _run_chain(layers, x0_dev, n, c, h, "f32", split=split) + \
+        _run_chain(layers, x0_dev, n, c, h, "f32", graph_replays=3, split=split)
     for out in runs[1:]:
         assert all(np.array_equal(runs[0][k], out[k]) for k in "DTUY"), "graph replay differs from eager steps"
     got = _chain_nchw(runs[0], n, c, h)
