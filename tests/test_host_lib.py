@@ -239,6 +239,29 @@ def test_descriptor_layout_matches_header(cbs):
     assert ctypes.sizeof(cbs.cbs_conv_desc) == 4 * len(names)
 
 
+def _header_fields(struct):
+    """Field names of `typedef struct <struct> {...} <struct>;` in the header, in order."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (struct, struct), src, re.S).group(1)
+    names = []
+    for decl in body.split(";"):
+        for part in decl.split(","):
+            part = re.sub(r"\[.*?\]", "", part)  # array bounds
+            ids = re.findall(r"[A-Za-z_]\w*", part)
+            if ids:
+                names.append(ids[-1])  # the declarator follows the type
+    return names
+
+
+def test_step_and_info_layouts_match_header(cbs):
+    """The ctypes step and layer-info structures name the header's fields in its order
+    (the binding's "in_" is the header's "in") and have the C sizes."""
+    step = [f for f, _ in cbs.cbs_step._fields_]
+    assert [("in" if f == "in_" else f) for f in step] == _header_fields("cbs_step")
+    assert ctypes.sizeof(cbs.cbs_step) == 5 * ctypes.sizeof(ctypes.c_void_p)
+    assert [f for f, _ in cbs.cbs_layer_info_t._fields_] == _header_fields("cbs_layer_info_t")
+
+
 def test_tile_table_entries(cbs):
     """Every tile-table entry names an existing configuration with a split-K the
     configuration allows, keys are unique, classes are 0-4, every class 2/3
