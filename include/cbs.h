@@ -206,7 +206,8 @@ void cbs_destroy_layer(cbs_layer *layer);
 /*
  * Enqueue the fused layer on `stream`: in (device, layout above) -> out
  * (device, layout above).  in and out must not overlap.  Errors: CBS_EINVAL
- * (null layer or buffer, or a layer created with a residual), CBS_ELAUNCH.
+ * (null layer or buffer, or a layer created with a residual or a second
+ * input), CBS_ELAUNCH.
  */
 cbs_status cbs_run_layer(const cbs_layer *layer, const void *in, void *out, void *stream);
 
