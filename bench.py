@@ -261,9 +261,9 @@ class ChainBench:
     two 3x3 convs read the second half of cv1's output in place and the second
     adds it back; cv2 1x1 reads the concatenation of cv1's output and the
     bottleneck's).  FP32 at batch 16 keeps that concatenation as two dense
-    tensors, which cv2 reads as its two inputs; INT8, and FP32 at batch 1, keep
-    one 1.5c-channel buffer T that cv1 (the first c channels) and the bottleneck
-    (the last c/2) write slices of.
+    tensors in the stages of up to 64 channels, which cv2 reads as its two
+    inputs; elsewhere one 1.5c-channel buffer T holds it, which cv1 (the first c
+    channels) and the bottleneck (the last c/2) write slices of.
     Each stage's output is the next stage's input.  One step = 25 kernels, no
     cat / chunk / add kernel, replayed as one captured graph.  INT8: every
     tensor is int8 codes (scales: the calibration of the list layers'
@@ -292,12 +292,12 @@ class ChainBench:
             down, cv1, b1, b2, cv2 = gen[5 * st: 5 * st + 5]
             c, h = cv1.spec.c_out, cv1.spec.h
             half = c // 2
-            # FP32 at batch 16 keeps the concatenation as two dense tensors (cv1's
-            # output and b2's), which cv2 reads as its two inputs; INT8, and FP32 at
-            # batch 1, keep one buffer that cv1 and b2 write slices of (at batch 1
-            # the second input would hold cv2 to the weight-stationary tiles, which
-            # lose there)
-            split = not int8 and batch > 1
+            # FP32 at batch 16 keeps the concatenation of the large stages (up to 64
+            # channels) as two dense tensors (cv1's output and b2's), which cv2 reads
+            # as its two inputs; INT8, FP32 at batch 1 and the 128- and 256-channel
+            # stages keep one buffer that cv1 and b2 write slices of (a second input
+            # holds cv2 to the weight-stationary tiles, which lose there)
+            split = not int8 and batch > 1 and c <= 64
             D = torch.empty(batch * h * h * c, dtype=tdt, device=dev)
             T = torch.empty(batch * h * h * (c if split else 3 * half), dtype=tdt, device=dev)
             T2 = torch.empty(batch * h * h * half, dtype=tdt, device=dev) if split else None
