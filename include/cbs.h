@@ -434,8 +434,9 @@ int32_t cbs_num_configs(void);
  * capture.  The compiled-in tile table (an offline sweep of the same kind)
  * stays the default at create; this call replaces it for one layer.
  * *config_out / *splitk_out (may be NULL) receive the choice.  Errors:
- * CBS_EINVAL (null layer or buffer, residual mismatch, bad iters or flags),
- * CBS_ELAUNCH / CBS_EDEVICE (the layer keeps its previous configuration).
+ * CBS_EINVAL (null layer or buffer, residual mismatch, a layer created with a
+ * second input, bad iters or flags), CBS_ELAUNCH / CBS_EDEVICE (the layer
+ * keeps its previous configuration).
  */
 #define CBS_TUNE_FORCE 1
 cbs_status cbs_layer_autotune(cbs_layer *layer, const void *in, void *out, const void *residual,
