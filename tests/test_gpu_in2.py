@@ -148,3 +148,6 @@ def test_second_input_refusals():
     with pytest.raises(cbs.CbsError) as e:
         cbs.cbs_group_create([layer])
     assert e.value.status == cbs.CBS_EUNSUPPORTED
+    with pytest.raises(cbs.CbsError) as e:                     # nor does the autotuner
+        cbs.cbs_layer_autotune(layer, x, o)
+    assert e.value.status == cbs.CBS_EINVAL
