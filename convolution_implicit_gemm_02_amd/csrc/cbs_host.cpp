@@ -319,13 +319,15 @@ bool config_fits(const cbs_layer *L, int cfg, int splitk) {
   if (c.lds == 4) {  // conv_ws: 1x1 stride 1, K steps (the last one may be partial) of the compiled depths
     if (L->d.k != 1 || L->d.stride != 1 || L->d.pad != 0) return false;
     const int ks = L->steps;
-    const bool partial = L->total_chunks < 4 * ks;
+    // chunks per K step: 4 (fp32, or int8 with 16-channel chunks), 16 (int8 with 4-channel chunks)
+    const int per_step = (L->d.dtype != CBS_F32 && L->chunk_ch == 4) ? 16 : 4;
+    const bool partial = L->total_chunks < per_step * ks;
     if (partial && ks > 3) return false;  // partial last steps compiled for depths 1-3
     if (L->d.dtype == CBS_F32) {
       if (!(ks == 1 || ks == 2 || ks == 3 || ks == 4 || ks == 6 || ks == 8 || ks == 12 || ks == 16 || ks == 24))
         return false;
-    } else {  // int8 and uint8: 16-channel chunks, 64-channel K steps, depths 1-4 and 6
-      if (L->chunk_ch != 16 || !(ks == 1 || ks == 2 || ks == 3 || ks == 4 || ks == 6)) return false;
+    } else {  // int8 and uint8: 64-channel K steps, depths 1-4 and 6
+      if (!(ks == 1 || ks == 2 || ks == 3 || ks == 4 || ks == 6)) return false;
     }
     if (ks > ws_max_steps(c.cb)) return false;  // deepest K the launcher instantiates
   }

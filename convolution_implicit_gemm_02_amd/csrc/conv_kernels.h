@@ -1399,10 +1399,15 @@ __global__ __launch_bounds__(256) void conv_halo(ConvParams p) {
 // than four chunks; that step has its own offset, out of range for the lanes
 // whose chunk lies past C_in.
 //
-// int8 and uint8 activations (1x1, 16-channel chunks): a K step is 64
-// channels and one 16x16x64 MFMA; the dequantising epilogue, the raw int32
-// accumulators and the uint8 zero-point start value (the interior border class:
-// a 1x1 window without padding never leaves the image) follow the other kernels.
+// int8 and uint8 activations (1x1): a K step is 64 channels and one 16x16x64
+// MFMA; the dequantising epilogue, the raw int32 accumulators and the uint8
+// zero-point start value (the interior border class: a 1x1 window without
+// padding never leaves the image) follow the other kernels.  A lane's 16 bytes
+// of a step are 16 consecutive channels of one pixel with 16- and with
+// 4-channel chunks alike (a 1x1 layer's weights are laid out the same way for
+// both); with 4-channel chunks (a C_in that is not a multiple of 16) the pixel
+// is only 4-byte aligned, so a lane reads them as four 4-byte loads, the last
+// step's masked one by one past C_in.
 //
 // IN2 (fp32 1x1): the input channels are a concatenation of two tensors, the
 // first c1 (a multiple of 16, so every K step lies in one of them) from x and
@@ -1413,7 +1418,7 @@ template <int VAR, int CBW, int WCO, int KS, int WPX = 1, bool GATHER = false, b
           bool IN2 = false>
 __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
   using V = Var<VAR>;
-  static_assert(!V::I8 || (V::VEC == 1 && !GATHER), "int8: 16-channel chunks, 1x1 only");
+  static_assert(!V::I8 || !GATHER, "int8: 1x1 only");
   static_assert(!IN2 || (!V::I8 && !GATHER && !PARTIAL), "second input: fp32 1x1");
   constexpr int CH = V::I8 ? 16 : 4;  // channels of one lane's chunk
   using Frag = typename V::Frag;
@@ -1488,7 +1493,24 @@ __global__ __launch_bounds__(64 * WCO * WPX) void conv_ws(ConvParams p) {
       }
     }
   };
+  // 4-channel chunks: bit j says chunk 4 (4 (KS-1) + g) + j of the last K step lies inside C_in
+  unsigned last_mask = 0;
+  if constexpr (V::I8 && V::VEC == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) last_mask |= (unsigned)(4 * (4 * (KS - 1) + g) + j < p.total_chunks) << j;
+  }
   auto load_block = [&](const unsigned(&o)[NOFF], Frag(&dst)[KS]) {
+    if constexpr (V::I8 && V::VEC == 4) {
+      // chunk 4 (4s + g) + j of K step s is dword j of the lane's 16 bytes
+#pragma unroll
+      for (int s = 0; s < KS; s++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const unsigned oj = (s == KS - 1 && !((last_mask >> j) & 1u)) ? kOutOfRange : o[0];
+          dst[s][j] = (int)__builtin_amdgcn_raw_buffer_load_b32(xr, oj, s * 64 + 4 * j, 0);
+        }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < KS; s++) {
       if constexpr (IN2) {
@@ -1687,13 +1709,12 @@ static hipError_t launch_wsg(const ConvParams &p, hipStream_t stream) {
 template <int VAR, int CBW, int WCO, int WPX>
 static hipError_t launch_ws(const ConvParams &p, hipStream_t stream) {
   using V = Var<VAR>;
-  if constexpr (V::I8 && V::VEC != 1) {  // int8 and uint8: 16-channel chunks only
-    (void)p, (void)stream;
-    return hipErrorInvalidValue;
-  } else if constexpr (V::I8) {
+  if constexpr (V::I8) {
     // K steps of 64 channels: depths 1-4 and 6, a partial last step at 1-3
-    if (p.splitk != 1 || p.k != 1 || p.stride != 1 || p.pad != 0 || p.chunk_ch != 16) return hipErrorInvalidValue;
-    if (p.total_chunks < 4 * p.steps) {
+    // (4-channel chunks: a C_in that is not a multiple of 16, always partial)
+    if (p.splitk != 1 || p.k != 1 || p.stride != 1 || p.pad != 0 || p.chunk_ch != (V::VEC == 1 ? 16 : 4))
+      return hipErrorInvalidValue;
+    if (p.total_chunks < (V::VEC == 1 ? 4 : 16) * p.steps) {
       switch (p.steps) {
         case 1: return launch_ws_k<VAR, CBW, WCO, 1, WPX, false, true>(p, stream);
         case 2: return launch_ws_k<VAR, CBW, WCO, 2, WPX, false, true>(p, stream);

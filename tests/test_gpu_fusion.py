@@ -318,7 +318,8 @@ def test_int8_output_equals_quantised_fp32_output():
 
 # ------------------------------------------ f2: asymmetric uint8 ----
 
-U8_SHAPES = SHAPES + [W.LayerSpec("f", 3, 16, 34, 30, 3, 2, 1, "uniform"), spec(40, 24, 9, 13, 3, 1),
+U8_SHAPES = SHAPES + [spec(24, 16, 14, 13, 1, 1),  # a 1x1 on 4-channel chunks
+                      W.LayerSpec("f", 3, 16, 34, 30, 3, 2, 1, "uniform"), spec(40, 24, 9, 13, 3, 1),
                       spec(12, 20, 6, 5, 3, 1), spec(20, 36, 10, 9, 3, 1),  # 36: three 16-channel blocks
                       spec(8, 8, 13, 11, 3, 1), spec(16, 6, 9, 12, 3, 1)]  # column-pair tiles, both gathers
 SENT_ACC = np.int32(np.uint32(0xA5A5A5A5).view(np.int32))
@@ -441,7 +442,7 @@ def runs_on(name, sp, dtype):
     that apply to some shapes only: halo tiles need 3x3, column pairs also stride 1
     and at most 8 output channels, weight-stationary tiles 1x1 stride 1 with fp32 1-4,
     6, 8, 12, 16 or 24 K steps of 16 channels up to the tile's register budget, or int8
-    / uint8 16-channel chunks in 1-4 or 6 steps of 64 (a partial last step at 1-3 steps),
+    / uint8 in 1-4 or 6 steps of 64 channels (a partial last step at 1-3 steps),
     their gather form fp32 3x3 with C_in 16 or 32)."""
     if name.startswith("P"):
         return sp.k == 3 and sp.stride == 1 and sp.c_out <= 8
@@ -456,9 +457,10 @@ def runs_on(name, sp, dtype):
             ks = -(-cin_pad // 16)
             return (ks in (1, 2, 3, 4, 6, 8, 12, 16, 24) and ks <= {1: 24, 2: 16, 5: 8}[cb]
                     and (cin_pad % 16 == 0 or ks <= 3))
-        # int8 and uint8: 16-channel chunks (these cases' slices are 16-channel aligned)
-        ks = -(-sp.c_in // 64)
-        return sp.c_in % 16 == 0 and ks in (1, 2, 3, 4, 6) and (sp.c_in % 64 == 0 or ks <= 3)
+        # int8 and uint8: 64-channel K steps, a partial last one at 1-3 steps
+        cin_pad = -(-sp.c_in // 4) * 4
+        ks = -(-cin_pad // 64)
+        return ks in (1, 2, 3, 4, 6) and (cin_pad % 64 == 0 or ks <= 3)
     if name.startswith("G."):
         return dtype == "f32" and sp.k == 3 and sp.c_in in (16, 32)
     return True

@@ -270,13 +270,19 @@ WSG_SPECS = [(W.LayerSpec("g16", 16, 16, 21, 23, 3, 1, 1), 2), (W.LayerSpec("g16
              (W.LayerSpec("g24", 24, 16, 9, 9, 3, 1, 1), 1), (W.LayerSpec("g48", 48, 16, 9, 9, 3, 1, 1), 1)]
 
 
-# int8 1x1 shapes for the weight-stationary tiles (16-channel chunks, 64-channel K
-# steps): depths 1, 2, 4 and 6, partial last steps (16, 32, 96 input channels),
-# runs of several blocks, channel counts that leave channel blocks empty.
+# int8 1x1 shapes for the weight-stationary tiles (64-channel K steps): depths 1,
+# 2, 4 and 6, partial last steps with 16-channel chunks (16, 32, 96 input
+# channels) and with 4-channel chunks (20, 24, 72, 136; 200 has no compiled
+# partial depth), runs of several blocks, channel counts that leave channel
+# blocks empty.
 WS_I8_SPECS = [(W.LayerSpec("wq16", 16, 16, 31, 29, 1, 1, 0), 3), (W.LayerSpec("wq32", 32, 24, 17, 21, 1, 1, 0), 2),
                (W.LayerSpec("wq64c80", 64, 80, 40, 40, 1, 1, 0), 4), (W.LayerSpec("wq96", 96, 64, 9, 11, 1, 1, 0), 2),
                (W.LayerSpec("wq128", 128, 136, 11, 5, 1, 1, 0), 2), (W.LayerSpec("wq256", 256, 48, 6, 6, 1, 1, 0), 2),
-               (W.LayerSpec("wq384", 384, 20, 3, 5, 1, 1, 0), 2), (W.LayerSpec("wq64runs", 64, 32, 49, 50, 1, 1, 0), 3)]
+               (W.LayerSpec("wq384", 384, 20, 3, 5, 1, 1, 0), 2), (W.LayerSpec("wq64runs", 64, 32, 49, 50, 1, 1, 0), 3),
+               # 4-channel chunks (C_in not a multiple of 16): one, two and three partial steps
+               (W.LayerSpec("wq24", 24, 16, 29, 31, 1, 1, 0), 3), (W.LayerSpec("wq20", 20, 40, 9, 11, 1, 1, 0), 2),
+               (W.LayerSpec("wq72", 72, 24, 7, 9, 1, 1, 0), 2), (W.LayerSpec("wq136", 136, 16, 6, 5, 1, 1, 0), 2),
+               (W.LayerSpec("wq200", 200, 16, 5, 5, 1, 1, 0), 1)]
 
 
 def test_weight_stationary_tiles_i8():
@@ -303,10 +309,11 @@ def test_weight_stationary_tiles_i8():
             assert check_guards(r["host"], L, r["info"]) == 0, name
             assert np.all(r["valid"][..., spec.c_out:] == 0), name
             ran.append(r["info"]["config_name"])
-        ks = -(-spec.c_in // 64)
+        cin_pad = -(-spec.c_in // 4) * 4
+        ks = -(-cin_pad // 64)
         max_steps = {"c16": 24, "c32": 16, "c80": 8}
         want = sorted(cbs.cbs_config_name(c) + "/sk1" for c in ws
-                      if ks in (1, 2, 3, 4, 6) and (spec.c_in % 64 == 0 or ks <= 3)
+                      if ks in (1, 2, 3, 4, 6) and (cin_pad % 64 == 0 or ks <= 3)
                       and ks <= max_steps[cbs.cbs_config_name(c)[2:5]])
         assert sorted(ran) == want, (spec.name, ran, want)
 
